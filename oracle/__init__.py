@@ -1,0 +1,172 @@
+"""fp64 CPU oracle for the swizzled-operand GEMM — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package.  It shares no code with the GPU library
+(``mma_swizzled_operand_amd``) and never imports it; the GPU library never
+imports this.
+
+Contents
+--------
+``oracle.c`` (built here into ``liboracle.so`` with gcc)
+    * element decoders (fp16, bf16, OCP E4M3, OCP E8M0) from the bit fields;
+    * ``gemm``: D = beta*D0 + A.B^T with B held as (N,K), in fp64, for dense
+      and block-scaled operands, K-major or MN-major
+      (tcgen05.mma page: "Operands and repeat axes", "Shared descriptors are
+      byte-stride contracts", "Example: four K16 issues for a 128x64x64
+      product", "Weight-stationary and block scaling").
+``walk.py``
+    * brute-force enumerators of the shared-descriptor address walk
+      (tcgen05.cp page, "Shared descriptor address walk"; tcgen05.mma page,
+      "Shared descriptors are byte-stride contracts") and of the LDS tile
+      layout the GPU kernels use.
+
+Parity pins (tests/test_oracle_*.py, tests/test_walk.py, run with -m "not gpu")
+-----------------------------------------------------------------------------
+* decoders: all 65,536 fp16 and bf16 patterns against numpy / torch, all 256
+  e4m3 patterns against torch.float8_e4m3fn, e8m0 against the definition;
+* gemm: all-ones closed form (every entry is K), identity and permutation
+  operands, A = 0 with beta = 1, majors invariance, tiny shapes against exact
+  rational arithmetic, the page's quarter-integer example, block-scale closed
+  forms, numpy float64 matmul on medium shapes;
+* walk: the page's printed descriptor examples and the printed mode-4
+  permutation; modes 1..3 are pinned only through the properties the page
+  states (periods, 16-byte atoms) — "parity unpinned" beyond those.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# The oracle's own element-kind and major numbering (independent of the GPU ABI).
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4}
+MAJORS = {"k": 0, "mn": 1}
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4}
+
+_lock = threading.Lock()
+_handle = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math, no
+    FMA contraction so every product and sum is rounded as written)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _lib():
+    global _handle
+    with _lock:
+        if _handle is None:
+            build(force=False)
+            h = ctypes.CDLL(_LIB)
+            i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+            h.orc_gemm.argtypes = [i64, i64, i64,
+                                   ctypes.c_int, ctypes.c_int, vp,
+                                   ctypes.c_int, ctypes.c_int, vp,
+                                   i32, vp, vp,
+                                   ctypes.c_int, vp,
+                                   i64, vp, i64, vp,
+                                   dp, dp]
+            h.orc_gemm.restype = ctypes.c_int
+            h.orc_decode.argtypes = [ctypes.c_int, vp, i64, dp]
+            h.orc_decode.restype = ctypes.c_int
+            h.orc_set_threads.argtypes = [ctypes.c_int]
+            h.orc_set_threads.restype = None
+            h.orc_get_threads.argtypes = []
+            h.orc_get_threads.restype = ctypes.c_int
+            _handle = h
+    return _handle
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads the oracle uses (0: OpenMP default)."""
+    _lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_lib().orc_get_threads())
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _raw(a: np.ndarray, kind: str) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype.itemsize != _ITEMSIZE[kind]:
+        raise ValueError(f"stored array itemsize {a.dtype.itemsize} does not match {kind}")
+    return a
+
+
+def decode(kind: str, stored: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of every stored element (bit patterns -> reals)."""
+    s = _raw(stored, kind)
+    out = np.empty(s.shape, dtype=np.float64)
+    rc = _lib().orc_decode(DTYPES[kind], _ptr(s), s.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"orc_decode failed ({rc})")
+    return out
+
+
+def decode_e8m0(stored: np.ndarray) -> np.ndarray:
+    """Exact value 2^(E-127) of each scale byte (NaN for 255)."""
+    s = np.ascontiguousarray(stored, dtype=np.uint8)
+    e = s.astype(np.int64)
+    out = np.ldexp(1.0, e - 127)
+    out[e == 255] = np.nan
+    return out
+
+
+def gemm(M, N, K, a_kind, a_major, A, b_kind, b_major, B, *, V=0, SFA=None, SFB=None,
+         beta=0, D0=None, rows=None, cols=None, with_mag=False):
+    """Reference D[rows][cols] = beta*D0 + sum_k a(m,k) b(n,k) in fp64.
+
+    A, B are the STORED arrays (raw bit patterns: uint16 for f16/bf16, uint8
+    for e4m3) in their stated majors: A K-major [M,K] or MN-major [K,M];
+    B K-major [N,K] or MN-major [K,N].  SFA [M,K/V] and SFB [N,K/V] are e8m0
+    bytes when V > 0.  D0 is fp32 [M,N] (read only when beta == 1).
+    rows/cols select a sub-grid of outputs (None: all).
+    """
+    A = _raw(A, a_kind)
+    B = _raw(B, b_kind)
+    if A.size != M * K or B.size != N * K:
+        raise ValueError("operand sizes do not match M, N, K")
+    sfa = sfb = None
+    if V:
+        sfa = np.ascontiguousarray(SFA, dtype=np.uint8)
+        sfb = np.ascontiguousarray(SFB, dtype=np.uint8)
+        if sfa.size != M * (K // V) or sfb.size != N * (K // V):
+            raise ValueError("scale sizes do not match")
+    d0 = None
+    if beta:
+        d0 = np.ascontiguousarray(D0, dtype=np.float32)
+        if d0.size != M * N:
+            raise ValueError("D0 size does not match")
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    out = np.empty((nr, nc), dtype=np.float64)
+    mag = np.empty((nr, nc), dtype=np.float64) if with_mag else None
+    rc = _lib().orc_gemm(M, N, K, DTYPES[a_kind], MAJORS[a_major], _ptr(A),
+                         DTYPES[b_kind], MAJORS[b_major], _ptr(B),
+                         int(V), _ptr(sfa), _ptr(sfb), int(beta), _ptr(d0),
+                         nr, _ptr(r), nc, _ptr(c), _ptr(out), _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"orc_gemm rejected its arguments ({rc})")
+    return (out, mag) if with_mag else out

@@ -1,0 +1,258 @@
+/*
+ * oracle.c — TEST INFRASTRUCTURE ONLY.  A plain, slow, obviously-correct fp64
+ * reference for the swizzled-operand GEMM.  Only tests/, the smoke() entry and
+ * bench.py's cpu_baseline leg may load this library.  It shares no code, header
+ * or constant with the GPU library (mma_swizzled_operand_amd/), and the GPU
+ * library never calls it.
+ *
+ * What it computes (tcgen05.mma page, sections "Operands and repeat axes" and
+ * "Example: four K16 issues for a 128x64x64 product"): D = A . B^T with B held
+ * as (N,K), accumulated into fp32 cells; `accum` off on the first K issue
+ * means the old D is ignored, on means it is added.  Block scaling (same page,
+ * "Weight-stationary and block scaling") attaches one scale per row and per
+ * block of consecutive K elements to each operand.
+ *
+ *   a(m,k) = A[m*K + k]   (A K-major, stored [M][K])
+ *          = A[k*M + m]   (A MN-major, stored [K][M])
+ *   b(n,k) = B[n*K + k]   (B K-major, stored [N][K])
+ *          = B[k*N + n]   (B MN-major, stored [K][N])
+ *   dense:        D[m][n] = beta*D0[m][n] + sum_k a(m,k) * b(n,k)
+ *   block-scaled: D[m][n] = beta*D0[m][n]
+ *                 + sum_k (2^(SFA[m][k/V]-127) a(m,k)) * (2^(SFB[n][k/V]-127) b(n,k))
+ *
+ * Every stored element is first decoded to the exact real number its bit
+ * pattern encodes (fp64 holds every fp16, bf16, e4m3 and e8m0 value exactly),
+ * then the K products are summed in fp64 in increasing k.  The componentwise
+ * magnitude S[m][n] = sum_k |a*b| is returned beside D for error bounds.
+ *
+ * Readings taken where the pages are silent: the 8-bit element format is OCP
+ * E4M3 (bias 7, no infinities, S.1111.111 is NaN); a scale byte E means
+ * 2^(E-127) (OCP E8M0, 255 is NaN); scale blocks start at k = 0, V, 2V, ...;
+ * beta is 0 or 1 and beta = 0 never reads D0.
+ *
+ * Parity status of each function is recorded in the header of oracle/__init__.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element kinds understood by the oracle (its own numbering). */
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4 };
+/* Operand majors (its own numbering). */
+enum { ORC_KMAJOR = 0, ORC_MNMAJOR = 1 };
+/* Return codes. */
+enum { ORC_OK = 0, ORC_BAD_ARG = -1, ORC_NO_MEM = -2 };
+
+/* ---- element decoders: bit fields -> exact real value ------------------- */
+
+/* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_decode_f16(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/2^10) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits. */
+double orc_decode_bf16(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 7) & 0xff, f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* f * 2^-126 * 2^-7 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);     /* (1 + f/2^7) * 2^(e-127) */
+    return s ? -v : v;
+}
+
+/* OCP E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; no infinities,
+ * exponent 15 with fraction 7 is NaN, so the largest finite value is 448. */
+double orc_decode_e4m3(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 0xf, f = b & 0x7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);                  /* f * 2^-6 * 2^-3 */
+    else
+        v = ldexp((double)(8 + f), e - 10);        /* (1 + f/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* OCP E8M0 scale: 2^(E-127); E = 255 is NaN. */
+double orc_decode_e8m0(uint8_t b)
+{
+    return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+static int elem_size(int dt)
+{
+    switch (dt) {
+    case ORC_F16: case ORC_BF16: return 2;
+    case ORC_E4M3: return 1;
+    case ORC_F32: return 4;
+    default: return 0;
+    }
+}
+
+static double decode_one(int dt, const void *base, int64_t idx)
+{
+    switch (dt) {
+    case ORC_F16: return orc_decode_f16(((const uint16_t *)base)[idx]);
+    case ORC_BF16: return orc_decode_bf16(((const uint16_t *)base)[idx]);
+    case ORC_E4M3: return orc_decode_e4m3(((const uint8_t *)base)[idx]);
+    case ORC_F32: return (double)((const float *)base)[idx];
+    default: return NAN;
+    }
+}
+
+/* Decode n stored elements of kind dt into fp64. */
+int orc_decode(int dt, const void *src, int64_t n, double *dst)
+{
+    if (!elem_size(dt) || (n > 0 && (!src || !dst)) || n < 0)
+        return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = decode_one(dt, src, i);
+    return ORC_OK;
+}
+
+/* ---- the GEMM ------------------------------------------------------------ */
+
+static int n_threads = 0; /* 0: OpenMP default */
+
+void orc_set_threads(int n) { n_threads = n; }
+
+int orc_get_threads(void)
+{
+#ifdef _OPENMP
+    return n_threads > 0 ? n_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Operand element (row `r` of the logical [R][K] operand, column k), read
+ * through its major: K-major storage is [R][K], MN-major storage is [K][R]. */
+static double operand_at(int dt, int major, const void *X, int64_t R, int64_t K,
+                         int64_t r, int64_t k)
+{
+    int64_t idx = (major == ORC_KMAJOR) ? r * K + k : k * R + r;
+    return decode_one(dt, X, idx);
+}
+
+/*
+ * Reference D for the selected rows x selected columns of the product.
+ *   rows: n_rows indices into [0,M) or NULL for all M rows (n_rows ignored)
+ *   cols: n_cols indices into [0,N) or NULL for all N columns
+ *   V:    0 for dense; otherwise the number of consecutive K elements that
+ *         share one scale byte (SFA is [M][K/V], SFB is [N][K/V])
+ *   Dref, Smag: [n_rows][n_cols] row-major fp64 outputs (Smag may be NULL)
+ * Returns ORC_OK, ORC_BAD_ARG or ORC_NO_MEM.
+ */
+int orc_gemm(int64_t M, int64_t N, int64_t K,
+             int a_dt, int a_major, const void *A,
+             int b_dt, int b_major, const void *B,
+             int32_t V, const uint8_t *SFA, const uint8_t *SFB,
+             int beta, const float *D0,
+             int64_t n_rows, const int64_t *rows,
+             int64_t n_cols, const int64_t *cols,
+             double *Dref, double *Smag)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || !A || !B || !Dref)
+        return ORC_BAD_ARG;
+    if (a_dt == ORC_F32 || b_dt == ORC_F32 || !elem_size(a_dt) || !elem_size(b_dt))
+        return ORC_BAD_ARG;
+    if ((a_major != ORC_KMAJOR && a_major != ORC_MNMAJOR) ||
+        (b_major != ORC_KMAJOR && b_major != ORC_MNMAJOR))
+        return ORC_BAD_ARG;
+    if (V < 0 || (V > 0 && (K % V != 0 || !SFA || !SFB)))
+        return ORC_BAD_ARG;
+    if (beta != 0 && beta != 1)
+        return ORC_BAD_ARG;
+    if (beta == 1 && !D0)
+        return ORC_BAD_ARG;
+    if (!rows) n_rows = M;
+    if (!cols) n_cols = N;
+    if (n_rows < 0 || n_cols < 0)
+        return ORC_BAD_ARG;
+    for (int64_t i = 0; rows && i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return ORC_BAD_ARG;
+    for (int64_t j = 0; cols && j < n_cols; ++j)
+        if (cols[j] < 0 || cols[j] >= N) return ORC_BAD_ARG;
+    if (n_rows == 0 || n_cols == 0)
+        return ORC_OK;
+
+    /* Step 1: decode the selected operand rows into K-contiguous fp64 copies,
+     * each element multiplied by its block scale (a power of two, so exact). */
+    double *a64 = (double *)malloc((size_t)n_rows * (size_t)K * sizeof(double));
+    double *b64 = (double *)malloc((size_t)n_cols * (size_t)K * sizeof(double));
+    if (!a64 || !b64) {
+        free(a64);
+        free(b64);
+        return ORC_NO_MEM;
+    }
+    const int64_t KB = V > 0 ? K / V : 0;
+    int nt = orc_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = operand_at(a_dt, a_major, A, M, K, m, k);
+            if (V > 0)
+                v *= orc_decode_e8m0(SFA[m * KB + k / V]);
+            a64[i * K + k] = v;
+        }
+    }
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t j = 0; j < n_cols; ++j) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = operand_at(b_dt, b_major, B, N, K, n, k);
+            if (V > 0)
+                v *= orc_decode_e8m0(SFB[n * KB + k / V]);
+            b64[j * K + k] = v;
+        }
+    }
+
+    /* Step 2: every output is the fp64 sum of its K products, k increasing;
+     * then beta*D0 is added. */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        const double *ar = a64 + i * K;
+        for (int64_t j = 0; j < n_cols; ++j) {
+            int64_t n = cols ? cols[j] : j;
+            const double *br = b64 + j * K;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = ar[k] * br[k];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (beta == 1) {
+                double d0 = (double)D0[m * N + n];
+                acc += d0;
+            }
+            Dref[i * n_cols + j] = acc;
+            if (Smag)
+                Smag[i * n_cols + j] = mag;
+        }
+    }
+    free(a64);
+    free(b64);
+    return ORC_OK;
+}

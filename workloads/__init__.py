@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for the swizzled-operand GEMM.
+
+This module is shared by the tests, the benchmark and the oracle side.  It
+holds no GEMM arithmetic: it only draws random numbers and rounds them into
+the stored element formats with numpy / torch conversions.
+
+Every config is described by its stored layouts (row-major, contiguous):
+    A: K-major [M,K] or MN-major [K,M];  B: K-major [N,K] or MN-major [K,N];
+    D0: fp32 [M,N] (beta = 1 only);  SFA [M,K/32], SFB [N,K/32] e8m0 bytes.
+
+Recipe (identical for every config): ``numpy.random.default_rng(seed)``,
+draws in the order A, B, D0, SFA, SFB, each in the C order of its stored
+layout; fp64 samples are rounded to nearest-even into the storage type
+(fp16 by numpy; bf16 and e4m3 through an fp32 intermediate by torch);
+e8m0 scale bytes are 127 + u with u a uniform integer in [-4, 4].
+The quarter-integer variant (the tcgen05.mma page's example test draws
+integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
+recipe and sets every scale byte to 127, so every product and partial sum is
+exact in fp32.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+#: Stored element kinds, named as in the oracle and the binding.
+KINDS = ("f16", "bf16", "e4m3")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    title: str
+    M: int
+    N: int
+    K: int
+    kind: str                 # operand element kind for A and B
+    a_major: str = "k"        # "k" or "mn"
+    b_major: str = "k"
+    beta: int = 0
+    V: int = 0                # 0 dense, 32 MX block-scaled
+    a_dist: tuple = ("uniform", 1.0)   # ("uniform", half-width) or ("normal", sigma)
+    b_dist: tuple = ("uniform", 1.0)
+    tags: tuple = field(default=())
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self) -> int:
+        """Minimal HBM traffic of one call: A + B (+ scales) + D write
+        (+ D read when beta = 1)."""
+        es = 1 if self.kind == "e4m3" else 2
+        b = (self.M + self.N) * self.K * es + self.M * self.N * 4
+        if self.V:
+            b += (self.M + self.N) * (self.K // self.V)
+        if self.beta:
+            b += self.M * self.N * 4
+        return b
+
+
+WORKLOADS = {
+    "c1": Workload("c1", "single tile: D[128,256] fp32 = A[128,64] fp16 . B[256,64]^T, K-major, U[-1,1)",
+                   128, 256, 64, "f16", tags=("oracle-full",)),
+    "c2": Workload("c2", "square dense 4096^3 bf16, A and B K-major, N(0,1)",
+                   4096, 4096, 4096, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c3": Workload("c3", "8192^3 fp16, A MN-major [K,M], B K-major [N,K], U[-1,1), beta=1 onto seeded D0",
+                   8192, 8192, 8192, "f16", a_major="mn", beta=1),
+    "c4": Workload("c4", "skinny weight-streaming M=64 N=16384 K=8192 bf16, A N(0,1), B N(0,0.02)",
+                   64, 16384, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02)),
+    "c5": Workload("c5", "MX-fp8 8192^3 e4m3 K-major, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                   8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
+                    8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+}
+
+
+def custom(M, N, K, kind, a_major="k", b_major="k", beta=0, V=0,
+           a_dist=("uniform", 1.0), b_dist=("uniform", 1.0), name="custom") -> Workload:
+    return Workload(name, f"{name} {M}x{N}x{K} {kind} A:{a_major} B:{b_major} beta={beta} V={V}",
+                    M, N, K, kind, a_major, b_major, beta, V, a_dist, b_dist)
+
+
+def scaled(w: Workload, M=None, N=None, K=None, name=None) -> Workload:
+    """Same recipe at another size (for parity cases the oracle finishes fast)."""
+    return replace(w, M=M or w.M, N=N or w.N, K=K or w.K, name=name or (w.name + "-small"))
+
+
+# ---- rounding of fp64 samples into stored formats (library conversions) -------
+
+def to_stored(x: np.ndarray, kind: str) -> np.ndarray:
+    """Round fp64 values into the stored bit patterns of ``kind``."""
+    if kind == "f16":
+        return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if kind == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if kind == "e4m3":
+        if np.abs(x).max(initial=0.0) > 448.0:
+            raise ValueError("value outside the e4m3 range")
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    raise ValueError(kind)
+
+
+def _draw(rng, dist, size):
+    kind, p = dist
+    if kind == "uniform":
+        return rng.uniform(-p, p, size)
+    if kind == "normal":
+        return rng.normal(0.0, p, size)
+    raise ValueError(kind)
+
+
+def _quarter(rng, size):
+    return rng.integers(-4, 5, size) / 4.0
+
+
+def stored_shapes(w: Workload) -> dict:
+    s = {
+        "A": (w.M, w.K) if w.a_major == "k" else (w.K, w.M),
+        "B": (w.N, w.K) if w.b_major == "k" else (w.K, w.N),
+    }
+    if w.beta:
+        s["D0"] = (w.M, w.N)
+    if w.V:
+        s["SFA"] = (w.M, w.K // w.V)
+        s["SFB"] = (w.N, w.K // w.V)
+    return s
+
+
+def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
+    """Stored inputs of workload ``w`` (numpy arrays, raw bit patterns).
+
+    values = "config": the config's distributions; "quarter": quarter-integer
+    operands in [-1, 1] with unit scales (exact in fp32 in any summation order).
+    """
+    if values not in ("config", "quarter"):
+        raise ValueError(values)
+    rng = np.random.default_rng(seed)
+    shapes = stored_shapes(w)
+    out = {}
+    for name, dist in (("A", w.a_dist), ("B", w.b_dist)):
+        x = _quarter(rng, shapes[name]) if values == "quarter" else _draw(rng, dist, shapes[name])
+        out[name] = to_stored(x, w.kind)
+    if w.beta:
+        out["D0"] = rng.uniform(-1.0, 1.0, shapes["D0"]).astype(np.float32)
+    if w.V:
+        for name in ("SFA", "SFB"):
+            u = rng.integers(-4, 5, shapes[name])
+            if values == "quarter":
+                u = np.zeros_like(u)
+            out[name] = (127 + u).astype(np.uint8)
+    return out
+
+
+def digest(inputs: dict) -> str:
+    """sha256 over the stored bytes, in key order (reproducibility check)."""
+    h = hashlib.sha256()
+    for k in sorted(inputs):
+        h.update(k.encode())
+        h.update(np.ascontiguousarray(inputs[k]).tobytes())
+    return h.hexdigest()
+
+
+def sample_points(w: Workload, n_rows: int = 8, n_cols: int = 8, seed: int = 1):
+    """Rows and columns whose full cross product is checked at full size.
+
+    Always includes the first and last row/column and rows/columns at every
+    position a 32x32 sub-tile and a 256x256 tile can take modulo their size,
+    then random others."""
+    rng = np.random.default_rng(seed)
+
+    def pick(n, total):
+        base = {0, total - 1}
+        for off in (31, 32, 127, 128, 255):
+            if off < total:
+                base.add(off)
+        while len(base) < min(n, total):
+            base.add(int(rng.integers(0, total)))
+        return np.array(sorted(base), dtype=np.int64)
+
+    return pick(n_rows, w.M), pick(n_cols, w.N)
