@@ -1,0 +1,144 @@
+/*
+ * mswz_gemm.h — C ABI of the swizzled-operand GEMM library for AMD Instinct
+ * MI355X (gfx950), libmswz.so.
+ *
+ * The operation (tcgen05.mma page, "Operands and repeat axes", "Shared
+ * descriptors are byte-stride contracts" and "Example: four K16 issues for a
+ * 128x64x64 product"):
+ *
+ *     D[m][n] = beta * D[m][n] + sum_k a(m,k) * b(n,k)          (dense)
+ *
+ * i.e. D = A . B^T with B held as (N,K), fp32 accumulation and output.  `beta`
+ * is the page's `accum` flag: 0 overwrites D (its old contents are never read,
+ * so NaNs in it do not propagate), 1 accumulates onto it.  Block-scaled
+ * operands (same page, "Weight-stationary and block scaling") attach one
+ * scale byte per row and per `scale_vec_len` consecutive K elements:
+ *
+ *     D[m][n] = beta * D[m][n]
+ *             + sum_k (2^(SFA[m][k/V]-127) a(m,k)) * (2^(SFB[n][k/V]-127) b(n,k))
+ *
+ * Storage (all tensors contiguous, row-major, device memory):
+ *     A  K-major: [M][K]      A  MN-major: [K][M]     ("K-major rows enumerate
+ *     B  K-major: [N][K]      B  MN-major: [K][N]      M/N, MN-major rows K")
+ *     D  fp32 [M][N]
+ *     SFA uint8 [M][K/V], SFB uint8 [N][K/V]: OCP E8M0 exponents, value 2^(E-127)
+ * Element formats: fp16 (IEEE binary16), bf16, fp8 = OCP E4M3 (bias 7, no
+ * infinities).  Results are fp32 sums of exact products; the summation order
+ * is fixed per plan, so a plan gives bit-identical results run to run.
+ *
+ * Ownership: the caller owns every device buffer and the stream.  A plan holds
+ * host metadata only and is immutable once created, so one plan may be used
+ * from several host threads and streams at once.  gemm_run* enqueue one kernel
+ * on `stream` and return; they allocate nothing, do not synchronise and keep
+ * no pointer.  Buffers must stay alive until the stream has passed the kernel
+ * (the pages' rule of keeping allocations alive until consumers complete).
+ * Scales are prepared by the caller in the layout above; supplying them does
+ * not change the plan.
+ *
+ * Errors: every call returns an int status (MSWZ_OK or a negative code);
+ * nothing is printed and there is no fallback path.  Layout requirements are
+ * checked against the explicit arguments and nothing is inferred: shapes the
+ * plan cannot tile, unsupported dtype or major combinations, misaligned or
+ * null pointers and beta outside {0,1} are rejected before any GPU work.
+ */
+#ifndef MSWZ_GEMM_H
+#define MSWZ_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSWZ_OK = 0,
+    MSWZ_ERR_INVALID = -1,      /* bad argument: size <= 0, null pointer, beta not 0/1, bad enum */
+    MSWZ_ERR_UNSUPPORTED = -2,  /* valid request this library has no kernel for (shape not a tile multiple, dtype/major combination) */
+    MSWZ_ERR_ALIGN = -3,        /* pointer not 16-byte aligned */
+    MSWZ_ERR_HIP = -4,          /* the HIP runtime reported an error on launch */
+    MSWZ_ERR_KIND = -5          /* dense plan passed to gemm_run_blockscaled or the reverse */
+} mswz_status;
+
+typedef enum {
+    MSWZ_DT_F16 = 1,
+    MSWZ_DT_BF16 = 2,
+    MSWZ_DT_E4M3 = 3,
+    MSWZ_DT_F32 = 4
+} mswz_dtype;
+
+typedef enum {
+    MSWZ_MAJOR_K = 0,
+    MSWZ_MAJOR_MN = 1
+} mswz_major;
+
+typedef struct gemm_plan gemm_plan;
+
+/*
+ * Create a plan for one problem shape.
+ *   out           receives the plan (set to NULL on failure)
+ *   M, N, K       problem sizes, each > 0
+ *   a_dt, b_dt    operand element formats; d_dt must be MSWZ_DT_F32.
+ *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) block-scaled.
+ *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (16-bit formats only for MN)
+ *   b_major       MSWZ_MAJOR_K
+ *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3
+ * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3); M and N multiples
+ * of 64 (M % 256 and N % 256 select the large square tile).
+ * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
+ */
+int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,
+                     int a_dt, int b_dt, int d_dt, int a_major, int b_major,
+                     int32_t scale_vec_len);
+
+/*
+ * Enqueue D = beta*D + A.B^T for a dense plan on `stream` (a hipStream_t;
+ * NULL is the default stream).  A, B, D are device pointers, 16-byte aligned.
+ * Returns MSWZ_OK, MSWZ_ERR_INVALID, MSWZ_ERR_ALIGN, MSWZ_ERR_KIND or
+ * MSWZ_ERR_HIP.
+ */
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *D,
+             int beta, void *stream);
+
+/*
+ * Enqueue the block-scaled product for a plan created with scale_vec_len > 0.
+ * SFA [M][K/V] and SFB [N][K/V] are device pointers to E8M0 bytes, 16-byte
+ * aligned.  Same returns as gemm_run.
+ */
+int gemm_run_blockscaled(const gemm_plan *plan, const void *A, const void *B,
+                         const uint8_t *SFA, const uint8_t *SFB, void *D,
+                         int beta, void *stream);
+
+/* Release a plan (NULL is allowed). */
+void gemm_plan_destroy(gemm_plan *plan);
+
+/* Static description of a status code (never NULL). */
+const char *gemm_status_str(int status);
+
+/*
+ * Launch geometry a plan chose, for reporting: fills up to `n` of
+ * {variant, tile_m, tile_n, tile_k, threads_per_block, blocks, lds_bytes,
+ *  group_m} and returns how many it wrote, or a negative status.
+ */
+int gemm_plan_describe(const gemm_plan *plan, int64_t *info, int n);
+
+/*
+ * Address functions the kernels use, exported for host-side checking (no GPU
+ * work).  mswz_desc_address is the pages' shared-descriptor walk (tcgen05.cp
+ * page, "Shared descriptor address walk"; tcgen05.mma page, "Shared
+ * descriptors are byte-stride contracts"): the physical byte address of
+ * 32-bit word w of row r for (ldo, sdo, swizzle mode 0..4, major, origin).
+ * mswz_desc_check returns 0 when (ldo, sdo, mode, origin) satisfy the pages'
+ * descriptor rules, else the number of the first rule broken.
+ * mswz_tile_offset is the byte offset of 16-byte chunk `chunk` (0..7) of row
+ * `row` in the kernels' LDS operand tile (128-byte rows).
+ */
+int64_t mswz_desc_address(int64_t r, int64_t w, int64_t ldo, int64_t sdo,
+                          int mode, int major, int64_t origin);
+int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin);
+uint32_t mswz_tile_offset(uint32_t row, uint32_t chunk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSWZ_GEMM_H */

@@ -1,0 +1,236 @@
+"""Python binding of libmswz.so — the swizzled-operand GEMM for MI355X (gfx950).
+
+A thin ctypes layer over the C ABI in include/mswz_gemm.h, with the same
+names.  It only marshals arguments: every step of the computation runs in the
+HIP kernels of libmswz.so.  PyTorch supplies device memory and the stream;
+tensors are checked against the plan's sizes so that a kernel never indexes
+outside the buffers it is given.  There is no fallback path: if the library
+is missing and cannot be built, importing this package fails.
+
+    plan = gemm_plan_create(M, N, K, "bf16", "bf16", "f32", "k", "k", 0)
+    gemm_run(plan, A, B, D, beta=0)            # D = beta*D + A.B^T
+    gemm_run_blockscaled(plan, A, B, SFA, SFB, D, beta=0)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import _build
+
+__all__ = [
+    "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_run",
+    "gemm_run_blockscaled", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
+    "desc_address", "desc_check", "tile_offset", "library_path", "load",
+]
+
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4}
+MAJORS = {"k": 0, "mn": 1}
+STATUS = {"ok": 0, "invalid": -1, "unsupported": -2, "align": -3, "hip": -4, "kind": -5}
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4}
+_DESCRIBE_KEYS = ("variant", "tile_m", "tile_n", "tile_k", "threads", "blocks", "lds_bytes", "group_m")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MswzError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        msg = gemm_status_str(code)
+        super().__init__(f"{what}: {msg} ({code})" if what else f"{msg} ({code})")
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load libmswz.so, building it first only if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        h = ctypes.CDLL(_build.LIB)
+        i64, i32, vp, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+        h.gemm_plan_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, c_int, c_int, c_int,
+                                       c_int, c_int, i32]
+        h.gemm_plan_create.restype = c_int
+        h.gemm_run.argtypes = [vp, vp, vp, vp, c_int, vp]
+        h.gemm_run.restype = c_int
+        h.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, c_int, vp]
+        h.gemm_run_blockscaled.restype = c_int
+        h.gemm_plan_destroy.argtypes = [vp]
+        h.gemm_plan_destroy.restype = None
+        h.gemm_status_str.argtypes = [c_int]
+        h.gemm_status_str.restype = ctypes.c_char_p
+        h.gemm_plan_describe.argtypes = [vp, ctypes.POINTER(i64), c_int]
+        h.gemm_plan_describe.restype = c_int
+        h.mswz_desc_address.argtypes = [i64, i64, i64, i64, c_int, c_int, i64]
+        h.mswz_desc_address.restype = i64
+        h.mswz_desc_check.argtypes = [i64, i64, c_int, i64]
+        h.mswz_desc_check.restype = c_int
+        h.mswz_tile_offset.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+        h.mswz_tile_offset.restype = ctypes.c_uint32
+        _lib = h
+        return _lib
+
+
+def gemm_status_str(code: int) -> str:
+    return load().gemm_status_str(int(code)).decode()
+
+
+def _code(x, table, what):
+    if isinstance(x, str):
+        if x not in table:
+            raise ValueError(f"unknown {what} {x!r}")
+        return table[x]
+    return int(x)
+
+
+class Plan:
+    """An immutable problem description; owns the C plan handle."""
+
+    def __init__(self, M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", scale_vec_len=0):
+        lib = load()
+        h = ctypes.c_void_p()
+        self.M, self.N, self.K = int(M), int(N), int(K)
+        self.a_dt = a_dt if isinstance(a_dt, str) else _name(DTYPES, a_dt)
+        self.b_dt = b_dt if isinstance(b_dt, str) else _name(DTYPES, b_dt)
+        self.d_dt = d_dt if isinstance(d_dt, str) else _name(DTYPES, d_dt)
+        self.a_major = a_major if isinstance(a_major, str) else _name(MAJORS, a_major)
+        self.b_major = b_major if isinstance(b_major, str) else _name(MAJORS, b_major)
+        self.scale_vec_len = int(scale_vec_len)
+        rc = lib.gemm_plan_create(ctypes.byref(h), self.M, self.N, self.K,
+                                  _code(a_dt, DTYPES, "dtype"), _code(b_dt, DTYPES, "dtype"),
+                                  _code(d_dt, DTYPES, "dtype"), _code(a_major, MAJORS, "major"),
+                                  _code(b_major, MAJORS, "major"), self.scale_vec_len)
+        if rc != 0:
+            self._h = None
+            raise MswzError(rc, "gemm_plan_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan has been destroyed")
+        return self._h
+
+    def describe(self) -> dict:
+        buf = (ctypes.c_int64 * len(_DESCRIBE_KEYS))()
+        n = load().gemm_plan_describe(self.handle, buf, len(_DESCRIBE_KEYS))
+        if n < 0:
+            raise MswzError(n, "gemm_plan_describe")
+        return {k: int(buf[i]) for i, k in enumerate(_DESCRIBE_KEYS[:n])}
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            load().gemm_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    # expected storage sizes in bytes
+    def a_bytes(self):
+        return self.M * self.K * _ITEMSIZE[self.a_dt]
+
+    def b_bytes(self):
+        return self.N * self.K * _ITEMSIZE[self.b_dt]
+
+    def d_bytes(self):
+        return self.M * self.N * 4
+
+    def sf_bytes(self):
+        v = self.scale_vec_len
+        return (self.M * (self.K // v), self.N * (self.K // v)) if v else (0, 0)
+
+
+def _name(table, code):
+    for k, v in table.items():
+        if v == code:
+            return k
+    return str(code)
+
+
+def gemm_plan_create(M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", scale_vec_len=0) -> Plan:
+    return Plan(M, N, K, a_dt, b_dt, d_dt, a_major, b_major, scale_vec_len)
+
+
+def gemm_plan_destroy(plan: Plan) -> None:
+    plan.destroy()
+
+
+def gemm_plan_describe(plan: Plan) -> dict:
+    return plan.describe()
+
+
+def _dev_ptr(t, nbytes: int, name: str):
+    """Device pointer of a tensor (or an int address) after checking that the
+    tensor is a contiguous CUDA/HIP tensor holding exactly ``nbytes``."""
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or an int device address")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    got = t.numel() * t.element_size()
+    if got != nbytes:
+        raise ValueError(f"{name}: holds {got} bytes, the plan needs {nbytes}")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_run(plan: Plan, A, B, D, beta: int = 0, stream=None) -> None:
+    """Enqueue D = beta*D + A.B^T on ``stream`` (default: torch's current stream)."""
+    a = _dev_ptr(A, plan.a_bytes(), "A")
+    b = _dev_ptr(B, plan.b_bytes(), "B")
+    d = _dev_ptr(D, plan.d_bytes(), "D")
+    rc = load().gemm_run(plan.handle, a, b, d, int(beta), _stream_ptr(stream))
+    if rc != 0:
+        raise MswzError(rc, "gemm_run")
+
+
+def gemm_run_blockscaled(plan: Plan, A, B, SFA, SFB, D, beta: int = 0, stream=None) -> None:
+    """Enqueue the block-scaled product on ``stream``."""
+    sfa_b, sfb_b = plan.sf_bytes()
+    a = _dev_ptr(A, plan.a_bytes(), "A")
+    b = _dev_ptr(B, plan.b_bytes(), "B")
+    sa = _dev_ptr(SFA, sfa_b, "SFA")
+    sb = _dev_ptr(SFB, sfb_b, "SFB")
+    d = _dev_ptr(D, plan.d_bytes(), "D")
+    rc = load().gemm_run_blockscaled(plan.handle, a, b, sa, sb, d, int(beta), _stream_ptr(stream))
+    if rc != 0:
+        raise MswzError(rc, "gemm_run_blockscaled")
+
+
+def desc_address(r, w, ldo, sdo, mode, major="k", origin=0) -> int:
+    """The library's shared-descriptor walk (physical byte address of word w of row r)."""
+    return int(load().mswz_desc_address(int(r), int(w), int(ldo), int(sdo), int(mode),
+                                        _code(major, MAJORS, "major"), int(origin)))
+
+
+def desc_check(ldo, sdo, mode, origin=0) -> int:
+    return int(load().mswz_desc_check(int(ldo), int(sdo), int(mode), int(origin)))
+
+
+def tile_offset(row, chunk) -> int:
+    """Byte offset of 16-byte chunk ``chunk`` of row ``row`` in the kernels' LDS tile."""
+    return int(load().mswz_tile_offset(int(row), int(chunk)))

@@ -1,0 +1,216 @@
+// abi.hip — the C ABI of libmswz.so (declared in include/mswz_gemm.h):
+// plan creation and validation, argument checks, and kernel dispatch.
+//
+// The checks follow the pages' contract style: layouts and shapes are checked
+// against explicit arguments, nothing is inferred, and whatever the library
+// cannot run is rejected with a status before any GPU work (tcgen05.mma page,
+// "Shared descriptors are byte-stride contracts"; ldmatrix / stmatrix page,
+// "Transpose and stores": misaligned rows and partial participation are
+// rejected).  Pointers must be 16-byte aligned, the pages' origin and row rule.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <stdlib.h>
+
+#include <new>
+
+#include "../../include/mswz_gemm.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+struct gemm_plan {
+    int64_t M, N, K;
+    int a_dt, b_dt, d_dt, a_major, b_major;
+    int32_t scale_vec_len;
+    int variant;
+    int group_m;
+    mswz::VariantInfo info;
+    int64_t blocks;
+};
+
+namespace mswz {
+
+bool variant_info(int variant, bool one_byte_elems, VariantInfo *info)
+{
+    const int tk = one_byte_elems ? 128 : 64;
+    int t = 0;
+    switch (variant) {
+    case kVarDense256: case kVarMx256: t = 256; break;
+    case kVarDense128: case kVarMx128: t = 128; break;
+    case kVarDense64: case kVarMx64: t = 64; break;
+    default: return false;
+    }
+    info->tile_m = t;
+    info->tile_n = t;
+    info->tile_k = tk;
+    info->threads = 256;
+    info->lds_bytes = 2 * (t + t) * 128;
+    return true;
+}
+
+}  // namespace mswz
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+
+bool is_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Choose the tile for an (M, N) output: the largest square tile dividing both
+// sizes, dropping to a smaller one while the grid would leave most compute
+// units idle (fewer than 128 tiles of 256 or 256 tiles of 128).  The
+// environment variable MSWZ_TILE (64, 128 or 256) overrides the choice when
+// that tile divides both sizes; it exists for tuning and tests.
+int pick_tile(int64_t M, int64_t N)
+{
+    if (const char *env = getenv("MSWZ_TILE")) {
+        const int t = atoi(env);
+        if ((t == 64 || t == 128 || t == 256) && M % t == 0 && N % t == 0)
+            return t;
+    }
+    auto tiles = [&](int t) { return (M / t) * (N / t); };
+    if (M % 256 == 0 && N % 256 == 0 && tiles(256) >= 128)
+        return 256;
+    if (M % 128 == 0 && N % 128 == 0 && (tiles(128) >= 128 || M % 64 || N % 64))
+        return 128;
+    if (M % 64 == 0 && N % 64 == 0)
+        return 64;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt, int b_dt,
+                     int d_dt, int a_major, int b_major, int32_t scale_vec_len)
+{
+    if (!out)
+        return MSWZ_ERR_INVALID;
+    *out = nullptr;
+    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return MSWZ_ERR_INVALID;
+    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_F32; };
+    if (!known_dt(a_dt) || !known_dt(b_dt) || !known_dt(d_dt))
+        return MSWZ_ERR_INVALID;
+    if ((a_major != MSWZ_MAJOR_K && a_major != MSWZ_MAJOR_MN) ||
+        (b_major != MSWZ_MAJOR_K && b_major != MSWZ_MAJOR_MN))
+        return MSWZ_ERR_INVALID;
+    if (scale_vec_len < 0)
+        return MSWZ_ERR_INVALID;
+    if (d_dt != MSWZ_DT_F32 || a_dt != b_dt || a_dt == MSWZ_DT_F32)
+        return MSWZ_ERR_UNSUPPORTED;
+    const bool fp8 = a_dt == MSWZ_DT_E4M3;
+    if (fp8 != (scale_vec_len != 0))
+        return MSWZ_ERR_UNSUPPORTED;     // E4M3 is block-scaled only; 16-bit is dense only
+    if (fp8 && scale_vec_len != 32)
+        return MSWZ_ERR_UNSUPPORTED;
+    if (b_major != MSWZ_MAJOR_K || (fp8 && a_major != MSWZ_MAJOR_K))
+        return MSWZ_ERR_UNSUPPORTED;
+    if (K % (fp8 ? 128 : 64) != 0)
+        return MSWZ_ERR_UNSUPPORTED;
+    const int tile = pick_tile(M, N);
+    if (!tile)
+        return MSWZ_ERR_UNSUPPORTED;
+
+    gemm_plan *p = new (std::nothrow) gemm_plan{};
+    if (!p)
+        return MSWZ_ERR_INVALID;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->a_dt = a_dt;
+    p->b_dt = b_dt;
+    p->d_dt = d_dt;
+    p->a_major = a_major;
+    p->b_major = b_major;
+    p->scale_vec_len = scale_vec_len;
+    if (fp8)
+        p->variant = tile == 256 ? mswz::kVarMx256 : tile == 128 ? mswz::kVarMx128 : mswz::kVarMx64;
+    else
+        p->variant = tile == 256 ? mswz::kVarDense256 : tile == 128 ? mswz::kVarDense128
+                                                                     : mswz::kVarDense64;
+    p->group_m = 4;
+    mswz::variant_info(p->variant, fp8, &p->info);
+    p->blocks = (M / p->info.tile_m) * (N / p->info.tile_n);
+    *out = p;
+    return MSWZ_OK;
+}
+
+int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta, void *stream)
+{
+    if (!p || !A || !B || !D)
+        return MSWZ_ERR_INVALID;
+    if (p->scale_vec_len != 0)
+        return MSWZ_ERR_KIND;
+    if (beta != 0 && beta != 1)
+        return MSWZ_ERR_INVALID;
+    if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D))
+        return MSWZ_ERR_ALIGN;
+    mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
+                      p->group_m};
+    hipError_t e = mswz::launch_dense(p->variant, p->a_dt == MSWZ_DT_BF16,
+                                      p->a_major == MSWZ_MAJOR_MN, a,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
+}
+
+int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const uint8_t *SFA,
+                         const uint8_t *SFB, void *D, int beta, void *stream)
+{
+    if (!p || !A || !B || !SFA || !SFB || !D)
+        return MSWZ_ERR_INVALID;
+    if (p->scale_vec_len == 0)
+        return MSWZ_ERR_KIND;
+    if (beta != 0 && beta != 1)
+        return MSWZ_ERR_INVALID;
+    if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D) || !is_aligned16(SFA) ||
+        !is_aligned16(SFB))
+        return MSWZ_ERR_ALIGN;
+    mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
+                   p->group_m};
+    hipError_t e = mswz::launch_mx(p->variant, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
+}
+
+void gemm_plan_destroy(gemm_plan *p) { delete p; }
+
+const char *gemm_status_str(int status)
+{
+    switch (status) {
+    case MSWZ_OK: return "ok";
+    case MSWZ_ERR_INVALID: return "invalid argument (size, null pointer, beta or enum value)";
+    case MSWZ_ERR_UNSUPPORTED: return "unsupported: no kernel for this dtype/major combination or shape";
+    case MSWZ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MSWZ_ERR_HIP: return "HIP runtime error on launch";
+    case MSWZ_ERR_KIND: return "plan kind does not match the run function (dense vs block-scaled)";
+    default: return "unknown status";
+    }
+}
+
+int gemm_plan_describe(const gemm_plan *p, int64_t *info, int n)
+{
+    if (!p || (!info && n > 0) || n < 0)
+        return MSWZ_ERR_INVALID;
+    const int64_t v[8] = {p->variant,      p->info.tile_m, p->info.tile_n,    p->info.tile_k,
+                          p->info.threads, p->blocks,      p->info.lds_bytes, p->group_m};
+    const int w = n < 8 ? n : 8;
+    for (int i = 0; i < w; ++i)
+        info[i] = v[i];
+    return w;
+}
+
+int64_t mswz_desc_address(int64_t r, int64_t w, int64_t ldo, int64_t sdo, int mode, int major,
+                          int64_t origin)
+{
+    return mswz::desc_address(r, w, ldo, sdo, mode, major, origin);
+}
+
+int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin)
+{
+    return mswz::desc_check(ldo, sdo, mode, origin);
+}
+
+uint32_t mswz_tile_offset(uint32_t row, uint32_t chunk) { return mswz::tile_offset(row, chunk); }
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// device_common.hpp — vector types, MFMA wrappers and the workgroup -> tile
+// mapping shared by the gfx950 GEMM kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace mswz {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x16 MFMA on 16-bit operands, fp32 accumulate.  Operand lane l holds
+// 8 consecutive K elements of row l % 32 (K half l / 32); both operands use
+// the same lane -> K assignment, so any K order inside the instruction gives
+// the same sum of products.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Block-scaled 32x32x64 MFMA on OCP E4M3 operands (format code 0 for both).
+// Lane l holds 32 consecutive K elements (one 32-element scale block) of row
+// l % 32; its scale byte is byte SEL of the 32-bit scale operand.
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_scale_32x32x64_e4m3(i32x8 a, i32x8 b, f32x16 c,
+                                                          int scale_a, int scale_b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, scale_a, SEL, scale_b);
+}
+
+// Workgroup -> output tile.  The hardware hands consecutive workgroups to the
+// eight XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has its own
+// L2.  Tile ids are therefore re-ordered so that each XCD receives one
+// contiguous run of ids, and ids are rastered in groups of `group_m` tile rows
+// (column by column inside a group) so that the workgroups resident on one XCD
+// at the same time share a few A row panels and B column panels.
+__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int group_m,
+                                              int &tm, int &tn)
+{
+    const int T = tiles_m * tiles_n;
+    int t = b;
+    if ((T & 7) == 0)
+        t = (b & 7) * (T >> 3) + (b >> 3);
+    const int per_group = group_m * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+// 16-byte LDS read / write.
+__device__ __forceinline__ u32x4 lds_read16(const uint8_t *lds, uint32_t off)
+{
+    return *reinterpret_cast<const u32x4 *>(lds + off);
+}
+__device__ __forceinline__ void lds_write16(uint8_t *lds, uint32_t off, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(lds + off) = v;
+}
+__device__ __forceinline__ u32x4 global_read16(const uint8_t *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Transpose an 8x8 block of 16-bit values held as eight 16-byte rows:
+// out[i] element j = in[j] element i.
+__device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = in[2 * p][i >> 1];
+            const uint32_t hi = in[2 * p + 1][i >> 1];
+            out[i][p] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                : ((lo & 0xffffu) | (hi << 16));
+        }
+    }
+}
+
+}  // namespace mswz

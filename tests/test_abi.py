@@ -1,0 +1,177 @@
+"""C ABI checks that need no GPU (CPU only).
+
+* libmswz.so loads and exports every function include/mswz_gemm.h declares;
+* every rejection gemm_plan_create / gemm_run / gemm_run_blockscaled document
+  happens on the host, before any GPU work (fake, never-dereferenced pointer
+  values are enough to reach them);
+* the library's address functions — the pages' descriptor walk and the
+  kernels' LDS tile layout — equal the oracle's brute-force enumerations bit
+  for bit (tcgen05.cp page, "Shared descriptor address walk"; tcgen05.mma
+  page, "Shared descriptors are byte-stride contracts").
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mma_swizzled_operand_amd as mswz
+from oracle import walk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mswz_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for required in ("gemm_plan_create", "gemm_run", "gemm_run_blockscaled", "gemm_plan_destroy",
+                     "gemm_status_str", "gemm_plan_describe", "mswz_desc_address",
+                     "mswz_desc_check", "mswz_tile_offset"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mswz.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = mswz.gemm_status_str(code)
+        assert s and s != "unknown status"
+    assert mswz.gemm_status_str(7) == "unknown status"
+
+
+# ---- plan creation ------------------------------------------------------------
+
+def _create(*args):
+    lib = mswz.load()
+    h = ctypes.c_void_p()
+    rc = lib.gemm_plan_create(ctypes.byref(h), *args)
+    if rc == 0:
+        lib.gemm_plan_destroy(h)
+    return rc
+
+
+F16, BF16, E4M3, F32 = 1, 2, 3, 4
+K_, MN = 0, 1
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((256, 256, 64, F16, F16, F32, K_, K_, 0), 0),
+    ((256, 256, 64, BF16, BF16, F32, MN, K_, 0), 0),
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 32), 0),
+    ((0, 256, 64, F16, F16, F32, K_, K_, 0), -1),            # empty M
+    ((256, -1, 64, F16, F16, F32, K_, K_, 0), -1),
+    ((256, 256, 0, F16, F16, F32, K_, K_, 0), -1),           # empty K
+    ((256, 256, 64, 9, F16, F32, K_, K_, 0), -1),            # unknown dtype
+    ((256, 256, 64, F16, F16, F32, 2, K_, 0), -1),           # unknown major
+    ((256, 256, 64, F16, F16, F32, K_, K_, -32), -1),
+    ((256, 256, 64, F16, BF16, F32, K_, K_, 0), -2),         # mixed 16-bit kinds
+    ((256, 256, 64, F16, F16, F16, K_, K_, 0), -2),          # fp16 output
+    ((256, 256, 64, F32, F32, F32, K_, K_, 0), -2),
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 0), -2),       # e4m3 needs scales
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 16), -2),      # only 32-element blocks
+    ((256, 256, 64, F16, F16, F32, K_, K_, 32), -2),         # 16-bit is dense only
+    ((256, 256, 64, F16, F16, F32, K_, MN, 0), -2),          # B MN-major not built
+    ((256, 256, 128, E4M3, E4M3, F32, MN, K_, 32), -2),      # MN-major fp8 not built
+    ((256, 256, 96, F16, F16, F32, K_, K_, 0), -2),          # K not a multiple of 64
+    ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
+    ((100, 256, 64, F16, F16, F32, K_, K_, 0), -2),          # ragged M
+    ((256, 96, 64, F16, F16, F32, K_, K_, 0), -2),           # ragged N
+    ((1 << 21, 64, 64, F16, F16, F32, K_, K_, 0), -1),       # beyond the size limit
+])
+def test_plan_create_rejections(args, expect):
+    assert _create(*args) == expect
+
+
+def test_plan_create_null_out():
+    lib = mswz.load()
+    assert lib.gemm_plan_create(None, 64, 64, 64, F16, F16, F32, K_, K_, 0) == -1
+
+
+def test_tile_choice():
+    assert mswz.gemm_plan_create(4096, 4096, 4096, "bf16", "bf16").describe()["tile_m"] == 256
+    d = mswz.gemm_plan_create(8192, 8192, 8192, "e4m3", "e4m3", scale_vec_len=32).describe()
+    assert (d["tile_m"], d["tile_k"], d["blocks"]) == (256, 128, 1024)
+    d = mswz.gemm_plan_create(128, 256, 64, "f16", "f16").describe()
+    assert d["tile_m"] * d["tile_n"] * d["blocks"] == 128 * 256
+
+
+# ---- run-time rejections (fake pointers: never dereferenced) -------------------
+
+def test_run_rejections_before_gpu_work():
+    lib = mswz.load()
+    dense = mswz.gemm_plan_create(256, 256, 64, "f16", "f16")
+    mx = mswz.gemm_plan_create(256, 256, 128, "e4m3", "e4m3", scale_vec_len=32)
+    P = 0x10000
+    assert lib.gemm_run(None, P, P, P, 0, None) == -1
+    assert lib.gemm_run(dense.handle, None, P, P, 0, None) == -1
+    assert lib.gemm_run(dense.handle, P, P, None, 0, None) == -1
+    assert lib.gemm_run(dense.handle, P, P, P, 2, None) == -1          # beta not 0/1
+    assert lib.gemm_run(dense.handle, P + 8, P, P, 0, None) == -3      # misaligned A
+    assert lib.gemm_run(dense.handle, P, P, P + 4, 0, None) == -3      # misaligned D
+    assert lib.gemm_run(mx.handle, P, P, P, 0, None) == -5             # wrong kind
+    assert lib.gemm_run_blockscaled(dense.handle, P, P, P, P, P, 0, None) == -5
+    assert lib.gemm_run_blockscaled(mx.handle, P, P, None, P, P, 0, None) == -1
+    assert lib.gemm_run_blockscaled(mx.handle, P, P, P + 1, P, P, 0, None) == -3
+    assert lib.gemm_run_blockscaled(mx.handle, P, P, P, P, P, -1, None) == -1
+
+
+def test_binding_checks_buffer_sizes_before_the_library():
+    import torch
+    plan = mswz.gemm_plan_create(256, 256, 64, "f16", "f16")
+    with pytest.raises((ValueError, TypeError)):
+        mswz.gemm_run(plan, torch.zeros(10), torch.zeros(10), torch.zeros(10))
+
+
+# ---- address functions vs brute force -----------------------------------------
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("major", ["k", "mn"])
+def test_desc_address_matches_bruteforce(mode, major):
+    rows, words = (16, 64) if mode == 4 else (24, 4 * (1 << mode) * 2)
+    for ldo, sdo, origin in [(16, 1024, 0), (256, 128, 0), (2048, 4096, 4096), (64, 512, 1024)]:
+        if mode in (1, 2, 3, 4) and origin % walk.PERIOD[mode]:
+            continue
+        ref = walk.desc_walk_bruteforce(rows, words, ldo, sdo, mode, major, origin)
+        got = np.array([[mswz.desc_address(r, w, ldo, sdo, mode, major, origin)
+                         for w in range(words)] for r in range(rows)])
+        assert np.array_equal(got, ref)
+
+
+def test_desc_address_page_examples():
+    # tcgen05.cp page: (128,4) b32 image, ldo=16, sdo=128, no swizzle -> 16r + 4w
+    for r, w in itertools.product(range(128), range(4)):
+        assert mswz.desc_address(r, w, 16, 128, 0) == 16 * r + 4 * w
+    # tcgen05.mma page mode 4: offset ^ ((offset >> 2) & 96) on a 4-rows-per-SDO walk
+    for r, w in itertools.product(range(8), range(32)):
+        pre = (r // 4) * 512 + (r % 4) * 128 + 4 * w
+        assert mswz.desc_address(r, w, 512, 512, 4, "mn") == pre ^ ((pre >> 2) & 96)
+
+
+@pytest.mark.parametrize("ldo,sdo,mode,origin,expect_ok", [
+    (16, 1024, 3, 0, True), (16, 128, 0, 16, True), (16, 1024, 3, 512, False),
+    (8, 1024, 3, 0, False), (16, 1 << 18, 0, 0, False), (16, 256, 1, 256, True),
+    (16, 256, 2, 256, False), (16, 512, 4, 512, True), (16, 512, 5, 0, False),
+    (-16, 128, 0, 0, False), (16, 128, 0, 8, False),
+])
+def test_desc_check_rules(ldo, sdo, mode, origin, expect_ok):
+    assert (mswz.desc_check(ldo, sdo, mode, origin) == 0) == expect_ok
+
+
+def test_tile_offset_matches_bruteforce():
+    ref = walk.lds_tile_bruteforce(256)
+    got = np.array([[mswz.tile_offset(r, c) for c in range(8)] for r in range(256)])
+    assert np.array_equal(got, ref)

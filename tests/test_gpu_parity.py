@@ -1,0 +1,161 @@
+"""GPU parity: libmswz.so (called through the C ABI) against the fp64 oracle on
+the same seeded inputs.  Tolerances are documented in tests/gpu_util.py.
+
+Small cases compare every output and span several tiles with each tile
+variant, odd K-step counts and grids whose size is and is not a multiple of
+eight (the XCD re-ordering path); the full-size workloads compare whole
+sampled rows and columns, in the launch configuration the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import mma_swizzled_operand_amd as mswz
+import workloads as wl
+from gpu_util import compare, plan_for, reference, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def tile_env():
+    old = os.environ.get("MSWZ_TILE")
+    yield
+    if old is None:
+        os.environ.pop("MSWZ_TILE", None)
+    else:
+        os.environ["MSWZ_TILE"] = old
+
+
+SMALL = {
+    "c1": wl.WORKLOADS["c1"],
+    "bf16-k": wl.custom(512, 768, 320, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bf16-k"),
+    "f16-k": wl.custom(768, 512, 192, "f16", name="f16-k"),
+    "f16-mn-beta": wl.custom(512, 512, 256, "f16", a_major="mn", beta=1, name="f16-mn-beta"),
+    "bf16-mn": wl.custom(256, 768, 128, "bf16", a_major="mn", name="bf16-mn"),
+    "e4m3-mx": wl.custom(512, 768, 384, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                         name="e4m3-mx"),
+    "e4m3-mx-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                              b_dist=("normal", 1.0), name="e4m3-mx-beta"),
+    "skinny": wl.custom(64, 2048, 1024, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02), name="skinny"),
+}
+
+
+@pytest.mark.parametrize("tile", ["256", "128", "64"])
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_full_compare(case, tile, tile_env):
+    w = SMALL[case]
+    if w.M % int(tile) or w.N % int(tile):
+        pytest.skip("tile does not divide the shape")
+    os.environ["MSWZ_TILE"] = tile
+    plan = plan_for(w)
+    assert plan.describe()["tile_m"] == int(tile)
+    say(f"[parity] {case} tile={tile} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} beta={w.beta}")
+    x = wl.generate(w, seed=0)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(case, tile, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("tile", ["256", "128", "64"])
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_quarter_integers_bit_exact(case, tile, tile_env):
+    """Quarter-integer operands (the tcgen05.mma page's example distribution)
+    with unit scales: every partial sum is exact in fp32, so the GPU result
+    must equal the oracle exactly, whatever the summation order."""
+    w = SMALL[case]
+    if w.M % int(tile) or w.N % int(tile):
+        pytest.skip("tile does not divide the shape")
+    os.environ["MSWZ_TILE"] = tile
+    say(f"[exact] {case} tile={tile}")
+    x = wl.generate(w, seed=0, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    ref = reference(w, x, with_mag=False)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_page_example_128x64x64():
+    """The tcgen05.mma page's 128x64x64 fp16 example, padded to the library's
+    64-column tile: B (64,64) stored (N,K), quarter-integer values from
+    default_rng(0); result compared with fp32 a @ b.T (exact)."""
+    rng = np.random.default_rng(0)
+    a = (rng.integers(-4, 5, (128, 64)) / 4).astype("float16")
+    b = (rng.integers(-4, 5, (64, 64)) / 4).astype("float16")
+    w = wl.custom(128, 64, 64, "f16", name="page-example")
+    say("[exact] page example 128x64x64")
+    got = run_gpu(w, {"A": a.view(np.uint16), "B": b.view(np.uint16)})
+    assert np.array_equal(got, a.astype("float32") @ b.astype("float32").T)
+
+
+def test_beta_zero_ignores_nan_in_D():
+    w = wl.custom(128, 128, 64, "bf16", name="nan-d")
+    x = wl.generate(w, seed=3)
+    say("[edge] beta=0 over NaN-filled D")
+    got = run_gpu(w, x, D_init=np.full((w.M, w.N), np.nan, dtype=np.float32))
+    ref, mag = reference(w, x)
+    compare(w, got, ref, mag)
+
+
+def test_single_k_step_single_tile():
+    w = wl.custom(64, 64, 64, "f16", name="one-tile")
+    x = wl.generate(w, seed=4)
+    say("[edge] 64x64x64")
+    got = run_gpu(w, x)
+    ref, mag = reference(w, x)
+    compare(w, got, ref, mag)
+
+
+def test_deterministic_bits():
+    w = wl.custom(1024, 1024, 512, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="det")
+    x = wl.generate(w, seed=5)
+    say("[det] two runs")
+    assert np.array_equal(run_gpu(w, x), run_gpu(w, x))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b"])
+def test_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration; whole
+    sampled rows and columns are compared with the oracle."""
+    w = wl.WORKLOADS[name]
+    say(f"[full] {name}: {w.title}")
+    x = wl.generate(w, seed=0)
+    plan = plan_for(w)
+    say(f"[full] {name} plan {plan.describe()}")
+    got = run_gpu(w, x, plan)
+    rows, cols = wl.sample_points(w, 8, 8)
+    ref_r, mag_r = reference(w, x, rows=rows)
+    ref_c, mag_c = reference(w, x, cols=cols)
+    d0 = x.get("D0")
+    r1 = compare(w, got[rows], ref_r, mag_r, None if d0 is None else d0[rows])
+    r2 = compare(w, got[:, cols], ref_c, mag_c, None if d0 is None else d0[:, cols])
+    print(name, r1, r2)
+
+
+def test_full_size_c5_quarter_exact():
+    """MX-fp8 8192^3 with quarter-integer operands and unit scales: exact."""
+    w = wl.WORKLOADS["c5"]
+    x = wl.generate(w, seed=0, values="quarter")
+    say("[full-exact] c5 quarter")
+    got = run_gpu(w, x)
+    rows, cols = wl.sample_points(w, 4, 4)
+    assert np.array_equal(got[rows].astype(np.float64), reference(w, x, rows=rows, with_mag=False))
+    assert np.array_equal(got[:, cols].astype(np.float64), reference(w, x, cols=cols, with_mag=False))
+
+
+def test_scale_bytes_select_the_right_block():
+    """Scales only: a = b = 1 everywhere, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
+    exactly (block-scale closed form); a wrong byte or lane for any scale
+    block changes the value."""
+    M, N, K = 256, 256, 512
+    w = wl.custom(M, N, K, "e4m3", V=32, name="scale-only")
+    rng = np.random.default_rng(6)
+    x = {"A": np.full((M, K), 0x38, np.uint8), "B": np.full((N, K), 0x38, np.uint8),
+         "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
+         "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
+    say("[scale] closed form")
+    got = run_gpu(w, x)
+    ua = x["SFA"].astype(np.int64) - 127
+    ub = x["SFB"].astype(np.int64) - 127
+    expect = 32.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
+    assert np.array_equal(got.astype(np.float64), expect)
