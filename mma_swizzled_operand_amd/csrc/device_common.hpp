@@ -31,8 +31,9 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c)
 }
 
 // Block-scaled 32x32x64 MFMA on OCP E4M3 operands (format code 0 for both).
-// Lane l holds 32 consecutive K elements (one 32-element scale block) of row
-// l % 32; its scale byte is byte SEL of the 32-bit scale operand.
+// Lane l holds K elements 16h..16h+15 and 32+16h..32+16h+15 (h = l / 32) of
+// row l % 32; the scale of K block h of that row is byte SEL of lane l's
+// 32-bit scale operand.
 template <int SEL>
 __device__ __forceinline__ f32x16 mfma_scale_32x32x64_e4m3(i32x8 a, i32x8 b, f32x16 c,
                                                           int scale_a, int scale_b)

@@ -6,9 +6,13 @@
 // Same workgroup structure as gemm_dense.hip: 4 waves, a BM x BN tile,
 // double-buffered swizzled LDS stages of 128 bytes per operand row (here 128
 // K elements), 16-byte global loads prefetched one K step ahead in registers.
-// The multiply is the gfx950 scaled MFMA 32x32x64: each lane supplies 32
-// consecutive K elements of one row (exactly one 32-element scale block) and
-// the E8M0 byte of that block, so the hardware applies 2^(E-127) per lane.
+// The multiply is the gfx950 scaled MFMA 32x32x64.  Its operand image, pinned
+// by an on-device probe: lane (r, h) of a 32-row block (r = lane % 32,
+// h = lane / 32) holds row r, K elements 16h..16h+15 in bytes 0..15 and
+// 32+16h..32+16h+15 in bytes 16..31; the scale of K block 0 (K 0..31) of row
+// r is taken from lane r and that of block 1 (K 32..63) from lane 32+r, byte
+// `op_sel` of the 32-bit scale operand.  So each lane supplies the scale of
+// block h of its row while its data straddles both blocks.
 // Scale bytes are read straight from global memory: the four bytes of one
 // row that cover a 128-element K step form one aligned 32-bit word, loaded one
 // step ahead with the tiles; each lane shifts its own half of the word into
@@ -98,22 +102,23 @@ gemm_mx_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     };
 
     // ---- MFMA operand read offsets -------------------------------------------
-    // Sub-step ks (64 K elements): lane (lr, lh) reads chunks 4ks + 2lh and
-    // 4ks + 2lh + 1 of its row; they sit at 4ks ^ (key ^ 2lh) and 4ks ^ (key ^ (2lh+1)).
+    // Sub-step ks (64 K elements): lane (lr, lh) reads 16-byte chunks
+    // 4ks + lh and 4ks + 2 + lh of its row; they sit at 4ks ^ (key ^ lh) and
+    // 4ks ^ (key ^ (2 + lh)).
     uint32_t aoff[TM], ak0[TM], ak1[TM], boff[TN], bk0[TN], bk1[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const uint32_t row = wm + 32 * i + lr;
         aoff[i] = row * kTileRowBytes;
-        ak0[i] = tile_key(row) ^ (2 * lh);
-        ak1[i] = tile_key(row) ^ (2 * lh + 1);
+        ak0[i] = tile_key(row) ^ lh;
+        ak1[i] = tile_key(row) ^ (2 + lh);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const uint32_t row = wn + 32 * j + lr;
         boff[j] = kATile + row * kTileRowBytes;
-        bk0[j] = tile_key(row) ^ (2 * lh);
-        bk1[j] = tile_key(row) ^ (2 * lh + 1);
+        bk0[j] = tile_key(row) ^ lh;
+        bk1[j] = tile_key(row) ^ (2 + lh);
     }
 
     f32x16 acc[TN][TM];
