@@ -166,6 +166,9 @@ def main():
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the GEMM, time a plain device-to-device copy of this many "
+                         "bytes (used to calibrate the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -182,6 +185,15 @@ def main():
     torch.cuda.set_device(0)
     import mma_swizzled_operand_amd as mswz
     mswz.load()
+
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        wall, avg_ms, _ = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps,
+                          "avg_ms": round(avg_ms, 5),
+                          "GB/s": round(2 * args.copy_bytes / (avg_ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
 
     if args.workload not in wl.WORKLOADS:
         raise SystemExit(f"unknown workload {args.workload}")

@@ -43,7 +43,7 @@ bool variant_info(int variant, bool one_byte_elems, VariantInfo *info)
     info->tile_m = t;
     info->tile_n = t;
     info->tile_k = tk;
-    info->threads = 256;
+    info->threads = t == 256 ? 512 : 256;
     info->lds_bytes = 2 * (t + t) * 128;
     return true;
 }
@@ -149,9 +149,10 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
         return MSWZ_ERR_ALIGN;
     mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                       p->group_m};
-    hipError_t e = mswz::launch_dense(p->variant, p->a_dt == MSWZ_DT_BF16,
-                                      p->a_major == MSWZ_MAJOR_MN, a,
-                                      static_cast<hipStream_t>(stream));
+    const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = p->variant == mswz::kVarDense256 ? mswz::launch_dense256(bf16, a_mn, a, st)
+                                                     : mswz::launch_dense(p->variant, bf16, a_mn, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
 
@@ -169,7 +170,9 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
         return MSWZ_ERR_ALIGN;
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                    p->group_m};
-    hipError_t e = mswz::launch_mx(p->variant, a, static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, st)
+                                                  : mswz::launch_mx(p->variant, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
 

@@ -63,6 +63,45 @@ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, i
     tn = r / gm;
 }
 
+// Buffer resource for raw (unstructured) buffer loads: base address, no
+// stride, `bytes` valid bytes (reads beyond it return zero), gfx9-family
+// word 3 (32-bit data format, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// [lds + 16*l, +16) (lds is wave-uniform); the source is base + voffset + soffset.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *lds,
+                                                  uint32_t voffset, uint32_t soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                               uint32_t soffset)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+}
+
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                                 uint32_t soffset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voffset, soffset, 0);
+}
+
+// Make a value opaque to the optimiser for one use site, so that values
+// derived from it (per sub-step LDS addresses) are recomputed where they are
+// used instead of being hoisted out of the K loop and held in registers.
+template <typename T>
+__device__ __forceinline__ T opaque(T v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // 16-byte LDS read / write.
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t *lds, uint32_t off)
 {

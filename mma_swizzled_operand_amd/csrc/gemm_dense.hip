@@ -3,6 +3,7 @@
 // 128x64x64 example; operand majors from "Shared descriptors are byte-stride
 // contracts").
 //
+// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256.hip).
 // Structure of one 256-thread workgroup (4 waves) computing a BM x BN tile:
 //   * K advances 64 elements per step; each step stages a [BM][128 B] A tile
 //     and a [BN][128 B] B tile in LDS, in the swizzled tile layout of
@@ -219,7 +220,6 @@ template <bool BF16, bool A_MN>
 hipError_t launch_variant(int variant, const DenseArgs &a, hipStream_t stream)
 {
     switch (variant) {
-    case kVarDense256: return launch_one<256, 256, 128, 128, BF16, A_MN>(a, stream);
     case kVarDense128: return launch_one<128, 128, 64, 64, BF16, A_MN>(a, stream);
     case kVarDense64: return launch_one<64, 64, 32, 32, BF16, A_MN>(a, stream);
     default: return hipErrorInvalidValue;

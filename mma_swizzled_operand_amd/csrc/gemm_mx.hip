@@ -3,6 +3,7 @@
 // (tcgen05.mma page, "Weight-stationary and block scaling": per-row scale
 // vectors for A and B, one scale per block of consecutive K elements).
 //
+// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256.hip).
 // Same workgroup structure as gemm_dense.hip: 4 waves, a BM x BN tile,
 // double-buffered swizzled LDS stages of 128 bytes per operand row (here 128
 // K elements), 16-byte global loads prefetched one K step ahead in registers.
@@ -226,7 +227,6 @@ hipError_t launch_one(const MxArgs &a, hipStream_t stream)
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream)
 {
     switch (variant) {
-    case kVarMx256: return launch_one<256, 256, 128, 128>(args, stream);
     case kVarMx128: return launch_one<128, 128, 64, 64>(args, stream);
     case kVarMx64: return launch_one<64, 64, 32, 32>(args, stream);
     default: return hipErrorInvalidValue;

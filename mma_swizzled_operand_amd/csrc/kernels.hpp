@@ -9,10 +9,10 @@ namespace mswz {
 // Kernel variants a plan can select.  The tile is BM x BN output elements per
 // 256-thread workgroup; each K step stages 128 bytes of every operand row.
 enum Variant : int {
-    kVarDense256 = 1,   // 16-bit, 256x256 tile, 4 waves of 128x128
+    kVarDense256 = 1,   // 16-bit, 256x256 tile, 8 waves of 128x64 (gemm256.hip)
     kVarDense128 = 2,   // 16-bit, 128x128 tile, 4 waves of 64x64
     kVarDense64 = 3,    // 16-bit, 64x64 tile, 4 waves of 32x32
-    kVarMx256 = 11,     // E4M3 block-scaled, 256x256 tile
+    kVarMx256 = 11,     // E4M3 block-scaled, 256x256 tile, 8 waves (gemm256.hip)
     kVarMx128 = 12,     // E4M3 block-scaled, 128x128 tile
     kVarMx64 = 13,      // E4M3 block-scaled, 64x64 tile
     kVarSkinny = 21,    // 16-bit, M <= 64: weight streaming, split K inside the workgroup
@@ -45,6 +45,8 @@ struct VariantInfo {
 bool variant_info(int variant, bool one_byte_elems, VariantInfo *info);
 
 hipError_t launch_dense(int variant, bool bf16, bool a_mn, const DenseArgs &args, hipStream_t stream);
+hipError_t launch_dense256(bool bf16, bool a_mn, const DenseArgs &args, hipStream_t stream);
+hipError_t launch_mx256(const MxArgs &args, hipStream_t stream);
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);
 hipError_t launch_skinny(bool bf16, const DenseArgs &args, hipStream_t stream);
 
