@@ -131,6 +131,11 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         p->variant = tile == 256 ? mswz::kVarDense256 : tile == 128 ? mswz::kVarDense128
                                                                      : mswz::kVarDense64;
     p->group_m = 4;
+    if (const char *env = getenv("MSWZ_GROUP_M")) {   // tuning override
+        const int g = atoi(env);
+        if (g >= 1 && g <= 64)
+            p->group_m = g;
+    }
     mswz::variant_info(p->variant, fp8, &p->info);
     p->blocks = (M / p->info.tile_m) * (N / p->info.tile_n);
     *out = p;

@@ -80,6 +80,38 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint
                                              voffset, soffset, 0, 0);
 }
 
+// 4 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// [lds + 4*l, +4).
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, uint8_t *lds,
+                                                 uint32_t voffset, uint32_t soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4,
+                                             voffset, soffset, 0, 0);
+}
+
+// Workgroup barrier for LDS pipelines: waits until at most `VM` of this
+// wave's vector-memory loads (the most recently issued ones) are still in
+// flight and all its LDS operations are done, then joins the barrier.  The
+// memory clobber keeps the compiler from moving memory operations across it.
+// The wait is the s_waitcnt builtin, which the compiler's own wait-count
+// tracking sees, so it does not wait for the same loads again later.
+// Encoding (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int VM>
+__device__ __forceinline__ void lds_barrier_keep_vm()
+{
+    static_assert(VM >= 0 && VM < 64, "vmcnt is 6 bits");
+    constexpr int kEnc = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8);
+    __builtin_amdgcn_s_waitcnt(kEnc);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Scheduling fence: no instruction is moved across it by the compiler.
+__device__ __forceinline__ void sched_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
                                                uint32_t soffset)
 {

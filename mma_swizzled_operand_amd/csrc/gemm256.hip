@@ -15,7 +15,16 @@
 // permutation is its own inverse, so lane l simply fetches the source chunk
 // that belongs at its destination: chunk (l % 8) ^ key(row).  An MN-major A
 // ([K][M]) is read into registers as 8x8 blocks, transposed, and written with
-// 16-byte LDS stores into the same K-contiguous layout.
+// 16-byte LDS stores into the same K-contiguous layout.  Scale bytes (MX) for
+// the step's 256 A rows and 256 B rows are copied into a small LDS stage by
+// direct 4-byte loads, one wave instruction per 64 rows.
+//
+// Latency.  LDS holds only two 64 KiB stages, so the copy of step k+1 (issued
+// when step k starts) must land within one step of MFMA work.  To keep it an
+// L2 hit, every step also touches one 4-byte word of each 128-byte line the
+// step after it will need (k+2), with a direct-to-LDS load into a throwaway
+// LDS sink; these touches are issued last and are the only loads allowed to
+// stay in flight across the end-of-step barrier.
 //
 // Compute.  Wave w owns output rows 128*(w/4) .. +127 and columns 64*(w%4)
 // .. +63: 4 x 2 blocks of 32x32 MFMA output, 128 fp32 accumulators per lane.
@@ -23,6 +32,7 @@
 // so four consecutive accumulator registers hold four consecutive N columns
 // of one M row and the epilogue stores 16 bytes per lane.
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -30,56 +40,106 @@
 namespace mswz {
 namespace {
 
-constexpr int kThreads = 512;
 constexpr int kBM = 256, kBN = 256;
 constexpr int kATile = kBM * 128, kBTile = kBN * 128, kStage = kATile + kBTile;
-constexpr int TM = 4, TN = 2;   // 32x32 blocks per wave along M and N
+constexpr int kScaleStage = (kBM + kBN) * 4;   // one 32-bit scale word per row
 
 enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2 };
 
 // Direct-to-LDS copy of one K-major operand tile (256 rows x 128 bytes per K
-// step) through a buffer resource on the workgroup's 256-row panel.  Wave w
-// copies rows 8*(w + 8i) .. +7 for i = 0..3; lane l takes row 8*(w + 8i) + l/8,
-// whose layout key is (l/8) ^ w, so it fetches chunk (l % 8) ^ (l/8) ^ w.
+// step) through a buffer resource on the workgroup's 256-row panel.  With W
+// waves, wave w copies rows 8*(w + W*i) .. +7 for i = 0 .. 32/W - 1; lane l
+// takes row 8*(w + W*i) + l/8, whose layout key is (l/8) ^ ((w + W*i) % 8), so
+// it fetches chunk (l % 8) ^ (l/8) ^ ((w + W*i) % 8).  For W = 8 the key does
+// not depend on i; for W = 4 it alternates between two values with i.
+template <int W>
 struct DmaOperand {
+    static constexpr int kInstr = 32 / W;
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff;       // this lane's byte offset in the panel for i = 0, K step 0
-    uint32_t step64;     // bytes between the row groups of consecutive i (64 rows)
+    uint32_t voff[2];    // this lane's byte offset in the panel at K step 0, for even / odd i
+    uint32_t row_bytes;
     uint32_t lds_off;    // LDS offset of this wave's first destination row inside a stage
 
-    __device__ void init(const uint8_t *X, int row0, uint32_t row_bytes, int wave, int lane,
+    __device__ void init(const uint8_t *X, int row0, uint32_t rb, int wave, int lane,
                          uint32_t tile_off)
     {
-        rsrc = make_rsrc(X + size_t(row0) * row_bytes, 256u * row_bytes);
+        row_bytes = rb;
+        rsrc = make_rsrc(X + size_t(row0) * rb, 256u * rb);
         const int r = 8 * wave + (lane >> 3);
-        const int chunk = (lane & 7) ^ (((lane >> 3) ^ wave) & 7);
-        voff = uint32_t(r) * row_bytes + chunk * 16;
-        step64 = 64u * row_bytes;
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+            const int chunk = (lane & 7) ^ (((lane >> 3) ^ (wave + W * odd)) & 7);
+            voff[odd] = uint32_t(r) * rb + chunk * 16;
+        }
         lds_off = tile_off + 8 * wave * kTileRowBytes;
     }
 
     __device__ void issue(uint8_t *stage, int kt) const
     {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            buffer_load_lds16(rsrc, stage + lds_off + i * 64 * kTileRowBytes, voff,
-                              i * step64 + uint32_t(kt) * 128);
+        for (int i = 0; i < kInstr; ++i)
+            buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i & 1],
+                              uint32_t(8 * W * i) * row_bytes + uint32_t(kt) * 128);
     }
 };
 
-template <int KIND, bool A_MN, bool BETA>
-__global__ void __launch_bounds__(kThreads)
+// Register-staged copy of one K-major operand tile: the 64*W threads each
+// load 2048/(64*W) 16-byte chunks per step into registers (thread t: row
+// t/8 + (8W/8)*8*i... i.e. rows t/8 + 8W*i, chunk t % 8) and, after the
+// step's MFMAs, store them to the other stage at row*128 + ((chunk ^ key) << 4).
+// Eight consecutive lanes cover one 128-byte row, so each wave-wide load reads
+// eight whole rows and each wave-wide store fills 1 KiB of LDS.
+template <int W>
+struct RegOperand {
+    static constexpr int kN = 2048 / (64 * W);
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff, row_bytes, lds0;
+    u32x4 r[kN];
+
+    __device__ void init(const uint8_t *X, int row0, uint32_t rb, int tid, uint32_t tile_off)
+    {
+        row_bytes = rb;
+        rsrc = make_rsrc(X + size_t(row0) * rb, 256u * rb);
+        const int row = tid >> 3, chunk = tid & 7;
+        voff = uint32_t(row) * rb + chunk * 16;
+        lds0 = tile_off + tile_offset(row, chunk);   // key(row + 8W*i) == key(row): period 64
+    }
+    __device__ void load(int kt)
+    {
+#pragma unroll
+        for (int i = 0; i < kN; ++i)
+            r[i] = buffer_load16(rsrc, voff, uint32_t(8 * W * i) * row_bytes + uint32_t(kt) * 128);
+    }
+    __device__ void store(uint8_t *stage) const
+    {
+#pragma unroll
+        for (int i = 0; i < kN; ++i)
+            lds_write16(stage, lds0 + i * 8 * W * kTileRowBytes, r[i]);
+    }
+};
+
+// W waves per workgroup: W = 8 gives each wave a 128 x 64 output sub-tile
+// (two waves per SIMD), W = 4 a 128 x 128 sub-tile (one wave per SIMD,
+// accumulators in AGPRs, a third fewer LDS bytes read per MFMA).
+template <int KIND, bool A_MN, bool BETA, int W, bool TOUCH, int REG>
+__global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
                float *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
 {
     static_assert(!(A_MN && KIND == kE4m3), "MN-major A is built for 16-bit operands only");
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
+    constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
+    constexpr int kWavesN = 256 / (32 * TN);     // waves along N
     constexpr bool kMx = KIND == kE4m3;
     constexpr int kElem = kMx ? 1 : 2;
     constexpr int kStepK = 128 / kElem;   // K elements per step
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+    __shared__ __attribute__((aligned(256))) uint8_t scl0[kMx ? kScaleStage : 4];
+    __shared__ __attribute__((aligned(256))) uint8_t scl1[kMx ? kScaleStage : 4];
+    __shared__ __attribute__((aligned(256))) uint8_t sink[TOUCH ? W * 256 : 4];   // L2 touches land here
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -88,30 +148,37 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBN;
-    const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+    const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
     const uint32_t row_bytes = uint32_t(K) * kElem;
+    const int KT = K / kStepK;
 
-    // ---- staging state ---------------------------------------------------------
-    DmaOperand db;
+    // ---- operand copies ---------------------------------------------------------
+    // REG bit 0: A staged through registers, bit 1: B staged through registers
+    // (K-major operands; otherwise copied straight into LDS)
+    constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) != 0;
+    DmaOperand<W> db;
     db.init(B, n0, row_bytes, wave, lane, kATile);
-    DmaOperand da;
+    DmaOperand<W> da;
     if constexpr (!A_MN)
         da.init(A, m0, row_bytes, wave, lane, 0);
+    RegOperand<W> rga, rgb;
+    if constexpr (kRegA)
+        rga.init(A, m0, row_bytes, tid, 0);
+    if constexpr (kRegB)
+        rgb.init(B, n0, row_bytes, tid, kATile);
 
-    // MN-major A ([K][M]): waves 0..3 each stage one 8x8 block per lane:
+    // MN-major A ([K][M]): threads 0..255 each stage one 8x8 block:
     // tile rows 8*mb .. +7 (M), K rows 8*kc .. +7 of the step, mb = tid % 32,
     // kc = tid / 32.  Read through a buffer resource on columns m0.. of A.
     const bool a_mn_active = tid < 256;
-    __amdgpu_buffer_rsrc_t ra_rsrc;
-    uint32_t ra_voff = 0, la_mn0 = 0;
     const uint32_t a_mn_row = uint32_t(M) * 2;
+    __amdgpu_buffer_rsrc_t ra_rsrc;
+    uint32_t ra_voff = 0;
     u32x4 ra[A_MN ? 8 : 1];
     if constexpr (A_MN) {
         const int mb = tid & 31, kc = (tid >> 5) & 7;
         ra_rsrc = make_rsrc(A + size_t(m0) * 2, uint32_t(K) * a_mn_row - uint32_t(m0) * 2);
         ra_voff = uint32_t(8 * kc) * a_mn_row + 16 * mb;
-        la_mn0 = tile_offset(8 * mb, kc);   // rows 8mb+i: key = i ^ mb, chunk kc
-        (void)la_mn0;
     }
     auto a_mn_load = [&](int kt) {
         if (a_mn_active) {
@@ -131,46 +198,85 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
-    // ---- scales (MX): one 32-bit word of 4 scale bytes per row per K step -------
-    __amdgpu_buffer_rsrc_t sfa_rsrc, sfb_rsrc;
-    uint32_t sfa_voff = 0, sfb_voff = 0;
+    // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
+    // for g >= 4) is copied by wave g % W; lane l copies the step's 32-bit
+    // scale word of row 64*(g%4) + l into scale-stage word 64*g + l.
+    constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / 32;
-    uint32_t sa[TM], sb[TN], sa_n[TM], sb_n[TN];
+    __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
+    uint32_t sf_voff = 0;
     if constexpr (kMx) {
-        sfa_rsrc = make_rsrc(SFA + size_t(m0) * sf_row, 256u * sf_row);
-        sfb_rsrc = make_rsrc(SFB + size_t(n0) * sf_row, 256u * sf_row);
-        sfa_voff = uint32_t(wm + lr) * sf_row;
-        sfb_voff = uint32_t(wn + lr) * sf_row;
+#pragma unroll
+        for (int q = 0; q < kSfInstr; ++q) {
+            const int g = wave + W * q;
+            const bool is_b = g >= 4;
+            sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row, 256u * sf_row);
+        }
+        sf_voff = uint32_t(64 * (wave & 3) + lane) * sf_row;
     }
-    auto scales_load = [&](int kt) {
-        if constexpr (kMx) {
+
+    // ---- L2 touches for a future step: line index t = 64*w' + l over the
+    // step's 512 lines (w' = w + W*q): lines 0..255 are A rows (K-major) or,
+    // for an MN-major A, K row t/4 and 128-byte piece t%4 of the tile's
+    // 512-byte segment of that row; lines 256..511 are B rows.
+    constexpr int kTouch = TOUCH ? 8 / W : 0;
+    __amdgpu_buffer_rsrc_t pf_rsrc[kTouch > 0 ? kTouch : 1];
+    uint32_t pf_voff[kTouch > 0 ? kTouch : 1], pf_kstride[kTouch > 0 ? kTouch : 1];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                sa_n[i] = buffer_load4(sfa_rsrc, sfa_voff, uint32_t(32 * i) * sf_row + 4u * kt);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                sb_n[j] = buffer_load4(sfb_rsrc, sfb_voff, uint32_t(32 * j) * sf_row + 4u * kt);
+    for (int q = 0; q < kTouch; ++q) {
+        const int g = wave + W * q;
+        const int idx = 64 * (g & 3) + lane;   // 0..255
+        if (g >= 4) {
+            pf_rsrc[q] = db.rsrc;
+            pf_voff[q] = uint32_t(idx) * row_bytes;
+            pf_kstride[q] = 128;
+        } else if constexpr (A_MN) {
+            pf_rsrc[q] = ra_rsrc;
+            pf_voff[q] = uint32_t(idx >> 2) * a_mn_row + 128 * (idx & 3);
+            pf_kstride[q] = 64 * a_mn_row;
+        } else {
+            pf_rsrc[q] = da.rsrc;
+            pf_voff[q] = uint32_t(idx) * row_bytes;
+            pf_kstride[q] = 128;
         }
-    };
-    auto scales_take = [&]() {
-        if constexpr (kMx) {
-            // lane half lh supplies the scale of K block lh of its row
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                sa[i] = sa_n[i] >> (8 * lh);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                sb[j] = sb_n[j] >> (8 * lh);
-        }
+    }
+
+    auto store_regs = [&](uint8_t *stage) {
+        if constexpr (A_MN)
+            a_mn_store(stage);
+        if constexpr (kRegA)
+            rga.store(stage);
+        if constexpr (kRegB)
+            rgb.store(stage);
     };
 
-    auto issue_step = [&](uint8_t *stage, int kt) {
+    auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
         if constexpr (A_MN)
             a_mn_load(kt);
+        else if constexpr (kRegA)
+            rga.load(kt);
         else
             da.issue(stage, kt);
-        db.issue(stage, kt);
-        scales_load(kt);
+        if constexpr (kRegB)
+            rgb.load(kt);
+        else
+            db.issue(stage, kt);
+        if constexpr (kMx) {
+#pragma unroll
+            for (int q = 0; q < kSfInstr; ++q)
+                buffer_load_lds4(sf_rsrc[q], sstage + 256 * (wave + W * q), sf_voff, 4u * kt);
+        }
+    };
+    // issued after issue_step; these are the only loads left in flight at the
+    // next end-of-step barrier
+    auto touch_step = [&](int kt) {
+        if constexpr (kTouch > 0) {
+            sched_fence();
+#pragma unroll
+            for (int q = 0; q < kTouch; ++q)
+                buffer_load_lds4(pf_rsrc[q], sink + 256 * wave, pf_voff[q], uint32_t(kt) * pf_kstride[q]);
+            sched_fence();
+        }
     };
 
     // ---- MFMA operand read addresses -------------------------------------------
@@ -227,7 +333,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
-    auto compute_mx = [&](const uint8_t *s) {
+    auto compute_mx = [&](const uint8_t *s, const uint8_t *ss) {
         uint32_t ab[TM], bb[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -235,6 +341,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             bb[j] = opaque(bbase[j]);
+        // lane half lh supplies the scale of K block lh of its row: byte lh (sub-step 0)
+        // and byte 2 + lh (sub-step 1) of the row's scale word
+        uint32_t sa[TM], sb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t *>(ss + 4 * (wm + 32 * i + lr)) >> (8 * lh);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            sb[j] = *reinterpret_cast<const uint32_t *>(ss + kBM * 4 + 4 * (wn + 32 * j + lr)) >> (8 * lh);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             i32x8 af[TM], bf[TN];
@@ -262,43 +377,39 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
-    auto compute = [&](const uint8_t *s) {
+    auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kMx)
-            compute_mx(s);
+            compute_mx(s, ss);
         else
             compute16(s);
     };
 
     // ---- main loop: two K steps per iteration, one stage array each; an odd
-    // final step (already in lds0) is computed after the loop ------------------
-    const int KT = K / kStepK;
-    issue_step(lds0, 0);
-    if constexpr (A_MN)
-        a_mn_store(lds0);
+    // final step (already in lds0) is computed after the loop.  The loop body
+    // has no branches: in the last pair of an even step count the copy into
+    // lds0 repeats step KT-1 into a stage nobody reads again, which keeps the
+    // compiler from draining the copies in flight at a control-flow merge. ------
+    issue_step(lds0, scl0, 0);
+    store_regs(lds0);
+    touch_step(min(1, KT - 1));
     __syncthreads();
-    scales_take();
 
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-        issue_step(lds1, kt + 1);
-        compute(lds0);
-        if constexpr (A_MN)
-            a_mn_store(lds1);
-        __syncthreads();
-        scales_take();
-        const bool more = kt + 2 < KT;
-        if (more)
-            issue_step(lds0, kt + 2);
-        compute(lds1);
-        if constexpr (A_MN) {
-            if (more)
-                a_mn_store(lds0);
-        }
-        __syncthreads();
-        scales_take();
+        issue_step(lds1, scl1, kt + 1);
+        touch_step(min(kt + 2, KT - 1));
+        compute(lds0, scl0);
+        store_regs(lds1);
+        lds_barrier_keep_vm<kTouch>();
+        issue_step(lds0, scl0, min(kt + 2, KT - 1));
+        touch_step(min(kt + 3, KT - 1));
+        compute(lds1, scl1);
+        store_regs(lds0);
+        lds_barrier_keep_vm<kTouch>();
     }
     if (kt < KT)
-        compute(lds0);
+        compute(lds0, scl0);
+    __syncthreads();   // no copy may still be writing LDS when the workgroup ends
 
     // ---- epilogue -------------------------------------------------------------
 #pragma unroll
@@ -319,7 +430,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
 }
 
-template <int KIND, bool A_MN>
+template <int KIND, bool A_MN, int W, bool TOUCH, int REG>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     const int tiles_m = a.M / kBM, tiles_n = a.N / kBN;
@@ -327,12 +438,37 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, true>), dim3(blocks), dim3(kThreads), 0, stream,
-                           A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, true, W, TOUCH, REG>), dim3(blocks), dim3(64 * W),
+                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, false>), dim3(blocks), dim3(kThreads), 0, stream,
-                           A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, false, W, TOUCH, REG>), dim3(blocks), dim3(64 * W),
+                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     return hipGetLastError();
+}
+
+// Pipeline configuration of the 256x256 tile, selected at run time by the
+// environment variable MSWZ_TILE256 (tuning only): bit 0 set = four waves
+// (else eight); bits 2..3 = operands staged through registers (bit 2: A,
+// bit 3: B).
+int config256()
+{
+    static int cfg = [] {
+        const char *e = getenv("MSWZ_TILE256");
+        return e ? atoi(e) & 13 : 0;
+    }();
+    return cfg;
+}
+
+template <int KIND, bool A_MN>
+hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
+{
+    switch (config256()) {
+    case 1: return launch_kind<KIND, A_MN, 4, false, 0>(a, stream);
+    case 4: return launch_kind<KIND, A_MN, 8, false, 1>(a, stream);
+    case 8: return launch_kind<KIND, A_MN, 8, false, 2>(a, stream);
+    case 12: return launch_kind<KIND, A_MN, 8, false, 3>(a, stream);
+    default: return launch_kind<KIND, A_MN, 8, false, 0>(a, stream);
+    }
 }
 
 }  // namespace
@@ -341,13 +477,13 @@ hipError_t launch_dense256(bool bf16, bool a_mn, const DenseArgs &d, hipStream_t
 {
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m};
     if (bf16)
-        return a_mn ? launch_kind<kBf16, true>(a, stream) : launch_kind<kBf16, false>(a, stream);
-    return a_mn ? launch_kind<kF16, true>(a, stream) : launch_kind<kF16, false>(a, stream);
+        return a_mn ? launch_cfg<kBf16, true>(a, stream) : launch_cfg<kBf16, false>(a, stream);
+    return a_mn ? launch_cfg<kF16, true>(a, stream) : launch_cfg<kF16, false>(a, stream);
 }
 
 hipError_t launch_mx256(const MxArgs &a, hipStream_t stream)
 {
-    return launch_kind<kE4m3, false>(a, stream);
+    return launch_cfg<kE4m3, false>(a, stream);
 }
 
 }  // namespace mswz
