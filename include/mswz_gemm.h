@@ -83,7 +83,9 @@ typedef struct gemm_plan gemm_plan;
  *   b_major       MSWZ_MAJOR_K
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3
  * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3); M and N multiples
- * of 64 (M % 256 and N % 256 select the large square tile).
+ * of 64 (M % 256 and N % 256 select the large square tile).  A 16-bit K-major
+ * A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
+ * weight-streaming kernel (M == 32 is accepted only there).
  * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
  */
 int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,

@@ -38,6 +38,13 @@ bool variant_info(int variant, bool one_byte_elems, VariantInfo *info)
     case kVarDense256: case kVarMx256: t = 256; break;
     case kVarDense128: case kVarMx128: t = 128; break;
     case kVarDense64: case kVarMx64: t = 64; break;
+    case kVarSkinny:
+        info->tile_m = 64;
+        info->tile_n = 64;
+        info->tile_k = 64;
+        info->threads = 512;
+        info->lds_bytes = 8 * 64 * 68 * 4;
+        return true;
     default: return false;
     }
     info->tile_m = t;
@@ -109,7 +116,10 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_UNSUPPORTED;
     if (K % (fp8 ? 128 : 64) != 0)
         return MSWZ_ERR_UNSUPPORTED;
-    const int tile = pick_tile(M, N);
+    // weight streaming: few rows of K-major 16-bit A against a large B
+    const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && (M == 64 || M == 32) && N % 64 == 0 &&
+                        K % 1024 == 0 && !getenv("MSWZ_TILE");
+    const int tile = skinny ? 64 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -127,6 +137,8 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     p->scale_vec_len = scale_vec_len;
     if (fp8)
         p->variant = tile == 256 ? mswz::kVarMx256 : tile == 128 ? mswz::kVarMx128 : mswz::kVarMx64;
+    else if (skinny)
+        p->variant = mswz::kVarSkinny;
     else
         p->variant = tile == 256 ? mswz::kVarDense256 : tile == 128 ? mswz::kVarDense128
                                                                      : mswz::kVarDense64;
@@ -137,6 +149,10 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
             p->group_m = g;
     }
     mswz::variant_info(p->variant, fp8, &p->info);
+    if (skinny) {
+        p->info.tile_m = int(M);
+        p->info.lds_bytes = 8 * int(M) * 68 * 4;
+    }
     p->blocks = (M / p->info.tile_m) * (N / p->info.tile_n);
     *out = p;
     return MSWZ_OK;
@@ -157,6 +173,7 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
     const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = p->variant == mswz::kVarDense256 ? mswz::launch_dense256(bf16, a_mn, a, st)
+                   : p->variant == mswz::kVarSkinny  ? mswz::launch_skinny(bf16, a, st)
                                                      : mswz::launch_dense(p->variant, bf16, a_mn, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }

@@ -30,6 +30,21 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c)
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// 16x16x32 MFMA on 16-bit operands, fp32 accumulate.  Operand lane l holds 8
+// consecutive K elements of row l % 16 (K group l / 16); the 16x16 result
+// sits in 4 registers per lane: register r of lane l is row 4*(l/16) + r of
+// the first operand's rows, column l % 16 of the second's.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Block-scaled 32x32x64 MFMA on OCP E4M3 operands (format code 0 for both).
 // Lane l holds K elements 16h..16h+15 and 32+16h..32+16h+15 (h = l / 32) of
 // row l % 32; the scale of K block h of that row is byte SEL of lane l's

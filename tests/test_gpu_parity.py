@@ -39,18 +39,32 @@ SMALL = {
     "e4m3-mx-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
                               b_dist=("normal", 1.0), name="e4m3-mx-beta"),
     "skinny": wl.custom(64, 2048, 1024, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02), name="skinny"),
+    "skinny-k4096": wl.custom(64, 1024, 4096, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                              name="skinny-k4096"),
+    "skinny-m32-beta": wl.custom(32, 1024, 2048, "f16", beta=1, name="skinny-m32-beta"),
 }
 
+# "plan": the library's own choice (no MSWZ_TILE override)
+TILES = ["plan", "256", "128", "64"]
 
-@pytest.mark.parametrize("tile", ["256", "128", "64"])
-@pytest.mark.parametrize("case", sorted(SMALL))
-def test_small_full_compare(case, tile, tile_env):
-    w = SMALL[case]
+
+def _set_tile(w, tile):
+    if tile == "plan":
+        os.environ.pop("MSWZ_TILE", None)
+        return
     if w.M % int(tile) or w.N % int(tile):
         pytest.skip("tile does not divide the shape")
     os.environ["MSWZ_TILE"] = tile
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_full_compare(case, tile, tile_env):
+    w = SMALL[case]
+    _set_tile(w, tile)
     plan = plan_for(w)
-    assert plan.describe()["tile_m"] == int(tile)
+    if tile != "plan":
+        assert plan.describe()["tile_m"] == int(tile)
     say(f"[parity] {case} tile={tile} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} beta={w.beta}")
     x = wl.generate(w, seed=0)
     got = run_gpu(w, x, plan)
@@ -58,7 +72,7 @@ def test_small_full_compare(case, tile, tile_env):
     print(case, tile, compare(w, got, ref, mag, x.get("D0")))
 
 
-@pytest.mark.parametrize("tile", ["256", "128", "64"])
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("case", sorted(SMALL))
 def test_quarter_integers_bit_exact(case, tile, tile_env):
     """Quarter-integer operands (the tcgen05.mma page's example distribution)
@@ -67,9 +81,7 @@ def test_quarter_integers_bit_exact(case, tile, tile_env):
     With beta = 1 the fp32 D0 is added last, so the result is the exact sum
     plus D0 rounded once to fp32."""
     w = SMALL[case]
-    if w.M % int(tile) or w.N % int(tile):
-        pytest.skip("tile does not divide the shape")
-    os.environ["MSWZ_TILE"] = tile
+    _set_tile(w, tile)
     say(f"[exact] {case} tile={tile}")
     x = wl.generate(w, seed=0, values="quarter")
     got = run_gpu(w, x, plan_for(w))
