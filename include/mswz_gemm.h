@@ -79,13 +79,13 @@ typedef struct gemm_plan gemm_plan;
  *   M, N, K       problem sizes, each > 0
  *   a_dt, b_dt    operand element formats; d_dt must be MSWZ_DT_F32.
  *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) block-scaled.
- *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (16-bit formats only for MN)
- *   b_major       MSWZ_MAJOR_K
+ *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
+ *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3
  * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3); M and N multiples
  * of 64 (M % 256 and N % 256 select the large square tile).  A 16-bit K-major
  * A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
- * weight-streaming kernel (M == 32 is accepted only there).
+ * weight-streaming kernel (M == 32 is accepted only there); it needs K-major B.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
  */
 int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,

@@ -112,12 +112,13 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_UNSUPPORTED;     // E4M3 is block-scaled only; 16-bit is dense only
     if (fp8 && scale_vec_len != 32)
         return MSWZ_ERR_UNSUPPORTED;
-    if (b_major != MSWZ_MAJOR_K || (fp8 && a_major != MSWZ_MAJOR_K))
-        return MSWZ_ERR_UNSUPPORTED;
+    if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
+        return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
     if (K % (fp8 ? 128 : 64) != 0)
         return MSWZ_ERR_UNSUPPORTED;
     // weight streaming: few rows of K-major 16-bit A against a large B
-    const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && (M == 64 || M == 32) && N % 64 == 0 &&
+    const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
+                        (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
     const int tile = skinny ? 64 : pick_tile(M, N);
     if (!tile)
@@ -142,10 +143,10 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     else
         p->variant = tile == 256 ? mswz::kVarDense256 : tile == 128 ? mswz::kVarDense128
                                                                      : mswz::kVarDense64;
-    p->group_m = 4;
+    p->group_m = -4;   // 2-D XCD regions, groups of 4 tile rows (device_common.hpp)
     if (const char *env = getenv("MSWZ_GROUP_M")) {   // tuning override
         const int g = atoi(env);
-        if (g >= 1 && g <= 64)
+        if ((g >= 1 && g <= 64) || (g <= -1 && g >= -64))
             p->group_m = g;
     }
     mswz::variant_info(p->variant, fp8, &p->info);
@@ -170,11 +171,12 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
         return MSWZ_ERR_ALIGN;
     mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                       p->group_m};
-    const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN;
+    const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN,
+               b_mn = p->b_major == MSWZ_MAJOR_MN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = p->variant == mswz::kVarDense256 ? mswz::launch_dense256(bf16, a_mn, a, st)
+    hipError_t e = p->variant == mswz::kVarDense256 ? mswz::launch_dense256(bf16, a_mn, b_mn, a, st)
                    : p->variant == mswz::kVarSkinny  ? mswz::launch_skinny(bf16, a, st)
-                                                     : mswz::launch_dense(p->variant, bf16, a_mn, a, st);
+                                                     : mswz::launch_dense(p->variant, bf16, a_mn, b_mn, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
 

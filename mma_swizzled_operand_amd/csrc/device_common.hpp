@@ -62,10 +62,30 @@ __device__ __forceinline__ f32x16 mfma_scale_32x32x64_e4m3(i32x8 a, i32x8 b, f32
 // contiguous run of ids, and ids are rastered in groups of `group_m` tile rows
 // (column by column inside a group) so that the workgroups resident on one XCD
 // at the same time share a few A row panels and B column panels.
+//
+// group_m < 0 selects a two-dimensional split instead: the tile grid is cut
+// into a 2 x 4 grid of regions (when both counts divide), XCD x takes region
+// (x / 4, x % 4), and inside a region tiles are rastered in groups of
+// -group_m tile rows.  Then each A row panel is fetched by 4 XCDs and each B
+// column panel by 2, instead of 1 and 8.
 __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int group_m,
                                               int &tm, int &tn)
 {
     const int T = tiles_m * tiles_n;
+    if (group_m < 0 && (tiles_m & 1) == 0 && (tiles_n & 3) == 0) {
+        const int rm = tiles_m >> 1, rn = tiles_n >> 2;   // region size in tiles
+        const int x = b & 7, t = b >> 3;                 // XCD, index inside its region
+        const int g = -group_m;
+        const int per_group = g * rn;
+        const int gi = t / per_group;
+        const int first = gi * g;
+        const int gm = min(rm - first, g);
+        const int r = t - gi * per_group;
+        tm = (x >> 2) * rm + first + r % gm;
+        tn = (x & 3) * rn + r / gm;
+        return;
+    }
+    group_m = group_m < 0 ? -group_m : group_m;
     int t = b;
     if ((T & 7) == 0)
         t = (b & 7) * (T >> 3) + (b >> 3);

@@ -13,18 +13,11 @@
 // contiguously, lane l at byte 16*l, i.e. eight 128-byte tile rows.  The
 // tile layout (layout.hpp) permutes 16-byte chunks inside a row, and the
 // permutation is its own inverse, so lane l simply fetches the source chunk
-// that belongs at its destination: chunk (l % 8) ^ key(row).  An MN-major A
-// ([K][M]) is read into registers as 8x8 blocks, transposed, and written with
-// 16-byte LDS stores into the same K-contiguous layout.  Scale bytes (MX) for
-// the step's 256 A rows and 256 B rows are copied into a small LDS stage by
-// direct 4-byte loads, one wave instruction per 64 rows.
-//
-// Latency.  LDS holds only two 64 KiB stages, so the copy of step k+1 (issued
-// when step k starts) must land within one step of MFMA work.  To keep it an
-// L2 hit, every step also touches one 4-byte word of each 128-byte line the
-// step after it will need (k+2), with a direct-to-LDS load into a throwaway
-// LDS sink; these touches are issued last and are the only loads allowed to
-// stay in flight across the end-of-step barrier.
+// that belongs at its destination: chunk (l % 8) ^ key(row).  An MN-major
+// operand ([K][M] or [K][N]) is read into registers as 8x8 blocks, transposed,
+// and written with 16-byte LDS stores into the same K-contiguous layout.
+// Scale bytes (MX) for the step's 256 A rows and 256 B rows are copied into a
+// small LDS stage by direct 4-byte loads, one wave instruction per 64 rows.
 //
 // Compute.  Wave w owns output rows 128*(w/4) .. +127 and columns 64*(w%4)
 // .. +63: 4 x 2 blocks of 32x32 MFMA output, 128 fp32 accumulators per lane.
@@ -118,16 +111,58 @@ struct RegOperand {
     }
 };
 
+// Register-staged copy of one MN-major 16-bit operand ([K][R] storage, R = M
+// or N) for a 256-row tile: block `blk` (0..255) is tile rows 8*(blk % 32)
+// .. +7 and K rows 8*(blk / 32) .. +7 of the step; the active thread loads
+// its eight 16-byte K-row pieces, transposes the 8x8 block in registers and
+// stores eight K-contiguous 16-byte chunks.
+struct MnOperand {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff, kstride, lds_base;
+    int mb, kc;
+    bool active;
+    u32x4 r[8];
+
+    __device__ void init(const uint8_t *X, int R, int row0, int K, int blk, bool act, uint32_t tile_off)
+    {
+        active = act;
+        mb = blk & 31;
+        kc = (blk >> 5) & 7;
+        kstride = uint32_t(R) * 2;
+        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * kstride - uint32_t(row0) * 2);
+        voff = uint32_t(8 * kc) * kstride + 16 * mb;
+        lds_base = tile_off;
+    }
+    __device__ void load(int kt)
+    {
+        if (active) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                r[j] = buffer_load16(rsrc, voff, (uint32_t(kt) * 64 + j) * kstride);
+        }
+    }
+    __device__ void store(uint8_t *stage) const
+    {
+        if (active) {
+            u32x4 t[8];
+            transpose8x8_b16(r, t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lds_write16(stage, lds_base + tile_offset(8 * mb + i, kc), t[i]);
+        }
+    }
+};
+
 // W waves per workgroup: W = 8 gives each wave a 128 x 64 output sub-tile
 // (two waves per SIMD), W = 4 a 128 x 128 sub-tile (one wave per SIMD,
 // accumulators in AGPRs, a third fewer LDS bytes read per MFMA).
-template <int KIND, bool A_MN, bool BETA, int W, bool TOUCH, int REG>
+template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
                float *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
 {
-    static_assert(!(A_MN && KIND == kE4m3), "MN-major A is built for 16-bit operands only");
+    static_assert(!((A_MN || B_MN) && KIND == kE4m3), "MN-major operands are built for 16-bit only");
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
@@ -139,7 +174,6 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[kMx ? kScaleStage : 4];
     __shared__ __attribute__((aligned(256))) uint8_t scl1[kMx ? kScaleStage : 4];
-    __shared__ __attribute__((aligned(256))) uint8_t sink[TOUCH ? W * 256 : 4];   // L2 touches land here
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,50 +187,27 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const int KT = K / kStepK;
 
     // ---- operand copies ---------------------------------------------------------
-    // REG bit 0: A staged through registers, bit 1: B staged through registers
-    // (K-major operands; otherwise copied straight into LDS)
-    constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) != 0;
-    DmaOperand<W> db;
-    db.init(B, n0, row_bytes, wave, lane, kATile);
-    DmaOperand<W> da;
-    if constexpr (!A_MN)
+    // K-major operands: copied straight into LDS, or through registers when
+    // REG bit 0 (A) / bit 1 (B) is set.  MN-major operands: 8x8 register
+    // transposes, A by threads 0..255 and B by threads 256..511 (eight waves)
+    // or both by every thread (four waves).
+    constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) && !B_MN;
+    constexpr bool kDmaA = !A_MN && !kRegA, kDmaB = !B_MN && !kRegB;
+    DmaOperand<W> da, db;
+    if constexpr (kDmaA)
         da.init(A, m0, row_bytes, wave, lane, 0);
+    if constexpr (kDmaB)
+        db.init(B, n0, row_bytes, wave, lane, kATile);
     RegOperand<W> rga, rgb;
     if constexpr (kRegA)
         rga.init(A, m0, row_bytes, tid, 0);
     if constexpr (kRegB)
         rgb.init(B, n0, row_bytes, tid, kATile);
-
-    // MN-major A ([K][M]): threads 0..255 each stage one 8x8 block:
-    // tile rows 8*mb .. +7 (M), K rows 8*kc .. +7 of the step, mb = tid % 32,
-    // kc = tid / 32.  Read through a buffer resource on columns m0.. of A.
-    const bool a_mn_active = tid < 256;
-    const uint32_t a_mn_row = uint32_t(M) * 2;
-    __amdgpu_buffer_rsrc_t ra_rsrc;
-    uint32_t ra_voff = 0;
-    u32x4 ra[A_MN ? 8 : 1];
-    if constexpr (A_MN) {
-        const int mb = tid & 31, kc = (tid >> 5) & 7;
-        ra_rsrc = make_rsrc(A + size_t(m0) * 2, uint32_t(K) * a_mn_row - uint32_t(m0) * 2);
-        ra_voff = uint32_t(8 * kc) * a_mn_row + 16 * mb;
-    }
-    auto a_mn_load = [&](int kt) {
-        if (a_mn_active) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                ra[j] = buffer_load16(ra_rsrc, ra_voff, (uint32_t(kt) * 64 + j) * a_mn_row);
-        }
-    };
-    auto a_mn_store = [&](uint8_t *stage) {
-        if (a_mn_active) {
-            const int mb = tid & 31, kc = (tid >> 5) & 7;
-            u32x4 t[8];
-            transpose8x8_b16(ra, t);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                lds_write16(stage, tile_offset(8 * mb + i, kc), t[i]);
-        }
-    };
+    MnOperand mna, mnb;
+    if constexpr (A_MN)
+        mna.init(A, M, m0, K, tid & 255, W == 4 || tid < 256, 0);
+    if constexpr (B_MN)
+        mnb.init(B, N, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
 
     // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
     // for g >= 4) is copied by wave g % W; lane l copies the step's 32-bit
@@ -215,35 +226,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         sf_voff = uint32_t(64 * (wave & 3) + lane) * sf_row;
     }
 
-    // ---- L2 touches for a future step: line index t = 64*w' + l over the
-    // step's 512 lines (w' = w + W*q): lines 0..255 are A rows (K-major) or,
-    // for an MN-major A, K row t/4 and 128-byte piece t%4 of the tile's
-    // 512-byte segment of that row; lines 256..511 are B rows.
-    constexpr int kTouch = TOUCH ? 8 / W : 0;
-    __amdgpu_buffer_rsrc_t pf_rsrc[kTouch > 0 ? kTouch : 1];
-    uint32_t pf_voff[kTouch > 0 ? kTouch : 1], pf_kstride[kTouch > 0 ? kTouch : 1];
-#pragma unroll
-    for (int q = 0; q < kTouch; ++q) {
-        const int g = wave + W * q;
-        const int idx = 64 * (g & 3) + lane;   // 0..255
-        if (g >= 4) {
-            pf_rsrc[q] = db.rsrc;
-            pf_voff[q] = uint32_t(idx) * row_bytes;
-            pf_kstride[q] = 128;
-        } else if constexpr (A_MN) {
-            pf_rsrc[q] = ra_rsrc;
-            pf_voff[q] = uint32_t(idx >> 2) * a_mn_row + 128 * (idx & 3);
-            pf_kstride[q] = 64 * a_mn_row;
-        } else {
-            pf_rsrc[q] = da.rsrc;
-            pf_voff[q] = uint32_t(idx) * row_bytes;
-            pf_kstride[q] = 128;
-        }
-    }
-
     auto store_regs = [&](uint8_t *stage) {
         if constexpr (A_MN)
-            a_mn_store(stage);
+            mna.store(stage);
+        if constexpr (B_MN)
+            mnb.store(stage);
         if constexpr (kRegA)
             rga.store(stage);
         if constexpr (kRegB)
@@ -252,30 +239,21 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
         if constexpr (A_MN)
-            a_mn_load(kt);
-        else if constexpr (kRegA)
+            mna.load(kt);
+        if constexpr (kRegA)
             rga.load(kt);
-        else
+        if constexpr (kDmaA)
             da.issue(stage, kt);
+        if constexpr (B_MN)
+            mnb.load(kt);
         if constexpr (kRegB)
             rgb.load(kt);
-        else
+        if constexpr (kDmaB)
             db.issue(stage, kt);
         if constexpr (kMx) {
 #pragma unroll
             for (int q = 0; q < kSfInstr; ++q)
                 buffer_load_lds4(sf_rsrc[q], sstage + 256 * (wave + W * q), sf_voff, 4u * kt);
-        }
-    };
-    // issued after issue_step; these are the only loads left in flight at the
-    // next end-of-step barrier
-    auto touch_step = [&](int kt) {
-        if constexpr (kTouch > 0) {
-            sched_fence();
-#pragma unroll
-            for (int q = 0; q < kTouch; ++q)
-                buffer_load_lds4(pf_rsrc[q], sink + 256 * wave, pf_voff[q], uint32_t(kt) * pf_kstride[q]);
-            sched_fence();
         }
     };
 
@@ -391,21 +369,18 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // compiler from draining the copies in flight at a control-flow merge. ------
     issue_step(lds0, scl0, 0);
     store_regs(lds0);
-    touch_step(min(1, KT - 1));
     __syncthreads();
 
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
         issue_step(lds1, scl1, kt + 1);
-        touch_step(min(kt + 2, KT - 1));
         compute(lds0, scl0);
         store_regs(lds1);
-        lds_barrier_keep_vm<kTouch>();
+        lds_barrier_keep_vm<0>();
         issue_step(lds0, scl0, min(kt + 2, KT - 1));
-        touch_step(min(kt + 3, KT - 1));
         compute(lds1, scl1);
         store_regs(lds0);
-        lds_barrier_keep_vm<kTouch>();
+        lds_barrier_keep_vm<0>();
     }
     if (kt < KT)
         compute(lds0, scl0);
@@ -430,7 +405,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
 }
 
-template <int KIND, bool A_MN, int W, bool TOUCH, int REG>
+template <int KIND, bool A_MN, bool B_MN, int W, int REG>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     const int tiles_m = a.M / kBM, tiles_n = a.N / kBN;
@@ -438,52 +413,57 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, true, W, TOUCH, REG>), dim3(blocks), dim3(64 * W),
-                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG>), dim3(blocks), dim3(64 * W), 0,
+                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, false, W, TOUCH, REG>), dim3(blocks), dim3(64 * W),
-                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG>), dim3(blocks), dim3(64 * W), 0,
+                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     return hipGetLastError();
 }
 
 // Pipeline configuration of the 256x256 tile, selected at run time by the
-// environment variable MSWZ_TILE256 (tuning only): bit 0 set = four waves
-// (else eight); bits 2..3 = operands staged through registers (bit 2: A,
-// bit 3: B).
+// environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
+// eight); 4 / 8 / 12 = K-major A / B / both staged through registers.
 int config256()
 {
     static int cfg = [] {
         const char *e = getenv("MSWZ_TILE256");
-        return e ? atoi(e) & 13 : 0;
+        return e ? atoi(e) : 0;
     }();
     return cfg;
 }
 
-template <int KIND, bool A_MN>
+template <int KIND, bool A_MN, bool B_MN>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
     switch (config256()) {
-    case 1: return launch_kind<KIND, A_MN, 4, false, 0>(a, stream);
-    case 4: return launch_kind<KIND, A_MN, 8, false, 1>(a, stream);
-    case 8: return launch_kind<KIND, A_MN, 8, false, 2>(a, stream);
-    case 12: return launch_kind<KIND, A_MN, 8, false, 3>(a, stream);
-    default: return launch_kind<KIND, A_MN, 8, false, 0>(a, stream);
+    case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);
+    case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);
+    case 8: return launch_kind<KIND, A_MN, B_MN, 8, 2>(a, stream);
+    case 12: return launch_kind<KIND, A_MN, B_MN, 8, 3>(a, stream);
+    default: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
     }
+}
+
+template <int KIND>
+hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stream)
+{
+    if (a_mn)
+        return b_mn ? launch_cfg<KIND, true, true>(a, stream) : launch_cfg<KIND, true, false>(a, stream);
+    return b_mn ? launch_cfg<KIND, false, true>(a, stream) : launch_cfg<KIND, false, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_dense256(bool bf16, bool a_mn, const DenseArgs &d, hipStream_t stream)
+hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m};
-    if (bf16)
-        return a_mn ? launch_cfg<kBf16, true>(a, stream) : launch_cfg<kBf16, false>(a, stream);
-    return a_mn ? launch_cfg<kF16, true>(a, stream) : launch_cfg<kF16, false>(a, stream);
+    return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
 }
 
 hipError_t launch_mx256(const MxArgs &a, hipStream_t stream)
 {
-    return launch_cfg<kE4m3, false>(a, stream);
+    return launch_cfg<kE4m3, false, false>(a, stream);
 }
 
 }  // namespace mswz

@@ -11,10 +11,10 @@
 //     16-byte global loads of step k+1 are in flight in registers and are
 //     written to the other stage afterwards; one barrier per step.
 //   * K-major operands are copied row by row (8 lanes cover one 128-byte row,
-//     so each wave-wide load reads eight whole rows).  An MN-major A ([K][M])
-//     is read as 8x8 blocks (eight 16-byte pieces of eight consecutive K
-//     rows), transposed in registers and written as K-contiguous tile rows, so
-//     the MFMA read path is the same for both majors.
+//     so each wave-wide load reads eight whole rows).  An MN-major operand
+//     ([K][M] or [K][N]) is read as 8x8 blocks (eight 16-byte pieces of eight
+//     consecutive K rows), transposed in registers and written as K-contiguous
+//     tile rows, so the MFMA read path is the same for both majors.
 //   * Each wave owns a WM x WN sub-tile made of 32x32 MFMA blocks.  The MFMA's
 //     first operand is the B fragment and its second the A fragment, which
 //     puts four consecutive N columns of one M row in four consecutive
@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int BM, int BN, int WM, int WN, bool BF16, bool A_MN, bool BETA>
+template <int BM, int BN, int WM, int WN, bool BF16, bool A_MN, bool B_MN, bool BETA>
 __global__ void __launch_bounds__(kThreads)
 gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, float *__restrict__ D,
               int M, int N, int K, int tiles_m, int tiles_n, int group_m)
@@ -39,8 +39,9 @@ gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, floa
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int kATile = BM * 128, kBTile = BN * 128, kStage = kATile + kBTile;
     constexpr int NA = A_MN ? 8 : BM / 32;   // 16-byte pieces of A per thread per step
-    constexpr int NB = BN / 32;              // 16-byte pieces of B per thread per step
+    constexpr int NB = B_MN ? 8 : BN / 32;   // 16-byte pieces of B per thread per step
     static_assert(!A_MN || BM <= kThreads, "one 8x8 block per thread at most");
+    static_assert(!B_MN || BN <= kThreads, "one 8x8 block per thread at most");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
 
@@ -55,11 +56,24 @@ gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, floa
     // ---- staging assignment (constant over the K loop) ----------------------
     const size_t row_bytes = size_t(K) * 2;   // one K-major row of A or B
     const int srow = tid >> 3, schunk = tid & 7;
-    const uint8_t *gb = B + size_t(n0 + srow) * row_bytes + schunk * 16;
+    const uint8_t *gb;
     uint32_t lb[NB];
+    bool b_active = true;
+    if constexpr (B_MN) {
+        // block (nb, kc): tile rows 8*nb .. 8*nb+7 (N), K rows 8*kc .. 8*kc+7
+        const int nb = tid % (BN / 8), kc = tid / (BN / 8);
+        b_active = tid < BN;
+        gb = B + (size_t(8 * kc) * N + n0 + 8 * nb) * 2;
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-        lb[i] = kATile + tile_offset(srow + 32 * i, schunk);
+        for (int i = 0; i < 8; ++i)
+            lb[i] = kATile + tile_offset(8 * nb + i, kc & 7);
+    } else {
+        gb = B + size_t(n0 + srow) * row_bytes + schunk * 16;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            lb[i] = kATile + tile_offset(srow + 32 * i, schunk);
+    }
+    const size_t b_mn_row = size_t(N) * 2;    // bytes between K rows of an MN-major B
 
     const uint8_t *ga;
     uint32_t la[A_MN ? 8 : NA];
@@ -94,9 +108,17 @@ gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, floa
             for (int i = 0; i < NA; ++i)
                 ra[i] = global_read16(ga + size_t(32 * i) * row_bytes + kb);
         }
+        if constexpr (B_MN) {
+            if (b_active) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            rb[i] = global_read16(gb + size_t(32 * i) * row_bytes + kb);
+                for (int j = 0; j < 8; ++j)
+                    rb[j] = global_read16(gb + (size_t(kt) * 64 + j) * b_mn_row);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                rb[i] = global_read16(gb + size_t(32 * i) * row_bytes + kb);
+        }
     };
     auto store_step = [&](int stage) {
         uint8_t *s = lds + stage * kStage;
@@ -113,9 +135,19 @@ gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, floa
             for (int i = 0; i < NA; ++i)
                 lds_write16(s, la[i], ra[i]);
         }
+        if constexpr (B_MN) {
+            if (b_active) {
+                u32x4 t[8];
+                transpose8x8_b16(rb, t);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            lds_write16(s, lb[i], rb[i]);
+                for (int i = 0; i < 8; ++i)
+                    lds_write16(s, lb[i], t[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                lds_write16(s, lb[i], rb[i]);
+        }
     };
 
     // ---- MFMA operand read offsets -------------------------------------------
@@ -198,7 +230,7 @@ gemm16_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, floa
         }
 }
 
-template <int BM, int BN, int WM, int WN, bool BF16, bool A_MN>
+template <int BM, int BN, int WM, int WN, bool BF16, bool A_MN, bool B_MN>
 hipError_t launch_one(const DenseArgs &a, hipStream_t stream)
 {
     const int tiles_m = a.M / BM, tiles_n = a.N / BN;
@@ -206,35 +238,43 @@ hipError_t launch_one(const DenseArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, BF16, A_MN, true>), dim3(blocks),
+        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, BF16, A_MN, B_MN, true>), dim3(blocks),
                            dim3(kThreads), 0, stream, A, B, a.D, a.M, a.N, a.K, tiles_m, tiles_n,
                            a.group_m);
     else
-        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, BF16, A_MN, false>), dim3(blocks),
+        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, BF16, A_MN, B_MN, false>), dim3(blocks),
                            dim3(kThreads), 0, stream, A, B, a.D, a.M, a.N, a.K, tiles_m, tiles_n,
                            a.group_m);
     return hipGetLastError();
 }
 
-template <bool BF16, bool A_MN>
+template <bool BF16, bool A_MN, bool B_MN>
 hipError_t launch_variant(int variant, const DenseArgs &a, hipStream_t stream)
 {
     switch (variant) {
-    case kVarDense128: return launch_one<128, 128, 64, 64, BF16, A_MN>(a, stream);
-    case kVarDense64: return launch_one<64, 64, 32, 32, BF16, A_MN>(a, stream);
+    case kVarDense128: return launch_one<128, 128, 64, 64, BF16, A_MN, B_MN>(a, stream);
+    case kVarDense64: return launch_one<64, 64, 32, 32, BF16, A_MN, B_MN>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
+template <bool BF16>
+hipError_t launch_majors(int variant, bool a_mn, bool b_mn, const DenseArgs &a, hipStream_t stream)
+{
+    if (a_mn)
+        return b_mn ? launch_variant<BF16, true, true>(variant, a, stream)
+                    : launch_variant<BF16, true, false>(variant, a, stream);
+    return b_mn ? launch_variant<BF16, false, true>(variant, a, stream)
+                : launch_variant<BF16, false, false>(variant, a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_dense(int variant, bool bf16, bool a_mn, const DenseArgs &args, hipStream_t stream)
+hipError_t launch_dense(int variant, bool bf16, bool a_mn, bool b_mn, const DenseArgs &args,
+                        hipStream_t stream)
 {
-    if (bf16)
-        return a_mn ? launch_variant<true, true>(variant, args, stream)
-                    : launch_variant<true, false>(variant, args, stream);
-    return a_mn ? launch_variant<false, true>(variant, args, stream)
-                : launch_variant<false, false>(variant, args, stream);
+    return bf16 ? launch_majors<true>(variant, a_mn, b_mn, args, stream)
+                : launch_majors<false>(variant, a_mn, b_mn, args, stream);
 }
 
 }  // namespace mswz

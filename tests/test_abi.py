@@ -84,7 +84,9 @@ K_, MN = 0, 1
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 0), -2),       # e4m3 needs scales
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 16), -2),      # only 32-element blocks
     ((256, 256, 64, F16, F16, F32, K_, K_, 32), -2),         # 16-bit is dense only
-    ((256, 256, 64, F16, F16, F32, K_, MN, 0), -2),          # B MN-major not built
+    ((256, 256, 64, F16, F16, F32, K_, MN, 0), 0),           # B MN-major (16-bit)
+    ((256, 256, 64, BF16, BF16, F32, MN, MN, 0), 0),         # both MN-major
+    ((256, 256, 128, E4M3, E4M3, F32, K_, MN, 32), -2),      # MN-major fp8 not built
     ((256, 256, 128, E4M3, E4M3, F32, MN, K_, 32), -2),      # MN-major fp8 not built
     ((256, 256, 96, F16, F16, F32, K_, K_, 0), -2),          # K not a multiple of 64
     ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 128

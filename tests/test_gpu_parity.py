@@ -38,6 +38,9 @@ SMALL = {
                          name="e4m3-mx"),
     "e4m3-mx-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
                               b_dist=("normal", 1.0), name="e4m3-mx-beta"),
+    "f16-bmn": wl.custom(512, 256, 192, "f16", b_major="mn", name="f16-bmn"),
+    "bf16-both-mn-beta": wl.custom(256, 512, 320, "bf16", a_major="mn", b_major="mn", beta=1,
+                                   a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bf16-both-mn-beta"),
     "skinny": wl.custom(64, 2048, 1024, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02), name="skinny"),
     "skinny-k4096": wl.custom(64, 1024, 4096, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
                               name="skinny-k4096"),
@@ -129,11 +132,17 @@ def test_deterministic_bits():
     assert np.array_equal(run_gpu(w, x), run_gpu(w, x))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b"])
+EXTRA_FULL = {
+    "bmn-4096": wl.custom(4096, 4096, 4096, "bf16", a_major="mn", b_major="mn",
+                          a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bmn-4096"),
+}
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b", "bmn-4096"])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""
-    w = wl.WORKLOADS[name]
+    w = wl.WORKLOADS[name] if name in wl.WORKLOADS else EXTRA_FULL[name]
     say(f"[full] {name}: {w.title}")
     x = wl.generate(w, seed=0)
     plan = plan_for(w)
