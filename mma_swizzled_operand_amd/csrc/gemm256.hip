@@ -421,9 +421,12 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+}  // namespace
+
 // Pipeline configuration of the 256x256 tile, selected at run time by the
 // environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
-// eight); 4 / 8 / 12 = K-major A / B / both staged through registers.
+// eight); 4 / 8 / 12 = K-major A / B / both staged through registers;
+// 16 = the ping-pong kernel for 16-bit K-major operands with K % 128 == 0.
 int config256()
 {
     static int cfg = [] {
@@ -432,6 +435,8 @@ int config256()
     }();
     return cfg;
 }
+
+namespace {
 
 template <int KIND, bool A_MN, bool B_MN>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
@@ -457,6 +462,8 @@ hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stre
 
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
+    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0)
+        return launch_dense256pp(bf16, d, stream);
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m};
     return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
 }
