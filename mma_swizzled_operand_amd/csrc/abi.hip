@@ -116,6 +116,12 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
     if (K % (fp8 ? 128 : 64) != 0)
         return MSWZ_ERR_UNSUPPORTED;
+    // MN-major operands are addressed with 32-bit offsets from the start of
+    // the [K][M] / [K][N] array
+    constexpr int64_t kMaxMnBytes = int64_t(1) << 32;
+    if ((a_major == MSWZ_MAJOR_MN && K * M * 2 >= kMaxMnBytes) ||
+        (b_major == MSWZ_MAJOR_MN && K * N * 2 >= kMaxMnBytes))
+        return MSWZ_ERR_UNSUPPORTED;
     // weight streaming: few rows of K-major 16-bit A against a large B
     const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
                         (M == 64 || M == 32) && N % 64 == 0 &&

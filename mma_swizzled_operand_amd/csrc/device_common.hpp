@@ -14,6 +14,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // 32x32x16 MFMA on 16-bit operands, fp32 accumulate.  Operand lane l holds
 // 8 consecutive K elements of row l % 32 (K half l / 32); both operands use
@@ -178,6 +180,18 @@ __device__ __forceinline__ void lds_write16(uint8_t *lds, uint32_t off, u32x4 v)
 {
     *reinterpret_cast<u32x4 *>(lds + off) = v;
 }
+// Transposing 8-byte LDS read of 16-bit values (ds_read_b64_tr_b16).  In
+// each group of 16 lanes, lanes 4j .. 4j+3 name four 8-byte pieces, i.e. 16
+// values v_j[0..15] in lane order; lane t of the group receives
+// (v_0[t], v_1[t], v_2[t], v_3[t]).  So four lanes per row pointing at 16
+// consecutive values of rows r0 .. r0+3 give lane t the column t of that 4x16
+// block.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t *lds, uint32_t off)
+{
+    auto *p = (__attribute__((address_space(3))) i16x4 *)(lds + off);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
+
 __device__ __forceinline__ u32x4 global_read16(const uint8_t *p)
 {
     return *reinterpret_cast<const u32x4 *>(p);

@@ -14,8 +14,10 @@
 // tile layout (layout.hpp) permutes 16-byte chunks inside a row, and the
 // permutation is its own inverse, so lane l simply fetches the source chunk
 // that belongs at its destination: chunk (l % 8) ^ key(row).  An MN-major
-// operand ([K][M] or [K][N]) is read into registers as 8x8 blocks, transposed,
-// and written with 16-byte LDS stores into the same K-contiguous layout.
+// operand ([K][M] or [K][N]) is copied the same way into an MN-major tile (64
+// K rows of 512 bytes, chunks XOR-permuted by K row) and its MFMA fragments
+// are read with gfx950's transposing LDS reads, which hand each lane one M
+// (or N) row with four consecutive K values.
 // Scale bytes (MX) for the step's 256 A rows and 256 B rows are copied into a
 // small LDS stage by direct 4-byte loads, one wave instruction per 64 rows.
 //
@@ -36,6 +38,8 @@ namespace {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kATile = kBM * 128, kBTile = kBN * 128, kStage = kATile + kBTile;
 constexpr int kScaleStage = (kBM + kBN) * 4;   // one 32-bit scale word per row
+
+constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
 
 enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2 };
 
@@ -110,6 +114,55 @@ struct RegOperand {
             lds_write16(stage, lds0 + i * 8 * W * kTileRowBytes, r[i]);
     }
 };
+
+// Direct-to-LDS copy of one MN-major 16-bit operand ([K][R] storage, R = M
+// or N) for a 256-wide tile.  The step's tile is 64 K rows of 512 bytes (256
+// values); 16-byte chunk c of K row k (values 8c .. 8c+7) sits at position
+// c ^ (4 * (k % 4)) of the row.  Wave instruction q = w + W*i fills K rows 2q
+// and 2q+1, lane l writing position l % 32 of row 2q + l/32, so it fetches
+// chunk (l % 32) ^ (4 * ((2w + l/32) % 4)): the key does not depend on i,
+// since 2W is a multiple of 4.  The fragments are read back with transposing
+// LDS reads (mn_frag_base below).
+template <int W>
+struct DmaMnOperand {
+    static constexpr int kInstr = 32 / W;
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff, pitch, lds_off;
+
+    __device__ void init(const uint8_t *X, int R, int row0, int K, int wave, int lane, uint32_t tile_off)
+    {
+        pitch = uint32_t(R) * 2;
+        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * pitch - uint32_t(row0) * 2);
+        const int kr = lane >> 5;
+        const int c = (lane & 31) ^ (4 * ((2 * wave + kr) & 3));
+        voff = uint32_t(2 * wave + kr) * pitch + 16 * c;
+        lds_off = tile_off + 2 * wave * kMnRowBytes;
+    }
+    __device__ void issue(uint8_t *stage, int kt) const
+    {
+#pragma unroll
+        for (int i = 0; i < kInstr; ++i)
+            buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, voff,
+                              (uint32_t(kt) * 64 + 2 * W * i) * pitch);
+    }
+};
+
+// LDS byte offset, at sub-step 0 and first half, of this lane's piece of the
+// 32-row MFMA fragment whose tile rows start at rbase (a multiple of 32) in an
+// MN-major tile.  The 32x32x16 operand wants, in lane l, row l % 32 and K
+// values 8*(l/32) .. +7.  With lane t = l % 16 = 4j + a of its group, the
+// lane points at K row 8*(l/32) + j, values rbase + 16*((l/16) % 2) + 4a ..
+// +3; the transposing read then hands lane l row rbase + l % 32 and K values
+// 8*(l/32) .. +3.  The second half (K + 4) is 4 rows further, sub-step ks
+// 16*ks rows further.  Within each half wave the 32 pieces cover 16 distinct
+// chunk positions of four K rows (k % 4 = j), so the read is free of bank
+// conflicts.
+__device__ __forceinline__ uint32_t mn_frag_base(uint32_t tile_off, int rbase, int lane)
+{
+    const int t = lane & 15, j = t >> 2, a = t & 3, g1 = (lane >> 4) & 1, h = lane >> 5;
+    const int chunk = rbase / 8 + 2 * g1 + (a >> 1);
+    return tile_off + uint32_t(8 * h + j) * kMnRowBytes + (uint32_t(chunk ^ (4 * j)) << 4) + 8 * (a & 1);
+}
 
 // Register-staged copy of one MN-major 16-bit operand ([K][R] storage, R = M
 // or N) for a 256-row tile: block `blk` (0..255) is tile rows 8*(blk % 32)
@@ -188,11 +241,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // ---- operand copies ---------------------------------------------------------
     // K-major operands: copied straight into LDS, or through registers when
-    // REG bit 0 (A) / bit 1 (B) is set.  MN-major operands: 8x8 register
-    // transposes, A by threads 0..255 and B by threads 256..511 (eight waves)
-    // or both by every thread (four waves).
+    // REG bit 0 (A) / bit 1 (B) is set.  MN-major operands: copied straight
+    // into an MN-major LDS tile and read with transposing LDS reads, or, when
+    // REG bit 2 is set, 8x8 register transposes into the K-contiguous layout
+    // (A by threads 0..255 and B by threads 256..511 with eight waves, both
+    // by every thread with four).
     constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) && !B_MN;
     constexpr bool kDmaA = !A_MN && !kRegA, kDmaB = !B_MN && !kRegB;
+    constexpr bool kMnReg = (REG & 4) != 0;
+    constexpr bool kTrA = A_MN && !kMnReg, kTrB = B_MN && !kMnReg;
     DmaOperand<W> da, db;
     if constexpr (kDmaA)
         da.init(A, m0, row_bytes, wave, lane, 0);
@@ -203,10 +260,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         rga.init(A, m0, row_bytes, tid, 0);
     if constexpr (kRegB)
         rgb.init(B, n0, row_bytes, tid, kATile);
+    DmaMnOperand<W> dma_mna, dma_mnb;
+    if constexpr (kTrA)
+        dma_mna.init(A, M, m0, K, wave, lane, 0);
+    if constexpr (kTrB)
+        dma_mnb.init(B, N, n0, K, wave, lane, kATile);
     MnOperand mna, mnb;
-    if constexpr (A_MN)
+    if constexpr (A_MN && kMnReg)
         mna.init(A, M, m0, K, tid & 255, W == 4 || tid < 256, 0);
-    if constexpr (B_MN)
+    if constexpr (B_MN && kMnReg)
         mnb.init(B, N, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
 
     // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
@@ -227,9 +289,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
 
     auto store_regs = [&](uint8_t *stage) {
-        if constexpr (A_MN)
+        if constexpr (A_MN && kMnReg)
             mna.store(stage);
-        if constexpr (B_MN)
+        if constexpr (B_MN && kMnReg)
             mnb.store(stage);
         if constexpr (kRegA)
             rga.store(stage);
@@ -238,14 +300,18 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     };
 
     auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
-        if constexpr (A_MN)
+        if constexpr (A_MN && kMnReg)
             mna.load(kt);
         if constexpr (kRegA)
             rga.load(kt);
         if constexpr (kDmaA)
             da.issue(stage, kt);
-        if constexpr (B_MN)
+        if constexpr (kTrA)
+            dma_mna.issue(stage, kt);
+        if constexpr (B_MN && kMnReg)
             mnb.load(kt);
+        if constexpr (kTrB)
+            dma_mnb.issue(stage, kt);
         if constexpr (kRegB)
             rgb.load(kt);
         if constexpr (kDmaB)
@@ -262,16 +328,20 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // row*128 + ((c ^ key(row)) << 4).  For sub-step ks the chunk is
     // 2ks ^ lh (16-bit) or 4ks ^ lh and 4ks ^ 2 ^ lh (8-bit), so every address
     // is one per-fragment base XOR a constant.
+    // In an MN-major tile read with transposing reads (kTrA / kTrB) the base
+    // is mn_frag_base and sub-step ks, half e sits (16ks + 4e) K rows further.
     uint32_t abase[TM], bbase[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const uint32_t row = wm + 32 * i + lr;
-        abase[i] = row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
+        abase[i] = kTrA ? mn_frag_base(0, wm + 32 * i, lane)
+                        : row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const uint32_t row = wn + 32 * j + lr;
-        bbase[j] = kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
+        bbase[j] = kTrB ? mn_frag_base(kATile, wn + 32 * j, lane)
+                        : kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
     }
 
     f32x16 acc[TN][TM];
@@ -290,13 +360,20 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < TN; ++j)
             bb[j] = opaque(bbase[j]);
         u32x4 af[2][TM], bf[2][TN];
+        auto frag = [&](uint32_t base, int ks, bool tr) {
+            if (!tr)
+                return lds_read16(s, base ^ (ks << 5));
+            const u32x2 lo = lds_read_tr16(s, base + uint32_t(16 * ks) * kMnRowBytes);
+            const u32x2 hi = lds_read_tr16(s, base + uint32_t(16 * ks + 4) * kMnRowBytes);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
         auto rd = [&](int ks, u32x4 *a, u32x4 *b) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                a[i] = lds_read16(s, ab[i] ^ (ks << 5));
+                a[i] = frag(ab[i], ks, kTrA);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                b[j] = lds_read16(s, bb[j] ^ (ks << 5));
+                b[j] = frag(bb[j], ks, kTrB);
         };
         rd(0, af[0], bf[0]);
 #pragma unroll
@@ -426,7 +503,8 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 // Pipeline configuration of the 256x256 tile, selected at run time by the
 // environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
 // eight); 4 / 8 / 12 = K-major A / B / both staged through registers;
-// 16 = the ping-pong kernel for 16-bit K-major operands with K % 128 == 0.
+// 16 = the ping-pong kernel for 16-bit K-major operands with K % 128 == 0;
+// 32 = MN-major operands through register transposes.
 int config256()
 {
     static int cfg = [] {
@@ -446,6 +524,7 @@ hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
     case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);
     case 8: return launch_kind<KIND, A_MN, B_MN, 8, 2>(a, stream);
     case 12: return launch_kind<KIND, A_MN, B_MN, 8, 3>(a, stream);
+    case 32: return launch_kind<KIND, A_MN, B_MN, 8, 4>(a, stream);
     default: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
     }
 }

@@ -93,6 +93,11 @@ K_, MN = 0, 1
     ((100, 256, 64, F16, F16, F32, K_, K_, 0), -2),          # ragged M
     ((256, 96, 64, F16, F16, F32, K_, K_, 0), -2),           # ragged N
     ((1 << 21, 64, 64, F16, F16, F32, K_, K_, 0), -1),       # beyond the size limit
+    # MN-major operands must span less than 4 GiB (32-bit offsets)
+    ((32768, 256, 65536, F16, F16, F32, MN, K_, 0), -2),     # A [K][M] is exactly 4 GiB
+    ((32512, 256, 65536, F16, F16, F32, MN, K_, 0), 0),      # just below
+    ((256, 65536, 65536, BF16, BF16, F32, K_, MN, 0), -2),   # B [K][N] is 8 GiB
+    ((65536, 65536, 65536, BF16, BF16, F32, K_, K_, 0), 0),  # K-major: no such limit
 ])
 def test_plan_create_rejections(args, expect):
     assert _create(*args) == expect
