@@ -22,7 +22,11 @@
 // small LDS stage by direct 4-byte loads, one wave instruction per 64 rows.
 //
 // Compute.  Wave w owns output rows 128*(w/4) .. +127 and columns 64*(w%4)
-// .. +63: 4 x 2 blocks of 32x32 MFMA output, 128 fp32 accumulators per lane.
+// .. +63, 128 fp32 accumulators per lane: 8 x 4 blocks of 16x16x32 MFMA
+// output for 16-bit operands (4 x 2 blocks of 32x32x16 when both are
+// MN-major), 4 x 2 blocks of the 32x32x64 block-scaled MFMA for E4M3.  The
+// 16x16 shape moves fewer register bytes per flop than the 32x32 one; under
+// the chip's power limit it runs at a higher clock and is faster overall.
 // The MFMA's first operand is the B fragment and its second the A fragment,
 // so four consecutive accumulator registers hold four consecutive N columns
 // of one M row and the epilogue stores 16 bytes per lane.
@@ -118,31 +122,35 @@ struct RegOperand {
 // Direct-to-LDS copy of one MN-major 16-bit operand ([K][R] storage, R = M
 // or N) for a 256-wide tile.  The step's tile is 64 K rows of 512 bytes (256
 // values); 16-byte chunk c of K row k (values 8c .. 8c+7) sits at position
-// c ^ (4 * (k % 4)) of the row.  Wave instruction q = w + W*i fills K rows 2q
-// and 2q+1, lane l writing position l % 32 of row 2q + l/32, so it fetches
-// chunk (l % 32) ^ (4 * ((2w + l/32) % 4)): the key does not depend on i,
-// since 2W is a multiple of 4.  The fragments are read back with transposing
-// LDS reads (mn_frag_base below).
+// c ^ mn_key(k) of the row, mn_key(k) = 4 * (k % 4) ^ 2 * ((k / 16) % 2).
+// Wave instruction q = w + W*i fills K rows 2q and 2q+1, lane l writing
+// position l % 32 of row k = 2q + l/32, so it fetches chunk
+// (l % 32) ^ mn_key(k).  Since 2w + l/32 < 2W and 2W*i is a multiple of 2W,
+// k % 4 comes from the lane and wave only and bit 4 of k from i only.  The
+// fragments are read back with transposing LDS reads (mn_frag_base below).
 template <int W>
 struct DmaMnOperand {
     static constexpr int kInstr = 32 / W;
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff, pitch, lds_off;
+    uint32_t voff[2], pitch, lds_off;   // voff[bit 4 of the instruction's K rows]
 
     __device__ void init(const uint8_t *X, int R, int row0, int K, int wave, int lane, uint32_t tile_off)
     {
         pitch = uint32_t(R) * 2;
         rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * pitch - uint32_t(row0) * 2);
         const int kr = lane >> 5;
-        const int c = (lane & 31) ^ (4 * ((2 * wave + kr) & 3));
-        voff = uint32_t(2 * wave + kr) * pitch + 16 * c;
+#pragma unroll
+        for (int b4 = 0; b4 < 2; ++b4) {
+            const int c = (lane & 31) ^ (4 * ((2 * wave + kr) & 3)) ^ (2 * b4);
+            voff[b4] = uint32_t(2 * wave + kr) * pitch + 16 * c;
+        }
         lds_off = tile_off + 2 * wave * kMnRowBytes;
     }
     __device__ void issue(uint8_t *stage, int kt) const
     {
 #pragma unroll
         for (int i = 0; i < kInstr; ++i)
-            buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, voff,
+            buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, voff[((2 * W * i) >> 4) & 1],
                               (uint32_t(kt) * 64 + 2 * W * i) * pitch);
     }
 };
@@ -154,14 +162,35 @@ struct DmaMnOperand {
 // lane points at K row 8*(l/32) + j, values rbase + 16*((l/16) % 2) + 4a ..
 // +3; the transposing read then hands lane l row rbase + l % 32 and K values
 // 8*(l/32) .. +3.  The second half (K + 4) is 4 rows further, sub-step ks
-// 16*ks rows further.  Within each half wave the 32 pieces cover 16 distinct
-// chunk positions of four K rows (k % 4 = j), so the read is free of bank
-// conflicts.
+// 16*ks rows further and, as bit 4 of its K rows is ks % 2, with its chunk
+// XOR 2 (byte offset XOR 32) for odd ks.  Within each half wave the 32
+// pieces cover 16 distinct chunk positions of four K rows (k % 4 = j), so the
+// read is free of bank conflicts.
 __device__ __forceinline__ uint32_t mn_frag_base(uint32_t tile_off, int rbase, int lane)
 {
     const int t = lane & 15, j = t >> 2, a = t & 3, g1 = (lane >> 4) & 1, h = lane >> 5;
     const int chunk = rbase / 8 + 2 * g1 + (a >> 1);
     return tile_off + uint32_t(8 * h + j) * kMnRowBytes + (uint32_t(chunk ^ (4 * j)) << 4) + 8 * (a & 1);
+}
+
+// K-block order of the 16x16x32 fragments.  Lane group g = l/16 of that
+// MFMA supplies 8 K values of its row; group g takes the 8-value block
+// kblk16(g) = 2*(g%2) + g/2 of the 32-wide sub-step, the same for A and B, so
+// the sum over K is unchanged.  With the natural order, 16-byte reads of
+// K-major tiles by lanes 8p .. 8p+7 and 32+8p .. 32+8p+7 (served together)
+// would hit the same banks; with this order the two chunks differ in their
+// lowest bit and never do.
+__device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
+
+// The same for the 16-row fragment of the 16x16x32 MFMA in an MN-major tile:
+// lane t = l % 16 = 4j + a of group g points at K row 8*kblk16(g) + j (bit 4
+// of which is g % 2), values rbase + 4a .. +3; the second half is 4 K rows
+// further, sub-step s 32*s rows further.
+__device__ __forceinline__ uint32_t mn_frag_base16(uint32_t tile_off, int rbase, int lane)
+{
+    const int t = lane & 15, j = t >> 2, a = t & 3, g = lane >> 4;
+    const int chunk = (rbase / 8 + (a >> 1)) ^ (4 * j) ^ (2 * (g & 1));
+    return tile_off + uint32_t(8 * kblk16(g) + j) * kMnRowBytes + (uint32_t(chunk) << 4) + 8 * (a & 1);
 }
 
 // Register-staged copy of one MN-major 16-bit operand ([K][R] storage, R = M
@@ -344,12 +373,43 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                         : kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
     }
 
-    f32x16 acc[TN][TM];
+    // 16x16x32 MFMA (REG bit 3, 16-bit only): the same wave tile as 2TM x 2TN
+    // blocks of 16 x 16; fragment rows l % 16, 16-byte chunk 4s + kblk16(l/16)
+    // for the 32-wide sub-step s, i.e. base XOR (s << 6).
+    constexpr bool kMf16 = (REG & 8) != 0 && !kMx;
+    constexpr int TM16 = kMf16 ? 2 * TM : 1, TN16 = kMf16 ? 2 * TN : 1;
+    uint32_t abase16[TM16], bbase16[TN16];
+    if constexpr (kMf16) {
+        const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+        for (int i = 0; i < TM16; ++i) {
+            const uint32_t row = wm + 16 * i + r16;
+            abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
+                              : row * kTileRowBytes + ((kblk16(g) ^ tile_key(row)) << 4);
+        }
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            acc[j][i] = f32x16{};
+        for (int j = 0; j < TN16; ++j) {
+            const uint32_t row = wn + 16 * j + r16;
+            bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
+                              : kATile + row * kTileRowBytes + ((kblk16(g) ^ tile_key(row)) << 4);
+        }
+    }
+
+    f32x16 acc[kMf16 ? 1 : TN][kMf16 ? 1 : TM];
+    f32x4 acc4[TN16][TM16];
+    if constexpr (kMf16) {
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+#pragma unroll
+            for (int i = 0; i < TM16; ++i)
+                acc4[j][i] = f32x4{};
+    } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[j][i] = f32x16{};
+    }
 
     auto compute16 = [&](const uint8_t *s) {
         uint32_t ab[TM], bb[TN];
@@ -363,8 +423,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         auto frag = [&](uint32_t base, int ks, bool tr) {
             if (!tr)
                 return lds_read16(s, base ^ (ks << 5));
-            const u32x2 lo = lds_read_tr16(s, base + uint32_t(16 * ks) * kMnRowBytes);
-            const u32x2 hi = lds_read_tr16(s, base + uint32_t(16 * ks + 4) * kMnRowBytes);
+            const uint32_t b = base ^ ((ks & 1) << 5);
+            const u32x2 lo = lds_read_tr16(s, b + uint32_t(16 * ks) * kMnRowBytes);
+            const u32x2 hi = lds_read_tr16(s, b + uint32_t(16 * ks + 4) * kMnRowBytes);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
         auto rd = [&](int ks, u32x4 *a, u32x4 *b) {
@@ -432,9 +493,43 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
+    auto compute16x16 = [&](const uint8_t *s) {
+        uint32_t ab[TM16], bb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            ab[i] = opaque(abase16[i]);
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bb[j] = opaque(bbase16[j]);
+        auto frag = [&](uint32_t base, int ks, bool tr) {
+            if (!tr)
+                return lds_read16(s, base ^ (ks << 6));
+            const u32x2 lo = lds_read_tr16(s, base + uint32_t(32 * ks) * kMnRowBytes);
+            const u32x2 hi = lds_read_tr16(s, base + uint32_t(32 * ks + 4) * kMnRowBytes);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 af[TM16], bf[TN16];
+#pragma unroll
+            for (int i = 0; i < TM16; ++i)
+                af[i] = frag(ab[i], ks, kTrA);
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+                bf[j] = frag(bb[j], ks, kTrB);
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+#pragma unroll
+                for (int i = 0; i < TM16; ++i)
+                    acc4[j][i] = mfma_16x16x32<KIND == kBf16>(bf[j], af[i], acc4[j][i]);
+        }
+    };
+
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kMx)
             compute_mx(s, ss);
+        else if constexpr (kMf16)
+            compute16x16(s);
         else
             compute16(s);
     };
@@ -464,6 +559,22 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     __syncthreads();   // no copy may still be writing LDS when the workgroup ends
 
     // ---- epilogue -------------------------------------------------------------
+    if constexpr (kMf16) {
+        // 16x16 block (j, i): lane l holds row 16i + l % 16, columns 16j + 4(l/16) .. +3
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+#pragma unroll
+            for (int i = 0; i < TM16; ++i) {
+                const size_t m = size_t(m0 + wm + 16 * i + (lane & 15));
+                const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+                f32x4 v = acc4[j][i];
+                f32x4 *p = reinterpret_cast<f32x4 *>(D + m * N + n);
+                if constexpr (BETA)
+                    v += *p;
+                *p = v;
+            }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -504,7 +615,8 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 // environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
 // eight); 4 / 8 / 12 = K-major A / B / both staged through registers;
 // 16 = the ping-pong kernel for 16-bit K-major operands with K % 128 == 0;
-// 32 = MN-major operands through register transposes.
+// 32 = MN-major operands through register transposes; 64 = 16x16x32 MFMAs
+// in every case; 128 = 32x32x16 MFMAs in every case.
 int config256()
 {
     static int cfg = [] {
@@ -525,7 +637,11 @@ hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
     case 8: return launch_kind<KIND, A_MN, B_MN, 8, 2>(a, stream);
     case 12: return launch_kind<KIND, A_MN, B_MN, 8, 3>(a, stream);
     case 32: return launch_kind<KIND, A_MN, B_MN, 8, 4>(a, stream);
-    default: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
+    case 64: return launch_kind<KIND, A_MN, B_MN, 8, 8>(a, stream);
+    case 128: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
+    // 16x16x32 MFMAs for 16-bit operands, except with both operands MN-major,
+    // where they would need more than 256 VGPRs
+    default: return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
     }
 }
 
