@@ -58,6 +58,16 @@ __device__ __forceinline__ f32x16 mfma_scale_32x32x64_e4m3(i32x8 a, i32x8 b, f32
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, scale_a, SEL, scale_b);
 }
 
+// Block-scaled 16x16x128 MFMA, E4M3 operands, scale byte 0 of each scale
+// register.  Lane l holds 32 bytes of row l % 16: bytes 0..15 lie in 32-wide
+// scale block (l/16)/2 and bytes 16..31 in block 2 + (l/16)/2, and lane
+// i + 16b supplies row i's scale for block b.
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c, int scale_a,
+                                                           int scale_b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
 // Workgroup -> output tile.  The hardware hands consecutive workgroups to the
 // eight XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has its own
 // L2.  Tile ids are therefore re-ordered so that each XCD receives one

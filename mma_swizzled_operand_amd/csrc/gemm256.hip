@@ -182,6 +182,28 @@ __device__ __forceinline__ uint32_t mn_frag_base(uint32_t tile_off, int rbase, i
 // lowest bit and never do.
 __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 
+// First-half chunk of lane group g for the block-scaled 16x16x128 MFMA
+// (second half: chunk + 4).  The chunk must lie in scale block g/2, i.e. be
+// 2*(g/2) or 2*(g/2) + 1, so groups 0 and 1 (and 2 and 3) read chunks that
+// differ only in their lowest bit, whose LDS positions collide for rows r and
+// r + 8 of the tile.  E4M3 fragments therefore take their 16 rows from two
+// runs of 8 rows 16 apart (row16 below), and groups g and g + 2 take chunks
+// of different parity.  Measured bank-conflict counts of the patterns used
+// here fit a 16-byte read that serves together the 16 lanes agreeing in lane
+// bits 1 and 5; these choices are conflict-free under that grouping and under
+// the grouping by lane bits 3 and 4.
+__device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
+
+// Tile row (relative to the wave's first row) of row x (0..15) of 16-row
+// fragment block b: 16-bit operands use 16 consecutive rows; E4M3 operands
+// rows 32*(b/2) + 8*(b%2) + {0..7, 16..23}.  Runs of 4 consecutive x stay
+// consecutive rows, so the epilogue still stores 16 bytes per lane.
+template <bool MX>
+__device__ __forceinline__ int row16(int b, int x)
+{
+    return MX ? 32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3) : 16 * b + x;
+}
+
 // The same for the 16-row fragment of the 16x16x32 MFMA in an MN-major tile:
 // lane t = l % 16 = 4j + a of group g points at K row 8*kblk16(g) + j (bit 4
 // of which is g % 2), values rbase + 4a .. +3; the second half is 4 K rows
@@ -373,25 +395,28 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                         : kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
     }
 
-    // 16x16x32 MFMA (REG bit 3, 16-bit only): the same wave tile as 2TM x 2TN
-    // blocks of 16 x 16; fragment rows l % 16, 16-byte chunk 4s + kblk16(l/16)
-    // for the 32-wide sub-step s, i.e. base XOR (s << 6).
-    constexpr bool kMf16 = (REG & 8) != 0 && !kMx;
+    // 16x16 MFMAs (REG bit 3): the same wave tile as 2TM x 2TN blocks of
+    // 16 x 16.  16-bit: fragment rows l % 16, 16-byte chunk 4s + kblk16(l/16)
+    // for the 32-wide sub-step s, i.e. base XOR (s << 6).  E4M3: one 16x16x128
+    // MFMA per K step, chunks mx_chunk16(l/16) and that + 4 (base XOR 64).
+    constexpr bool kMf16 = (REG & 8) != 0;
     constexpr int TM16 = kMf16 ? 2 * TM : 1, TN16 = kMf16 ? 2 * TN : 1;
     uint32_t abase16[TM16], bbase16[TN16];
     if constexpr (kMf16) {
         const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < TM16; ++i) {
-            const uint32_t row = wm + 16 * i + r16;
+            const uint32_t row = wm + row16<kMx>(i, r16);
+            const int c = kMx ? mx_chunk16(g) : kblk16(g);
             abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
-                              : row * kTileRowBytes + ((kblk16(g) ^ tile_key(row)) << 4);
+                              : row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < TN16; ++j) {
-            const uint32_t row = wn + 16 * j + r16;
+            const uint32_t row = wn + row16<kMx>(j, r16);
+            const int c = kMx ? mx_chunk16(g) : kblk16(g);
             bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
-                              : kATile + row * kTileRowBytes + ((kblk16(g) ^ tile_key(row)) << 4);
+                              : kATile + row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
     }
 
@@ -525,8 +550,46 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
+    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss) {
+        uint32_t ab[TM16], bb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            ab[i] = opaque(abase16[i]);
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bb[j] = opaque(bbase16[j]);
+        // lane l supplies the scale of K block l/16 of row l % 16: byte l/16 of
+        // the row's scale word
+        const int r16 = lane & 15, sh = 8 * (lane >> 4);
+        uint32_t sa[TM16], sb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t *>(ss + 4 * (wm + row16<true>(i, r16))) >> sh;
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            sb[j] = *reinterpret_cast<const uint32_t *>(ss + kBM * 4 + 4 * (wn + row16<true>(j, r16))) >> sh;
+        auto frag = [&](uint32_t base) {
+            const u32x4 lo = lds_read16(s, base);
+            const u32x4 hi = lds_read16(s, base ^ 64u);
+            return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        i32x8 bf[TN16];
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bf[j] = frag(bb[j]);
+#pragma unroll
+        for (int i = 0; i < TM16; ++i) {
+            const i32x8 af = frag(ab[i]);
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+                acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af, acc4[j][i], sb[j], sa[i]);
+        }
+    };
+
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
-        if constexpr (kMx)
+        if constexpr (kMx && kMf16)
+            compute_mx16(s, ss);
+        else if constexpr (kMx)
             compute_mx(s, ss);
         else if constexpr (kMf16)
             compute16x16(s);
@@ -560,13 +623,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // ---- epilogue -------------------------------------------------------------
     if constexpr (kMf16) {
-        // 16x16 block (j, i): lane l holds row 16i + l % 16, columns 16j + 4(l/16) .. +3
+        // 16x16 block (j, i): lane l holds fragment row l % 16 of A block i
+        // and fragment rows 4(l/16) .. +3 of B block j
 #pragma unroll
         for (int j = 0; j < TN16; ++j)
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
-                const size_t m = size_t(m0 + wm + 16 * i + (lane & 15));
-                const int n = n0 + wn + 16 * j + 4 * (lane >> 4);
+                const size_t m = size_t(m0 + wm + row16<kMx>(i, lane & 15));
+                const int n = n0 + wn + row16<kMx>(j, 4 * (lane >> 4));
                 f32x4 v = acc4[j][i];
                 f32x4 *p = reinterpret_cast<f32x4 *>(D + m * N + n);
                 if constexpr (BETA)
