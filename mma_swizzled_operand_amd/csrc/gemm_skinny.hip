@@ -89,13 +89,23 @@ gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // blocks is even (K % 1024 == 0 is required by the plan); the final pair
     // re-loads the last block into a buffer that is not used again, so the
     // loop body has no branches
+    // The fences keep each buffer's 16 loads together and in this order, so
+    // the wait before computing on one buffer leaves the other buffer's loads
+    // in flight (without them the compiler interleaves the two buffers' loads
+    // and has to wait for all of them).
     load(0, 0);
+    sched_fence();
     load(1, min(1, blocks - 1));
+    sched_fence();
     for (int b = 0; b < blocks; b += 2) {
         compute(0);
+        sched_fence();
         load(0, min(b + 2, blocks - 1));
+        sched_fence();
         compute(1);
+        sched_fence();
         load(1, min(b + 3, blocks - 1));
+        sched_fence();
     }
 
     // ---- reduce the eight K-slice partials through LDS ---------------------------
