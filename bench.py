@@ -90,21 +90,23 @@ def setup(w, seed=0):
 
 
 def time_steps(step, steps, warmup):
+    """Wall time of `steps` launches, and their mean duration from two HIP
+    events on the launch stream bracketing the timed region (events between
+    launches would each add a few microseconds of idle GPU time)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(steps):
+    ev0.record(stream)
+    for _ in range(steps):
         step()
-        ev[i + 1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]   # ms, on the launch stream
-    return wall, sum(per) / len(per), min(per)
+    return wall, ev0.elapsed_time(ev1) / steps
 
 
 def measure(name, steps, warmup):
@@ -113,7 +115,7 @@ def measure(name, steps, warmup):
     log(f"{name}: generating inputs ({w.title})")
     x, plan, step = setup(w)
     log(f"{name}: plan {plan.describe()}; timing {steps} steps after {warmup} warm-up")
-    wall, avg_ms, min_ms = time_steps(step, steps, warmup)
+    wall, avg_ms = time_steps(step, steps, warmup)
     r = {
         "workload": w,
         "inputs": x,
@@ -121,7 +123,6 @@ def measure(name, steps, warmup):
         "wall_s": wall,
         "ms_per_step": wall / steps * 1e3,
         "kernel_avg_ms": avg_ms,
-        "kernel_min_ms": min_ms,
         "tflops": w.flops / (wall / steps) / 1e12,
         "kernel_tflops": w.flops / (avg_ms * 1e-3) / 1e12,
         "kernel_gbs": w.algorithmic_bytes() / (avg_ms * 1e-3) / 1e9,
@@ -189,7 +190,7 @@ def main():
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").random_(0, 255)
         dst = torch.empty_like(src)
-        wall, avg_ms, _ = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        wall, avg_ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps,
                           "avg_ms": round(avg_ms, 5),
                           "GB/s": round(2 * args.copy_bytes / (avg_ms * 1e-3) / 1e9, 1)}), flush=True)
@@ -246,6 +247,7 @@ def main():
                    "scale_vec_len": w.V, "tile": head["plan"], "frac_mfma_peak":
                    round(head["kernel_tflops"] / MFMA_PEAK[w.kind], 4)},
         "roofline": roofline,
+        "kernel_avg_us": round(head["kernel_avg_ms"] * 1e3, 2),
         "cpu_baseline": cpu,
         "also": also,
         "kernel_source_hash": kernel_source_hash(),

@@ -132,13 +132,21 @@ def test_deterministic_bits():
     assert np.array_equal(run_gpu(w, x), run_gpu(w, x))
 
 
+# the remaining dense operand layouts at full size (fp16 K-major, bf16 with
+# MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
     "bmn-4096": wl.custom(4096, 4096, 4096, "bf16", a_major="mn", b_major="mn",
                           a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bmn-4096"),
+    "f16-k-8192": wl.custom(8192, 8192, 8192, "f16", name="f16-k-8192"),
+    "bf16-amn-8192": wl.custom(8192, 8192, 8192, "bf16", a_major="mn",
+                               a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bf16-amn-8192"),
+    "f16-bmn-4096": wl.custom(4096, 4096, 4096, "f16", b_major="mn", name="f16-bmn-4096"),
+    "bf16-both-mn-beta-4096": wl.custom(4096, 4096, 4096, "bf16", a_major="mn", b_major="mn", beta=1,
+                                        name="bf16-both-mn-beta-4096"),
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b", "bmn-4096"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b", *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""
