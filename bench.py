@@ -83,6 +83,13 @@ def setup(w, seed=0):
 
         def step():
             mswz.gemm_run_blockscaled(plan, A, B, SFA, SFB, D, w.beta)
+    elif plan.workspace_bytes() > 0:
+        # weight streaming with K split over workgroups: the library's
+        # workspace path (zero-filled once; every call leaves it so)
+        ws = torch.zeros(plan.workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+        def step():
+            mswz.gemm_run_ws(plan, A, B, D, ws, w.beta)
     else:
         def step():
             mswz.gemm_run(plan, A, B, D, w.beta)

@@ -28,9 +28,9 @@
  *
  * Ownership: the caller owns every device buffer and the stream.  A plan holds
  * host metadata only and is immutable once created, so one plan may be used
- * from several host threads and streams at once.  gemm_run* enqueue one kernel
- * on `stream` and return; they allocate nothing, do not synchronise and keep
- * no pointer.  Buffers must stay alive until the stream has passed the kernel
+ * from several host threads and streams at once.  gemm_run* enqueue their
+ * kernels on `stream` (one; two for gemm_run_ws's split path) and return; they
+ * allocate nothing, do not synchronise and keep no pointer.  Buffers must stay alive until the stream has passed the kernel
  * (the pages' rule of keeping allocations alive until consumers complete).
  * Scales are prepared by the caller in the layout above; supplying them does
  * not change the plan.
@@ -100,6 +100,39 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,
  */
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *D,
              int beta, void *stream);
+
+/*
+ * Device workspace, in bytes, that gemm_run_ws can use for this plan: > 0 for
+ * weight-streaming plans (the skinny kernel above) with M == 64, N % 256 == 0
+ * and K a multiple of 512 (K split into S parts, each a multiple of 256: the
+ * smallest power of two up to 16 giving N/256 * S >= 256 workgroups, else the
+ * largest that fits); 0 otherwise.
+ * MSWZ_ERR_INVALID for a NULL plan.
+ */
+int64_t gemm_plan_workspace_size(const gemm_plan *plan);
+
+/*
+ * gemm_run with a caller-provided device workspace (tcgen05.mma page,
+ * "Weight-stationary and block scaling": the weight-streaming workload).  For
+ * a plan with gemm_plan_workspace_size(plan) > 0 it splits K over S
+ * workgroups per 256 output columns, each storing an fp32 partial in the
+ * workspace, and enqueues a second kernel that sums the S partials of every
+ * output in a fixed order and applies beta; results are bit-identical run to
+ * run (not necessarily to gemm_run's, whose summation order differs).  For
+ * other plans it is gemm_run and ignores the workspace.
+ *   workspace        device pointer, 16-byte aligned, at least
+ *                    gemm_plan_workspace_size(plan) bytes; the caller owns it.
+ *                    Its first 256 * ceil(N/256 * 4 / 256) bytes are counters
+ *                    for the in-kernel reduction (selectable for tuning); they
+ *                    must be zero before the first call (fill the whole
+ *                    workspace with zero bytes once) and every call leaves
+ *                    them zero again.  Two calls that may run at the same time
+ *                    must not share a workspace.
+ *   workspace_bytes  its size.
+ * Returns as gemm_run; MSWZ_ERR_INVALID also for a NULL or too small workspace.
+ */
+int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *D,
+                int beta, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Enqueue the block-scaled product for a plan created with scale_vec_len > 0.

@@ -61,6 +61,10 @@ def load():
         h.gemm_plan_create.restype = c_int
         h.gemm_run.argtypes = [vp, vp, vp, vp, c_int, vp]
         h.gemm_run.restype = c_int
+        h.gemm_plan_workspace_size.argtypes = [vp]
+        h.gemm_plan_workspace_size.restype = i64
+        h.gemm_run_ws.argtypes = [vp, vp, vp, vp, c_int, vp, i64, vp]
+        h.gemm_run_ws.restype = c_int
         h.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, c_int, vp]
         h.gemm_run_blockscaled.restype = c_int
         h.gemm_plan_destroy.argtypes = [vp]
@@ -151,6 +155,13 @@ class Plan:
         v = self.scale_vec_len
         return (self.M * (self.K // v), self.N * (self.K // v)) if v else (0, 0)
 
+    def workspace_bytes(self) -> int:
+        """Device workspace gemm_run_ws can use for this plan (0: none)."""
+        n = int(load().gemm_plan_workspace_size(self.handle))
+        if n < 0:
+            raise MswzError(n, "gemm_plan_workspace_size")
+        return n
+
 
 def _name(table, code):
     for k, v in table.items():
@@ -206,6 +217,29 @@ def gemm_run(plan: Plan, A, B, D, beta: int = 0, stream=None) -> None:
     rc = load().gemm_run(plan.handle, a, b, d, int(beta), _stream_ptr(stream))
     if rc != 0:
         raise MswzError(rc, "gemm_run")
+
+
+def gemm_run_ws(plan: Plan, A, B, D, workspace, beta: int = 0, stream=None) -> None:
+    """gemm_run with a device workspace (a contiguous GPU tensor of at least
+    ``plan.workspace_bytes()`` bytes, zero-filled before its first use; every
+    call leaves its counters zero again).  Plans without a workspace path run
+    as gemm_run."""
+    a = _dev_ptr(A, plan.a_bytes(), "A")
+    b = _dev_ptr(B, plan.b_bytes(), "B")
+    d = _dev_ptr(D, plan.d_bytes(), "D")
+    need = plan.workspace_bytes()
+    if isinstance(workspace, int):
+        w, wb = workspace, need
+    else:
+        import torch
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace: expected a contiguous GPU tensor")
+        w, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if wb < need:
+            raise ValueError(f"workspace: holds {wb} bytes, the plan needs {need}")
+    rc = load().gemm_run_ws(plan.handle, a, b, d, int(beta), w, int(wb), _stream_ptr(stream))
+    if rc != 0:
+        raise MswzError(rc, "gemm_run_ws")
 
 
 def gemm_run_blockscaled(plan: Plan, A, B, SFA, SFB, D, beta: int = 0, stream=None) -> None:

@@ -26,6 +26,8 @@ struct gemm_plan {
     int group_m;
     mswz::VariantInfo info;
     int64_t blocks;
+    int split_parts;        // K parts of the split weight-streaming kernel (0: none)
+    int64_t ws_bytes;       // workspace gemm_run_ws needs for it
 };
 
 namespace mswz {
@@ -161,8 +163,17 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         p->info.lds_bytes = 8 * int(M) * 68 * 4;
     }
     p->blocks = (M / p->info.tile_m) * (N / p->info.tile_n);
+    if (skinny) {
+        p->split_parts = mswz::skinny_split_parts(M, N, K);
+        p->ws_bytes = p->split_parts ? mswz::skinny_split_workspace_bytes(M, N, p->split_parts) : 0;
+    }
     *out = p;
     return MSWZ_OK;
+}
+
+int64_t gemm_plan_workspace_size(const gemm_plan *p)
+{
+    return p ? p->ws_bytes : int64_t(MSWZ_ERR_INVALID);
 }
 
 int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta, void *stream)
@@ -183,6 +194,24 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
     hipError_t e = p->variant == mswz::kVarDense256 ? mswz::launch_dense256(bf16, a_mn, b_mn, a, st)
                    : p->variant == mswz::kVarSkinny  ? mswz::launch_skinny(bf16, a, st)
                                                      : mswz::launch_dense(p->variant, bf16, a_mn, b_mn, a, st);
+    return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
+}
+
+int gemm_run_ws(const gemm_plan *p, const void *A, const void *B, void *D, int beta, void *workspace,
+                int64_t workspace_bytes, void *stream)
+{
+    if (!p || p->ws_bytes == 0)
+        return gemm_run(p, A, B, D, beta, stream);
+    if (!A || !B || !D || !workspace || workspace_bytes < p->ws_bytes)
+        return MSWZ_ERR_INVALID;
+    if (beta != 0 && beta != 1)
+        return MSWZ_ERR_INVALID;
+    if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D) || !is_aligned16(workspace))
+        return MSWZ_ERR_ALIGN;
+    mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
+                      p->group_m};
+    const hipError_t e = mswz::launch_skinny_split(p->a_dt == MSWZ_DT_BF16, a, workspace,
+                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
 

@@ -1,0 +1,329 @@
+// gemm_skinny_sk.hip — weight-streaming GEMM with K split over workgroups:
+//     D[64][N] = beta*D + A[64][K] . B[N][K]^T,  fp16 / bf16, K-major A and B
+// (tcgen05.mma page, "Operands and repeat axes"; the weight-stationary
+// workload of "Weight-stationary and block scaling").
+//
+// Why split K.  With 64 columns per workgroup (gemm_skinny.hip) every
+// workgroup reads all of A (64 x K) for 64 x K of B: half of the bytes its
+// loads move are A re-reads from L2, and those, not HBM, bound the kernel.  A
+// workgroup here owns 256 columns and 1/S of K, so it reads 256 rows of B
+// against 64 rows of A, and the N/256 x S workgroups still cover the chip.
+//
+// Workgroup (512 threads, 8 waves): column block cb (256 columns of D), K part
+// `part`.  Every wave takes 32 of the 256 columns (two 16-row blocks of B) and
+// all waves walk the part's 64-element K blocks together:
+//   * A's K block (64 rows x 128 bytes) is copied global -> LDS with direct
+//     16-byte buffer-to-LDS loads, one instruction per wave, into a ring of
+//     kSlots stages (layout.hpp tile layout), kAhead = kSlots - 1 blocks
+//     ahead; one barrier per block makes each stage visible and frees the
+//     oldest one.  The stages are distinct LDS arrays and the K loop is
+//     unrolled kSlots times, so the compiler sees which stage each copy
+//     writes and never waits for copies into other stages before a read;
+//   * B's fragments go straight from global memory into registers in the
+//     16x16x32 operand form, kAhead blocks ahead (no LDS);
+//   * the K order inside a 32-wide sub-step is kblk16 (gemm256.hip), the same
+//     for A and B, so the LDS fragment reads are free of bank conflicts.
+//
+// Reduction (deterministic, no waiting), two ways:
+//   * default: each workgroup stores its 64 x 256 fp32 partial into the
+//     caller's workspace; a second kernel (splitk_reduce_kernel) sums the S
+//     partials of every output in part order 0 .. S-1 and adds beta*D;
+//   * inline (selectable): after storing its partial, each workgroup
+//     increments its column block's counter (agent-scope release); the one
+//     that sees the count S-1 is the last: it acquires, sums the S partials
+//     in part order (its own from registers), adds beta*D, writes D and
+//     resets the counter, so the counters are zero again after every call.
+// Both give the same bits.  All workgroups finish streaming at about the same
+// time, so the inline reduction's store acknowledgements, L2 write-backs,
+// atomic round trip and partial reads form an exposed tail of ~16 us on
+// 64 x 16384 x 8192, against ~6 us for the second kernel (including its
+// launch): the second kernel is the default.
+#include <hip/hip_runtime.h>
+#include <stdlib.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mswz {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kBM = 64;            // rows of A (and of D)
+constexpr int kBN = 256;           // columns of D per workgroup
+constexpr int kSlots = 4;          // A stages and B register slots
+constexpr int kAhead = kSlots - 1; // K blocks in flight ahead of the one computed
+constexpr int kStageBytes = kBM * 128;
+
+__device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
+
+// INLINE: reduce inside the kernel (counters, last workgroup); otherwise only
+// store the partials, which splitk_reduce_kernel then sums.
+template <bool BF16, bool BETA, bool INLINE>
+__global__ void __launch_bounds__(kThreads)
+gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, float *__restrict__ D,
+                      float *__restrict__ part_ws, uint32_t *__restrict__ counters, int N, int K, int S)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
+    __shared__ uint32_t last_flag;
+    static_assert(kSlots == 4, "one named LDS array per stage");
+    auto stage = [&](int u) { return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_cb = N / kBN;
+    // consecutive workgroups take consecutive column blocks, so the S parts of
+    // a column block run on the same XCD (workgroup b runs on XCD b % 8)
+    const int cb = blockIdx.x % n_cb, part = blockIdx.x / n_cb;
+    const int n0 = cb * kBN;
+    const uint32_t row_bytes = uint32_t(K) * 2;
+    const int T = K / 64 / S;          // K blocks of this part (a multiple of kSlots)
+    const int kb0 = part * T;
+
+    // ---- A: direct copy of one K block per step, wave w fills tile rows 8w .. 8w+7
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(kBM) * row_bytes);
+    const int arow = 8 * wave + (lane >> 3);
+    const uint32_t a_voff = uint32_t(arow) * row_bytes + 16u * uint32_t((lane & 7) ^ tile_key(arow));
+    auto issue_a = [&](int slot, int t) {
+        buffer_load_lds16(ra, stage(slot) + wave * 1024, a_voff, uint32_t(kb0 + t) * 128);
+    };
+
+    // ---- B: wave w owns rows 32w .. 32w+31 of the workgroup's 256; lane
+    // (r, g) = (l % 16, l / 16) loads row r of a 16-row block, K chunk
+    // 4s + kblk16(g) of sub-step s
+    const int r16 = lane & 15, g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + size_t(n0) * row_bytes, uint32_t(kBN) * row_bytes);
+    const uint32_t b_voff = uint32_t(32 * wave + r16) * row_bytes + 16u * uint32_t(kblk16(g));
+    u32x4 bf[kSlots][2][2];   // [slot][16-row block][sub-step]
+    auto issue_b = [&](int slot, int t) {
+        const uint32_t k_off = uint32_t(kb0 + t) * 128;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                bf[slot][jb][s] = buffer_load16(rb, b_voff + 64 * s, k_off + uint32_t(16 * jb) * row_bytes);
+    };
+
+    // A fragment bases: 16-row block i, lane row 16i + r16, chunk kblk16(g)
+    uint32_t abase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * i + r16;
+        abase[i] = uint32_t(row) * kTileRowBytes + (uint32_t(kblk16(g) ^ tile_key(row)) << 4);
+    }
+
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[jb][i] = f32x4{};
+
+    // prologue: blocks 0 .. kAhead-1 into slots 0 .. kAhead-1
+#pragma unroll
+    for (int t = 0; t < kAhead; ++t) {
+        issue_b(t, t);
+        issue_a(t, t);
+        sched_fence();
+    }
+
+    // Step t uses slot t % kSlots.  Wait until this wave's B loads and A copy
+    // of block t have landed (the kAhead-1 younger steps' 5 operations each
+    // may stay in flight), barrier (every wave's copy of block t is in LDS,
+    // and every wave has finished reading slot (t-1) % kSlots, which the next
+    // copy overwrites), MFMAs, then the loads of block t + kAhead into that
+    // slot, clamped to the last block so that the loop has no branches (the
+    // repeated loads are never used).
+    for (int t0 = 0; t0 < T; t0 += kSlots) {
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u) {
+            const int t = t0 + u;
+            lds_barrier_keep_vm<(kAhead - 1) * 5>();
+            sched_fence();
+            const uint8_t *st = stage(u);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 af[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = lds_read16(st, opaque(abase[i]) ^ uint32_t(s << 6));
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[jb][i] = mfma_16x16x32<BF16>(bf[u][jb][s], af[i], acc[jb][i]);
+            }
+            sched_fence();
+            const int tn = min(t + kAhead, T - 1);
+            issue_b((u + kAhead) % kSlots, tn);
+            issue_a((u + kAhead) % kSlots, tn);
+            sched_fence();
+        }
+    }
+    // no copy may still be writing LDS when the workgroup ends
+    lds_barrier_keep_vm<0>();
+
+    // ---- partial -> workspace; lane holds row 16i + r16, columns 32w + 16jb + 4g .. +3
+    const size_t MN = size_t(kBM) * N;
+    float *mine = part_ws + size_t(part) * MN;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
+            *reinterpret_cast<f32x4 *>(mine + idx) = acc[jb][i];
+        }
+    if constexpr (!INLINE)
+        return;
+    // every wave's stores are complete before the barrier; thread 0's
+    // agent-scope release then publishes them with the count.  Only the last
+    // workgroup acquires: an acquire invalidates the XCD's L2, which would
+    // cost the workgroups still streaming their cached A and half-read B lines.
+    lds_barrier_keep_vm<0>();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&counters[cb], 1u, __ATOMIC_RELEASE,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == uint32_t(S - 1);
+    }
+    __syncthreads();
+    if (!last_flag)
+        return;
+
+    // ---- last workgroup of the column block: fixed-order sum of the S partials
+    // (part by part, the eight loads of one part in flight together)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    f32x4 sum[2][4];
+    for (int p = 0; p < S; ++p) {
+        f32x4 v[2][4];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
+                v[jb][i] = p == part ? acc[jb][i]
+                                     : *reinterpret_cast<const f32x4 *>(part_ws + size_t(p) * MN + idx);
+            }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sum[jb][i] = p == 0 ? v[jb][i] : sum[jb][i] + v[jb][i];
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
+            f32x4 *dp = reinterpret_cast<f32x4 *>(D + idx);
+            f32x4 out = sum[jb][i];
+            if constexpr (BETA)
+                out += *dp;
+            *dp = out;
+        }
+    if (tid == 0)
+        __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Second pass of the two-kernel reduction: D = sum_p partial[p] (+ D), the S
+// partials added in part order, one 16-byte group of outputs per thread.
+template <bool BETA>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float *__restrict__ part_ws, float *__restrict__ D, int64_t n4, int S)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4)
+        return;
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(part_ws) + i;
+    f32x4 sum = p[0];
+    for (int s = 1; s < S; ++s)
+        sum += p[int64_t(s) * n4];
+    f32x4 *d = reinterpret_cast<f32x4 *>(D) + i;
+    if constexpr (BETA)
+        sum += *d;
+    *d = sum;
+}
+
+// Reduction mode, selected at run time by the environment variable
+// MSWZ_SPLITK_REDUCE (tuning only): "inline" = in the streaming kernel
+// (counters), anything else = a second kernel.
+bool reduce_inline()
+{
+    static const bool v = [] {
+        const char *e = getenv("MSWZ_SPLITK_REDUCE");
+        return e && e[0] == 'i';
+    }();
+    return v;
+}
+
+template <bool BF16, bool BETA>
+hipError_t launch_bb(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
+{
+    const uint8_t *A = static_cast<const uint8_t *>(a.A);
+    const uint8_t *B = static_cast<const uint8_t *>(a.B);
+    const dim3 grid(a.N / kBN * sk.parts);
+    if (reduce_inline()) {
+        hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, true>), grid, dim3(kThreads), 0, stream, A, B,
+                           a.D, sk.partials, sk.counters, a.N, a.K, sk.parts);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, false>), grid, dim3(kThreads), 0, stream, A, B, a.D,
+                       sk.partials, sk.counters, a.N, a.K, sk.parts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t n4 = int64_t(a.M) * a.N / 4;
+    hipLaunchKernelGGL((splitk_reduce_kernel<BETA>), dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream,
+                       sk.partials, a.D, n4, sk.parts);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_bf(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
+{
+    return a.beta ? launch_bb<BF16, true>(a, sk, stream) : launch_bb<BF16, false>(a, sk, stream);
+}
+
+}  // namespace
+
+// K parts: the smallest power of two up to 16 that gives at least 256
+// workgroups, else the largest one that fits K; each part must hold a
+// multiple of kSlots 64-element K blocks.
+int skinny_split_parts(int64_t M, int64_t N, int64_t K)
+{
+    if (M != kBM || N % kBN != 0)
+        return 0;
+    const int64_t n_cb = N / kBN;
+    int best = 0;
+    for (int s = 2; s <= 16; s *= 2) {
+        if (K % (int64_t(64) * kSlots * s) != 0)
+            continue;
+        best = s;
+        if (n_cb * s >= 256)
+            break;
+    }
+    return best;
+}
+
+int64_t skinny_split_workspace_bytes(int64_t M, int64_t N, int parts)
+{
+    // counters (one per 256-column block) first, padded to 256 bytes, then the partials
+    const int64_t counter_bytes = ((N / kBN) * 4 + 255) / 256 * 256;
+    return counter_bytes + int64_t(parts) * M * N * 4;
+}
+
+hipError_t launch_skinny_split(bool bf16, const DenseArgs &a, void *workspace, hipStream_t stream)
+{
+    SplitK sk;
+    sk.parts = skinny_split_parts(a.M, a.N, a.K);
+    if (!sk.parts)
+        return hipErrorInvalidValue;
+    const int64_t counter_bytes = ((a.N / kBN) * 4 + 255) / 256 * 256;
+    sk.counters = static_cast<uint32_t *>(workspace);
+    sk.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + counter_bytes);
+    return bf16 ? launch_bf<true>(a, sk, stream) : launch_bf<false>(a, sk, stream);
+}
+
+}  // namespace mswz

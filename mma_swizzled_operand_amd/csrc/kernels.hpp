@@ -53,4 +53,16 @@ int config256();
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);
 hipError_t launch_skinny(bool bf16, const DenseArgs &args, hipStream_t stream);
 
+// Weight streaming with K split over workgroups (gemm_skinny_sk.hip): the
+// number of K parts for an (M, N, K) problem (0 when the split kernel does not
+// apply), the workspace it needs, and the launch on a caller's workspace.
+struct SplitK {
+    int parts;
+    uint32_t *counters;   // one per 256-column block, zero between calls
+    float *partials;      // parts x M x N fp32
+};
+int skinny_split_parts(int64_t M, int64_t N, int64_t K);
+int64_t skinny_split_workspace_bytes(int64_t M, int64_t N, int parts);
+hipError_t launch_skinny_split(bool bf16, const DenseArgs &args, void *workspace, hipStream_t stream);
+
 }  // namespace mswz

@@ -39,8 +39,9 @@ def plan_for(w: wl.Workload) -> mswz.Plan:
     return mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, "f32", w.a_major, w.b_major, w.V)
 
 
-def run_gpu(w: wl.Workload, x: dict, plan=None, D_init=None) -> np.ndarray:
-    """One library call on fresh device copies; returns D as fp32 numpy."""
+def run_gpu(w: wl.Workload, x: dict, plan=None, D_init=None, workspace=None) -> np.ndarray:
+    """One library call on fresh device copies; returns D as fp32 numpy.  With
+    a workspace tensor the call goes through gemm_run_ws."""
     plan = plan or plan_for(w)
     A, B = to_device(x["A"]), to_device(x["B"])
     if w.beta:
@@ -51,10 +52,19 @@ def run_gpu(w: wl.Workload, x: dict, plan=None, D_init=None) -> np.ndarray:
         D = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
     if w.V:
         mswz.gemm_run_blockscaled(plan, A, B, to_device(x["SFA"]), to_device(x["SFB"]), D, w.beta)
+    elif workspace is not None:
+        mswz.gemm_run_ws(plan, A, B, D, workspace, w.beta)
     else:
         mswz.gemm_run(plan, A, B, D, w.beta)
     torch.cuda.synchronize()
     return D.cpu().numpy()
+
+
+def zero_workspace(plan):
+    """A zero-filled device workspace of the size the plan asks for."""
+    n = plan.workspace_bytes()
+    assert n > 0, "plan has no workspace path"
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
 
 
 def reference(w: wl.Workload, x: dict, rows=None, cols=None, with_mag=True):

@@ -136,6 +136,34 @@ def test_run_rejections_before_gpu_work():
     assert lib.gemm_run_blockscaled(mx.handle, P, P, P, P, P, -1, None) == -1
 
 
+def test_workspace_size_query():
+    lib = mswz.load()
+    assert lib.gemm_plan_workspace_size(None) == -1
+    # weight streaming 64 x 16384 x 8192: 64 column blocks x 4 K parts; 256 bytes
+    # of counters, then 4 fp32 partials of 64 x 16384
+    assert mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16").workspace_bytes() == 256 + 4 * 64 * 16384 * 4
+    assert mswz.gemm_plan_create(64, 2048, 4096, "f16", "f16").workspace_bytes() == 256 + 16 * 64 * 2048 * 4
+    assert mswz.gemm_plan_create(32, 16384, 8192, "bf16", "bf16").workspace_bytes() == 0   # M = 32
+    assert mswz.gemm_plan_create(4096, 4096, 4096, "bf16", "bf16").workspace_bytes() == 0
+    assert mswz.gemm_plan_create(256, 256, 128, "e4m3", "e4m3", scale_vec_len=32).workspace_bytes() == 0
+
+
+def test_run_ws_rejections_before_gpu_work():
+    lib = mswz.load()
+    sk = mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16")
+    need = sk.workspace_bytes()
+    P = 0x10000
+    assert lib.gemm_run_ws(sk.handle, P, P, P, 0, None, need, None) == -1          # no workspace
+    assert lib.gemm_run_ws(sk.handle, P, P, P, 0, P, need - 1, None) == -1         # too small
+    assert lib.gemm_run_ws(sk.handle, P, P, P, 2, P, need, None) == -1             # beta
+    assert lib.gemm_run_ws(sk.handle, P, P, P, 0, P + 8, need, None) == -3         # misaligned
+    assert lib.gemm_run_ws(sk.handle, None, P, P, 0, P, need, None) == -1
+    # a plan without a workspace path runs as gemm_run (same checks)
+    dense = mswz.gemm_plan_create(256, 256, 64, "f16", "f16")
+    assert lib.gemm_run_ws(dense.handle, P + 8, P, P, 0, None, 0, None) == -3
+    assert lib.gemm_run_ws(None, P, P, P, 0, P, need, None) == -1
+
+
 def test_binding_checks_buffer_sizes_before_the_library():
     import torch
     plan = mswz.gemm_plan_create(256, 256, 64, "f16", "f16")
