@@ -82,8 +82,11 @@ typedef struct gemm_plan gemm_plan;
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3
- * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3); M and N multiples
- * of 64 (M % 256 and N % 256 select the large square tile).  A 16-bit K-major
+ * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3).  M and N
+ * multiples of 64 choose among 256, 128 and 64 square tiles; otherwise (tails)
+ * the 256 tile is used with masked stores, and N % 4 == 0 is required (16-byte
+ * rows of D), as well as M % 8 == 0 for MN-major A and N % 8 == 0 for MN-major
+ * B.  MN-major operands must be smaller than 4 GiB.  A 16-bit K-major
  * A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
  * weight-streaming kernel (M == 32 is accepted only there); it needs K-major B.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
@@ -167,6 +170,15 @@ int gemm_plan_describe(const gemm_plan *plan, int64_t *info, int n);
  * mswz_tile_offset is the byte offset of 16-byte chunk `chunk` (0..7) of row
  * `row` in the kernels' LDS operand tile (128-byte rows).
  */
+/*
+ * The kernels' workgroup -> output tile map (XCD-aware raster): tile
+ * (tile_m, tile_n) of a tiles_m x tiles_n grid computed by workgroup `block`
+ * for the raster parameter group_m (the value gemm_plan_describe reports).
+ * Returns MSWZ_OK, or MSWZ_ERR_INVALID for arguments outside the grid.
+ */
+int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m,
+                       int *tile_m, int *tile_n);
+
 int64_t mswz_desc_address(int64_t r, int64_t w, int64_t ldo, int64_t sdo,
                           int mode, int major, int64_t origin);
 int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin);

@@ -15,6 +15,7 @@
 #include <new>
 
 #include "../../include/mswz_gemm.h"
+#include "device_common.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -118,6 +119,12 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
     if (K % (fp8 ? 128 : 64) != 0)
         return MSWZ_ERR_UNSUPPORTED;
+    // M or N not a multiple of 64: the 256x256 tile with masked stores; D rows
+    // (and MN-major operand rows) must keep 16-byte alignment
+    const bool tail = M % 64 != 0 || N % 64 != 0;
+    if (tail && (N % 4 != 0 || (a_major == MSWZ_MAJOR_MN && M % 8 != 0) ||
+                 (b_major == MSWZ_MAJOR_MN && N % 8 != 0)))
+        return MSWZ_ERR_UNSUPPORTED;
     // MN-major operands are addressed with 32-bit offsets from the start of
     // the [K][M] / [K][N] array
     constexpr int64_t kMaxMnBytes = int64_t(1) << 32;
@@ -128,7 +135,7 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
                         (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : pick_tile(M, N);
+    const int tile = skinny ? 64 : tail ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -162,7 +169,7 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         p->info.tile_m = int(M);
         p->info.lds_bytes = 8 * int(M) * 68 * 4;
     }
-    p->blocks = (M / p->info.tile_m) * (N / p->info.tile_n);
+    p->blocks = ((M + p->info.tile_m - 1) / p->info.tile_m) * ((N + p->info.tile_n - 1) / p->info.tile_n);
     if (skinny) {
         p->split_parts = mswz::skinny_split_parts(M, N, K);
         p->ws_bytes = p->split_parts ? mswz::skinny_split_workspace_bytes(M, N, p->split_parts) : 0;
@@ -274,5 +281,14 @@ int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin)
 }
 
 uint32_t mswz_tile_offset(uint32_t row, uint32_t chunk) { return mswz::tile_offset(row, chunk); }
+
+int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m, int *tile_m, int *tile_n)
+{
+    if (!tile_m || !tile_n || tiles_m <= 0 || tiles_n <= 0 || block < 0 || block >= tiles_m * tiles_n ||
+        group_m == 0 || group_m > 64 || group_m < -64)
+        return MSWZ_ERR_INVALID;
+    mswz::tile_of_block(block, tiles_m, tiles_n, group_m, *tile_m, *tile_n);
+    return MSWZ_OK;
+}
 
 }  // extern "C"

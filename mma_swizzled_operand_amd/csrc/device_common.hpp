@@ -80,8 +80,8 @@ __device__ __forceinline__ f32x4 mfma_scale_16x16x128_e4m3(i32x8 a, i32x8 b, f32
 // (x / 4, x % 4), and inside a region tiles are rastered in groups of
 // -group_m tile rows.  Then each A row panel is fetched by 4 XCDs and each B
 // column panel by 2, instead of 1 and 8.
-__device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int group_m,
-                                              int &tm, int &tn)
+__host__ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, int group_m,
+                                                       int &tm, int &tn)
 {
     const int T = tiles_m * tiles_n;
     if (group_m < 0 && (tiles_m & 1) == 0 && (tiles_n & 3) == 0) {
@@ -91,7 +91,7 @@ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, i
         const int per_group = g * rn;
         const int gi = t / per_group;
         const int first = gi * g;
-        const int gm = min(rm - first, g);
+        const int gm = rm - first < g ? rm - first : g;
         const int r = t - gi * per_group;
         tm = (x >> 2) * rm + first + r % gm;
         tn = (x & 3) * rn + r / gm;
@@ -104,7 +104,7 @@ __device__ __forceinline__ void tile_of_block(int b, int tiles_m, int tiles_n, i
     const int per_group = group_m * tiles_n;
     const int g = t / per_group;
     const int first_m = g * group_m;
-    const int gm = min(tiles_m - first_m, group_m);
+    const int gm = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
     const int r = t - g * per_group;
     tm = first_m + r % gm;
     tn = r / gm;

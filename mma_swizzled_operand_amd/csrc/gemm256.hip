@@ -51,26 +51,29 @@ enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2 };
 // step) through a buffer resource on the workgroup's 256-row panel.  With W
 // waves, wave w copies rows 8*(w + W*i) .. +7 for i = 0 .. 32/W - 1; lane l
 // takes row 8*(w + W*i) + l/8, whose layout key is (l/8) ^ ((w + W*i) % 8), so
-// it fetches chunk (l % 8) ^ (l/8) ^ ((w + W*i) % 8).  For W = 8 the key does
-// not depend on i; for W = 4 it alternates between two values with i.
+// it fetches chunk (l % 8) ^ (l/8) ^ ((w + W*i) % 8).
+//
+// The row is part of the per-lane offset, which the buffer's range check
+// covers (the scalar offset, here only the K step, is not checked), so in a
+// tail panel the rows beyond the operand read as zeros and no address beyond
+// the operand is formed.
 template <int W>
 struct DmaOperand {
     static constexpr int kInstr = 32 / W;
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[2];    // this lane's byte offset in the panel at K step 0, for even / odd i
-    uint32_t row_bytes;
-    uint32_t lds_off;    // LDS offset of this wave's first destination row inside a stage
+    uint32_t voff[kInstr];   // this lane's byte offset in the panel at K step 0, per instruction
+    uint32_t lds_off;        // LDS offset of this wave's first destination row inside a stage
 
-    __device__ void init(const uint8_t *X, int row0, uint32_t rb, int wave, int lane,
+    // rows: rows of the panel inside the operand (fewer than 256 in a tail panel)
+    __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int wave, int lane,
                          uint32_t tile_off)
     {
-        row_bytes = rb;
-        rsrc = make_rsrc(X + size_t(row0) * rb, 256u * rb);
-        const int r = 8 * wave + (lane >> 3);
+        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
 #pragma unroll
-        for (int odd = 0; odd < 2; ++odd) {
-            const int chunk = (lane & 7) ^ (((lane >> 3) ^ (wave + W * odd)) & 7);
-            voff[odd] = uint32_t(r) * rb + chunk * 16;
+        for (int i = 0; i < kInstr; ++i) {
+            const int r = 8 * (wave + W * i) + (lane >> 3);
+            const int chunk = (lane & 7) ^ (((lane >> 3) ^ (wave + W * i)) & 7);
+            voff[i] = uint32_t(r) * rb + chunk * 16;
         }
         lds_off = tile_off + 8 * wave * kTileRowBytes;
     }
@@ -79,37 +82,39 @@ struct DmaOperand {
     {
 #pragma unroll
         for (int i = 0; i < kInstr; ++i)
-            buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i & 1],
-                              uint32_t(8 * W * i) * row_bytes + uint32_t(kt) * 128);
+            buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i], uint32_t(kt) * 128);
     }
 };
 
-// Register-staged copy of one K-major operand tile: the 64*W threads each
-// load 2048/(64*W) 16-byte chunks per step into registers (thread t: row
-// t/8 + (8W/8)*8*i... i.e. rows t/8 + 8W*i, chunk t % 8) and, after the
-// step's MFMAs, store them to the other stage at row*128 + ((chunk ^ key) << 4).
-// Eight consecutive lanes cover one 128-byte row, so each wave-wide load reads
-// eight whole rows and each wave-wide store fills 1 KiB of LDS.
+// Register-staged copy of one K-major operand tile (eight waves): the 512
+// threads each load four 16-byte chunks per step into registers (thread t:
+// rows t/8 + 64i, chunk t % 8; the row in the range-checked per-lane offset,
+// as in DmaOperand) and, after the step's MFMAs, store them to the other
+// stage at row*128 + ((chunk ^ key) << 4).  Eight consecutive lanes cover one
+// 128-byte row, so each wave-wide load reads eight whole rows and each
+// wave-wide store fills 1 KiB of LDS.
 template <int W>
 struct RegOperand {
     static constexpr int kN = 2048 / (64 * W);
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff, row_bytes, lds0;
+    uint32_t voff[kN], lds0;
     u32x4 r[kN];
 
-    __device__ void init(const uint8_t *X, int row0, uint32_t rb, int tid, uint32_t tile_off)
+    __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int tid, uint32_t tile_off)
     {
-        row_bytes = rb;
-        rsrc = make_rsrc(X + size_t(row0) * rb, 256u * rb);
+        static_assert(W == 8, "register staging is built for eight waves");
+        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
         const int row = tid >> 3, chunk = tid & 7;
-        voff = uint32_t(row) * rb + chunk * 16;
-        lds0 = tile_off + tile_offset(row, chunk);   // key(row + 8W*i) == key(row): period 64
+#pragma unroll
+        for (int i = 0; i < kN; ++i)
+            voff[i] = uint32_t(row + 8 * W * i) * rb + chunk * 16;
+        lds0 = tile_off + tile_offset(row, chunk);   // key(row + 64i) == key(row): period 64
     }
     __device__ void load(int kt)
     {
 #pragma unroll
         for (int i = 0; i < kN; ++i)
-            r[i] = buffer_load16(rsrc, voff, uint32_t(8 * W * i) * row_bytes + uint32_t(kt) * 128);
+            r[i] = buffer_load16(rsrc, voff[i], uint32_t(kt) * 128);
     }
     __device__ void store(uint8_t *stage) const
     {
@@ -134,6 +139,9 @@ struct DmaMnOperand {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t voff[2], pitch, lds_off;   // voff[bit 4 of the instruction's K rows]
 
+    // A chunk whose columns lie beyond the operand (a tail tile) is fetched
+    // from the tile's first columns instead: its values only reach outputs
+    // beyond M or N, and every address stays inside the operand.
     __device__ void init(const uint8_t *X, int R, int row0, int K, int wave, int lane, uint32_t tile_off)
     {
         pitch = uint32_t(R) * 2;
@@ -142,7 +150,8 @@ struct DmaMnOperand {
 #pragma unroll
         for (int b4 = 0; b4 < 2; ++b4) {
             const int c = (lane & 31) ^ (4 * ((2 * wave + kr) & 3)) ^ (2 * b4);
-            voff[b4] = uint32_t(2 * wave + kr) * pitch + 16 * c;
+            const int cs = row0 + 8 * c < R ? c : 0;
+            voff[b4] = uint32_t(2 * wave + kr) * pitch + 16 * cs;
         }
         lds_off = tile_off + 2 * wave * kMnRowBytes;
     }
@@ -234,7 +243,9 @@ struct MnOperand {
         kc = (blk >> 5) & 7;
         kstride = uint32_t(R) * 2;
         rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * kstride - uint32_t(row0) * 2);
-        voff = uint32_t(8 * kc) * kstride + 16 * mb;
+        // columns beyond the operand (tail tile): fetch the tile's first columns
+        // instead, as in DmaMnOperand
+        voff = uint32_t(8 * kc) * kstride + 16 * (row0 + 8 * mb < R ? mb : 0);
         lds_base = tile_off;
     }
     __device__ void load(int kt)
@@ -289,6 +300,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
     const uint32_t row_bytes = uint32_t(K) * kElem;
     const int KT = K / kStepK;
+    // M and N need not be multiples of 256: a tail tile reads zeros (K-major
+    // rows beyond the operand, through the buffer range) or values that only
+    // reach outputs beyond M or N (MN-major), and the epilogue stores only
+    // outputs inside D
+    const int rows_a = min(kBM, M - m0), rows_b = min(kBN, N - n0);
 
     // ---- operand copies ---------------------------------------------------------
     // K-major operands: copied straight into LDS, or through registers when
@@ -303,14 +319,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr bool kTrA = A_MN && !kMnReg, kTrB = B_MN && !kMnReg;
     DmaOperand<W> da, db;
     if constexpr (kDmaA)
-        da.init(A, m0, row_bytes, wave, lane, 0);
+        da.init(A, m0, rows_a, row_bytes, wave, lane, 0);
     if constexpr (kDmaB)
-        db.init(B, n0, row_bytes, wave, lane, kATile);
+        db.init(B, n0, rows_b, row_bytes, wave, lane, kATile);
     RegOperand<W> rga, rgb;
     if constexpr (kRegA)
-        rga.init(A, m0, row_bytes, tid, 0);
+        rga.init(A, m0, rows_a, row_bytes, tid, 0);
     if constexpr (kRegB)
-        rgb.init(B, n0, row_bytes, tid, kATile);
+        rgb.init(B, n0, rows_b, row_bytes, tid, kATile);
     DmaMnOperand<W> dma_mna, dma_mnb;
     if constexpr (kTrA)
         dma_mna.init(A, M, m0, K, wave, lane, 0);
@@ -334,7 +350,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int q = 0; q < kSfInstr; ++q) {
             const int g = wave + W * q;
             const bool is_b = g >= 4;
-            sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row, 256u * sf_row);
+            sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row,
+                                   uint32_t(is_b ? rows_b : rows_a) * sf_row);
         }
         sf_voff = uint32_t(64 * (wave & 3) + lane) * sf_row;
     }
@@ -629,10 +646,12 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < TN16; ++j)
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
-                const size_t m = size_t(m0 + wm + row16<kMx>(i, lane & 15));
+                const int m = m0 + wm + row16<kMx>(i, lane & 15);
                 const int n = n0 + wn + row16<kMx>(j, 4 * (lane >> 4));
+                if (m >= M || n >= N)
+                    continue;
                 f32x4 v = acc4[j][i];
-                f32x4 *p = reinterpret_cast<f32x4 *>(D + m * N + n);
+                f32x4 *p = reinterpret_cast<f32x4 *>(D + size_t(m) * N + n);
                 if constexpr (BETA)
                     v += *p;
                 *p = v;
@@ -643,13 +662,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const size_t m = size_t(m0 + wm + 32 * i + lr);
+            const int m = m0 + wm + 32 * i + lr;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn + 32 * j + 8 * q + 4 * lh;
+                if (m >= M || n >= N)
+                    continue;
                 f32x4 v = {acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
                            acc[j][i][4 * q + 3]};
-                f32x4 *p = reinterpret_cast<f32x4 *>(D + m * N + n);
+                f32x4 *p = reinterpret_cast<f32x4 *>(D + size_t(m) * N + n);
                 if constexpr (BETA)
                     v += *p;
                 *p = v;
@@ -660,7 +681,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 template <int KIND, bool A_MN, bool B_MN, int W, int REG>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
-    const int tiles_m = a.M / kBM, tiles_n = a.N / kBN;
+    const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
     const int blocks = tiles_m * tiles_n;
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
@@ -721,7 +742,7 @@ hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stre
 
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
-    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0)
+    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % kBM == 0 && d.N % kBN == 0)
         return launch_dense256pp(bf16, d, stream);
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m};
     return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);

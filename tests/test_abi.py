@@ -90,8 +90,13 @@ K_, MN = 0, 1
     ((256, 256, 128, E4M3, E4M3, F32, MN, K_, 32), -2),      # MN-major fp8 not built
     ((256, 256, 96, F16, F16, F32, K_, K_, 0), -2),          # K not a multiple of 64
     ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
-    ((100, 256, 64, F16, F16, F32, K_, K_, 0), -2),          # ragged M
-    ((256, 96, 64, F16, F16, F32, K_, K_, 0), -2),           # ragged N
+    ((100, 256, 64, F16, F16, F32, K_, K_, 0), 0),           # ragged M: 256 tile, masked stores
+    ((256, 96, 64, F16, F16, F32, K_, K_, 0), 0),            # ragged N
+    ((100, 260, 128, E4M3, E4M3, F32, K_, K_, 32), 0),       # ragged MX
+    ((256, 90, 64, F16, F16, F32, K_, K_, 0), -2),           # N % 4: D rows not 16-byte aligned
+    ((100, 256, 64, BF16, BF16, F32, MN, K_, 0), -2),        # MN-major A needs M % 8
+    ((104, 256, 64, BF16, BF16, F32, MN, K_, 0), 0),
+    ((256, 100, 64, F16, F16, F32, K_, MN, 0), -2),          # MN-major B needs N % 8
     ((1 << 21, 64, 64, F16, F16, F32, K_, K_, 0), -1),       # beyond the size limit
     # MN-major operands must span less than 4 GiB (32-bit offsets)
     ((32768, 256, 65536, F16, F16, F32, MN, K_, 0), -2),     # A [K][M] is exactly 4 GiB
@@ -106,6 +111,27 @@ def test_plan_create_rejections(args, expect):
 def test_plan_create_null_out():
     lib = mswz.load()
     assert lib.gemm_plan_create(None, 64, 64, 64, F16, F16, F32, K_, K_, 0) == -1
+
+
+def test_tail_plans_use_the_256_tile():
+    d = mswz.gemm_plan_create(1000, 520, 128, "bf16", "bf16").describe()
+    assert (d["tile_m"], d["tile_n"], d["blocks"]) == (256, 256, 4 * 3)
+
+
+@pytest.mark.parametrize("group_m", [-4, -1, 1, 4, 16])
+def test_tile_raster_is_a_bijection(group_m):
+    """Every workgroup maps to one tile and every tile to one workgroup, for
+    grids that are and are not multiples of the XCD region grid."""
+    lib = mswz.load()
+    tm, tn = ctypes.c_int(), ctypes.c_int()
+    for tiles_m, tiles_n in [(1, 1), (2, 4), (3, 5), (4, 4), (16, 16), (32, 32), (7, 12), (13, 1), (1, 9)]:
+        seen = set()
+        for b in range(tiles_m * tiles_n):
+            assert lib.mswz_tile_of_block(b, tiles_m, tiles_n, group_m, ctypes.byref(tm), ctypes.byref(tn)) == 0
+            assert 0 <= tm.value < tiles_m and 0 <= tn.value < tiles_n
+            seen.add((tm.value, tn.value))
+        assert len(seen) == tiles_m * tiles_n
+    assert lib.mswz_tile_of_block(4, 2, 2, group_m, ctypes.byref(tm), ctypes.byref(tn)) == -1
 
 
 def test_tile_choice():

@@ -132,6 +132,48 @@ def test_deterministic_bits():
     assert np.array_equal(run_gpu(w, x), run_gpu(w, x))
 
 
+# M and N that are not multiples of the tile (the 256 tile with masked
+# stores): both ragged, each major combination, MX, degenerate outputs
+TAILS = {
+    "tail-bf16-k": wl.custom(1000, 520, 128, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                             name="tail-bf16-k"),
+    "tail-f16-amn-beta": wl.custom(200, 264, 192, "f16", a_major="mn", beta=1, name="tail-f16-amn-beta"),
+    "tail-bf16-bmn": wl.custom(136, 776, 64, "bf16", b_major="mn", name="tail-bf16-bmn"),
+    "tail-f16-both-mn": wl.custom(264, 520, 128, "f16", a_major="mn", b_major="mn", name="tail-f16-both-mn"),
+    "tail-e4m3-mx": wl.custom(300, 292, 256, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                              name="tail-e4m3-mx"),
+    "tail-one-row": wl.custom(1, 4, 64, "bf16", name="tail-one-row"),
+    "tail-257": wl.custom(257, 256, 64, "f16", beta=1, name="tail-257"),
+}
+
+
+@pytest.mark.parametrize("name", list(TAILS))
+def test_tail_shapes_full_compare(name):
+    w = TAILS[name]
+    plan = plan_for(w)
+    say(f"[tail] {name} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} B:{w.b_major} beta={w.beta} {plan.describe()}")
+    x = wl.generate(w, seed=21)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+def test_tail_output_untouched_outside_d():
+    """Stores stay inside D: a canary buffer around D is unchanged."""
+    w = TAILS["tail-bf16-k"]
+    plan = plan_for(w)
+    x = wl.generate(w, seed=22)
+    import torch
+    A, B = (torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).cuda() for k in ("A", "B"))
+    n = w.M * w.N
+    buf = torch.full((n + 2 * 4096,), 7.0, dtype=torch.float32, device="cuda")
+    D = buf[4096:4096 + n]
+    say("[tail] canary")
+    mswz.gemm_run(plan, A, B, D, 0)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + n:] == 7.0)
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
@@ -143,6 +185,8 @@ EXTRA_FULL = {
     "f16-bmn-4096": wl.custom(4096, 4096, 4096, "f16", b_major="mn", name="f16-bmn-4096"),
     "bf16-both-mn-beta-4096": wl.custom(4096, 4096, 4096, "bf16", a_major="mn", b_major="mn", beta=1,
                                         name="bf16-both-mn-beta-4096"),
+    "tail-4000x4004": wl.custom(4000, 4004, 512, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="tail-4000x4004"),
 }
 
 
