@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kATile = kBM * 128, kBTile = kBN * 128, kStage = kATile + kBTile;
-constexpr int kScaleStage = (kBM + kBN) * 4;   // one 32-bit scale word per row
+constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K steps) per row
 
 constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
 
@@ -339,8 +339,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         mnb.init(B, N, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
 
     // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
-    // for g >= 4) is copied by wave g % W; lane l copies the step's 32-bit
-    // scale word of row 64*(g%4) + l into scale-stage word 64*g + l.
+    // for g >= 4) is copied by wave g % W.  Per K step (kScaleGroups false):
+    // lane l copies the step's 32-bit scale word of row 64*(g%4) + l into
+    // scale-stage word 64*g + l.  Per group of four K steps (kScaleGroups, the
+    // 16x16 path with eight waves and K a multiple of 1024): lane l copies the
+    // row's 16 scale bytes of the four steps into stage bytes 16*(64g + l) ..
+    // +15.  A row's scales for one step are only 4 bytes and consecutive rows
+    // are K/32 bytes apart, so a per-step copy touches one cache line per lane
+    // for 4 useful bytes; fetching four steps at once cuts those line accesses
+    // fourfold, and they cost as much address-unit time as the operand copies.
+    constexpr bool kScaleGroups = kMx && (REG & 8) != 0 && W == 8;   // the 16x16 MX path
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / 32;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -389,6 +397,18 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             for (int q = 0; q < kSfInstr; ++q)
                 buffer_load_lds4(sf_rsrc[q], sstage + 256 * (wave + W * q), sf_voff, 4u * kt);
         }
+    };
+    // the operand copies of one step without its scale words (grouped scales)
+    auto issue_ab = [&](uint8_t *stage, int kt) {
+        if constexpr (kDmaA)
+            da.issue(stage, kt);
+        if constexpr (kDmaB)
+            db.issue(stage, kt);
+    };
+    // scale group `grp` (K steps 4grp .. 4grp+3), kScaleGroups only
+    auto issue_scales = [&](uint8_t *sstage, int grp) {
+        if constexpr (kScaleGroups)
+            buffer_load_lds16(sf_rsrc[0], sstage + 1024 * wave, sf_voff, 16u * uint32_t(grp));
     };
 
     // ---- MFMA operand read addresses -------------------------------------------
@@ -567,7 +587,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
-    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss) {
+    // sf_stride: scale-stage bytes per row (4: one step's word; 16: a group of
+    // four steps); widx: which of the row's words (the step inside its group)
+    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx) {
         uint32_t ab[TM16], bb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
@@ -577,14 +599,20 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             bb[j] = opaque(bbase16[j]);
         // lane l supplies the scale of K block l/16 of row l % 16: byte l/16 of
         // the row's scale word
+        // (row16(b, x) = row16(0, x) + 32*(b/2) + 8*(b%2): one per-lane base
+        // and constant offsets, kept opaque so that they are not hoisted)
         const int r16 = lane & 15, sh = 8 * (lane >> 4);
+        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + row16<true>(0, r16))));
+        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + row16<true>(0, r16))));
         uint32_t sa[TM16], sb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
-            sa[i] = *reinterpret_cast<const uint32_t *>(ss + 4 * (wm + row16<true>(i, r16))) >> sh;
+            sa[i] = *reinterpret_cast<const uint32_t *>(ss + sfa + sf_stride * (32 * (i >> 1) + 8 * (i & 1)) +
+                                                        4 * widx) >> sh;
 #pragma unroll
         for (int j = 0; j < TN16; ++j)
-            sb[j] = *reinterpret_cast<const uint32_t *>(ss + kBM * 4 + 4 * (wn + row16<true>(j, r16))) >> sh;
+            sb[j] = *reinterpret_cast<const uint32_t *>(ss + sfb + sf_stride * (32 * (j >> 1) + 8 * (j & 1)) +
+                                                        4 * widx) >> sh;
         auto frag = [&](uint32_t base) {
             const u32x4 lo = lds_read16(s, base);
             const u32x4 hi = lds_read16(s, base ^ 64u);
@@ -605,7 +633,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kMx && kMf16)
-            compute_mx16(s, ss);
+            compute_mx16(s, ss, 4, 0);
         else if constexpr (kMx)
             compute_mx(s, ss);
         else if constexpr (kMf16)
@@ -619,6 +647,68 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // has no branches: in the last pair of an even step count the copy into
     // lds0 repeats step KT-1 into a stage nobody reads again, which keeps the
     // compiler from draining the copies in flight at a control-flow merge. ------
+    if constexpr (kScaleGroups) {
+        if (KT % 8 == 0) {
+            // Eight K steps per iteration: operand stages alternate lds0 /
+            // lds1, scale groups alternate scl0 / scl1 every four steps.  A
+            // group's scales are copied during the third step of the group
+            // before it, as that step's last copy, and that step's barrier
+            // leaves this one copy in flight (vector-memory completions are
+            // counted in order, so it cannot hold up the step's operand
+            // copies): the scattered scale reads get two steps to land, and
+            // the stage they overwrite was last read four steps earlier.
+            // Copies beyond the last step or group repeat the last one into a
+            // stage nobody reads again, so the loop has no branches.
+            const int NG = KT / 4;
+            // a step's work is not moved across its closing barrier, which
+            // keeps the eight unrolled steps from overlapping in registers
+            auto step_end = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step_end_keep1 = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<1>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            issue_scales(scl0, 0);
+            issue_ab(lds0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 8) {
+                const int g = kt / 4;
+                issue_ab(lds1, kt + 1);
+                compute_mx16(lds0, scl0, 16, 0);
+                step_end();
+                issue_ab(lds0, kt + 2);
+                compute_mx16(lds1, scl0, 16, 1);
+                step_end();
+                issue_ab(lds1, kt + 3);
+                issue_scales(scl1, g + 1);
+                compute_mx16(lds0, scl0, 16, 2);
+                step_end_keep1();
+                issue_ab(lds0, kt + 4);
+                compute_mx16(lds1, scl0, 16, 3);
+                step_end();
+                issue_ab(lds1, kt + 5);
+                compute_mx16(lds0, scl1, 16, 0);
+                step_end();
+                issue_ab(lds0, kt + 6);
+                compute_mx16(lds1, scl1, 16, 1);
+                step_end();
+                issue_ab(lds1, kt + 7);
+                issue_scales(scl0, min(g + 2, NG - 1));
+                compute_mx16(lds0, scl1, 16, 2);
+                step_end_keep1();
+                issue_ab(lds0, min(kt + 8, KT - 1));
+                compute_mx16(lds1, scl1, 16, 3);
+                step_end();
+            }
+            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+            goto epilogue;
+        }
+    }
+    {
     issue_step(lds0, scl0, 0);
     store_regs(lds0);
     __syncthreads();
@@ -637,8 +727,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     if (kt < KT)
         compute(lds0, scl0);
     __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+    }
 
     // ---- epilogue -------------------------------------------------------------
+epilogue:
     if constexpr (kMf16) {
         // 16x16 block (j, i): lane l holds fragment row l % 16 of A block i
         // and fragment rows 4(l/16) .. +3 of B block j

@@ -38,6 +38,8 @@ SMALL = {
                          name="e4m3-mx"),
     "e4m3-mx-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
                               b_dist=("normal", 1.0), name="e4m3-mx-beta"),
+    "e4m3-mx-k2048": wl.custom(512, 512, 2048, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e4m3-mx-k2048"),
     "f16-bmn": wl.custom(512, 256, 192, "f16", b_major="mn", name="f16-bmn"),
     "bf16-both-mn-beta": wl.custom(256, 512, 320, "bf16", a_major="mn", b_major="mn", beta=1,
                                    a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="bf16-both-mn-beta"),
@@ -142,6 +144,8 @@ TAILS = {
     "tail-f16-both-mn": wl.custom(264, 520, 128, "f16", a_major="mn", b_major="mn", name="tail-f16-both-mn"),
     "tail-e4m3-mx": wl.custom(300, 292, 256, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                               name="tail-e4m3-mx"),
+    "tail-e4m3-mx-k1024-beta": wl.custom(264, 520, 1024, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="tail-e4m3-mx-k1024-beta"),
     "tail-one-row": wl.custom(1, 4, 64, "bf16", name="tail-one-row"),
     "tail-257": wl.custom(257, 256, 64, "f16", beta=1, name="tail-257"),
 }
@@ -220,11 +224,12 @@ def test_full_size_c5_quarter_exact():
     assert np.array_equal(got[:, cols].astype(np.float64), reference(w, x, cols=cols, with_mag=False))
 
 
-def test_scale_bytes_select_the_right_block():
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (512, 256, 2048), (300, 260, 1024)])
+def test_scale_bytes_select_the_right_block(M, N, K):
     """Scales only: a = b = 1 everywhere, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
     exactly (block-scale closed form); a wrong byte or lane for any scale
-    block changes the value."""
-    M, N, K = 256, 256, 512
+    block changes the value.  K = 512 copies scales per K step; K a multiple
+    of 1024 copies them per group of four steps (ragged M, N too)."""
     w = wl.custom(M, N, K, "e4m3", V=32, name="scale-only")
     rng = np.random.default_rng(6)
     x = {"A": np.full((M, K), 0x38, np.uint8), "B": np.full((N, K), 0x38, np.uint8),
