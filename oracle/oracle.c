@@ -21,14 +21,15 @@
  *                 + sum_k (2^(SFA[m][k/V]-127) a(m,k)) * (2^(SFB[n][k/V]-127) b(n,k))
  *
  * Every stored element is first decoded to the exact real number its bit
- * pattern encodes (fp64 holds every fp16, bf16, e4m3 and e8m0 value exactly),
+ * pattern encodes (fp64 holds every fp16, bf16, e4m3, e2m1 and e8m0 value exactly),
  * then the K products are summed in fp64 in increasing k.  The componentwise
  * magnitude S[m][n] = sum_k |a*b| is returned beside D for error bounds.
  *
  * Readings taken where the pages are silent: the 8-bit element format is OCP
- * E4M3 (bias 7, no infinities, S.1111.111 is NaN); a scale byte E means
- * 2^(E-127) (OCP E8M0, 255 is NaN); scale blocks start at k = 0, V, 2V, ...;
- * beta is 0 or 1 and beta = 0 never reads D0.
+ * E4M3 (bias 7, no infinities, S.1111.111 is NaN); the 4-bit one (the pages'
+ * FP4, "four-bit values") is OCP E2M1, packed two per byte, low nibble first;
+ * a scale byte E means 2^(E-127) (OCP E8M0, 255 is NaN); scale blocks start
+ * at k = 0, V, 2V, ...; beta is 0 or 1 and beta = 0 never reads D0.
  *
  * Parity status of each function is recorded in the header of oracle/__init__.py.
  */
@@ -40,8 +41,10 @@
 #include <omp.h>
 #endif
 
-/* Element kinds understood by the oracle (its own numbering). */
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4 };
+/* Element kinds understood by the oracle (its own numbering).  ORC_E2M1
+ * elements are packed two per byte: element 2j in bits 0..3 of byte j,
+ * element 2j+1 in bits 4..7. */
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4, ORC_E2M1 = 5 };
 /* Operand majors (its own numbering). */
 enum { ORC_KMAJOR = 0, ORC_MNMAJOR = 1 };
 /* Return codes. */
@@ -92,6 +95,16 @@ double orc_decode_e4m3(uint8_t b)
     return s ? -v : v;
 }
 
+/* OCP E2M1 (4-bit): 1 sign, 2 exponent (bias 1), 1 fraction bit; no
+ * infinities or NaN.  Exponent 0 is subnormal: f * 2^-1; otherwise
+ * (1 + f/2) * 2^(e-1), so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double orc_decode_e2m1(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, f = nibble & 1;
+    double v = e == 0 ? ldexp((double)f, -1) : ldexp((double)(2 + f), e - 2);
+    return s ? -v : v;
+}
+
 /* OCP E8M0 scale: 2^(E-127); E = 255 is NaN. */
 double orc_decode_e8m0(uint8_t b)
 {
@@ -104,6 +117,7 @@ static int elem_size(int dt)
     case ORC_F16: case ORC_BF16: return 2;
     case ORC_E4M3: return 1;
     case ORC_F32: return 4;
+    case ORC_E2M1: return 1;   /* storage byte (two elements) */
     default: return 0;
     }
 }
@@ -115,6 +129,10 @@ static double decode_one(int dt, const void *base, int64_t idx)
     case ORC_BF16: return orc_decode_bf16(((const uint16_t *)base)[idx]);
     case ORC_E4M3: return orc_decode_e4m3(((const uint8_t *)base)[idx]);
     case ORC_F32: return (double)((const float *)base)[idx];
+    case ORC_E2M1: {
+        const uint8_t byte = ((const uint8_t *)base)[idx >> 1];
+        return orc_decode_e2m1((idx & 1) ? byte >> 4 : byte & 0xf);
+    }
     default: return NAN;
     }
 }

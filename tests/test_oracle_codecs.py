@@ -77,3 +77,32 @@ def test_decode_rejects_bad_kind():
     import pytest
     with pytest.raises(ValueError):
         oracle.decode("e4m3", np.zeros(4, dtype=np.uint16))
+
+
+def test_e2m1_all_patterns_match_the_format_table():
+    """OCP E2M1 (FP4): sign, 2 exponent bits (bias 1), 1 fraction bit, no
+    infinities or NaN; the format's eight magnitudes, in code order."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    codes = np.arange(16, dtype=np.uint8)
+    got = oracle.decode("e2m1", codes)[0::2]          # low nibbles carry the codes
+    want = np.array(table + [-v for v in table])
+    assert np.array_equal(got, want)
+    assert np.signbit(got[8]) and not np.signbit(got[0])   # 0x8 is -0
+
+
+def test_e2m1_nibble_order():
+    """Two elements per byte: element 2j in bits 0..3, element 2j+1 in bits 4..7."""
+    got = oracle.decode("e2m1", np.array([[0x21, 0xE7]], dtype=np.uint8))
+    assert got.shape == (1, 4)
+    assert list(got[0]) == [0.5, 1.0, 6.0, -4.0]
+
+
+def test_generator_e2m1_rounding():
+    """Input generation: every E2M1 value round-trips; exact midpoints go to the
+    even code; magnitudes beyond 6 saturate (the workload recipe)."""
+    import workloads as wl
+    vals = oracle.decode("e2m1", np.arange(256, dtype=np.uint8))
+    assert np.array_equal(oracle.decode("e2m1", wl.to_stored(vals[None, :], "e2m1"))[0], vals)
+    mids = np.array([[0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 9.0]])
+    got = oracle.decode("e2m1", wl.to_stored(mids, "e2m1"))[0]
+    assert list(got) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0]

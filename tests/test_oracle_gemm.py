@@ -12,6 +12,7 @@ from fractions import Fraction
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads as wl
@@ -269,3 +270,38 @@ def test_rejections():
     with pytest.raises(ValueError):
         oracle.gemm(4, 4, 3, "f16", "k", A[:12], "f16", "k", A[:12], V=2,
                     SFA=np.zeros(8, np.uint8), SFB=np.zeros(8, np.uint8))
+
+
+def _e2m1_to_e4m3(packed: np.ndarray) -> np.ndarray:
+    """The same values as E4M3 bytes (every E2M1 value is an E4M3 value)."""
+    vals = oracle.decode("e2m1", packed)
+    t = torch.from_numpy(vals.astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 64), (16, 9, 256)])
+def test_e2m1_gemm_equals_e4m3_gemm_of_the_same_values(M, N, K):
+    """Packed-nibble access and the E2M1 decoder against the torch-pinned E4M3
+    path: both operands re-encoded as E4M3 give the identical result, with
+    random block scales and beta = 1."""
+    rng = np.random.default_rng(41)
+    A = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    B = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    SFA = (127 + rng.integers(-3, 4, (M, K // 32))).astype(np.uint8)
+    SFB = (127 + rng.integers(-3, 4, (N, K // 32))).astype(np.uint8)
+    D0 = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    got = oracle.gemm(M, N, K, "e2m1", "k", A, "e2m1", "k", B, V=32, SFA=SFA, SFB=SFB, beta=1, D0=D0)
+    ref = oracle.gemm(M, N, K, "e4m3", "k", _e2m1_to_e4m3(A), "e4m3", "k", _e2m1_to_e4m3(B),
+                      V=32, SFA=SFA, SFB=SFB, beta=1, D0=D0)
+    assert np.array_equal(got, ref)
+
+
+def test_e2m1_all_ones_closed_form():
+    """Every element 1.0 (code 0x2, byte 0x22) with unit scales: every entry is K."""
+    M, N, K = 4, 6, 128
+    A = np.full((M, K // 2), 0x22, np.uint8)
+    B = np.full((N, K // 2), 0x22, np.uint8)
+    one = np.full((M, K // 32), 127, np.uint8)
+    got = oracle.gemm(M, N, K, "e2m1", "k", A, "e2m1", "k", B, V=32, SFA=one,
+                      SFB=np.full((N, K // 32), 127, np.uint8))
+    assert np.array_equal(got, np.full((M, N), float(K)))

@@ -11,12 +11,15 @@ Every config is described by its stored layouts (row-major, contiguous):
 Recipe (identical for every config): ``numpy.random.default_rng(seed)``,
 draws in the order A, B, D0, SFA, SFB, each in the C order of its stored
 layout; fp64 samples are rounded to nearest-even into the storage type
-(fp16 by numpy; bf16 and e4m3 through an fp32 intermediate by torch);
+(fp16 by numpy; bf16 and e4m3 through an fp32 intermediate by torch; e2m1 to
+the nearest of its 16 values, ties to the even code, magnitudes above 6
+saturating to 6, then packed two per byte, element 2j in the low nibble);
 e8m0 scale bytes are 127 + u with u a uniform integer in [-4, 4].
 The quarter-integer variant (the tcgen05.mma page's example test draws
 integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
 recipe and sets every scale byte to 127, so every product and partial sum is
-exact in fp32.
+exact in fp32; for e2m1, which has no 0.25 or 0.75, it draws integers in
+[-2, 2] divided by 2 instead.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ import numpy as np
 import torch
 
 #: Stored element kinds, named as in the oracle and the binding.
-KINDS = ("f16", "bf16", "e4m3")
+KINDS = ("f16", "bf16", "e4m3", "e2m1")
 
 
 @dataclass(frozen=True)
@@ -53,8 +56,8 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Minimal HBM traffic of one call: A + B (+ scales) + D write
         (+ D read when beta = 1)."""
-        es = 1 if self.kind == "e4m3" else 2
-        b = (self.M + self.N) * self.K * es + self.M * self.N * 4
+        num, den = {"e4m3": (1, 1), "e2m1": (1, 2)}.get(self.kind, (2, 1))
+        b = (self.M + self.N) * self.K * num // den + self.M * self.N * 4
         if self.V:
             b += (self.M + self.N) * (self.K // self.V)
         if self.beta:
@@ -93,6 +96,8 @@ def scaled(w: Workload, M=None, N=None, K=None, name=None) -> Workload:
 
 def to_stored(x: np.ndarray, kind: str) -> np.ndarray:
     """Round fp64 values into the stored bit patterns of ``kind``."""
+    if kind == "e2m1":
+        return _to_e2m1_packed(x)
     if kind == "f16":
         return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
@@ -105,6 +110,24 @@ def to_stored(x: np.ndarray, kind: str) -> np.ndarray:
     raise ValueError(kind)
 
 
+# E2M1 magnitudes by code 0..7, and the midpoints between neighbours
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = (_E2M1_MAG[1:] + _E2M1_MAG[:-1]) / 2
+
+
+def _to_e2m1_packed(x: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (ties to the even code, saturating at 6), packed two
+    per byte along the last axis, element 2j in the low nibble."""
+    if x.shape[-1] % 2:
+        raise ValueError("e2m1 rows need an even number of elements")
+    a = np.abs(x)
+    lo = np.searchsorted(_E2M1_MID, a, side="left")
+    hi = np.searchsorted(_E2M1_MID, a, side="right")
+    code = np.where((lo != hi) & (lo % 2 == 1), hi, lo).astype(np.uint8)   # exact tie: even code
+    code |= (np.signbit(x).astype(np.uint8) << 3)
+    return np.ascontiguousarray(code[..., 0::2] | (code[..., 1::2] << 4))
+
+
 def _draw(rng, dist, size):
     kind, p = dist
     if kind == "uniform":
@@ -114,11 +137,14 @@ def _draw(rng, dist, size):
     raise ValueError(kind)
 
 
-def _quarter(rng, size):
+def _quarter(rng, size, kind="f16"):
+    if kind == "e2m1":
+        return rng.integers(-2, 3, size) / 2.0
     return rng.integers(-4, 5, size) / 4.0
 
 
-def stored_shapes(w: Workload) -> dict:
+def value_shapes(w: Workload) -> dict:
+    """Shapes of the drawn values (one per element, before packing)."""
     s = {
         "A": (w.M, w.K) if w.a_major == "k" else (w.K, w.M),
         "B": (w.N, w.K) if w.b_major == "k" else (w.K, w.N),
@@ -131,6 +157,16 @@ def stored_shapes(w: Workload) -> dict:
     return s
 
 
+def stored_shapes(w: Workload) -> dict:
+    """Shapes of the stored arrays (e2m1 rows hold two elements per byte)."""
+    s = value_shapes(w)
+    if w.kind == "e2m1":
+        for name in ("A", "B"):
+            r, c = s[name]
+            s[name] = (r, c // 2)
+    return s
+
+
 def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
     """Stored inputs of workload ``w`` (numpy arrays, raw bit patterns).
 
@@ -140,10 +176,10 @@ def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
     if values not in ("config", "quarter"):
         raise ValueError(values)
     rng = np.random.default_rng(seed)
-    shapes = stored_shapes(w)
+    shapes = value_shapes(w)
     out = {}
     for name, dist in (("A", w.a_dist), ("B", w.b_dist)):
-        x = _quarter(rng, shapes[name]) if values == "quarter" else _draw(rng, dist, shapes[name])
+        x = _quarter(rng, shapes[name], w.kind) if values == "quarter" else _draw(rng, dist, shapes[name])
         out[name] = to_stored(x, w.kind)
     if w.beta:
         out["D0"] = rng.uniform(-1.0, 1.0, shapes["D0"]).astype(np.float32)
