@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s on 1 MI355X (bf16 8192³, MX-fp8 8192³) and % of MFMA peak"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
-MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
+MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4}
 HBM_PEAK = 8000.0
 
 
@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--also", default="c3,c3b,c4,c5",
+    ap.add_argument("--also", default="c3,c3b,c4,c5,c6",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

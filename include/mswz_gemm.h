@@ -20,10 +20,12 @@
  * Storage (all tensors contiguous, row-major, device memory):
  *     A  K-major: [M][K]      A  MN-major: [K][M]     ("K-major rows enumerate
  *     B  K-major: [N][K]      B  MN-major: [K][N]      M/N, MN-major rows K")
+ *     (E2M1: K-major only, [M][K/2] and [N][K/2] bytes, two elements a byte)
  *     D  fp32 [M][N]
  *     SFA uint8 [M][K/V], SFB uint8 [N][K/V]: OCP E8M0 exponents, value 2^(E-127)
  * Element formats: fp16 (IEEE binary16), bf16, fp8 = OCP E4M3 (bias 7, no
- * infinities).  Results are fp32 sums of exact products; the summation order
+ * infinities), fp4 = OCP E2M1 (bias 1, no infinities or NaN; the pages'
+ * "four-bit values").  Results are fp32 sums of exact products; the summation order
  * is fixed per plan, so a plan gives bit-identical results run to run.
  *
  * Ownership: the caller owns every device buffer and the stream.  A plan holds
@@ -63,7 +65,8 @@ typedef enum {
     MSWZ_DT_F16 = 1,
     MSWZ_DT_BF16 = 2,
     MSWZ_DT_E4M3 = 3,
-    MSWZ_DT_F32 = 4
+    MSWZ_DT_F32 = 4,
+    MSWZ_DT_E2M1 = 5            /* OCP FP4, two per byte, element 2j in the low nibble of byte j */
 } mswz_dtype;
 
 typedef enum {
@@ -78,11 +81,13 @@ typedef struct gemm_plan gemm_plan;
  *   out           receives the plan (set to NULL on failure)
  *   M, N, K       problem sizes, each > 0
  *   a_dt, b_dt    operand element formats; d_dt must be MSWZ_DT_F32.
- *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) block-scaled.
+ *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) and
+ *                 (E2M1,E2M1) block-scaled.
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
- *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3
- * Shape rules: K % 64 == 0 (16-bit) or K % 128 == 0 (E4M3).  M and N
+ *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3 and E2M1
+ * Shape rules: K % 64 == 0 (16-bit), K % 128 == 0 (E4M3) or K % 256 == 0
+ * (E2M1, which always uses the 256 tile).  M and N
  * multiples of 64 choose among 256, 128 and 64 square tiles; otherwise (tails)
  * the 256 tile is used with masked stores, and N % 4 == 0 is required (16-byte
  * rows of D), as well as M % 8 == 0 for MN-major A and N % 8 == 0 for MN-major

@@ -25,10 +25,10 @@ __all__ = [
     "desc_address", "desc_check", "tile_offset", "library_path", "load",
 ]
 
-DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4}
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5}
 MAJORS = {"k": 0, "mn": 1}
 STATUS = {"ok": 0, "invalid": -1, "unsupported": -2, "align": -3, "hip": -4, "kind": -5}
-_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4}
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 0.5}   # bytes per element
 _DESCRIBE_KEYS = ("variant", "tile_m", "tile_n", "tile_k", "threads", "blocks", "lds_bytes", "group_m")
 
 _lock = threading.Lock()
@@ -143,10 +143,10 @@ class Plan:
 
     # expected storage sizes in bytes
     def a_bytes(self):
-        return self.M * self.K * _ITEMSIZE[self.a_dt]
+        return int(self.M * self.K * _ITEMSIZE[self.a_dt])
 
     def b_bytes(self):
-        return self.N * self.K * _ITEMSIZE[self.b_dt]
+        return int(self.N * self.K * _ITEMSIZE[self.b_dt])
 
     def d_bytes(self):
         return self.M * self.N * 4

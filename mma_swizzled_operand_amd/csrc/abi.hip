@@ -100,7 +100,7 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     *out = nullptr;
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MSWZ_ERR_INVALID;
-    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_F32; };
+    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_E2M1; };
     if (!known_dt(a_dt) || !known_dt(b_dt) || !known_dt(d_dt))
         return MSWZ_ERR_INVALID;
     if ((a_major != MSWZ_MAJOR_K && a_major != MSWZ_MAJOR_MN) ||
@@ -110,14 +110,15 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_INVALID;
     if (d_dt != MSWZ_DT_F32 || a_dt != b_dt || a_dt == MSWZ_DT_F32)
         return MSWZ_ERR_UNSUPPORTED;
-    const bool fp8 = a_dt == MSWZ_DT_E4M3;
+    const bool fp4 = a_dt == MSWZ_DT_E2M1;
+    const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
-        return MSWZ_ERR_UNSUPPORTED;     // E4M3 is block-scaled only; 16-bit is dense only
+        return MSWZ_ERR_UNSUPPORTED;     // E4M3 / E2M1 are block-scaled only; 16-bit is dense only
     if (fp8 && scale_vec_len != 32)
         return MSWZ_ERR_UNSUPPORTED;
     if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
-    if (K % (fp8 ? 128 : 64) != 0)
+    if (K % (fp4 ? 256 : fp8 ? 128 : 64) != 0)
         return MSWZ_ERR_UNSUPPORTED;
     // M or N not a multiple of 64: the 256x256 tile with masked stores; D rows
     // (and MN-major operand rows) must keep 16-byte alignment
@@ -135,7 +136,7 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
                         (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : tail ? 256 : pick_tile(M, N);
+    const int tile = skinny ? 64 : (tail || fp4) ? 256 : pick_tile(M, N);   // E2M1: the 256 tile only
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -165,6 +166,10 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
             p->group_m = g;
     }
     mswz::variant_info(p->variant, fp8, &p->info);
+    if (fp4)
+        p->info.tile_k = 256;                              // K elements per 128-byte row step
+    if (p->variant == mswz::kVarMx256)
+        p->info.lds_bytes += 2 * 512 * 16;                 // the two scale stages
     if (skinny) {
         p->info.tile_m = int(M);
         p->info.lds_bytes = 8 * int(M) * 68 * 4;
@@ -237,7 +242,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                    p->group_m};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, st)
+    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st)
                                                   : mswz::launch_mx(p->variant, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }

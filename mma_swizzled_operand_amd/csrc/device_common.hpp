@@ -68,6 +68,16 @@ __device__ __forceinline__ f32x4 mfma_scale_16x16x128_e4m3(i32x8 a, i32x8 b, f32
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
 
+// The same MFMA with OCP E2M1 (FP4) operands (format code 4): lane l holds
+// 32 elements (16 bytes, low nibble first) of row l % 16 in the low four
+// registers of each operand, all in scale block l/16, and lane i + 16b
+// supplies row i's scale for block b.
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_e2m1(i32x8 a, i32x8 b, f32x4 c, int scale_a,
+                                                           int scale_b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, scale_a, 0, scale_b);
+}
+
 // Workgroup -> output tile.  The hardware hands consecutive workgroups to the
 // eight XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has its own
 // L2.  Tile ids are therefore re-ordered so that each XCD receives one

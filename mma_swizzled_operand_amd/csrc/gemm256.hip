@@ -45,7 +45,7 @@ constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K s
 
 constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
 
-enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2 };
+enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3 };
 
 // Direct-to-LDS copy of one K-major operand tile (256 rows x 128 bytes per K
 // step) through a buffer resource on the workgroup's 256-row panel.  With W
@@ -277,13 +277,17 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
                float *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
 {
-    static_assert(!((A_MN || B_MN) && KIND == kE4m3), "MN-major operands are built for 16-bit only");
+    static_assert(!((A_MN || B_MN) && (KIND == kE4m3 || KIND == kE2m1)),
+                  "MN-major operands are built for 16-bit only");
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
-    constexpr bool kMx = KIND == kE4m3;
-    constexpr int kElem = kMx ? 1 : 2;
-    constexpr int kStepK = 128 / kElem;   // K elements per step
+    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1;
+    constexpr bool kMx = kFp8 || kFp4;
+    static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
+    // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
+    // E2M1 (packed two per byte) K elements
+    constexpr int kStepK = kFp4 ? 256 : kFp8 ? 128 : 64;
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
@@ -298,7 +302,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
-    const uint32_t row_bytes = uint32_t(K) * kElem;
+    const uint32_t row_bytes = uint32_t(K) * 128 / kStepK;   // bytes of one K-major operand row
     const int KT = K / kStepK;
     // M and N need not be multiples of 256: a tail tile reads zeros (K-major
     // rows beyond the operand, through the buffer range) or values that only
@@ -348,7 +352,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kMx && (REG & 8) != 0 && W == 8;   // the 16x16 MX path
+    constexpr bool kScaleGroups = kFp8 && (REG & 8) != 0 && W == 8;   // the 16x16 E4M3 path
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / 32;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -393,9 +397,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         if constexpr (kDmaB)
             db.issue(stage, kt);
         if constexpr (kMx) {
+            // scale words per row per step: one (E4M3, four 32-element blocks)
+            // or two (E2M1, eight blocks); word w of 64-row group g lands at
+            // stage byte 2048w + 256g + 4*(row in group)
+            constexpr int kWords = kFp4 ? 2 : 1;
 #pragma unroll
             for (int q = 0; q < kSfInstr; ++q)
-                buffer_load_lds4(sf_rsrc[q], sstage + 256 * (wave + W * q), sf_voff, 4u * kt);
+#pragma unroll
+                for (int w = 0; w < kWords; ++w)
+                    buffer_load_lds4(sf_rsrc[q], sstage + 2048 * w + 256 * (wave + W * q), sf_voff,
+                                     4u * uint32_t(kWords * kt + w));
         }
     };
     // the operand copies of one step without its scale words (grouped scales)
@@ -443,15 +454,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < TM16; ++i) {
-            const uint32_t row = wm + row16<kMx>(i, r16);
-            const int c = kMx ? mx_chunk16(g) : kblk16(g);
+            const uint32_t row = wm + row16<kFp8>(i, r16);
+            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
             abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
                               : row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < TN16; ++j) {
-            const uint32_t row = wn + row16<kMx>(j, r16);
-            const int c = kMx ? mx_chunk16(g) : kblk16(g);
+            const uint32_t row = wn + row16<kFp8>(j, r16);
+            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
             bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
                               : kATile + row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
@@ -631,8 +642,53 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
+    // E2M1: two 128-element sub-steps per step; lane (r, g) reads chunk
+    // 4ks + kblk16(g) of its row (one 32-element scale block, 16 bytes) into
+    // the low half of the operand and supplies that block's scale: byte
+    // kblk16(g) of the row's scale word ks.
+    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss) {
+        uint32_t ab[TM16], bb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            ab[i] = opaque(abase16[i]);
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bb[j] = opaque(bbase16[j]);
+        const int r16 = lane & 15, sh = 8 * kblk16(lane >> 4);
+        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16)));
+        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16)));
+        const u32x4 zero = {0, 0, 0, 0};
+        auto frag = [&](uint32_t base, int ks) {
+            const u32x4 v = lds_read16(s, base ^ uint32_t(ks << 6));
+            return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t sa[TM16], sb[TN16];
+#pragma unroll
+            for (int i = 0; i < TM16; ++i)
+                sa[i] = *reinterpret_cast<const uint32_t *>(ss + 2048 * ks + sfa + 64 * i) >> sh;
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+                sb[j] = *reinterpret_cast<const uint32_t *>(ss + 2048 * ks + sfb + 64 * j) >> sh;
+            i32x8 bf[TN16];
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+                bf[j] = frag(bb[j], ks);
+#pragma unroll
+            for (int i = 0; i < TM16; ++i) {
+                const i32x8 af = frag(ab[i], ks);
+#pragma unroll
+                for (int j = 0; j < TN16; ++j)
+                    acc4[j][i] = mfma_scale_16x16x128_e2m1(bf[j], af, acc4[j][i], sb[j], sa[i]);
+            }
+        }
+    };
+
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
-        if constexpr (kMx && kMf16)
+        if constexpr (kFp4)
+            compute_fp4(s, ss);
+        else if constexpr (kMx && kMf16)
             compute_mx16(s, ss, 4, 0);
         else if constexpr (kMx)
             compute_mx(s, ss);
@@ -738,8 +794,8 @@ epilogue:
         for (int j = 0; j < TN16; ++j)
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
-                const int m = m0 + wm + row16<kMx>(i, lane & 15);
-                const int n = n0 + wn + row16<kMx>(j, 4 * (lane >> 4));
+                const int m = m0 + wm + row16<kFp8>(i, lane & 15);
+                const int n = n0 + wn + row16<kFp8>(j, 4 * (lane >> 4));
                 if (m >= M || n >= N)
                     continue;
                 f32x4 v = acc4[j][i];
@@ -840,8 +896,10 @@ hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, 
     return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
 }
 
-hipError_t launch_mx256(const MxArgs &a, hipStream_t stream)
+hipError_t launch_mx256(const MxArgs &a, bool fp4, hipStream_t stream)
 {
+    if (fp4)
+        return launch_kind<kE2m1, false, false, 8, 8>(a, stream);
     return launch_cfg<kE4m3, false, false>(a, stream);
 }
 

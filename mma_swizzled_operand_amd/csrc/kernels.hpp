@@ -47,7 +47,7 @@ bool variant_info(int variant, bool one_byte_elems, VariantInfo *info);
 hipError_t launch_dense(int variant, bool bf16, bool a_mn, bool b_mn, const DenseArgs &args,
                         hipStream_t stream);
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &args, hipStream_t stream);
-hipError_t launch_mx256(const MxArgs &args, hipStream_t stream);
+hipError_t launch_mx256(const MxArgs &args, bool fp4, hipStream_t stream);
 hipError_t launch_dense256pp(bool bf16, const DenseArgs &args, hipStream_t stream);
 int config256();
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);

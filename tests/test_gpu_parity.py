@@ -178,6 +178,59 @@ def test_tail_output_untouched_outside_d():
     assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + n:] == 7.0)
 
 
+# MX-fp4 (OCP E2M1, two per byte; the 256 tile only): several tiles and K
+# steps, ragged M and N, beta = 1
+FP4 = {
+    "e2m1-mx": wl.custom(512, 768, 512, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                         name="e2m1-mx"),
+    "e2m1-mx-beta-k1280": wl.custom(256, 512, 1280, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="e2m1-mx-beta-k1280"),
+    "e2m1-mx-tail": wl.custom(300, 292, 768, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                              name="e2m1-mx-tail"),
+}
+
+
+@pytest.mark.parametrize("name", list(FP4))
+def test_fp4_full_compare(name):
+    w = FP4[name]
+    plan = plan_for(w)
+    say(f"[fp4] {name} {w.M}x{w.N}x{w.K} beta={w.beta} {plan.describe()}")
+    x = wl.generate(w, seed=31)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(FP4))
+def test_fp4_half_integers_bit_exact(name):
+    """E2M1 half-integer operands in [-1, 1] with unit scales: every product
+    and partial sum is exact in fp32, so the result equals the oracle exactly."""
+    w = FP4[name]
+    say(f"[fp4-exact] {name}")
+    x = wl.generate(w, seed=32, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    ref = reference(w, x, with_mag=False)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_fp4_scale_bytes_select_the_right_block():
+    """Scales only: every E2M1 element 1.0 (byte 0x22), so D[m,n] =
+    32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a wrong scale byte, lane or word
+    for any of the eight blocks of a K step changes the value."""
+    M, N, K = 256, 512, 1024
+    w = wl.custom(M, N, K, "e2m1", V=32, name="fp4-scale-only")
+    rng = np.random.default_rng(7)
+    x = {"A": np.full((M, K // 2), 0x22, np.uint8), "B": np.full((N, K // 2), 0x22, np.uint8),
+         "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
+         "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
+    say("[fp4] scale closed form")
+    got = run_gpu(w, x)
+    ua = x["SFA"].astype(np.int64) - 127
+    ub = x["SFB"].astype(np.int64) - 127
+    expect = 32.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
+    assert np.array_equal(got.astype(np.float64), expect)
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
@@ -194,7 +247,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3b", *EXTRA_FULL])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c3b", *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""

@@ -76,6 +76,8 @@ WORKLOADS = {
                    64, 16384, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02)),
     "c5": Workload("c5", "MX-fp8 8192^3 e4m3 K-major, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c6": Workload("c6", "MX-fp4 8192^3 e2m1 K-major, N(0,1) rounded to e2m1, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                   8192, 8192, 8192, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
     "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
                     8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
 }
