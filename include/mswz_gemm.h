@@ -8,7 +8,8 @@
  *
  *     D[m][n] = beta * D[m][n] + sum_k a(m,k) * b(n,k)          (dense)
  *
- * i.e. D = A . B^T with B held as (N,K), fp32 accumulation and output.  `beta`
+ * i.e. D = A . B^T with B held as (N,K), fp32 accumulation, fp32 (or rounded
+ * bf16 / fp16) output.  `beta`
  * is the page's `accum` flag: 0 overwrites D (its old contents are never read,
  * so NaNs in it do not propagate), 1 accumulates onto it.  Block-scaled
  * operands (same page, "Weight-stationary and block scaling") attach one
@@ -21,7 +22,7 @@
  *     A  K-major: [M][K]      A  MN-major: [K][M]     ("K-major rows enumerate
  *     B  K-major: [N][K]      B  MN-major: [K][N]      M/N, MN-major rows K")
  *     (E2M1: K-major only, [M][K/2] and [N][K/2] bytes, two elements a byte)
- *     D  fp32 [M][N]
+ *     D  [M][N] in the plan's d_dt (fp32, bf16 or fp16)
  *     SFA uint8 [M][K/V], SFB uint8 [N][K/V]: OCP E8M0 exponents, value 2^(E-127)
  * Element formats: fp16 (IEEE binary16), bf16, fp8 = OCP E4M3 (bias 7, no
  * infinities), fp4 = OCP E2M1 (bias 1, no infinities or NaN; the pages'
@@ -80,7 +81,11 @@ typedef struct gemm_plan gemm_plan;
  * Create a plan for one problem shape.
  *   out           receives the plan (set to NULL on failure)
  *   M, N, K       problem sizes, each > 0
- *   a_dt, b_dt    operand element formats; d_dt must be MSWZ_DT_F32.
+ *   a_dt, b_dt    operand element formats
+ *   d_dt          MSWZ_DT_F32, or MSWZ_DT_BF16 / MSWZ_DT_F16: the fp32 result
+ *                 rounded to nearest even into D's format (beta = 1 then
+ *                 reads D in that format and adds it in fp32 before
+ *                 rounding); narrow D always uses the 256 tile
  *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) and
  *                 (E2M1,E2M1) block-scaled.
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)

@@ -149,7 +149,7 @@ class Plan:
         return int(self.N * self.K * _ITEMSIZE[self.b_dt])
 
     def d_bytes(self):
-        return self.M * self.N * 4
+        return int(self.M * self.N * _ITEMSIZE[self.d_dt])
 
     def sf_bytes(self):
         v = self.scale_vec_len

@@ -66,6 +66,11 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 
 bool is_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int out_kind(int d_dt)
+{
+    return d_dt == MSWZ_DT_BF16 ? mswz::kOutBf16 : d_dt == MSWZ_DT_F16 ? mswz::kOutF16 : mswz::kOutF32;
+}
+
 // Choose the tile for an (M, N) output: the largest square tile dividing both
 // sizes, dropping to a smaller one while the grid would leave most compute
 // units idle (fewer than 128 tiles of 256 or 256 tiles of 128).  The
@@ -108,8 +113,12 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         return MSWZ_ERR_INVALID;
     if (scale_vec_len < 0)
         return MSWZ_ERR_INVALID;
-    if (d_dt != MSWZ_DT_F32 || a_dt != b_dt || a_dt == MSWZ_DT_F32)
+    if (a_dt != b_dt || a_dt == MSWZ_DT_F32)
         return MSWZ_ERR_UNSUPPORTED;
+    // D: fp32, or the fp32 result rounded to bf16 / fp16 (the 256 tile only)
+    if (d_dt != MSWZ_DT_F32 && d_dt != MSWZ_DT_BF16 && d_dt != MSWZ_DT_F16)
+        return MSWZ_ERR_UNSUPPORTED;
+    const bool narrow_d = d_dt != MSWZ_DT_F32;
     const bool fp4 = a_dt == MSWZ_DT_E2M1;
     const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
@@ -133,10 +142,10 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
         (b_major == MSWZ_MAJOR_MN && K * N * 2 >= kMaxMnBytes))
         return MSWZ_ERR_UNSUPPORTED;
     // weight streaming: few rows of K-major 16-bit A against a large B
-    const bool skinny = !fp8 && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
+    const bool skinny = !fp8 && !narrow_d && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
                         (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : (tail || fp4) ? 256 : pick_tile(M, N);   // E2M1: the 256 tile only
+    const int tile = skinny ? 64 : (tail || fp4 || narrow_d) ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -199,7 +208,7 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
     if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D))
         return MSWZ_ERR_ALIGN;
     mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                      p->group_m};
+                      p->group_m, out_kind(p->d_dt)};
     const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN,
                b_mn = p->b_major == MSWZ_MAJOR_MN;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -240,7 +249,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
         !is_aligned16(SFB))
         return MSWZ_ERR_ALIGN;
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                   p->group_m};
+                   p->group_m, out_kind(p->d_dt)};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st)
                                                   : mswz::launch_mx(p->variant, a, st);

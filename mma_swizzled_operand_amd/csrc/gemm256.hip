@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -271,11 +273,40 @@ struct MnOperand {
 // W waves per workgroup: W = 8 gives each wave a 128 x 64 output sub-tile
 // (two waves per SIMD), W = 4 a 128 x 128 sub-tile (one wave per SIMD,
 // accumulators in AGPRs, a third fewer LDS bytes read per MFMA).
-template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG>
+// Four consecutive outputs of one row of D, as fp32 or rounded to nearest
+// even into bf16 / fp16 (OUT, see OutKind); with BETA the old values, read in
+// the same kind, are added first.
+template <int OUT, bool BETA>
+__device__ __forceinline__ void store_d4(void *D, size_t idx, f32x4 v)
+{
+    if constexpr (OUT == kOutF32) {
+        f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(D) + idx);
+        if constexpr (BETA)
+            v += *p;
+        *p = v;
+    } else {
+        using T = std::conditional_t<OUT == kOutBf16, __bf16, _Float16>;
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        t4 *p = reinterpret_cast<t4 *>(static_cast<T *>(D) + idx);
+        if constexpr (BETA) {
+            const t4 old = *p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] += float(old[e]);
+        }
+        t4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[e] = T(v[e]);
+        *p = out;
+    }
+}
+
+template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
-               float *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
+               void *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
 {
     static_assert(!((A_MN || B_MN) && (KIND == kE4m3 || KIND == kE2m1)),
                   "MN-major operands are built for 16-bit only");
@@ -798,11 +829,7 @@ epilogue:
                 const int n = n0 + wn + row16<kFp8>(j, 4 * (lane >> 4));
                 if (m >= M || n >= N)
                     continue;
-                f32x4 v = acc4[j][i];
-                f32x4 *p = reinterpret_cast<f32x4 *>(D + size_t(m) * N + n);
-                if constexpr (BETA)
-                    v += *p;
-                *p = v;
+                store_d4<OUT, BETA>(D, size_t(m) * N + n, acc4[j][i]);
             }
         return;
     }
@@ -816,17 +843,14 @@ epilogue:
                 const int n = n0 + wn + 32 * j + 8 * q + 4 * lh;
                 if (m >= M || n >= N)
                     continue;
-                f32x4 v = {acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                           acc[j][i][4 * q + 3]};
-                f32x4 *p = reinterpret_cast<f32x4 *>(D + size_t(m) * N + n);
-                if constexpr (BETA)
-                    v += *p;
-                *p = v;
+                const f32x4 v = {acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                                 acc[j][i][4 * q + 3]};
+                store_d4<OUT, BETA>(D, size_t(m) * N + n, v);
             }
         }
 }
 
-template <int KIND, bool A_MN, bool B_MN, int W, int REG>
+template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
@@ -834,12 +858,21 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
     return hipGetLastError();
+}
+
+// bf16 / fp16 output: the default pipeline only
+template <int KIND, bool A_MN, bool B_MN>
+hipError_t launch_out(const MxArgs &a, hipStream_t stream)
+{
+    constexpr int kReg = (A_MN && B_MN) ? 0 : 8;
+    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16>(a, stream)
+                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16>(a, stream);
 }
 
 }  // namespace
@@ -864,6 +897,8 @@ namespace {
 template <int KIND, bool A_MN, bool B_MN>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
+    if (a.out != kOutF32)
+        return launch_out<KIND, A_MN, B_MN>(a, stream);
     switch (config256()) {
     case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);
     case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);
@@ -890,16 +925,18 @@ hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stre
 
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
-    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % kBM == 0 && d.N % kBN == 0)
+    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % kBM == 0 && d.N % kBN == 0 &&
+        d.out == kOutF32)
         return launch_dense256pp(bf16, d, stream);
-    const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m};
+    const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m, d.out};
     return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
 }
 
 hipError_t launch_mx256(const MxArgs &a, bool fp4, hipStream_t stream)
 {
     if (fp4)
-        return launch_kind<kE2m1, false, false, 8, 8>(a, stream);
+        return a.out == kOutF32 ? launch_kind<kE2m1, false, false, 8, 8>(a, stream)
+                                : launch_out<kE2m1, false, false>(a, stream);
     return launch_cfg<kE4m3, false, false>(a, stream);
 }
 

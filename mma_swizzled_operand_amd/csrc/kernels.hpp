@@ -18,13 +18,18 @@ enum Variant : int {
     kVarSkinny = 21,    // 16-bit, M <= 64: weight streaming, split K inside the workgroup
 };
 
+// Output element kind of D: fp32, or the fp32 result rounded to nearest even
+// into bf16 / fp16 (beta = 1 then reads D in that kind).
+enum OutKind { kOutF32 = 0, kOutBf16 = 1, kOutF16 = 2 };
+
 struct DenseArgs {
     const void *A;
     const void *B;
-    float *D;
+    float *D;          // element kind given by `out`
     int M, N, K;
     int beta;
     int group_m;
+    int out = kOutF32;
 };
 
 struct MxArgs {
@@ -32,10 +37,11 @@ struct MxArgs {
     const void *B;
     const uint8_t *SFA;
     const uint8_t *SFB;
-    float *D;
+    float *D;          // element kind given by `out`
     int M, N, K;
     int beta;
     int group_m;
+    int out = kOutF32;
 };
 
 struct VariantInfo {

@@ -86,7 +86,10 @@ K_, MN = 0, 1
     ((256, 256, 64, F16, F16, F32, 2, K_, 0), -1),           # unknown major
     ((256, 256, 64, F16, F16, F32, K_, K_, -32), -1),
     ((256, 256, 64, F16, BF16, F32, K_, K_, 0), -2),         # mixed 16-bit kinds
-    ((256, 256, 64, F16, F16, F16, K_, K_, 0), -2),          # fp16 output
+    ((256, 256, 64, F16, F16, F16, K_, K_, 0), 0),           # fp16 output (rounded)
+    ((256, 256, 64, BF16, BF16, BF16, K_, K_, 0), 0),        # bf16 output
+    ((256, 256, 128, E4M3, E4M3, BF16, K_, K_, 32), 0),      # MX with bf16 output
+    ((256, 256, 64, F16, F16, E4M3, K_, K_, 0), -2),         # e4m3 output
     ((256, 256, 64, F32, F32, F32, K_, K_, 0), -2),
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 0), -2),       # e4m3 needs scales
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 16), -2),      # only 32-element blocks
