@@ -10,6 +10,9 @@ is missing and cannot be built, importing this package fails.
     plan = gemm_plan_create(M, N, K, "bf16", "bf16", "f32", "k", "k", 0)
     gemm_run(plan, A, B, D, beta=0)            # D = beta*D + A.B^T
     gemm_run_blockscaled(plan, A, B, SFA, SFB, D, beta=0)
+
+A plan made with row pitches (``gemm_plan_create_ld``) takes operands and D
+as 2-D views whose rows are ``ld`` elements apart, e.g. ``big[:, :K]``.
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import threading
 from . import _build
 
 __all__ = [
-    "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_run",
+    "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_plan_create_ld", "gemm_run",
     "gemm_run_blockscaled", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
     "desc_address", "desc_check", "tile_offset", "library_path", "load",
 ]
@@ -59,6 +62,9 @@ def load():
         h.gemm_plan_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, c_int, c_int, c_int,
                                        c_int, c_int, i32]
         h.gemm_plan_create.restype = c_int
+        h.gemm_plan_create_ld.argtypes = [ctypes.POINTER(vp), i64, i64, i64, c_int, c_int, c_int,
+                                          c_int, c_int, i32, i64, i64, i64]
+        h.gemm_plan_create_ld.restype = c_int
         h.gemm_run.argtypes = [vp, vp, vp, vp, c_int, vp]
         h.gemm_run.restype = c_int
         h.gemm_plan_workspace_size.argtypes = [vp]
@@ -98,7 +104,8 @@ def _code(x, table, what):
 class Plan:
     """An immutable problem description; owns the C plan handle."""
 
-    def __init__(self, M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", scale_vec_len=0):
+    def __init__(self, M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", scale_vec_len=0,
+                 lda=0, ldb=0, ldd=0):
         lib = load()
         h = ctypes.c_void_p()
         self.M, self.N, self.K = int(M), int(N), int(K)
@@ -108,14 +115,21 @@ class Plan:
         self.a_major = a_major if isinstance(a_major, str) else _name(MAJORS, a_major)
         self.b_major = b_major if isinstance(b_major, str) else _name(MAJORS, b_major)
         self.scale_vec_len = int(scale_vec_len)
-        rc = lib.gemm_plan_create(ctypes.byref(h), self.M, self.N, self.K,
-                                  _code(a_dt, DTYPES, "dtype"), _code(b_dt, DTYPES, "dtype"),
-                                  _code(d_dt, DTYPES, "dtype"), _code(a_major, MAJORS, "major"),
-                                  _code(b_major, MAJORS, "major"), self.scale_vec_len)
+        rc = lib.gemm_plan_create_ld(ctypes.byref(h), self.M, self.N, self.K,
+                                     _code(a_dt, DTYPES, "dtype"), _code(b_dt, DTYPES, "dtype"),
+                                     _code(d_dt, DTYPES, "dtype"), _code(a_major, MAJORS, "major"),
+                                     _code(b_major, MAJORS, "major"), self.scale_vec_len,
+                                     int(lda), int(ldb), int(ldd))
         if rc != 0:
             self._h = None
-            raise MswzError(rc, "gemm_plan_create")
+            raise MswzError(rc, "gemm_plan_create_ld")
         self._h = h
+        # stored rows and row lengths in elements, and pitches (packed when 0)
+        self.a_rows, self.a_cols = (self.K, self.M) if self.a_major == "mn" else (self.M, self.K)
+        self.b_rows, self.b_cols = (self.K, self.N) if self.b_major == "mn" else (self.N, self.K)
+        self.lda = int(lda) or self.a_cols
+        self.ldb = int(ldb) or self.b_cols
+        self.ldd = int(ldd) or self.N
 
     @property
     def handle(self):
@@ -174,6 +188,12 @@ def gemm_plan_create(M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", 
     return Plan(M, N, K, a_dt, b_dt, d_dt, a_major, b_major, scale_vec_len)
 
 
+def gemm_plan_create_ld(M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k", scale_vec_len=0,
+                        lda=0, ldb=0, ldd=0) -> Plan:
+    """A plan whose A, B and D rows are lda, ldb, ldd elements apart (0: packed)."""
+    return Plan(M, N, K, a_dt, b_dt, d_dt, a_major, b_major, scale_vec_len, lda, ldb, ldd)
+
+
 def gemm_plan_destroy(plan: Plan) -> None:
     plan.destroy()
 
@@ -200,6 +220,31 @@ def _dev_ptr(t, nbytes: int, name: str):
     return t.data_ptr()
 
 
+def _view_ptr(t, rows: int, cols: int, ld: int, itemsize, name: str):
+    """Device pointer of operand or output storage of ``rows`` rows of
+    ``cols`` elements, ``ld`` elements apart.  Packed storage takes any
+    contiguous tensor of the right size; otherwise ``t`` must be a 2-D view
+    with unit column stride whose rows hold exactly ``cols`` elements and lie
+    ``ld`` elements apart (in ``itemsize`` bytes per element)."""
+    if ld == cols or isinstance(t, int):
+        return _dev_ptr(t, int(rows * cols * itemsize), name)
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    es = t.element_size()
+    if (t.dim() != 2 or t.shape[0] != rows or t.shape[1] * es != cols * itemsize or
+            (rows > 1 and t.stride(0) * es != ld * itemsize) or (t.shape[1] > 1 and t.stride(1) != 1)):
+        raise ValueError(f"{name}: expected a ({rows}, {cols}) view with rows {ld} elements apart, "
+                         f"got shape {tuple(t.shape)} strides {t.stride()}")
+    return t.data_ptr()
+
+
+def _operands(plan: Plan, A, B, D):
+    return (_view_ptr(A, plan.a_rows, plan.a_cols, plan.lda, _ITEMSIZE[plan.a_dt], "A"),
+            _view_ptr(B, plan.b_rows, plan.b_cols, plan.ldb, _ITEMSIZE[plan.b_dt], "B"),
+            _view_ptr(D, plan.M, plan.N, plan.ldd, _ITEMSIZE[plan.d_dt], "D"))
+
+
 def _stream_ptr(stream):
     if stream is None:
         import torch
@@ -211,9 +256,7 @@ def _stream_ptr(stream):
 
 def gemm_run(plan: Plan, A, B, D, beta: int = 0, stream=None) -> None:
     """Enqueue D = beta*D + A.B^T on ``stream`` (default: torch's current stream)."""
-    a = _dev_ptr(A, plan.a_bytes(), "A")
-    b = _dev_ptr(B, plan.b_bytes(), "B")
-    d = _dev_ptr(D, plan.d_bytes(), "D")
+    a, b, d = _operands(plan, A, B, D)
     rc = load().gemm_run(plan.handle, a, b, d, int(beta), _stream_ptr(stream))
     if rc != 0:
         raise MswzError(rc, "gemm_run")
@@ -224,9 +267,7 @@ def gemm_run_ws(plan: Plan, A, B, D, workspace, beta: int = 0, stream=None) -> N
     ``plan.workspace_bytes()`` bytes, zero-filled before its first use; every
     call leaves its counters zero again).  Plans without a workspace path run
     as gemm_run."""
-    a = _dev_ptr(A, plan.a_bytes(), "A")
-    b = _dev_ptr(B, plan.b_bytes(), "B")
-    d = _dev_ptr(D, plan.d_bytes(), "D")
+    a, b, d = _operands(plan, A, B, D)
     need = plan.workspace_bytes()
     if isinstance(workspace, int):
         w, wb = workspace, need
@@ -245,11 +286,9 @@ def gemm_run_ws(plan: Plan, A, B, D, workspace, beta: int = 0, stream=None) -> N
 def gemm_run_blockscaled(plan: Plan, A, B, SFA, SFB, D, beta: int = 0, stream=None) -> None:
     """Enqueue the block-scaled product on ``stream``."""
     sfa_b, sfb_b = plan.sf_bytes()
-    a = _dev_ptr(A, plan.a_bytes(), "A")
-    b = _dev_ptr(B, plan.b_bytes(), "B")
+    a, b, d = _operands(plan, A, B, D)
     sa = _dev_ptr(SFA, sfa_b, "SFA")
     sb = _dev_ptr(SFB, sfb_b, "SFB")
-    d = _dev_ptr(D, plan.d_bytes(), "D")
     rc = load().gemm_run_blockscaled(plan.handle, a, b, sa, sb, d, int(beta), _stream_ptr(stream))
     if rc != 0:
         raise MswzError(rc, "gemm_run_blockscaled")

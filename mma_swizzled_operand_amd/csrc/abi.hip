@@ -29,6 +29,7 @@ struct gemm_plan {
     int64_t blocks;
     int split_parts;        // K parts of the split weight-streaming kernel (0: none)
     int64_t ws_bytes;       // workspace gemm_run_ws needs for it
+    int64_t lda, ldb, ldd;  // row pitches in elements (packed values when none were given)
 };
 
 namespace mswz {
@@ -100,6 +101,13 @@ extern "C" {
 int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt, int b_dt,
                      int d_dt, int a_major, int b_major, int32_t scale_vec_len)
 {
+    return gemm_plan_create_ld(out, M, N, K, a_dt, b_dt, d_dt, a_major, b_major, scale_vec_len, 0, 0, 0);
+}
+
+int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt, int b_dt,
+                        int d_dt, int a_major, int b_major, int32_t scale_vec_len, int64_t lda,
+                        int64_t ldb, int64_t ldd)
+{
     if (!out)
         return MSWZ_ERR_INVALID;
     *out = nullptr;
@@ -135,17 +143,33 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     if (tail && (N % 4 != 0 || (a_major == MSWZ_MAJOR_MN && M % 8 != 0) ||
                  (b_major == MSWZ_MAJOR_MN && N % 8 != 0)))
         return MSWZ_ERR_UNSUPPORTED;
+    // row pitches (0: packed).  A stored row of A or B must start 16 bytes
+    // aligned (the copies move 16-byte chunks), a row of D on a 4-element
+    // boundary (D is written four elements per store).
+    if (lda < 0 || ldb < 0 || ldd < 0)
+        return MSWZ_ERR_INVALID;
+    const int64_t a_cols = a_major == MSWZ_MAJOR_MN ? M : K, b_cols = b_major == MSWZ_MAJOR_MN ? N : K;
+    const int64_t lda_v = lda ? lda : a_cols, ldb_v = ldb ? ldb : b_cols, ldd_v = ldd ? ldd : N;
+    if (lda_v < a_cols || ldb_v < b_cols || ldd_v < N)
+        return MSWZ_ERR_INVALID;
+    constexpr int64_t kMaxLd = int64_t(1) << 22;
+    if (lda_v > kMaxLd || ldb_v > kMaxLd || ldd_v > kMaxLd)
+        return MSWZ_ERR_UNSUPPORTED;
+    const int64_t align_elems = fp4 ? 32 : fp8 ? 16 : 8;   // elements in 16 bytes
+    const bool strided = lda_v != a_cols || ldb_v != b_cols || ldd_v != N;
+    if (strided && (lda_v % align_elems || ldb_v % align_elems || ldd_v % 4))
+        return MSWZ_ERR_UNSUPPORTED;
     // MN-major operands are addressed with 32-bit offsets from the start of
     // the [K][M] / [K][N] array
     constexpr int64_t kMaxMnBytes = int64_t(1) << 32;
-    if ((a_major == MSWZ_MAJOR_MN && K * M * 2 >= kMaxMnBytes) ||
-        (b_major == MSWZ_MAJOR_MN && K * N * 2 >= kMaxMnBytes))
+    if ((a_major == MSWZ_MAJOR_MN && ((K - 1) * lda_v + M) * 2 >= kMaxMnBytes) ||
+        (b_major == MSWZ_MAJOR_MN && ((K - 1) * ldb_v + N) * 2 >= kMaxMnBytes))
         return MSWZ_ERR_UNSUPPORTED;
     // weight streaming: few rows of K-major 16-bit A against a large B
-    const bool skinny = !fp8 && !narrow_d && a_major == MSWZ_MAJOR_K && b_major == MSWZ_MAJOR_K &&
-                        (M == 64 || M == 32) && N % 64 == 0 &&
+    const bool skinny = !fp8 && !narrow_d && !strided && a_major == MSWZ_MAJOR_K &&
+                        b_major == MSWZ_MAJOR_K && (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : (tail || fp4 || narrow_d) ? 256 : pick_tile(M, N);
+    const int tile = skinny ? 64 : (tail || fp4 || narrow_d || strided) ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -161,6 +185,9 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_dt,
     p->a_major = a_major;
     p->b_major = b_major;
     p->scale_vec_len = scale_vec_len;
+    p->lda = lda_v;
+    p->ldb = ldb_v;
+    p->ldd = ldd_v;
     if (fp8)
         p->variant = tile == 256 ? mswz::kVarMx256 : tile == 128 ? mswz::kVarMx128 : mswz::kVarMx64;
     else if (skinny)
@@ -208,7 +235,7 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta
     if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D))
         return MSWZ_ERR_ALIGN;
     mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                      p->group_m, out_kind(p->d_dt)};
+                      p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd)};
     const bool bf16 = p->a_dt == MSWZ_DT_BF16, a_mn = p->a_major == MSWZ_MAJOR_MN,
                b_mn = p->b_major == MSWZ_MAJOR_MN;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -230,7 +257,7 @@ int gemm_run_ws(const gemm_plan *p, const void *A, const void *B, void *D, int b
     if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D) || !is_aligned16(workspace))
         return MSWZ_ERR_ALIGN;
     mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                      p->group_m};
+                      p->group_m, mswz::kOutF32, int(p->lda), int(p->ldb), int(p->ldd)};
     const hipError_t e = mswz::launch_skinny_split(p->a_dt == MSWZ_DT_BF16, a, workspace,
                                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
@@ -249,7 +276,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
         !is_aligned16(SFB))
         return MSWZ_ERR_ALIGN;
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                   p->group_m, out_kind(p->d_dt)};
+                   p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd)};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st)
                                                   : mswz::launch_mx(p->variant, a, st);

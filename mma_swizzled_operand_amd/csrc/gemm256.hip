@@ -144,10 +144,12 @@ struct DmaMnOperand {
     // A chunk whose columns lie beyond the operand (a tail tile) is fetched
     // from the tile's first columns instead: its values only reach outputs
     // beyond M or N, and every address stays inside the operand.
-    __device__ void init(const uint8_t *X, int R, int row0, int K, int wave, int lane, uint32_t tile_off)
+    // ld: elements from one K row of the operand to the next (>= R)
+    __device__ void init(const uint8_t *X, int R, int ld, int row0, int K, int wave, int lane,
+                         uint32_t tile_off)
     {
-        pitch = uint32_t(R) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * pitch - uint32_t(row0) * 2);
+        pitch = uint32_t(ld) * 2;
+        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * pitch + uint32_t(R - row0) * 2);
         const int kr = lane >> 5;
 #pragma unroll
         for (int b4 = 0; b4 < 2; ++b4) {
@@ -238,13 +240,14 @@ struct MnOperand {
     bool active;
     u32x4 r[8];
 
-    __device__ void init(const uint8_t *X, int R, int row0, int K, int blk, bool act, uint32_t tile_off)
+    __device__ void init(const uint8_t *X, int R, int ld, int row0, int K, int blk, bool act,
+                         uint32_t tile_off)
     {
         active = act;
         mb = blk & 31;
         kc = (blk >> 5) & 7;
-        kstride = uint32_t(R) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K) * kstride - uint32_t(row0) * 2);
+        kstride = uint32_t(ld) * 2;
+        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * kstride + uint32_t(R - row0) * 2);
         // columns beyond the operand (tail tile): fetch the tile's first columns
         // instead, as in DmaMnOperand
         voff = uint32_t(8 * kc) * kstride + 16 * (row0 + 8 * mb < R ? mb : 0);
@@ -306,7 +309,8 @@ template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = k
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
-               void *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
+               void *__restrict__ D, int M, int N, int K, int lda, int ldb, int ldd, int tiles_m,
+               int tiles_n, int group_m)
 {
     static_assert(!((A_MN || B_MN) && (KIND == kE4m3 || KIND == kE2m1)),
                   "MN-major operands are built for 16-bit only");
@@ -333,7 +337,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
-    const uint32_t row_bytes = uint32_t(K) * 128 / kStepK;   // bytes of one K-major operand row
+    // bytes from one K-major operand row to the next (lda, ldb are in elements)
+    const uint32_t a_row_bytes = uint32_t(lda) * 128 / kStepK, b_row_bytes = uint32_t(ldb) * 128 / kStepK;
     const int KT = K / kStepK;
     // M and N need not be multiples of 256: a tail tile reads zeros (K-major
     // rows beyond the operand, through the buffer range) or values that only
@@ -354,24 +359,24 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr bool kTrA = A_MN && !kMnReg, kTrB = B_MN && !kMnReg;
     DmaOperand<W> da, db;
     if constexpr (kDmaA)
-        da.init(A, m0, rows_a, row_bytes, wave, lane, 0);
+        da.init(A, m0, rows_a, a_row_bytes, wave, lane, 0);
     if constexpr (kDmaB)
-        db.init(B, n0, rows_b, row_bytes, wave, lane, kATile);
+        db.init(B, n0, rows_b, b_row_bytes, wave, lane, kATile);
     RegOperand<W> rga, rgb;
     if constexpr (kRegA)
-        rga.init(A, m0, rows_a, row_bytes, tid, 0);
+        rga.init(A, m0, rows_a, a_row_bytes, tid, 0);
     if constexpr (kRegB)
-        rgb.init(B, n0, rows_b, row_bytes, tid, kATile);
+        rgb.init(B, n0, rows_b, b_row_bytes, tid, kATile);
     DmaMnOperand<W> dma_mna, dma_mnb;
     if constexpr (kTrA)
-        dma_mna.init(A, M, m0, K, wave, lane, 0);
+        dma_mna.init(A, M, lda, m0, K, wave, lane, 0);
     if constexpr (kTrB)
-        dma_mnb.init(B, N, n0, K, wave, lane, kATile);
+        dma_mnb.init(B, N, ldb, n0, K, wave, lane, kATile);
     MnOperand mna, mnb;
     if constexpr (A_MN && kMnReg)
-        mna.init(A, M, m0, K, tid & 255, W == 4 || tid < 256, 0);
+        mna.init(A, M, lda, m0, K, tid & 255, W == 4 || tid < 256, 0);
     if constexpr (B_MN && kMnReg)
-        mnb.init(B, N, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
+        mnb.init(B, N, ldb, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
 
     // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
     // for g >= 4) is copied by wave g % W.  Per K step (kScaleGroups false):
@@ -829,7 +834,7 @@ epilogue:
                 const int n = n0 + wn + row16<kFp8>(j, 4 * (lane >> 4));
                 if (m >= M || n >= N)
                     continue;
-                store_d4<OUT, BETA>(D, size_t(m) * N + n, acc4[j][i]);
+                store_d4<OUT, BETA>(D, size_t(m) * ldd + n, acc4[j][i]);
             }
         return;
     }
@@ -845,7 +850,7 @@ epilogue:
                     continue;
                 const f32x4 v = {acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
                                  acc[j][i][4 * q + 3]};
-                store_d4<OUT, BETA>(D, size_t(m) * N + n, v);
+                store_d4<OUT, BETA>(D, size_t(m) * ldd + n, v);
             }
         }
 }
@@ -859,10 +864,12 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
         hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
+                           tiles_n, a.group_m);
     else
         hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, tiles_m, tiles_n, a.group_m);
+                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
+                           tiles_n, a.group_m);
     return hipGetLastError();
 }
 
@@ -926,9 +933,10 @@ hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stre
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
     if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % kBM == 0 && d.N % kBN == 0 &&
-        d.out == kOutF32)
+        d.out == kOutF32 && d.lda == d.K && d.ldb == d.K && d.ldd == d.N)
         return launch_dense256pp(bf16, d, stream);
-    const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m, d.out};
+    const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m, d.out,
+                   d.lda, d.ldb, d.ldd};
     return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
 }
 

@@ -30,6 +30,9 @@ struct DenseArgs {
     int beta;
     int group_m;
     int out = kOutF32;
+    // elements from one stored row to the next: A, B (K-major: >= K;
+    // MN-major: >= M / N) and D (>= N)
+    int lda = 0, ldb = 0, ldd = 0;
 };
 
 struct MxArgs {
@@ -42,6 +45,7 @@ struct MxArgs {
     int beta;
     int group_m;
     int out = kOutF32;
+    int lda = 0, ldb = 0, ldd = 0;   // as in DenseArgs (scale arrays are packed)
 };
 
 struct VariantInfo {

@@ -246,3 +246,57 @@ def test_tile_offset_matches_bruteforce():
     ref = walk.lds_tile_bruteforce(256)
     got = np.array([[mswz.tile_offset(r, c) for c in range(8)] for r in range(256)])
     assert np.array_equal(got, ref)
+
+
+# ---- row pitches (gemm_plan_create_ld) -----------------------------------------
+
+def _create_ld(*args):
+    lib = mswz.load()
+    h = ctypes.c_void_p()
+    rc = lib.gemm_plan_create_ld(ctypes.byref(h), *args)
+    if rc == 0:
+        lib.gemm_plan_destroy(h)
+    return rc
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 0, 0, 0), 0),          # packed
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 64, 64, 256), 0),      # packed, spelled out
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 72, 128, 260), 0),     # views into wider rows
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 60, 0, 0), -1),        # lda < K
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 0, 0, 252), -1),       # ldd < N
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, -8, 0, 0), -1),
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 68, 0, 0), -2),        # A rows not 16-byte aligned
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 0, 0, 258), -2),       # D rows: ldd % 4
+    ((256, 256, 64, BF16, BF16, F32, K_, K_, 0, 1 << 23, 0, 0), -2),   # beyond the pitch limit
+    ((256, 256, 64, BF16, BF16, F32, MN, K_, 0, 200, 0, 0), -1),       # MN-major A: lda >= M
+    ((256, 256, 64, BF16, BF16, F32, MN, MN, 0, 264, 272, 0), 0),
+    ((256, 256, 64, BF16, BF16, F32, MN, K_, 0, 260, 0, 0), -2),       # lda % 8
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 32, 136, 0, 0), -2),     # E4M3 rows: lda % 16
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 32, 144, 160, 0), 0),
+    ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 32, 528, 0, 0), -2),     # E2M1 rows: lda % 32
+    ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 32, 544, 0, 0), 0),
+    ((100, 260, 64, F16, F16, BF16, K_, K_, 0, 128, 64, 264), 0),      # ragged, narrow D
+    # MN-major spans below 4 GiB, counted with the pitch
+    ((16384, 256, 65536, F16, F16, F32, MN, K_, 0, 0, 0, 0), 0),
+    ((16384, 256, 65536, F16, F16, F32, MN, K_, 0, 32776, 0, 0), -2),
+])
+def test_plan_create_ld_rejections(args, expect):
+    assert _create_ld(*args) == expect
+
+
+def test_plan_create_ld_chooses_the_256_tile():
+    # strided plans take the 256 tile, also where the packed shape would not
+    assert mswz.gemm_plan_create(512, 512, 64, "bf16", "bf16").describe()["tile_m"] == 64
+    d = mswz.gemm_plan_create_ld(512, 512, 64, "bf16", "bf16", ldd=520).describe()
+    assert d["tile_m"] == 256 and d["blocks"] == 4
+    # a weight-streaming shape with a pitch is not routed to the skinny kernels
+    sk = mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16")
+    assert sk.describe()["tile_n"] == 64 and sk.workspace_bytes() > 0
+    st = mswz.gemm_plan_create_ld(64, 16384, 8192, "bf16", "bf16", lda=8200)
+    assert st.describe()["tile_n"] == 256 and st.workspace_bytes() == 0
+    # the pitches the binding will check tensors against
+    p = mswz.gemm_plan_create_ld(256, 512, 128, "f16", "f16", "f32", "mn", "k", 0, lda=264)
+    assert (p.a_rows, p.a_cols, p.lda) == (128, 256, 264)
+    assert (p.b_rows, p.b_cols, p.ldb) == (512, 128, 128)
+    assert p.ldd == 512
