@@ -5,8 +5,8 @@ One step = one library call (one kernel launch) computing the whole product
 for the workload on inputs already resident in HBM.  Default workload: the
 square dense 4096^3 bf16 GEMM with both operands K-major (N(0,1) inputs,
 seed 0).  The other full-size workloads (8192^3 fp16 MN-major A with beta=1,
-8192^3 bf16, the skinny 64x16384x8192 weight-streaming shape and 8192^3
-MX-fp8) are timed in the same run and reported under "also".
+8192^3 bf16, the skinny 64x16384x8192 weight-streaming shape, 8192^3 MX-fp8
+and 8192^3 MX-fp4) are timed in the same run and reported under "also".
 
 Prints ONE JSON line (rank 0).  ``roofline`` reports the dominant kernel
 against the MI355X dense MFMA peak (or HBM peak for the skinny shape), using
@@ -167,8 +167,13 @@ def cpu_baseline(w, x, target_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The default warm-up (400 launches, 45 ms to 0.4 s of back-to-back work
+    # depending on the workload) outlasts the chip's power-management settling
+    # after an idle start, about the first 40 ms of sustained MFMA load,
+    # during which launches run up to 20 % slower; the timed steps then see
+    # the steady clock that a continuously loaded GPU runs at.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--also", default="c3,c3b,c4,c5,c6",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
@@ -219,7 +224,7 @@ def main():
 
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2))
+        r = measure(name, args.steps, args.warmup)
         ow = r["workload"]
         entry = {"title": ow.title, "us_per_call": round(r["kernel_avg_ms"] * 1e3, 2),
                  "TFLOP/s": round(r["kernel_tflops"], 1),
