@@ -106,6 +106,30 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,
                      int32_t scale_vec_len);
 
 /*
+ * gemm_plan_create for operands and D stored with a row pitch, so that each
+ * can be a view into a wider matrix (tcgen05.mma page, "Shared descriptors are
+ * byte-stride contracts": the layout is given by explicit strides, 16-byte
+ * multiples, and checked, never inferred).
+ *   lda   elements from one stored row of A to the next: a K-major A is
+ *         [M][lda] with lda >= K, an MN-major A is [K][lda] with lda >= M
+ *   ldb   the same for B ([N][ldb], ldb >= K; or [K][ldb], ldb >= N)
+ *   ldd   elements from one row of D to the next, ldd >= N
+ * 0 for any of them means packed (K, M / N, N).  A plan with any pitch other
+ * than packed uses the 256 tile and needs every stored row 16-byte aligned:
+ * lda and ldb multiples of 8 (16-bit), 16 (E4M3) or 32 (E2M1), ldd a multiple
+ * of 4; pitches are at most 2^22, and an MN-major operand's span
+ * ((K - 1) * ld + M or N elements) must stay below 4 GiB.  The elements
+ * between a row's end and the next row's start are neither read (operands)
+ * nor written (D).  Scale arrays stay packed.  Other arguments and the
+ * returns are those of gemm_plan_create, which is this function with three
+ * zero pitches.
+ */
+int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
+                        int a_dt, int b_dt, int d_dt, int a_major, int b_major,
+                        int32_t scale_vec_len, int64_t lda, int64_t ldb,
+                        int64_t ldd);
+
+/*
  * Enqueue D = beta*D + A.B^T for a dense plan on `stream` (a hipStream_t;
  * NULL is the default stream).  A, B, D are device pointers, 16-byte aligned.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID, MSWZ_ERR_ALIGN, MSWZ_ERR_KIND or
