@@ -207,6 +207,16 @@ __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 // the grouping by lane bits 3 and 4.
 __device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
 
+// Row of a 64-row group held by stage slot l when each row's scales take 16
+// bytes (four K steps): l with bits 3 and 4 swapped (an involution).  A scale
+// read of 16-row fragment block b touches rows row16(b, x), x = 0..15: bits
+// 0-2 and 4 from x, bits 3 and 5 from b.  In this order they are the 16
+// consecutive slots 16 * b + x (16 bytes apart, on 16 different 4-bank groups
+// of the 64 banks of 4 bytes), so the read is conflict-free and block b sits
+// 256 * b bytes from a per-lane base.  In row order, rows x and x + 8 of one
+// block would share their banks.
+__device__ __forceinline__ int sf_slot_row(int l) { return (l & ~24) | ((l & 8) << 1) | ((l & 16) >> 1); }
+
 // Tile row (relative to the wave's first row) of row x (0..15) of 16-row
 // fragment block b: 16-bit operands use 16 consecutive rows; E4M3 operands
 // rows 32*(b/2) + 8*(b%2) + {0..7, 16..23}.  Runs of 4 consecutive x stay
@@ -383,8 +393,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // lane l copies the step's 32-bit scale word of row 64*(g%4) + l into
     // scale-stage word 64*g + l.  Per group of four K steps (kScaleGroups, the
     // 16x16 path with eight waves and K a multiple of 1024): lane l copies the
-    // row's 16 scale bytes of the four steps into stage bytes 16*(64g + l) ..
-    // +15.  A row's scales for one step are only 4 bytes and consecutive rows
+    // 16 scale bytes of the four steps of row 64*(g%4) + sf_slot_row(l) into
+    // stage bytes 16*(64g + l) .. +15 (the slot order keeps the scale reads
+    // free of bank conflicts).  A row's scales for one step are only 4 bytes and consecutive rows
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
@@ -401,7 +412,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row,
                                    uint32_t(is_b ? rows_b : rows_a) * sf_row);
         }
-        sf_voff = uint32_t(64 * (wave & 3) + lane) * sf_row;
+        // with kScaleGroups lane l copies row sf_slot_row(l) of its group
+        sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
 
     auto store_regs = [&](uint8_t *stage) {
@@ -645,21 +657,25 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < TN16; ++j)
             bb[j] = opaque(bbase16[j]);
         // lane l supplies the scale of K block l/16 of row l % 16: byte l/16 of
-        // the row's scale word
+        // the row's scale word, read as one byte (a word and a per-lane shift
+        // would keep one more register live through the loop)
         // (row16(b, x) = row16(0, x) + 32*(b/2) + 8*(b%2): one per-lane base
-        // and constant offsets, kept opaque so that they are not hoisted)
-        const int r16 = lane & 15, sh = 8 * (lane >> 4);
-        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + row16<true>(0, r16))));
-        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + row16<true>(0, r16))));
+        // and constant offsets, kept opaque so that they are not hoisted).
+        // With kScaleGroups the rows sit in the slot order of sf_slot_row
+        // (both the per-step words and the 16-byte groups): block b of row x
+        // is slot (wave's first row) + 16 * b + x.
+        const int r16 = lane & 15;
+        static_assert(!kScaleGroups || (32 * TN) % 64 == 0, "wave rows start 64-row groups");
+        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
         uint32_t sa[TM16], sb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
-            sa[i] = *reinterpret_cast<const uint32_t *>(ss + sfa + sf_stride * (32 * (i >> 1) + 8 * (i & 1)) +
-                                                        4 * widx) >> sh;
+            sa[i] = ss[sfa + sf_off(i) + 4 * widx];
 #pragma unroll
         for (int j = 0; j < TN16; ++j)
-            sb[j] = *reinterpret_cast<const uint32_t *>(ss + sfb + sf_stride * (32 * (j >> 1) + 8 * (j & 1)) +
-                                                        4 * widx) >> sh;
+            sb[j] = ss[sfb + sf_off(j) + 4 * widx];
         auto frag = [&](uint32_t base) {
             const u32x4 lo = lds_read16(s, base);
             const u32x4 hi = lds_read16(s, base ^ 64u);
