@@ -207,6 +207,52 @@ __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 // the grouping by lane bits 3 and 4.
 __device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
 
+// Compile-time loop: fn(std::integral_constant<int, F>), ..., up to L - 1.
+template <int F, int L, class Fn>
+__device__ __forceinline__ void static_for(Fn &&fn)
+{
+    if constexpr (F < L) {
+        fn(std::integral_constant<int, F>{});
+        static_for<F + 1, L>(fn);
+    }
+}
+
+// Read order of one K step's fragments for a TM x TN grid of 16x16 MFMAs
+// issued A-block-major (MFMA m = TN * i + j): every A block i and B block j
+// is read before the first MFMA that uses it (MFMA TN * i, resp. j), in the
+// order of that first use, and `ahead` MFMAs early.  issued(m) counts the
+// reads issued before MFMA m + 1; item(r) names read r: i + 1 for A block i,
+// -(j + 1) for B block j.
+template <int TM, int TN, int ahead>
+struct FragSchedule {
+    static constexpr int issued(int m)
+    {
+        int c = 0;
+        for (int i = 0; i < TM; ++i)
+            c += TN * i <= m + ahead;
+        for (int j = 0; j < TN; ++j)
+            c += j <= m + ahead;
+        return c;
+    }
+    static constexpr int item(int r)
+    {
+        int ia = 0, ib = 0;
+        for (int k = 0; k < TM + TN; ++k) {
+            const int na = ia < TM ? TN * ia : 1 << 20, nb = ib < TN ? ib : 1 << 20;
+            if (na <= nb) {
+                if (k == r)
+                    return ia + 1;
+                ++ia;
+            } else {
+                if (k == r)
+                    return -(ib + 1);
+                ++ib;
+            }
+        }
+        return 0;
+    }
+};
+
 // Row of a 64-row group held by stage slot l when each row's scales take 16
 // bytes (four K steps): l with bits 3 and 4 swapped (an involution).  A scale
 // read of 16-row fragment block b touches rows row16(b, x), x = 0..15: bits
@@ -669,29 +715,38 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
-        uint32_t sa[TM16], sb[TN16];
-#pragma unroll
-        for (int i = 0; i < TM16; ++i)
-            sa[i] = ss[sfa + sf_off(i) + 4 * widx];
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-            sb[j] = ss[sfb + sf_off(j) + 4 * widx];
         auto frag = [&](uint32_t base) {
             const u32x4 lo = lds_read16(s, base);
             const u32x4 hi = lds_read16(s, base ^ 64u);
             return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        i32x8 bf[TN16];
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-            bf[j] = frag(bb[j]);
-#pragma unroll
-        for (int i = 0; i < TM16; ++i) {
-            const i32x8 af = frag(ab[i]);
-#pragma unroll
-            for (int j = 0; j < TN16; ++j)
-                acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af, acc4[j][i], sb[j], sa[i]);
-        }
+        // MFMA m = TN16 * i + j; each block's fragment and scale are read two
+        // MFMAs ahead of first use, in that order (FragSchedule), so that a
+        // wave's first MFMA waits for a few reads rather than for the whole
+        // step's B fragments and scales, which all eight waves request at once
+        // after the barrier.
+        using Sched = FragSchedule<TM16, TN16, 2>;
+        uint32_t sa[TM16], sb[TN16];
+        i32x8 bf[TN16], af[TM16];
+        static_for<0, TM16 * TN16>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
+            static_for<c0, c1>([&](auto rc) {
+                constexpr int it = Sched::item(decltype(rc)::value);
+                if constexpr (it > 0) {
+                    sa[it - 1] = ss[sfa + sf_off(it - 1) + 4 * widx];
+                    af[it - 1] = frag(ab[it - 1]);
+                } else {
+                    sb[-it - 1] = ss[sfb + sf_off(-it - 1) + 4 * widx];
+                    bf[-it - 1] = frag(bb[-it - 1]);
+                }
+            });
+            if constexpr (c1 > c0)
+                __builtin_amdgcn_sched_group_barrier(0x100, 3 * (c1 - c0), 0);   // DS reads
+            constexpr int i = m / TN16, j = m % TN16;
+            acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+        });
     };
 
     // E2M1: two 128-element sub-steps per step; lane (r, g) reads chunk
@@ -706,35 +761,42 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < TN16; ++j)
             bb[j] = opaque(bbase16[j]);
-        const int r16 = lane & 15, sh = 8 * kblk16(lane >> 4);
-        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16)));
-        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16)));
+        // lane group g supplies the scale of block kblk16(g): that byte of its
+        // row's scale word, read as one byte
+        const int r16 = lane & 15, sbyte = kblk16(lane >> 4);
+        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16) + sbyte));
+        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16) + sbyte));
         const u32x4 zero = {0, 0, 0, 0};
         auto frag = [&](uint32_t base, int ks) {
             const u32x4 v = lds_read16(s, base ^ uint32_t(ks << 6));
             return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        // reads two MFMAs ahead of first use, as in compute_mx16
+        using Sched = FragSchedule<TM16, TN16, 2>;
+        static_for<0, 2>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
             uint32_t sa[TM16], sb[TN16];
-#pragma unroll
-            for (int i = 0; i < TM16; ++i)
-                sa[i] = *reinterpret_cast<const uint32_t *>(ss + 2048 * ks + sfa + 64 * i) >> sh;
-#pragma unroll
-            for (int j = 0; j < TN16; ++j)
-                sb[j] = *reinterpret_cast<const uint32_t *>(ss + 2048 * ks + sfb + 64 * j) >> sh;
-            i32x8 bf[TN16];
-#pragma unroll
-            for (int j = 0; j < TN16; ++j)
-                bf[j] = frag(bb[j], ks);
-#pragma unroll
-            for (int i = 0; i < TM16; ++i) {
-                const i32x8 af = frag(ab[i], ks);
-#pragma unroll
-                for (int j = 0; j < TN16; ++j)
-                    acc4[j][i] = mfma_scale_16x16x128_e2m1(bf[j], af, acc4[j][i], sb[j], sa[i]);
-            }
-        }
+            i32x8 bf[TN16], af[TM16];
+            static_for<0, TM16 * TN16>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
+                static_for<c0, c1>([&](auto rc) {
+                    constexpr int it = Sched::item(decltype(rc)::value);
+                    if constexpr (it > 0) {
+                        sa[it - 1] = ss[2048 * ks + sfa + 64 * (it - 1)];
+                        af[it - 1] = frag(ab[it - 1], ks);
+                    } else {
+                        sb[-it - 1] = ss[2048 * ks + sfb + 64 * (-it - 1)];
+                        bf[-it - 1] = frag(bb[-it - 1], ks);
+                    }
+                });
+                if constexpr (c1 > c0)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (c1 - c0), 0);   // DS reads
+                constexpr int i = m / TN16, j = m % TN16;
+                acc4[j][i] = mfma_scale_16x16x128_e2m1(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+            });
+        });
     };
 
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
