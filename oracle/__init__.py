@@ -15,6 +15,13 @@ Contents
       (tcgen05.mma page: "Operands and repeat axes", "Shared descriptors are
       byte-stride contracts", "Example: four K16 issues for a 128x64x64
       product", "Weight-stationary and block scaling").
+``apply_opts`` (this file)
+    * the per-call options of the GEMM (tcgen05.mma page, "Weight-stationary
+      and block scaling": neg_a, neg_b, sat_d, disable-output-lane and
+      zero-column masks, pred are named there without a definition; the
+      plainest readings are written out here: sign of the product, clamp of
+      the stored value to D's largest finite magnitude, rows left untouched,
+      columns with a zero product).
 ``walk.py``
     * brute-force enumerators of the shared-descriptor address walk
       (tcgen05.cp page, "Shared descriptor address walk"; tcgen05.mma page,
@@ -179,3 +186,48 @@ def gemm(M, N, K, a_kind, a_major, A, b_kind, b_major, B, *, V=0, SFA=None, SFB=
     if rc != 0:
         raise ValueError(f"orc_gemm rejected its arguments ({rc})")
     return (out, mag) if with_mag else out
+
+
+# largest finite magnitude of each D format
+D_MAX = {"f32": float(np.finfo(np.float32).max), "bf16": 3.3895313892515355e38, "f16": 65504.0}
+
+
+def mask_bits(words, n: int) -> np.ndarray:
+    """Bits 0 .. n-1 of a word mask (bit x is bit x % 32 of word x // 32)."""
+    w = np.asarray(words, dtype=np.uint32)
+    x = np.arange(n)
+    return ((w[x // 32] >> (x % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def apply_opts(P, D_before, *, beta=0, D0=None, neg_a=False, neg_b=False, sat_d=False,
+               row_mask=None, col_zero=None, pred=True, d_kind="f32"):
+    """Expected D after a call with options, in fp64, from the product
+    P[m][n] = sum_k a(m,k) b(n,k) (``gemm`` with beta = 0) and the content of
+    D before the call (D_before; with beta = 1 it is also D0):
+
+        pred false          -> D unchanged
+        sign                = -1 if exactly one of neg_a, neg_b else +1
+        P'[m][n]            = 0 if column n is set in col_zero else sign * P[m][n]
+        V[m][n]             = beta * D0[m][n] + P'[m][n]
+        sat_d               -> V clamped to [-D_MAX, D_MAX] (NaN kept)
+        rows set in row_mask keep D_before.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    Db = np.asarray(D_before, dtype=np.float64)
+    if not pred:
+        return Db.copy()
+    M, N = P.shape
+    sign = -1.0 if bool(neg_a) != bool(neg_b) else 1.0
+    Pp = sign * P
+    if col_zero is not None:
+        Pp[:, mask_bits(col_zero, N)] = 0.0
+    V = Pp + (np.asarray(D0 if D0 is not None else Db, dtype=np.float64) if beta else 0.0)
+    if sat_d:
+        mx = D_MAX[d_kind]
+        with np.errstate(invalid="ignore"):
+            big = np.abs(V) > mx
+        V = np.where(big, np.copysign(mx, V), V)
+    if row_mask is not None:
+        rm = mask_bits(row_mask, M)
+        V[rm, :] = Db[rm, :]
+    return V
