@@ -180,6 +180,46 @@ int gemm_run_blockscaled(const gemm_plan *plan, const void *A, const void *B,
                          const uint8_t *SFA, const uint8_t *SFB, void *D,
                          int beta, void *stream);
 
+/*
+ * Per-call options (tcgen05.mma page, "Weight-stationary and block scaling":
+ * neg_a, neg_b, sat_d, the dense disable-output-lane masks, the zero-column
+ * mask of the weight-stationary form, and pred are explicit parameters; the
+ * page names them without defining them, so the readings are stated here).
+ */
+typedef struct {
+    int neg_a, neg_b;           /* nonzero: A (B) enters negated; the product's sign
+                                   is (-1)^(neg_a + neg_b) (negation is exact) */
+    int sat_d;                  /* nonzero: every stored D value is clamped to D's
+                                   largest finite magnitude (fp32 3.40282347e38,
+                                   bf16 3.38953139e38, fp16 65504), infinities
+                                   included; NaN is stored unchanged */
+    const uint32_t *row_mask;   /* device pointer or NULL: ceil(M/32) words; bit m % 32
+                                   of word m / 32 set leaves row m of D untouched
+                                   (neither read nor written) */
+    const uint32_t *col_zero;   /* device pointer or NULL: ceil(N/32) words; bit n % 32
+                                   of word n / 32 set makes column n of the product
+                                   zero (row n of B treated as zero), so that column
+                                   of D becomes beta * D */
+    int pred;                   /* zero: nothing is enqueued and D is unchanged (the
+                                   arguments are still checked first) */
+} gemm_opts;
+
+/*
+ * gemm_run / gemm_run_blockscaled with options.  SFA and SFB must be NULL for
+ * a dense plan and non-NULL for a block-scaled one.  opts == NULL, or options
+ * that change nothing (neg_a == neg_b, no saturation, no masks, pred != 0),
+ * run exactly as gemm_run / gemm_run_blockscaled.  Otherwise the call runs
+ * on the 256x256 tile whatever tile the plan chose (any plan's shape is
+ * valid for it); the masks are read once per output row / column group and
+ * must be 4-byte aligned (else MSWZ_ERR_ALIGN).  Returns as gemm_run, and
+ * MSWZ_ERR_INVALID for scale pointers that do not match the plan.  Calls with
+ * options that change something are asynchronous like gemm_run and allocate
+ * nothing; the masks must stay alive until the stream passes the kernel.
+ */
+int gemm_run_opts(const gemm_plan *plan, const void *A, const void *B,
+                  const uint8_t *SFA, const uint8_t *SFB, void *D, int beta,
+                  const gemm_opts *opts, void *stream);
+
 /* Release a plan (NULL is allowed). */
 void gemm_plan_destroy(gemm_plan *plan);
 

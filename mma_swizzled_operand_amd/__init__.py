@@ -24,7 +24,7 @@ from . import _build
 
 __all__ = [
     "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_plan_create_ld", "gemm_run",
-    "gemm_run_blockscaled", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
+    "gemm_run_blockscaled", "gemm_run_opts", "GemmOpts", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
     "desc_address", "desc_check", "tile_offset", "library_path", "load",
 ]
 
@@ -36,6 +36,12 @@ _DESCRIBE_KEYS = ("variant", "tile_m", "tile_n", "tile_k", "threads", "blocks", 
 
 _lock = threading.Lock()
 _lib = None
+
+
+class GemmOpts(ctypes.Structure):
+    """The C struct gemm_opts (include/mswz_gemm.h)."""
+    _fields_ = [("neg_a", ctypes.c_int), ("neg_b", ctypes.c_int), ("sat_d", ctypes.c_int),
+                ("row_mask", ctypes.c_void_p), ("col_zero", ctypes.c_void_p), ("pred", ctypes.c_int)]
 
 
 class MswzError(RuntimeError):
@@ -73,6 +79,8 @@ def load():
         h.gemm_run_ws.restype = c_int
         h.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, c_int, vp]
         h.gemm_run_blockscaled.restype = c_int
+        h.gemm_run_opts.argtypes = [vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(GemmOpts), vp]
+        h.gemm_run_opts.restype = c_int
         h.gemm_plan_destroy.argtypes = [vp]
         h.gemm_plan_destroy.restype = None
         h.gemm_status_str.argtypes = [c_int]
@@ -292,6 +300,35 @@ def gemm_run_blockscaled(plan: Plan, A, B, SFA, SFB, D, beta: int = 0, stream=No
     rc = load().gemm_run_blockscaled(plan.handle, a, b, sa, sb, d, int(beta), _stream_ptr(stream))
     if rc != 0:
         raise MswzError(rc, "gemm_run_blockscaled")
+
+
+def _mask_ptr(t, nbits: int, name: str):
+    """Device pointer of a bit mask of ``nbits`` bits (ceil(nbits/32) 32-bit
+    words, bit x of word x // 32), or None."""
+    if t is None:
+        return None
+    return _dev_ptr(t, 4 * ((nbits + 31) // 32), name)
+
+
+def gemm_run_opts(plan: Plan, A, B, D, beta: int = 0, SFA=None, SFB=None, neg_a=False, neg_b=False,
+                  sat_d=False, row_mask=None, col_zero=None, pred=True, stream=None) -> None:
+    """gemm_run / gemm_run_blockscaled with the per-call options of gemm_opts:
+    negated operands, saturated D, a row mask (rows left untouched), a column
+    mask (columns whose product is zero) and a predicate.  Masks are GPU
+    tensors of ceil(M/32) / ceil(N/32) 32-bit words (int32 or uint32)."""
+    a, b, d = _operands(plan, A, B, D)
+    sa = sb = None
+    if plan.scale_vec_len:
+        sfa_b, sfb_b = plan.sf_bytes()
+        sa, sb = _dev_ptr(SFA, sfa_b, "SFA"), _dev_ptr(SFB, sfb_b, "SFB")
+    elif SFA is not None or SFB is not None:
+        raise ValueError("dense plan: SFA and SFB must be None")
+    o = GemmOpts(int(bool(neg_a)), int(bool(neg_b)), int(bool(sat_d)),
+                 _mask_ptr(row_mask, plan.M, "row_mask"), _mask_ptr(col_zero, plan.N, "col_zero"),
+                 int(bool(pred)))
+    rc = load().gemm_run_opts(plan.handle, a, b, sa, sb, d, int(beta), ctypes.byref(o), _stream_ptr(stream))
+    if rc != 0:
+        raise MswzError(rc, "gemm_run_opts")
 
 
 def desc_address(r, w, ldo, sdo, mode, major="k", origin=0) -> int:

@@ -45,13 +45,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile every csrc/*.hip and link libmswz.so (always rebuilds)."""
+def _stale(src: str) -> bool:
+    """True if src's object is missing or older than src or any csrc header."""
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + glob.glob(os.path.join(CSRC, "*.hpp"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(jobs: int | None = None, only_changed: bool = False) -> str:
+    """Compile every csrc/*.hip and link libmswz.so (always rebuilds, unless
+    only_changed: then sources whose objects are current are not recompiled)."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
+    if only_changed:
+        fresh = [s for s in srcs if not _stale(s)]
+        srcs = [s for s in srcs if _stale(s)]
+    else:
+        fresh = []
     jobs = jobs or min(len(srcs), 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))
+    objs = sorted(objs + [os.path.join(OBJ, os.path.basename(f) + ".o") for f in fresh])
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,4 +79,5 @@ def build(jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    import sys
+    print(build(only_changed="--changed" in sys.argv[1:]))

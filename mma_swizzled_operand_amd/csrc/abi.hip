@@ -283,6 +283,46 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
 
+int gemm_run_opts(const gemm_plan *p, const void *A, const void *B, const uint8_t *SFA, const uint8_t *SFB,
+                  void *D, int beta, const gemm_opts *o, void *stream)
+{
+    if (!p || !A || !B || !D)
+        return MSWZ_ERR_INVALID;
+    const bool mx = p->scale_vec_len != 0;
+    if (mx != (SFA != nullptr) || mx != (SFB != nullptr))
+        return MSWZ_ERR_INVALID;
+    if (beta != 0 && beta != 1)
+        return MSWZ_ERR_INVALID;
+    if (!is_aligned16(A) || !is_aligned16(B) || !is_aligned16(D) || (mx && (!is_aligned16(SFA) || !is_aligned16(SFB))))
+        return MSWZ_ERR_ALIGN;
+    mswz::EpiOpts e{};
+    if (o) {
+        e.neg = (o->neg_a != 0) != (o->neg_b != 0);
+        e.sat = o->sat_d != 0;
+        e.row_mask = o->row_mask;
+        e.col_zero = o->col_zero;
+        if ((reinterpret_cast<uintptr_t>(e.row_mask) & 3u) || (reinterpret_cast<uintptr_t>(e.col_zero) & 3u))
+            return MSWZ_ERR_ALIGN;
+        if (!o->pred)
+            return MSWZ_OK;
+    }
+    if (!e.neg && !e.sat && !e.row_mask && !e.col_zero)
+        return mx ? gemm_run_blockscaled(p, A, B, SFA, SFB, D, beta, stream) : gemm_run(p, A, B, D, beta, stream);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool a_mn = p->a_major == MSWZ_MAJOR_MN, b_mn = p->b_major == MSWZ_MAJOR_MN;
+    hipError_t err;
+    if (mx) {
+        mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
+                       p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};
+        err = mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st);
+    } else {
+        mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
+                          p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};
+        err = mswz::launch_dense256(p->a_dt == MSWZ_DT_BF16, a_mn, b_mn, a, st);
+    }
+    return err == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
+}
+
 void gemm_plan_destroy(gemm_plan *p) { delete p; }
 
 const char *gemm_status_str(int status)

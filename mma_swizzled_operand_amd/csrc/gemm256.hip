@@ -1,966 +1,14 @@
-// gemm256.hip — the large-tile GEMM for gfx950: one 512-thread workgroup (8
-// waves, two per SIMD) computes a 256 x 256 tile of
-//     D = beta*D + A.B^T                                   (fp16 / bf16)
-//     D = beta*D + sum_k (2^(SFA-127) a) (2^(SFB-127) b)   (OCP E4M3, 32-element blocks)
-// (tcgen05.mma page, "Operands and repeat axes", "Shared descriptors are
-// byte-stride contracts", "Weight-stationary and block scaling").
-//
-// Staging.  Each K step moves 128 bytes of every A and B tile row (64 16-bit
-// or 128 8-bit K elements) into one of two LDS stages, held in two distinct
-// LDS arrays with the K loop unrolled by two, so that reads of one stage never
-// wait for copies into the other.  K-major operands are copied with direct
-// global-to-LDS 16-byte loads: one wave instruction fills 1 KiB of LDS
-// contiguously, lane l at byte 16*l, i.e. eight 128-byte tile rows.  The
-// tile layout (layout.hpp) permutes 16-byte chunks inside a row, and the
-// permutation is its own inverse, so lane l simply fetches the source chunk
-// that belongs at its destination: chunk (l % 8) ^ key(row).  An MN-major
-// operand ([K][M] or [K][N]) is copied the same way into an MN-major tile (64
-// K rows of 512 bytes, chunks XOR-permuted by K row) and its MFMA fragments
-// are read with gfx950's transposing LDS reads, which hand each lane one M
-// (or N) row with four consecutive K values.
-// Scale bytes (MX) for the step's 256 A rows and 256 B rows are copied into a
-// small LDS stage by direct 4-byte loads, one wave instruction per 64 rows.
-//
-// Compute.  Wave w owns output rows 128*(w/4) .. +127 and columns 64*(w%4)
-// .. +63, 128 fp32 accumulators per lane: 8 x 4 blocks of 16x16x32 MFMA
-// output for 16-bit operands (4 x 2 blocks of 32x32x16 when both are
-// MN-major), 4 x 2 blocks of the 32x32x64 block-scaled MFMA for E4M3.  The
-// 16x16 shape moves fewer register bytes per flop than the 32x32 one; under
-// the chip's power limit it runs at a higher clock and is faster overall.
-// The MFMA's first operand is the B fragment and its second the A fragment,
-// so four consecutive accumulator registers hold four consecutive N columns
-// of one M row and the epilogue stores 16 bytes per lane.
+// gemm256.hip — run-time dispatch of the 256x256-tile GEMM (gemm256_kernel.hpp)
+// to its instantiations, one translation unit per operand kind and A major
+// (gemm256_bf16_ak.hip, gemm256_bf16_amn.hip, gemm256_f16_ak.hip,
+// gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e2m1.hip), so that they
+// compile in parallel.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
-#include <type_traits>
-
-#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace mswz {
-namespace {
-
-constexpr int kBM = 256, kBN = 256;
-constexpr int kATile = kBM * 128, kBTile = kBN * 128, kStage = kATile + kBTile;
-constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K steps) per row
-
-constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
-
-enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3 };
-
-// Direct-to-LDS copy of one K-major operand tile (256 rows x 128 bytes per K
-// step) through a buffer resource on the workgroup's 256-row panel.  With W
-// waves, wave w copies rows 8*(w + W*i) .. +7 for i = 0 .. 32/W - 1; lane l
-// takes row 8*(w + W*i) + l/8, whose layout key is (l/8) ^ ((w + W*i) % 8), so
-// it fetches chunk (l % 8) ^ (l/8) ^ ((w + W*i) % 8).
-//
-// The row is part of the per-lane offset, which the buffer's range check
-// covers (the scalar offset, here only the K step, is not checked), so in a
-// tail panel the rows beyond the operand read as zeros and no address beyond
-// the operand is formed.
-template <int W>
-struct DmaOperand {
-    static constexpr int kInstr = 32 / W;
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[kInstr];   // this lane's byte offset in the panel at K step 0, per instruction
-    uint32_t lds_off;        // LDS offset of this wave's first destination row inside a stage
-
-    // rows: rows of the panel inside the operand (fewer than 256 in a tail panel)
-    __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int wave, int lane,
-                         uint32_t tile_off)
-    {
-        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
-#pragma unroll
-        for (int i = 0; i < kInstr; ++i) {
-            const int r = 8 * (wave + W * i) + (lane >> 3);
-            const int chunk = (lane & 7) ^ (((lane >> 3) ^ (wave + W * i)) & 7);
-            voff[i] = uint32_t(r) * rb + chunk * 16;
-        }
-        lds_off = tile_off + 8 * wave * kTileRowBytes;
-    }
-
-    __device__ void issue(uint8_t *stage, int kt) const
-    {
-#pragma unroll
-        for (int i = 0; i < kInstr; ++i)
-            buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i], uint32_t(kt) * 128);
-    }
-};
-
-// Register-staged copy of one K-major operand tile (eight waves): the 512
-// threads each load four 16-byte chunks per step into registers (thread t:
-// rows t/8 + 64i, chunk t % 8; the row in the range-checked per-lane offset,
-// as in DmaOperand) and, after the step's MFMAs, store them to the other
-// stage at row*128 + ((chunk ^ key) << 4).  Eight consecutive lanes cover one
-// 128-byte row, so each wave-wide load reads eight whole rows and each
-// wave-wide store fills 1 KiB of LDS.
-template <int W>
-struct RegOperand {
-    static constexpr int kN = 2048 / (64 * W);
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[kN], lds0;
-    u32x4 r[kN];
-
-    __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int tid, uint32_t tile_off)
-    {
-        static_assert(W == 8, "register staging is built for eight waves");
-        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
-        const int row = tid >> 3, chunk = tid & 7;
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            voff[i] = uint32_t(row + 8 * W * i) * rb + chunk * 16;
-        lds0 = tile_off + tile_offset(row, chunk);   // key(row + 64i) == key(row): period 64
-    }
-    __device__ void load(int kt)
-    {
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            r[i] = buffer_load16(rsrc, voff[i], uint32_t(kt) * 128);
-    }
-    __device__ void store(uint8_t *stage) const
-    {
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            lds_write16(stage, lds0 + i * 8 * W * kTileRowBytes, r[i]);
-    }
-};
-
-// Direct-to-LDS copy of one MN-major 16-bit operand ([K][R] storage, R = M
-// or N) for a 256-wide tile.  The step's tile is 64 K rows of 512 bytes (256
-// values); 16-byte chunk c of K row k (values 8c .. 8c+7) sits at position
-// c ^ mn_key(k) of the row, mn_key(k) = 4 * (k % 4) ^ 2 * ((k / 16) % 2).
-// Wave instruction q = w + W*i fills K rows 2q and 2q+1, lane l writing
-// position l % 32 of row k = 2q + l/32, so it fetches chunk
-// (l % 32) ^ mn_key(k).  Since 2w + l/32 < 2W and 2W*i is a multiple of 2W,
-// k % 4 comes from the lane and wave only and bit 4 of k from i only.  The
-// fragments are read back with transposing LDS reads (mn_frag_base below).
-template <int W>
-struct DmaMnOperand {
-    static constexpr int kInstr = 32 / W;
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[2], pitch, lds_off;   // voff[bit 4 of the instruction's K rows]
-
-    // A chunk whose columns lie beyond the operand (a tail tile) is fetched
-    // from the tile's first columns instead: its values only reach outputs
-    // beyond M or N, and every address stays inside the operand.
-    // ld: elements from one K row of the operand to the next (>= R)
-    __device__ void init(const uint8_t *X, int R, int ld, int row0, int K, int wave, int lane,
-                         uint32_t tile_off)
-    {
-        pitch = uint32_t(ld) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * pitch + uint32_t(R - row0) * 2);
-        const int kr = lane >> 5;
-#pragma unroll
-        for (int b4 = 0; b4 < 2; ++b4) {
-            const int c = (lane & 31) ^ (4 * ((2 * wave + kr) & 3)) ^ (2 * b4);
-            const int cs = row0 + 8 * c < R ? c : 0;
-            voff[b4] = uint32_t(2 * wave + kr) * pitch + 16 * cs;
-        }
-        lds_off = tile_off + 2 * wave * kMnRowBytes;
-    }
-    __device__ void issue(uint8_t *stage, int kt) const
-    {
-#pragma unroll
-        for (int i = 0; i < kInstr; ++i)
-            buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, voff[((2 * W * i) >> 4) & 1],
-                              (uint32_t(kt) * 64 + 2 * W * i) * pitch);
-    }
-};
-
-// LDS byte offset, at sub-step 0 and first half, of this lane's piece of the
-// 32-row MFMA fragment whose tile rows start at rbase (a multiple of 32) in an
-// MN-major tile.  The 32x32x16 operand wants, in lane l, row l % 32 and K
-// values 8*(l/32) .. +7.  With lane t = l % 16 = 4j + a of its group, the
-// lane points at K row 8*(l/32) + j, values rbase + 16*((l/16) % 2) + 4a ..
-// +3; the transposing read then hands lane l row rbase + l % 32 and K values
-// 8*(l/32) .. +3.  The second half (K + 4) is 4 rows further, sub-step ks
-// 16*ks rows further and, as bit 4 of its K rows is ks % 2, with its chunk
-// XOR 2 (byte offset XOR 32) for odd ks.  Within each half wave the 32
-// pieces cover 16 distinct chunk positions of four K rows (k % 4 = j), so the
-// read is free of bank conflicts.
-__device__ __forceinline__ uint32_t mn_frag_base(uint32_t tile_off, int rbase, int lane)
-{
-    const int t = lane & 15, j = t >> 2, a = t & 3, g1 = (lane >> 4) & 1, h = lane >> 5;
-    const int chunk = rbase / 8 + 2 * g1 + (a >> 1);
-    return tile_off + uint32_t(8 * h + j) * kMnRowBytes + (uint32_t(chunk ^ (4 * j)) << 4) + 8 * (a & 1);
-}
-
-// K-block order of the 16x16x32 fragments.  Lane group g = l/16 of that
-// MFMA supplies 8 K values of its row; group g takes the 8-value block
-// kblk16(g) = 2*(g%2) + g/2 of the 32-wide sub-step, the same for A and B, so
-// the sum over K is unchanged.  With the natural order, 16-byte reads of
-// K-major tiles by lanes 8p .. 8p+7 and 32+8p .. 32+8p+7 (served together)
-// would hit the same banks; with this order the two chunks differ in their
-// lowest bit and never do.
-__device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
-
-// First-half chunk of lane group g for the block-scaled 16x16x128 MFMA
-// (second half: chunk + 4).  The chunk must lie in scale block g/2, i.e. be
-// 2*(g/2) or 2*(g/2) + 1, so groups 0 and 1 (and 2 and 3) read chunks that
-// differ only in their lowest bit, whose LDS positions collide for rows r and
-// r + 8 of the tile.  E4M3 fragments therefore take their 16 rows from two
-// runs of 8 rows 16 apart (row16 below), and groups g and g + 2 take chunks
-// of different parity.  Measured bank-conflict counts of the patterns used
-// here fit a 16-byte read that serves together the 16 lanes agreeing in lane
-// bits 1 and 5; these choices are conflict-free under that grouping and under
-// the grouping by lane bits 3 and 4.
-__device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
-
-// Compile-time loop: fn(std::integral_constant<int, F>), ..., up to L - 1.
-template <int F, int L, class Fn>
-__device__ __forceinline__ void static_for(Fn &&fn)
-{
-    if constexpr (F < L) {
-        fn(std::integral_constant<int, F>{});
-        static_for<F + 1, L>(fn);
-    }
-}
-
-// Read order of one K step's fragments for a TM x TN grid of 16x16 MFMAs
-// issued A-block-major (MFMA m = TN * i + j): every A block i and B block j
-// is read before the first MFMA that uses it (MFMA TN * i, resp. j), in the
-// order of that first use, and `ahead` MFMAs early.  issued(m) counts the
-// reads issued before MFMA m + 1; item(r) names read r: i + 1 for A block i,
-// -(j + 1) for B block j.
-template <int TM, int TN, int ahead>
-struct FragSchedule {
-    static constexpr int issued(int m)
-    {
-        int c = 0;
-        for (int i = 0; i < TM; ++i)
-            c += TN * i <= m + ahead;
-        for (int j = 0; j < TN; ++j)
-            c += j <= m + ahead;
-        return c;
-    }
-    static constexpr int item(int r)
-    {
-        int ia = 0, ib = 0;
-        for (int k = 0; k < TM + TN; ++k) {
-            const int na = ia < TM ? TN * ia : 1 << 20, nb = ib < TN ? ib : 1 << 20;
-            if (na <= nb) {
-                if (k == r)
-                    return ia + 1;
-                ++ia;
-            } else {
-                if (k == r)
-                    return -(ib + 1);
-                ++ib;
-            }
-        }
-        return 0;
-    }
-};
-
-// Row of a 64-row group held by stage slot l when each row's scales take 16
-// bytes (four K steps): l with bits 3 and 4 swapped (an involution).  A scale
-// read of 16-row fragment block b touches rows row16(b, x), x = 0..15: bits
-// 0-2 and 4 from x, bits 3 and 5 from b.  In this order they are the 16
-// consecutive slots 16 * b + x (16 bytes apart, on 16 different 4-bank groups
-// of the 64 banks of 4 bytes), so the read is conflict-free and block b sits
-// 256 * b bytes from a per-lane base.  In row order, rows x and x + 8 of one
-// block would share their banks.
-__device__ __forceinline__ int sf_slot_row(int l) { return (l & ~24) | ((l & 8) << 1) | ((l & 16) >> 1); }
-
-// Tile row (relative to the wave's first row) of row x (0..15) of 16-row
-// fragment block b: 16-bit operands use 16 consecutive rows; E4M3 operands
-// rows 32*(b/2) + 8*(b%2) + {0..7, 16..23}.  Runs of 4 consecutive x stay
-// consecutive rows, so the epilogue still stores 16 bytes per lane.
-template <bool MX>
-__device__ __forceinline__ int row16(int b, int x)
-{
-    return MX ? 32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3) : 16 * b + x;
-}
-
-// The same for the 16-row fragment of the 16x16x32 MFMA in an MN-major tile:
-// lane t = l % 16 = 4j + a of group g points at K row 8*kblk16(g) + j (bit 4
-// of which is g % 2), values rbase + 4a .. +3; the second half is 4 K rows
-// further, sub-step s 32*s rows further.
-__device__ __forceinline__ uint32_t mn_frag_base16(uint32_t tile_off, int rbase, int lane)
-{
-    const int t = lane & 15, j = t >> 2, a = t & 3, g = lane >> 4;
-    const int chunk = (rbase / 8 + (a >> 1)) ^ (4 * j) ^ (2 * (g & 1));
-    return tile_off + uint32_t(8 * kblk16(g) + j) * kMnRowBytes + (uint32_t(chunk) << 4) + 8 * (a & 1);
-}
-
-// Register-staged copy of one MN-major 16-bit operand ([K][R] storage, R = M
-// or N) for a 256-row tile: block `blk` (0..255) is tile rows 8*(blk % 32)
-// .. +7 and K rows 8*(blk / 32) .. +7 of the step; the active thread loads
-// its eight 16-byte K-row pieces, transposes the 8x8 block in registers and
-// stores eight K-contiguous 16-byte chunks.
-struct MnOperand {
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff, kstride, lds_base;
-    int mb, kc;
-    bool active;
-    u32x4 r[8];
-
-    __device__ void init(const uint8_t *X, int R, int ld, int row0, int K, int blk, bool act,
-                         uint32_t tile_off)
-    {
-        active = act;
-        mb = blk & 31;
-        kc = (blk >> 5) & 7;
-        kstride = uint32_t(ld) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * kstride + uint32_t(R - row0) * 2);
-        // columns beyond the operand (tail tile): fetch the tile's first columns
-        // instead, as in DmaMnOperand
-        voff = uint32_t(8 * kc) * kstride + 16 * (row0 + 8 * mb < R ? mb : 0);
-        lds_base = tile_off;
-    }
-    __device__ void load(int kt)
-    {
-        if (active) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r[j] = buffer_load16(rsrc, voff, (uint32_t(kt) * 64 + j) * kstride);
-        }
-    }
-    __device__ void store(uint8_t *stage) const
-    {
-        if (active) {
-            u32x4 t[8];
-            transpose8x8_b16(r, t);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                lds_write16(stage, lds_base + tile_offset(8 * mb + i, kc), t[i]);
-        }
-    }
-};
-
-// W waves per workgroup: W = 8 gives each wave a 128 x 64 output sub-tile
-// (two waves per SIMD), W = 4 a 128 x 128 sub-tile (one wave per SIMD,
-// accumulators in AGPRs, a third fewer LDS bytes read per MFMA).
-// Four consecutive outputs of one row of D, as fp32 or rounded to nearest
-// even into bf16 / fp16 (OUT, see OutKind); with BETA the old values, read in
-// the same kind, are added first.
-template <int OUT, bool BETA>
-__device__ __forceinline__ void store_d4(void *D, size_t idx, f32x4 v)
-{
-    if constexpr (OUT == kOutF32) {
-        f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(D) + idx);
-        if constexpr (BETA)
-            v += *p;
-        *p = v;
-    } else {
-        using T = std::conditional_t<OUT == kOutBf16, __bf16, _Float16>;
-        typedef T t4 __attribute__((ext_vector_type(4)));
-        t4 *p = reinterpret_cast<t4 *>(static_cast<T *>(D) + idx);
-        if constexpr (BETA) {
-            const t4 old = *p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] += float(old[e]);
-        }
-        t4 out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            out[e] = T(v[e]);
-        *p = out;
-    }
-}
-
-template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32>
-__global__ void __launch_bounds__(64 * W)
-gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
-               const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
-               void *__restrict__ D, int M, int N, int K, int lda, int ldb, int ldd, int tiles_m,
-               int tiles_n, int group_m)
-{
-    static_assert(!((A_MN || B_MN) && (KIND == kE4m3 || KIND == kE2m1)),
-                  "MN-major operands are built for 16-bit only");
-    static_assert(W == 4 || W == 8, "4 or 8 waves");
-    constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
-    constexpr int kWavesN = 256 / (32 * TN);     // waves along N
-    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1;
-    constexpr bool kMx = kFp8 || kFp4;
-    static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
-    // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
-    // E2M1 (packed two per byte) K elements
-    constexpr int kStepK = kFp4 ? 256 : kFp8 ? 128 : 64;
-
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    __shared__ __attribute__((aligned(256))) uint8_t scl0[kMx ? kScaleStage : 4];
-    __shared__ __attribute__((aligned(256))) uint8_t scl1[kMx ? kScaleStage : 4];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 31, lh = lane >> 5;
-    int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * kBM, n0 = tn * kBN;
-    const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
-    // bytes from one K-major operand row to the next (lda, ldb are in elements)
-    const uint32_t a_row_bytes = uint32_t(lda) * 128 / kStepK, b_row_bytes = uint32_t(ldb) * 128 / kStepK;
-    const int KT = K / kStepK;
-    // M and N need not be multiples of 256: a tail tile reads zeros (K-major
-    // rows beyond the operand, through the buffer range) or values that only
-    // reach outputs beyond M or N (MN-major), and the epilogue stores only
-    // outputs inside D
-    const int rows_a = min(kBM, M - m0), rows_b = min(kBN, N - n0);
-
-    // ---- operand copies ---------------------------------------------------------
-    // K-major operands: copied straight into LDS, or through registers when
-    // REG bit 0 (A) / bit 1 (B) is set.  MN-major operands: copied straight
-    // into an MN-major LDS tile and read with transposing LDS reads, or, when
-    // REG bit 2 is set, 8x8 register transposes into the K-contiguous layout
-    // (A by threads 0..255 and B by threads 256..511 with eight waves, both
-    // by every thread with four).
-    constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) && !B_MN;
-    constexpr bool kDmaA = !A_MN && !kRegA, kDmaB = !B_MN && !kRegB;
-    constexpr bool kMnReg = (REG & 4) != 0;
-    constexpr bool kTrA = A_MN && !kMnReg, kTrB = B_MN && !kMnReg;
-    DmaOperand<W> da, db;
-    if constexpr (kDmaA)
-        da.init(A, m0, rows_a, a_row_bytes, wave, lane, 0);
-    if constexpr (kDmaB)
-        db.init(B, n0, rows_b, b_row_bytes, wave, lane, kATile);
-    RegOperand<W> rga, rgb;
-    if constexpr (kRegA)
-        rga.init(A, m0, rows_a, a_row_bytes, tid, 0);
-    if constexpr (kRegB)
-        rgb.init(B, n0, rows_b, b_row_bytes, tid, kATile);
-    DmaMnOperand<W> dma_mna, dma_mnb;
-    if constexpr (kTrA)
-        dma_mna.init(A, M, lda, m0, K, wave, lane, 0);
-    if constexpr (kTrB)
-        dma_mnb.init(B, N, ldb, n0, K, wave, lane, kATile);
-    MnOperand mna, mnb;
-    if constexpr (A_MN && kMnReg)
-        mna.init(A, M, lda, m0, K, tid & 255, W == 4 || tid < 256, 0);
-    if constexpr (B_MN && kMnReg)
-        mnb.init(B, N, ldb, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
-
-    // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
-    // for g >= 4) is copied by wave g % W.  Per K step (kScaleGroups false):
-    // lane l copies the step's 32-bit scale word of row 64*(g%4) + l into
-    // scale-stage word 64*g + l.  Per group of four K steps (kScaleGroups, the
-    // 16x16 path with eight waves and K a multiple of 1024): lane l copies the
-    // 16 scale bytes of the four steps of row 64*(g%4) + sf_slot_row(l) into
-    // stage bytes 16*(64g + l) .. +15 (the slot order keeps the scale reads
-    // free of bank conflicts).  A row's scales for one step are only 4 bytes and consecutive rows
-    // are K/32 bytes apart, so a per-step copy touches one cache line per lane
-    // for 4 useful bytes; fetching four steps at once cuts those line accesses
-    // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kFp8 && (REG & 8) != 0 && W == 8;   // the 16x16 E4M3 path
-    constexpr int kSfInstr = 8 / W;
-    const uint32_t sf_row = uint32_t(K) / 32;
-    __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
-    uint32_t sf_voff = 0;
-    if constexpr (kMx) {
-#pragma unroll
-        for (int q = 0; q < kSfInstr; ++q) {
-            const int g = wave + W * q;
-            const bool is_b = g >= 4;
-            sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row,
-                                   uint32_t(is_b ? rows_b : rows_a) * sf_row);
-        }
-        // with kScaleGroups lane l copies row sf_slot_row(l) of its group
-        sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
-    }
-
-    auto store_regs = [&](uint8_t *stage) {
-        if constexpr (A_MN && kMnReg)
-            mna.store(stage);
-        if constexpr (B_MN && kMnReg)
-            mnb.store(stage);
-        if constexpr (kRegA)
-            rga.store(stage);
-        if constexpr (kRegB)
-            rgb.store(stage);
-    };
-
-    auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
-        if constexpr (A_MN && kMnReg)
-            mna.load(kt);
-        if constexpr (kRegA)
-            rga.load(kt);
-        if constexpr (kDmaA)
-            da.issue(stage, kt);
-        if constexpr (kTrA)
-            dma_mna.issue(stage, kt);
-        if constexpr (B_MN && kMnReg)
-            mnb.load(kt);
-        if constexpr (kTrB)
-            dma_mnb.issue(stage, kt);
-        if constexpr (kRegB)
-            rgb.load(kt);
-        if constexpr (kDmaB)
-            db.issue(stage, kt);
-        if constexpr (kMx) {
-            // scale words per row per step: one (E4M3, four 32-element blocks)
-            // or two (E2M1, eight blocks); word w of 64-row group g lands at
-            // stage byte 2048w + 256g + 4*(row in group)
-            constexpr int kWords = kFp4 ? 2 : 1;
-#pragma unroll
-            for (int q = 0; q < kSfInstr; ++q)
-#pragma unroll
-                for (int w = 0; w < kWords; ++w)
-                    buffer_load_lds4(sf_rsrc[q], sstage + 2048 * w + 256 * (wave + W * q), sf_voff,
-                                     4u * uint32_t(kWords * kt + w));
-        }
-    };
-    // the operand copies of one step without its scale words (grouped scales)
-    auto issue_ab = [&](uint8_t *stage, int kt) {
-        if constexpr (kDmaA)
-            da.issue(stage, kt);
-        if constexpr (kDmaB)
-            db.issue(stage, kt);
-    };
-    // scale group `grp` (K steps 4grp .. 4grp+3), kScaleGroups only
-    auto issue_scales = [&](uint8_t *sstage, int grp) {
-        if constexpr (kScaleGroups)
-            buffer_load_lds16(sf_rsrc[0], sstage + 1024 * wave, sf_voff, 16u * uint32_t(grp));
-    };
-
-    // ---- MFMA operand read addresses -------------------------------------------
-    // Block row `row` of a fragment, 16-byte chunk c, sits at
-    // row*128 + ((c ^ key(row)) << 4).  For sub-step ks the chunk is
-    // 2ks ^ lh (16-bit) or 4ks ^ lh and 4ks ^ 2 ^ lh (8-bit), so every address
-    // is one per-fragment base XOR a constant.
-    // In an MN-major tile read with transposing reads (kTrA / kTrB) the base
-    // is mn_frag_base and sub-step ks, half e sits (16ks + 4e) K rows further.
-    uint32_t abase[TM], bbase[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const uint32_t row = wm + 32 * i + lr;
-        abase[i] = kTrA ? mn_frag_base(0, wm + 32 * i, lane)
-                        : row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const uint32_t row = wn + 32 * j + lr;
-        bbase[j] = kTrB ? mn_frag_base(kATile, wn + 32 * j, lane)
-                        : kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
-    }
-
-    // 16x16 MFMAs (REG bit 3): the same wave tile as 2TM x 2TN blocks of
-    // 16 x 16.  16-bit: fragment rows l % 16, 16-byte chunk 4s + kblk16(l/16)
-    // for the 32-wide sub-step s, i.e. base XOR (s << 6).  E4M3: one 16x16x128
-    // MFMA per K step, chunks mx_chunk16(l/16) and that + 4 (base XOR 64).
-    constexpr bool kMf16 = (REG & 8) != 0;
-    constexpr int TM16 = kMf16 ? 2 * TM : 1, TN16 = kMf16 ? 2 * TN : 1;
-    uint32_t abase16[TM16], bbase16[TN16];
-    if constexpr (kMf16) {
-        const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int i = 0; i < TM16; ++i) {
-            const uint32_t row = wm + row16<kFp8>(i, r16);
-            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
-            abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
-                              : row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
-        }
-#pragma unroll
-        for (int j = 0; j < TN16; ++j) {
-            const uint32_t row = wn + row16<kFp8>(j, r16);
-            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
-            bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
-                              : kATile + row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
-        }
-    }
-
-    f32x16 acc[kMf16 ? 1 : TN][kMf16 ? 1 : TM];
-    f32x4 acc4[TN16][TM16];
-    if constexpr (kMf16) {
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-#pragma unroll
-            for (int i = 0; i < TM16; ++i)
-                acc4[j][i] = f32x4{};
-    } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                acc[j][i] = f32x16{};
-    }
-
-    auto compute16 = [&](const uint8_t *s) {
-        uint32_t ab[TM], bb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            ab[i] = opaque(abase[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bb[j] = opaque(bbase[j]);
-        u32x4 af[2][TM], bf[2][TN];
-        auto frag = [&](uint32_t base, int ks, bool tr) {
-            if (!tr)
-                return lds_read16(s, base ^ (ks << 5));
-            const uint32_t b = base ^ ((ks & 1) << 5);
-            const u32x2 lo = lds_read_tr16(s, b + uint32_t(16 * ks) * kMnRowBytes);
-            const u32x2 hi = lds_read_tr16(s, b + uint32_t(16 * ks + 4) * kMnRowBytes);
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
-        auto rd = [&](int ks, u32x4 *a, u32x4 *b) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = frag(ab[i], ks, kTrA);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                b[j] = frag(bb[j], ks, kTrB);
-        };
-        rd(0, af[0], bf[0]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks + 1 < 4)
-                rd(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[j][i] = mfma_32x32x16<KIND == kBf16>(bf[ks & 1][j], af[ks & 1][i], acc[j][i]);
-        }
-    };
-
-    auto compute_mx = [&](const uint8_t *s, const uint8_t *ss) {
-        uint32_t ab[TM], bb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            ab[i] = opaque(abase[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bb[j] = opaque(bbase[j]);
-        // lane half lh supplies the scale of K block lh of its row: byte lh (sub-step 0)
-        // and byte 2 + lh (sub-step 1) of the row's scale word
-        uint32_t sa[TM], sb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            sa[i] = *reinterpret_cast<const uint32_t *>(ss + 4 * (wm + 32 * i + lr)) >> (8 * lh);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            sb[j] = *reinterpret_cast<const uint32_t *>(ss + kBM * 4 + 4 * (wn + 32 * j + lr)) >> (8 * lh);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            i32x8 af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const u32x4 lo = lds_read16(s, ab[i] ^ (ks << 6));
-                const u32x4 hi = lds_read16(s, ab[i] ^ (ks << 6) ^ 32u);
-                af[i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const u32x4 lo = lds_read16(s, bb[j] ^ (ks << 6));
-                const u32x4 hi = lds_read16(s, bb[j] ^ (ks << 6) ^ 32u);
-                bf[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    if (ks == 0)
-                        acc[j][i] = mfma_scale_32x32x64_e4m3<0>(bf[j], af[i], acc[j][i], sb[j], sa[i]);
-                    else
-                        acc[j][i] = mfma_scale_32x32x64_e4m3<2>(bf[j], af[i], acc[j][i], sb[j], sa[i]);
-                }
-        }
-    };
-
-    auto compute16x16 = [&](const uint8_t *s) {
-        uint32_t ab[TM16], bb[TN16];
-#pragma unroll
-        for (int i = 0; i < TM16; ++i)
-            ab[i] = opaque(abase16[i]);
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-            bb[j] = opaque(bbase16[j]);
-        auto frag = [&](uint32_t base, int ks, bool tr) {
-            if (!tr)
-                return lds_read16(s, base ^ (ks << 6));
-            const u32x2 lo = lds_read_tr16(s, base + uint32_t(32 * ks) * kMnRowBytes);
-            const u32x2 hi = lds_read_tr16(s, base + uint32_t(32 * ks + 4) * kMnRowBytes);
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 af[TM16], bf[TN16];
-#pragma unroll
-            for (int i = 0; i < TM16; ++i)
-                af[i] = frag(ab[i], ks, kTrA);
-#pragma unroll
-            for (int j = 0; j < TN16; ++j)
-                bf[j] = frag(bb[j], ks, kTrB);
-#pragma unroll
-            for (int j = 0; j < TN16; ++j)
-#pragma unroll
-                for (int i = 0; i < TM16; ++i)
-                    acc4[j][i] = mfma_16x16x32<KIND == kBf16>(bf[j], af[i], acc4[j][i]);
-        }
-    };
-
-    // sf_stride: scale-stage bytes per row (4: one step's word; 16: a group of
-    // four steps); widx: which of the row's words (the step inside its group)
-    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx) {
-        uint32_t ab[TM16], bb[TN16];
-#pragma unroll
-        for (int i = 0; i < TM16; ++i)
-            ab[i] = opaque(abase16[i]);
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-            bb[j] = opaque(bbase16[j]);
-        // lane l supplies the scale of K block l/16 of row l % 16: byte l/16 of
-        // the row's scale word, read as one byte (a word and a per-lane shift
-        // would keep one more register live through the loop)
-        // (row16(b, x) = row16(0, x) + 32*(b/2) + 8*(b%2): one per-lane base
-        // and constant offsets, kept opaque so that they are not hoisted).
-        // With kScaleGroups the rows sit in the slot order of sf_slot_row
-        // (both the per-step words and the 16-byte groups): block b of row x
-        // is slot (wave's first row) + 16 * b + x.
-        const int r16 = lane & 15;
-        static_assert(!kScaleGroups || (32 * TN) % 64 == 0, "wave rows start 64-row groups");
-        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
-        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
-        auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
-        auto frag = [&](uint32_t base) {
-            const u32x4 lo = lds_read16(s, base);
-            const u32x4 hi = lds_read16(s, base ^ 64u);
-            return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        // MFMA m = TN16 * i + j; each block's fragment and scale are read two
-        // MFMAs ahead of first use, in that order (FragSchedule), so that a
-        // wave's first MFMA waits for a few reads rather than for the whole
-        // step's B fragments and scales, which all eight waves request at once
-        // after the barrier.
-        using Sched = FragSchedule<TM16, TN16, 2>;
-        uint32_t sa[TM16], sb[TN16];
-        i32x8 bf[TN16], af[TM16];
-        static_for<0, TM16 * TN16>([&](auto mc) {
-            constexpr int m = decltype(mc)::value;
-            constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
-            static_for<c0, c1>([&](auto rc) {
-                constexpr int it = Sched::item(decltype(rc)::value);
-                if constexpr (it > 0) {
-                    sa[it - 1] = ss[sfa + sf_off(it - 1) + 4 * widx];
-                    af[it - 1] = frag(ab[it - 1]);
-                } else {
-                    sb[-it - 1] = ss[sfb + sf_off(-it - 1) + 4 * widx];
-                    bf[-it - 1] = frag(bb[-it - 1]);
-                }
-            });
-            if constexpr (c1 > c0)
-                __builtin_amdgcn_sched_group_barrier(0x100, 3 * (c1 - c0), 0);   // DS reads
-            constexpr int i = m / TN16, j = m % TN16;
-            acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
-        });
-    };
-
-    // E2M1: two 128-element sub-steps per step; lane (r, g) reads chunk
-    // 4ks + kblk16(g) of its row (one 32-element scale block, 16 bytes) into
-    // the low half of the operand and supplies that block's scale: byte
-    // kblk16(g) of the row's scale word ks.
-    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss) {
-        uint32_t ab[TM16], bb[TN16];
-#pragma unroll
-        for (int i = 0; i < TM16; ++i)
-            ab[i] = opaque(abase16[i]);
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-            bb[j] = opaque(bbase16[j]);
-        // lane group g supplies the scale of block kblk16(g): that byte of its
-        // row's scale word, read as one byte
-        const int r16 = lane & 15, sbyte = kblk16(lane >> 4);
-        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16) + sbyte));
-        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16) + sbyte));
-        const u32x4 zero = {0, 0, 0, 0};
-        auto frag = [&](uint32_t base, int ks) {
-            const u32x4 v = lds_read16(s, base ^ uint32_t(ks << 6));
-            return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        // reads two MFMAs ahead of first use, as in compute_mx16
-        using Sched = FragSchedule<TM16, TN16, 2>;
-        static_for<0, 2>([&](auto ksc) {
-            constexpr int ks = decltype(ksc)::value;
-            uint32_t sa[TM16], sb[TN16];
-            i32x8 bf[TN16], af[TM16];
-            static_for<0, TM16 * TN16>([&](auto mc) {
-                constexpr int m = decltype(mc)::value;
-                constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
-                static_for<c0, c1>([&](auto rc) {
-                    constexpr int it = Sched::item(decltype(rc)::value);
-                    if constexpr (it > 0) {
-                        sa[it - 1] = ss[2048 * ks + sfa + 64 * (it - 1)];
-                        af[it - 1] = frag(ab[it - 1], ks);
-                    } else {
-                        sb[-it - 1] = ss[2048 * ks + sfb + 64 * (-it - 1)];
-                        bf[-it - 1] = frag(bb[-it - 1], ks);
-                    }
-                });
-                if constexpr (c1 > c0)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (c1 - c0), 0);   // DS reads
-                constexpr int i = m / TN16, j = m % TN16;
-                acc4[j][i] = mfma_scale_16x16x128_e2m1(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
-            });
-        });
-    };
-
-    auto compute = [&](const uint8_t *s, const uint8_t *ss) {
-        if constexpr (kFp4)
-            compute_fp4(s, ss);
-        else if constexpr (kMx && kMf16)
-            compute_mx16(s, ss, 4, 0);
-        else if constexpr (kMx)
-            compute_mx(s, ss);
-        else if constexpr (kMf16)
-            compute16x16(s);
-        else
-            compute16(s);
-    };
-
-    // ---- main loop: two K steps per iteration, one stage array each; an odd
-    // final step (already in lds0) is computed after the loop.  The loop body
-    // has no branches: in the last pair of an even step count the copy into
-    // lds0 repeats step KT-1 into a stage nobody reads again, which keeps the
-    // compiler from draining the copies in flight at a control-flow merge. ------
-    if constexpr (kScaleGroups) {
-        if (KT % 8 == 0) {
-            // Eight K steps per iteration: operand stages alternate lds0 /
-            // lds1, scale groups alternate scl0 / scl1 every four steps.  A
-            // group's scales are copied during the third step of the group
-            // before it, as that step's last copy, and that step's barrier
-            // leaves this one copy in flight (vector-memory completions are
-            // counted in order, so it cannot hold up the step's operand
-            // copies): the scattered scale reads get two steps to land, and
-            // the stage they overwrite was last read four steps earlier.
-            // Copies beyond the last step or group repeat the last one into a
-            // stage nobody reads again, so the loop has no branches.
-            const int NG = KT / 4;
-            // a step's work is not moved across its closing barrier, which
-            // keeps the eight unrolled steps from overlapping in registers
-            auto step_end = [] {
-                __builtin_amdgcn_sched_barrier(0);
-                lds_barrier_keep_vm<0>();
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            auto step_end_keep1 = [] {
-                __builtin_amdgcn_sched_barrier(0);
-                lds_barrier_keep_vm<1>();
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            issue_scales(scl0, 0);
-            issue_ab(lds0, 0);
-            __syncthreads();
-            for (int kt = 0; kt < KT; kt += 8) {
-                const int g = kt / 4;
-                issue_ab(lds1, kt + 1);
-                compute_mx16(lds0, scl0, 16, 0);
-                step_end();
-                issue_ab(lds0, kt + 2);
-                compute_mx16(lds1, scl0, 16, 1);
-                step_end();
-                issue_ab(lds1, kt + 3);
-                issue_scales(scl1, g + 1);
-                compute_mx16(lds0, scl0, 16, 2);
-                step_end_keep1();
-                issue_ab(lds0, kt + 4);
-                compute_mx16(lds1, scl0, 16, 3);
-                step_end();
-                issue_ab(lds1, kt + 5);
-                compute_mx16(lds0, scl1, 16, 0);
-                step_end();
-                issue_ab(lds0, kt + 6);
-                compute_mx16(lds1, scl1, 16, 1);
-                step_end();
-                issue_ab(lds1, kt + 7);
-                issue_scales(scl0, min(g + 2, NG - 1));
-                compute_mx16(lds0, scl1, 16, 2);
-                step_end_keep1();
-                issue_ab(lds0, min(kt + 8, KT - 1));
-                compute_mx16(lds1, scl1, 16, 3);
-                step_end();
-            }
-            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
-            goto epilogue;
-        }
-    }
-    {
-    issue_step(lds0, scl0, 0);
-    store_regs(lds0);
-    __syncthreads();
-
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-        issue_step(lds1, scl1, kt + 1);
-        compute(lds0, scl0);
-        store_regs(lds1);
-        lds_barrier_keep_vm<0>();
-        issue_step(lds0, scl0, min(kt + 2, KT - 1));
-        compute(lds1, scl1);
-        store_regs(lds0);
-        lds_barrier_keep_vm<0>();
-    }
-    if (kt < KT)
-        compute(lds0, scl0);
-    __syncthreads();   // no copy may still be writing LDS when the workgroup ends
-    }
-
-    // ---- epilogue -------------------------------------------------------------
-epilogue:
-    if constexpr (kMf16) {
-        // 16x16 block (j, i): lane l holds fragment row l % 16 of A block i
-        // and fragment rows 4(l/16) .. +3 of B block j
-#pragma unroll
-        for (int j = 0; j < TN16; ++j)
-#pragma unroll
-            for (int i = 0; i < TM16; ++i) {
-                const int m = m0 + wm + row16<kFp8>(i, lane & 15);
-                const int n = n0 + wn + row16<kFp8>(j, 4 * (lane >> 4));
-                if (m >= M || n >= N)
-                    continue;
-                store_d4<OUT, BETA>(D, size_t(m) * ldd + n, acc4[j][i]);
-            }
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm + 32 * i + lr;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn + 32 * j + 8 * q + 4 * lh;
-                if (m >= M || n >= N)
-                    continue;
-                const f32x4 v = {acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                                 acc[j][i][4 * q + 3]};
-                store_d4<OUT, BETA>(D, size_t(m) * ldd + n, v);
-            }
-        }
-}
-
-template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32>
-hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
-{
-    const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
-    const int blocks = tiles_m * tiles_n;
-    const uint8_t *A = static_cast<const uint8_t *>(a.A);
-    const uint8_t *B = static_cast<const uint8_t *>(a.B);
-    if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
-                           tiles_n, a.group_m);
-    else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
-                           tiles_n, a.group_m);
-    return hipGetLastError();
-}
-
-// bf16 / fp16 output: the default pipeline only
-template <int KIND, bool A_MN, bool B_MN>
-hipError_t launch_out(const MxArgs &a, hipStream_t stream)
-{
-    constexpr int kReg = (A_MN && B_MN) ? 0 : 8;
-    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16>(a, stream)
-                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16>(a, stream);
-}
-
-}  // namespace
 
 // Pipeline configuration of the 256x256 tile, selected at run time by the
 // environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
@@ -977,53 +25,22 @@ int config256()
     return cfg;
 }
 
-namespace {
-
-template <int KIND, bool A_MN, bool B_MN>
-hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
-{
-    if (a.out != kOutF32)
-        return launch_out<KIND, A_MN, B_MN>(a, stream);
-    switch (config256()) {
-    case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);
-    case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);
-    case 8: return launch_kind<KIND, A_MN, B_MN, 8, 2>(a, stream);
-    case 12: return launch_kind<KIND, A_MN, B_MN, 8, 3>(a, stream);
-    case 32: return launch_kind<KIND, A_MN, B_MN, 8, 4>(a, stream);
-    case 64: return launch_kind<KIND, A_MN, B_MN, 8, 8>(a, stream);
-    case 128: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
-    // 16x16x32 MFMAs for 16-bit operands, except with both operands MN-major,
-    // where they would need more than 256 VGPRs
-    default: return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
-    }
-}
-
-template <int KIND>
-hipError_t launch_majors(bool a_mn, bool b_mn, const MxArgs &a, hipStream_t stream)
-{
-    if (a_mn)
-        return b_mn ? launch_cfg<KIND, true, true>(a, stream) : launch_cfg<KIND, true, false>(a, stream);
-    return b_mn ? launch_cfg<KIND, false, true>(a, stream) : launch_cfg<KIND, false, false>(a, stream);
-}
-
-}  // namespace
-
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
-    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % kBM == 0 && d.N % kBN == 0 &&
-        d.out == kOutF32 && d.lda == d.K && d.ldb == d.K && d.ldd == d.N)
+    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % 256 == 0 && d.N % 256 == 0 &&
+        d.out == kOutF32 && d.lda == d.K && d.ldb == d.K && d.ldd == d.N && !d.opts.neg && !d.opts.sat &&
+        !d.opts.row_mask && !d.opts.col_zero)
         return launch_dense256pp(bf16, d, stream);
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m, d.out,
-                   d.lda, d.ldb, d.ldd};
-    return bf16 ? launch_majors<kBf16>(a_mn, b_mn, a, stream) : launch_majors<kF16>(a_mn, b_mn, a, stream);
+                   d.lda, d.ldb, d.ldd, d.opts};
+    if (bf16)
+        return a_mn ? launch256_bf16_amn(b_mn, a, stream) : launch256_bf16_ak(b_mn, a, stream);
+    return a_mn ? launch256_f16_amn(b_mn, a, stream) : launch256_f16_ak(b_mn, a, stream);
 }
 
 hipError_t launch_mx256(const MxArgs &a, bool fp4, hipStream_t stream)
 {
-    if (fp4)
-        return a.out == kOutF32 ? launch_kind<kE2m1, false, false, 8, 8>(a, stream)
-                                : launch_out<kE2m1, false, false>(a, stream);
-    return launch_cfg<kE4m3, false, false>(a, stream);
+    return fp4 ? launch256_e2m1(a, stream) : launch256_e4m3(a, stream);
 }
 
 }  // namespace mswz

@@ -1,0 +1,11 @@
+// gemm256_bf16_amn.hip — instantiations of the 256x256-tile GEMM for bf16 operands, A MN-major (B either major).
+#include "gemm256_kernel.hpp"
+
+namespace mswz {
+
+hipError_t launch256_bf16_amn(bool b_mn, const MxArgs &a, hipStream_t stream)
+{
+    return b_mn ? launch_cfg<kBf16, true, true>(a, stream) : launch_cfg<kBf16, true, false>(a, stream);
+}
+
+}  // namespace mswz

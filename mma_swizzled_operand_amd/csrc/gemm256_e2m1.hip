@@ -1,0 +1,13 @@
+// gemm256_e2m1.hip — instantiations of the 256x256-tile GEMM for block-scaled
+// OCP E2M1 (FP4) operands (both K-major).
+#include "gemm256_kernel.hpp"
+
+namespace mswz {
+
+hipError_t launch256_e2m1(const MxArgs &a, hipStream_t stream)
+{
+    return a.out == kOutF32 ? launch_kind<kE2m1, false, false, 8, 8>(a, stream)
+                            : launch_out<kE2m1, false, false>(a, stream);
+}
+
+}  // namespace mswz

@@ -3,7 +3,7 @@
 // "Operands and repeat axes" and the 128x64x64 example).
 //
 // Same tile, LDS layout, direct buffer-to-LDS copies and epilogue as
-// gemm256.hip (eight waves of 128x64 outputs, two waves per SIMD, two LDS
+// gemm256_kernel.hpp (eight waves of 128x64 outputs, two waves per SIMD, two LDS
 // stages), but the eight waves run in two groups, waves 0-3 (group 0) and
 // waves 4-7 (group 1), so that the two waves on a SIMD (w and w+4) never
 // issue MFMAs at the same time.  Each wave repeats four phases per K step k

@@ -3,7 +3,7 @@
 // 128x64x64 example; operand majors from "Shared descriptors are byte-stride
 // contracts").
 //
-// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256.hip).
+// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256_kernel.hpp).
 // Structure of one 256-thread workgroup (4 waves) computing a BM x BN tile:
 //   * K advances 64 elements per step; each step stages a [BM][128 B] A tile
 //     and a [BN][128 B] B tile in LDS, in the swizzled tile layout of

@@ -3,7 +3,7 @@
 // (tcgen05.mma page, "Weight-stationary and block scaling": per-row scale
 // vectors for A and B, one scale per block of consecutive K elements).
 //
-// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256.hip).
+// The 128x128 and 64x64 tiles (the 256x256 tile lives in gemm256_kernel.hpp).
 // Same workgroup structure as gemm_dense.hip: 4 waves, a BM x BN tile,
 // double-buffered swizzled LDS stages of 128 bytes per operand row (here 128
 // K elements), 16-byte global loads prefetched one K step ahead in registers.

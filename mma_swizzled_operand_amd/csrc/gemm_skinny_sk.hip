@@ -21,7 +21,7 @@
 //     writes and never waits for copies into other stages before a read;
 //   * B's fragments go straight from global memory into registers in the
 //     16x16x32 operand form, kAhead blocks ahead (no LDS);
-//   * the K order inside a 32-wide sub-step is kblk16 (gemm256.hip), the same
+//   * the K order inside a 32-wide sub-step is kblk16 (gemm256_kernel.hpp), the same
 //     for A and B, so the LDS fragment reads are free of bank conflicts.
 //
 // Reduction (deterministic, no waiting), two ways:

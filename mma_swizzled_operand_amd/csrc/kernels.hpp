@@ -9,10 +9,10 @@ namespace mswz {
 // Kernel variants a plan can select.  The tile is BM x BN output elements per
 // 256-thread workgroup; each K step stages 128 bytes of every operand row.
 enum Variant : int {
-    kVarDense256 = 1,   // 16-bit, 256x256 tile, 8 waves of 128x64 (gemm256.hip)
+    kVarDense256 = 1,   // 16-bit, 256x256 tile, 8 waves of 128x64 (gemm256_kernel.hpp)
     kVarDense128 = 2,   // 16-bit, 128x128 tile, 4 waves of 64x64
     kVarDense64 = 3,    // 16-bit, 64x64 tile, 4 waves of 32x32
-    kVarMx256 = 11,     // E4M3 block-scaled, 256x256 tile, 8 waves (gemm256.hip)
+    kVarMx256 = 11,     // E4M3 block-scaled, 256x256 tile, 8 waves (gemm256_kernel.hpp)
     kVarMx128 = 12,     // E4M3 block-scaled, 128x128 tile
     kVarMx64 = 13,      // E4M3 block-scaled, 64x64 tile
     kVarSkinny = 21,    // 16-bit, M <= 64: weight streaming, split K inside the workgroup
@@ -21,6 +21,17 @@ enum Variant : int {
 // Output element kind of D: fp32, or the fp32 result rounded to nearest even
 // into bf16 / fp16 (beta = 1 then reads D in that kind).
 enum OutKind { kOutF32 = 0, kOutBf16 = 1, kOutF16 = 2 };
+
+// Epilogue options of the 256x256 kernel (all off by default): the product
+// enters D negated; D values stored clamped to D's largest finite magnitude;
+// rows of D whose bit is set in row_mask left untouched; columns whose bit is
+// set in col_zero receive a zero product (bit x of word x / 32 in both).
+struct EpiOpts {
+    int neg = 0;
+    int sat = 0;
+    const uint32_t *row_mask = nullptr;
+    const uint32_t *col_zero = nullptr;
+};
 
 struct DenseArgs {
     const void *A;
@@ -33,6 +44,7 @@ struct DenseArgs {
     // elements from one stored row to the next: A, B (K-major: >= K;
     // MN-major: >= M / N) and D (>= N)
     int lda = 0, ldb = 0, ldd = 0;
+    EpiOpts opts = {};
 };
 
 struct MxArgs {
@@ -46,6 +58,7 @@ struct MxArgs {
     int group_m;
     int out = kOutF32;
     int lda = 0, ldb = 0, ldd = 0;   // as in DenseArgs (scale arrays are packed)
+    EpiOpts opts = {};
 };
 
 struct VariantInfo {
@@ -58,6 +71,13 @@ hipError_t launch_dense(int variant, bool bf16, bool a_mn, bool b_mn, const Dens
                         hipStream_t stream);
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &args, hipStream_t stream);
 hipError_t launch_mx256(const MxArgs &args, bool fp4, hipStream_t stream);
+// the 256x256-tile instantiations, one translation unit each (gemm256_*.hip)
+hipError_t launch256_bf16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_bf16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_f16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_f16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
+hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch_dense256pp(bool bf16, const DenseArgs &args, hipStream_t stream);
 int config256();
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);

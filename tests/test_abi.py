@@ -172,6 +172,35 @@ def test_run_rejections_before_gpu_work():
     assert lib.gemm_run_blockscaled(mx.handle, P, P, P, P, P, -1, None) == -1
 
 
+def test_run_opts_rejections_before_gpu_work():
+    lib = mswz.load()
+    dense = mswz.gemm_plan_create(256, 256, 64, "f16", "f16")
+    mx = mswz.gemm_plan_create(256, 256, 128, "e4m3", "e4m3", scale_vec_len=32)
+    P = 0x10000
+    run = lib.gemm_run_opts
+
+    def opts(**kw):
+        o = mswz.GemmOpts(0, 0, 0, None, None, 1)
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return ctypes.byref(o)
+
+    assert run(None, P, P, None, None, P, 0, None, None) == -1
+    assert run(dense.handle, P, P, P, P, P, 0, None, None) == -1            # scales on a dense plan
+    assert run(mx.handle, P, P, None, P, P, 0, None, None) == -1            # missing SFA
+    assert run(dense.handle, P, P, None, None, P, 2, opts(neg_a=1), None) == -1
+    assert run(dense.handle, P + 8, P, None, None, P, 0, opts(neg_a=1), None) == -3
+    assert run(mx.handle, P, P, P + 1, P, P, 0, opts(sat_d=1), None) == -3
+    assert run(dense.handle, P, P, None, None, P, 0, opts(row_mask=P + 2), None) == -3
+    assert run(dense.handle, P, P, None, None, P, 0, opts(col_zero=P + 1), None) == -3
+    # the checks come before the predicate
+    assert run(dense.handle, P + 8, P, None, None, P, 0, opts(pred=0), None) == -3
+    assert run(dense.handle, P, P, None, None, P, 2, opts(pred=0), None) == -1
+    # pred = 0 with valid arguments enqueues nothing (no GPU needed) and succeeds
+    assert run(dense.handle, P, P, None, None, P, 0, opts(pred=0, neg_a=1, row_mask=P), None) == 0
+    assert run(mx.handle, P, P, P, P, P, 1, opts(pred=0), None) == 0
+
+
 def test_workspace_size_query():
     lib = mswz.load()
     assert lib.gemm_plan_workspace_size(None) == -1
