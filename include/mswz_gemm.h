@@ -91,14 +91,16 @@ typedef struct gemm_plan gemm_plan;
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3 and E2M1
- * Shape rules: K % 64 == 0 (16-bit), K % 128 == 0 (E4M3) or K % 256 == 0
- * (E2M1, which always uses the 256 tile).  M and N
+ * Shape rules: K % 128 == 0 (E4M3) or K % 256 == 0 (E2M1, which always uses
+ * the 256 tile).  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
+ * K when both operands are MN-major); a K that is not a multiple of 64 uses
+ * the 256 tile, whose last K step reads the values beyond K as zeros.  M and N
  * multiples of 64 choose among 256, 128 and 64 square tiles; otherwise (tails)
  * the 256 tile is used with masked stores, and N % 4 == 0 is required (16-byte
  * rows of D), as well as M % 8 == 0 for MN-major A and N % 8 == 0 for MN-major
- * B.  MN-major operands must be smaller than 4 GiB.  A 16-bit K-major
- * A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
- * weight-streaming kernel (M == 32 is accepted only there); it needs K-major B.
+ * B.  MN-major operands must be smaller than 4 GiB - 256 bytes.  A 16-bit
+ * K-major A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
+ * weight-streaming kernel; it needs K-major B.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
  */
 int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,

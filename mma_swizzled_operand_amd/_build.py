@@ -65,7 +65,7 @@ def build(jobs: int | None = None, only_changed: bool = False) -> str:
         srcs = [s for s in srcs if _stale(s)]
     else:
         fresh = []
-    jobs = jobs or min(len(srcs), 8)
+    jobs = jobs or max(1, min(len(srcs), 8))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     objs = sorted(objs + [os.path.join(OBJ, os.path.basename(f) + ".o") for f in fresh])

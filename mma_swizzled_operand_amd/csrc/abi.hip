@@ -135,7 +135,14 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
-    if (K % (fp4 ? 256 : fp8 ? 128 : 64) != 0)
+    // block-scaled: K a multiple of the K step (scale rows stay 4-byte words
+    // per step).  16-bit: any K whose K-major rows keep 16-byte alignment
+    // (K % 8 == 0 unless both operands are MN-major); a K that is not a
+    // multiple of 64 takes the 256x256 tile with a zero-padded last step.
+    if (fp8 && K % (fp4 ? 256 : 128) != 0)
+        return MSWZ_ERR_UNSUPPORTED;
+    const bool ktail = !fp8 && K % 64 != 0;
+    if (ktail && K % 8 != 0 && (a_major == MSWZ_MAJOR_K || b_major == MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;
     // M or N not a multiple of 64: the 256x256 tile with masked stores; D rows
     // (and MN-major operand rows) must keep 16-byte alignment
@@ -161,7 +168,9 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     // MN-major operands are addressed with 32-bit offsets from the start of
     // the [K][M] / [K][N] array
-    constexpr int64_t kMaxMnBytes = int64_t(1) << 32;
+    // (256 bytes short of 4 GiB: a masked copy points at the range's end,
+    // which must not wrap around)
+    constexpr int64_t kMaxMnBytes = (int64_t(1) << 32) - 256;
     if ((a_major == MSWZ_MAJOR_MN && ((K - 1) * lda_v + M) * 2 >= kMaxMnBytes) ||
         (b_major == MSWZ_MAJOR_MN && ((K - 1) * ldb_v + N) * 2 >= kMaxMnBytes))
         return MSWZ_ERR_UNSUPPORTED;
@@ -169,7 +178,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     const bool skinny = !fp8 && !narrow_d && !strided && a_major == MSWZ_MAJOR_K &&
                         b_major == MSWZ_MAJOR_K && (M == 64 || M == 32) && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : (tail || fp4 || narrow_d || strided) ? 256 : pick_tile(M, N);
+    const int tile = skinny ? 64 : (tail || ktail || fp4 || narrow_d || strided) ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 

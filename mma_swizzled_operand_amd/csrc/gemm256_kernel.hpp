@@ -67,12 +67,14 @@ struct DmaOperand {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t voff[kInstr];   // this lane's byte offset in the panel at K step 0, per instruction
     uint32_t lds_off;        // LDS offset of this wave's first destination row inside a stage
+    uint32_t nbytes;         // the buffer's range: bytes of the panel inside the operand
 
     // rows: rows of the panel inside the operand (fewer than 256 in a tail panel)
     __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int wave, int lane,
                          uint32_t tile_off)
     {
-        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
+        nbytes = uint32_t(rows) * rb;
+        rsrc = make_rsrc(X + size_t(row0) * rb, nbytes);
 #pragma unroll
         for (int i = 0; i < kInstr; ++i) {
             const int r = 8 * (wave + W * i) + (lane >> 3);
@@ -87,6 +89,22 @@ struct DmaOperand {
 #pragma unroll
         for (int i = 0; i < kInstr; ++i)
             buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i], uint32_t(kt) * 128);
+    }
+
+    // The partial last K step kt of a K that is not a multiple of the step:
+    // only the first `lim` bytes of each row's 128-byte slice lie inside K (a
+    // multiple of 16, so chunks are whole).  The whole offset goes into the
+    // range-checked per-lane offset and a chunk beyond K points at the end
+    // of the range, so it reads as zeros without forming an address outside
+    // the operand.
+    __device__ void issue_tail(uint8_t *stage, int kt, uint32_t lim, int wave, int lane) const
+    {
+#pragma unroll
+        for (int i = 0; i < kInstr; ++i) {
+            const uint32_t chunk = uint32_t((lane & 7) ^ (((lane >> 3) ^ (wave + W * i)) & 7));
+            const uint32_t off = 16 * chunk < lim ? voff[i] + uint32_t(kt) * 128 : nbytes;
+            buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, off, 0);
+        }
     }
 };
 
@@ -142,6 +160,7 @@ struct DmaMnOperand {
     static constexpr int kInstr = 32 / W;
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t voff[2], pitch, lds_off;   // voff[bit 4 of the instruction's K rows]
+    uint32_t nbytes;                    // the buffer's range
 
     // A chunk whose columns lie beyond the operand (a tail tile) is fetched
     // from the tile's first columns instead: its values only reach outputs
@@ -151,7 +170,8 @@ struct DmaMnOperand {
                          uint32_t tile_off)
     {
         pitch = uint32_t(ld) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * pitch + uint32_t(R - row0) * 2);
+        nbytes = uint32_t(K - 1) * pitch + uint32_t(R - row0) * 2;
+        rsrc = make_rsrc(X + size_t(row0) * 2, nbytes);
         const int kr = lane >> 5;
 #pragma unroll
         for (int b4 = 0; b4 < 2; ++b4) {
@@ -167,6 +187,21 @@ struct DmaMnOperand {
         for (int i = 0; i < kInstr; ++i)
             buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, voff[((2 * W * i) >> 4) & 1],
                               (uint32_t(kt) * 64 + 2 * W * i) * pitch);
+    }
+
+    // The partial last K step kt: K rows at or beyond K read as zeros.  The
+    // whole offset goes into the range-checked per-lane offset and a row
+    // beyond K points at the end of the range, so no address outside the
+    // operand is formed.
+    __device__ void issue_tail(uint8_t *stage, int kt, int K, int wave, int lane) const
+    {
+#pragma unroll
+        for (int i = 0; i < kInstr; ++i) {
+            const int k = 64 * kt + 2 * (wave + W * i) + (lane >> 5);
+            const uint32_t off = k < K ? voff[((2 * W * i) >> 4) & 1] + (uint32_t(kt) * 64 + 2 * W * i) * pitch
+                                       : nbytes;
+            buffer_load_lds16(rsrc, stage + lds_off + i * 2 * W * kMnRowBytes, off, 0);
+        }
     }
 };
 
@@ -910,7 +945,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             goto epilogue;
         }
     }
-    {
+    if (KT > 0) {
     issue_step(lds0, scl0, 0);
     store_regs(lds0);
     __syncthreads();
@@ -929,6 +964,26 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     if (kt < KT)
         compute(lds0, scl0);
     __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+    }
+    // K not a multiple of the step (16-bit operands copied straight into LDS;
+    // the host launches no other configuration for it): one more step after
+    // the loop whose K values beyond K are copied as zeros into both
+    // operands, so they add nothing.
+    if constexpr (!kMx && !kRegA && !kRegB && !kMnReg) {
+        if (K % kStepK) {
+            lds_barrier_keep_vm<0>();   // every copy landed, every wave done reading lds0
+            const uint32_t lim = uint32_t(K % kStepK) * 2;   // bytes of each K-major row slice inside K
+            if constexpr (kDmaA)
+                da.issue_tail(lds0, KT, lim, wave, lane);
+            if constexpr (kTrA)
+                dma_mna.issue_tail(lds0, KT, K, wave, lane);
+            if constexpr (kDmaB)
+                db.issue_tail(lds0, KT, lim, wave, lane);
+            if constexpr (kTrB)
+                dma_mnb.issue_tail(lds0, KT, K, wave, lane);
+            lds_barrier_keep_vm<0>();
+            compute(lds0, scl0);
+        }
     }
 
     // ---- epilogue -------------------------------------------------------------
@@ -1004,6 +1059,9 @@ hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
     if (a.out != kOutF32)
         return launch_out<KIND, A_MN, B_MN>(a, stream);
+    // a K that is not a multiple of the step takes the default pipeline
+    if (KIND != kE4m3 && KIND != kE2m1 && a.K % 64 != 0)
+        return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
     switch (config256()) {
     case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);
     case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);

@@ -98,7 +98,12 @@ K_, MN = 0, 1
     ((256, 256, 64, BF16, BF16, F32, MN, MN, 0), 0),         # both MN-major
     ((256, 256, 128, E4M3, E4M3, F32, K_, MN, 32), -2),      # MN-major fp8 not built
     ((256, 256, 128, E4M3, E4M3, F32, MN, K_, 32), -2),      # MN-major fp8 not built
-    ((256, 256, 96, F16, F16, F32, K_, K_, 0), -2),          # K not a multiple of 64
+    ((256, 256, 96, F16, F16, F32, K_, K_, 0), 0),           # 16-bit K tail: 256 tile, zero-padded step
+    ((256, 256, 8, BF16, BF16, F32, K_, MN, 0), 0),          # K below one step
+    ((256, 256, 100, F16, F16, F32, K_, K_, 0), -2),         # K-major rows not 16-byte aligned
+    ((256, 256, 100, F16, F16, F32, MN, K_, 0), -2),         # (B is K-major)
+    ((256, 256, 100, F16, F16, F32, MN, MN, 0), 0),          # both MN-major: any K
+    ((256, 256, 1, BF16, BF16, F32, MN, MN, 0), 0),
     ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
     ((100, 256, 64, F16, F16, F32, K_, K_, 0), 0),           # ragged M: 256 tile, masked stores
     ((256, 96, 64, F16, F16, F32, K_, K_, 0), 0),            # ragged N
@@ -126,6 +131,10 @@ def test_plan_create_null_out():
 def test_tail_plans_use_the_256_tile():
     d = mswz.gemm_plan_create(1000, 520, 128, "bf16", "bf16").describe()
     assert (d["tile_m"], d["tile_n"], d["blocks"]) == (256, 256, 4 * 3)
+    for K in (72, 4104):   # K tails, including shapes that would otherwise pick a smaller tile or streaming
+        for M, N in ((128, 128), (64, 16384), (4096, 4096)):
+            d = mswz.gemm_plan_create(M, N, K, "f16", "f16").describe()
+            assert (d["tile_m"], d["tile_n"]) == (256, 256), (M, N, K)
 
 
 @pytest.mark.parametrize("group_m", [-4, -1, 1, 4, 16])

@@ -178,6 +178,60 @@ def test_tail_output_untouched_outside_d():
     assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + n:] == 7.0)
 
 
+# K not a multiple of the 64-element step (16-bit; the 256 tile, whose last
+# step reads the values beyond K as zeros): each major combination, K below
+# one step, K % 8 != 0 with both operands MN-major, ragged M and N, beta = 1,
+# narrow D, and shapes that would otherwise take another kernel
+KTAILS = {
+    "ktail-bf16-k": wl.custom(512, 256, 72, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                              name="ktail-bf16-k"),
+    "ktail-f16-amn-beta": wl.custom(264, 300, 200, "f16", a_major="mn", beta=1, name="ktail-f16-amn-beta"),
+    "ktail-bf16-bmn": wl.custom(256, 512, 40, "bf16", b_major="mn", name="ktail-bf16-bmn"),
+    "ktail-f16-both-mn-k100": wl.custom(256, 320, 100, "f16", a_major="mn", b_major="mn", beta=1,
+                                        name="ktail-f16-both-mn-k100"),
+    "ktail-bf16-both-mn-k1": wl.custom(256, 256, 1, "bf16", a_major="mn", b_major="mn",
+                                       name="ktail-bf16-both-mn-k1"),
+    "ktail-f16-k8": wl.custom(128, 256, 8, "f16", name="ktail-f16-k8"),
+    "ktail-skinny-shape": wl.custom(64, 1024, 1032, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                                    name="ktail-skinny-shape"),
+    "ktail-bf16-k-odd-steps": wl.custom(512, 512, 3 * 64 + 24, "bf16", beta=1, name="ktail-bf16-k-odd-steps"),
+}
+
+
+@pytest.mark.parametrize("name", list(KTAILS))
+def test_k_tail_full_compare(name):
+    w = KTAILS[name]
+    plan = plan_for(w)
+    assert plan.describe()["tile_m"] == 256
+    say(f"[k-tail] {name} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} B:{w.b_major} beta={w.beta}")
+    x = wl.generate(w, seed=31)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(KTAILS))
+def test_k_tail_quarter_integers_bit_exact(name):
+    w = KTAILS[name]
+    say(f"[k-tail exact] {name}")
+    x = wl.generate(w, seed=32, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    ref = reference(w, x, with_mag=False)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_k_tail_full_size_sampled():
+    """4096 x 4096 x 4040 bf16 (63 full steps and a 8-element tail), both
+    K-major, on sampled rows and columns."""
+    w = wl.custom(4096, 4096, 4040, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="ktail-4096")
+    say("[k-tail full] 4096x4096x4040 bf16")
+    x = wl.generate(w, seed=33)
+    got = run_gpu(w, x)
+    rows, cols = wl.sample_points(w, 12, 12, seed=34)
+    ref, mag = reference(w, x, rows=rows, cols=cols)
+    print(compare(w, got[np.ix_(rows, cols)], ref, mag))
+
+
 # MX-fp4 (OCP E2M1, two per byte; the 256 tile only): several tiles and K
 # steps, ragged M and N, beta = 1
 FP4 = {

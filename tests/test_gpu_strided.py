@@ -44,6 +44,13 @@ CASES = {
                             b_dist=("normal", 1.0), name="e2m1-beta"), 544, 576, 388, "f32"),
     "bf16-out-tail": (wl.custom(264, 300, 192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                 name="bf16-out-tail"), 256, 200, 304, "bf16"),
+    # K tails: the poisoned storage between K and the pitch must never reach the sums
+    "bf16-ktail": (wl.custom(256, 256, 72, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                             name="bf16-ktail"), 136, 80, 0, "f32"),
+    "f16-amn-ktail-beta": (wl.custom(264, 260, 200, "f16", a_major="mn", beta=1, name="f16-amn-ktail-beta"),
+                           272, 264, 268, "f32"),
+    "bf16-bmn-ktail-out": (wl.custom(256, 264, 24, "bf16", b_major="mn", name="bf16-bmn-ktail-out"),
+                           32, 272, 0, "bf16"),
 }
 
 
