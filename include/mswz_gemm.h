@@ -99,8 +99,9 @@ typedef struct gemm_plan gemm_plan;
  * the 256 tile is used with masked stores, and N % 4 == 0 is required (16-byte
  * rows of D), as well as M % 8 == 0 for MN-major A and N % 8 == 0 for MN-major
  * B.  MN-major operands must be smaller than 4 GiB - 256 bytes.  A 16-bit
- * K-major A with M == 32 or 64, N % 64 == 0 and K % 1024 == 0 selects the
- * weight-streaming kernel; it needs K-major B.
+ * K-major A with M <= 64, N % 64 == 0 and K % 1024 == 0 (K-major B, fp32 D,
+ * packed storage) selects the weight-streaming kernel (M padded to 32 or 64
+ * rows, the padding never read from memory nor stored).
  * Returns MSWZ_OK, MSWZ_ERR_INVALID or MSWZ_ERR_UNSUPPORTED.
  */
 int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,
@@ -142,10 +143,11 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *D,
 
 /*
  * Device workspace, in bytes, that gemm_run_ws can use for this plan: > 0 for
- * weight-streaming plans (the skinny kernel above) with M == 64, N % 256 == 0
- * and K a multiple of 512 (K split into S parts, each a multiple of 256: the
- * smallest power of two up to 16 giving N/256 * S >= 256 workgroups, else the
- * largest that fits); 0 otherwise.
+ * weight-streaming plans (the skinny kernel above) with N % 256 == 0 (K split
+ * into S parts, each a multiple of 256: the smallest power of two up to 16
+ * giving N/256 * S >= 256 workgroups, else the largest that fits): 256 bytes
+ * of counters (rounded up from 4 per 256 columns) plus S * M * N * 4 bytes of
+ * fp32 partials; 0 otherwise.
  * MSWZ_ERR_INVALID for a NULL plan.
  */
 int64_t gemm_plan_workspace_size(const gemm_plan *plan);

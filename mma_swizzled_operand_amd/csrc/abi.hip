@@ -176,7 +176,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     // weight streaming: few rows of K-major 16-bit A against a large B
     const bool skinny = !fp8 && !narrow_d && !strided && a_major == MSWZ_MAJOR_K &&
-                        b_major == MSWZ_MAJOR_K && (M == 64 || M == 32) && N % 64 == 0 &&
+                        b_major == MSWZ_MAJOR_K && M <= 64 && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
     const int tile = skinny ? 64 : (tail || ktail || fp4 || narrow_d || strided) ? 256 : pick_tile(M, N);
     if (!tile)
@@ -216,8 +216,8 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     if (p->variant == mswz::kVarMx256)
         p->info.lds_bytes += 2 * 512 * 16;                 // the two scale stages
     if (skinny) {
-        p->info.tile_m = int(M);
-        p->info.lds_bytes = 8 * int(M) * 68 * 4;
+        p->info.tile_m = M > 32 ? 64 : 32;   // M padded to 32 or 64 rows
+        p->info.lds_bytes = 8 * p->info.tile_m * 68 * 4;
     }
     p->blocks = ((M + p->info.tile_m - 1) / p->info.tile_m) * ((N + p->info.tile_n - 1) / p->info.tile_n);
     if (skinny) {

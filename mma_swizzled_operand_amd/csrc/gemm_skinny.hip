@@ -1,5 +1,5 @@
 // gemm_skinny.hip — weight-streaming GEMM for small M on gfx950:
-//     D[M][N] = beta*D + A[M][K] . B[N][K]^T,  M in {32, 64}, fp16 / bf16
+//     D[M][N] = beta*D + A[M][K] . B[N][K]^T,  1 <= M <= 64, fp16 / bf16
 // (tcgen05.mma page, "Operands and repeat axes"; the weight-stationary
 // workload of "Weight-stationary and block scaling": few activation rows
 // against a large weight matrix streamed once).
@@ -19,6 +19,11 @@
 // sub-step s the four lanes of a row read bytes 64s .. 64s+63 of it: every
 // 16-byte load instruction consumes whole 64-byte lines of 16 rows.  Blocks
 // are double-buffered two ahead in registers.
+//
+// M is padded to BM = 32 or 64 rows: every A load carries its row in the
+// range-checked per-lane offset and the buffer covers the M rows of A, so the
+// rows beyond M read as zeros without a memory access, and only rows below M
+// are stored.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -35,7 +40,7 @@ constexpr int kRedPitch = 68;   // floats per row of a partial block in LDS (pad
 template <bool BF16, int BM, bool BETA>
 __global__ void __launch_bounds__(kThreads)
 gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, float *__restrict__ D,
-                   int N, int K)
+                   int M, int N, int K)
 {
     constexpr int TM = BM / 16, TN = kBN / 16;   // 16-row operand blocks of A and of B
     __shared__ __attribute__((aligned(16))) float red[kWaves * BM * kRedPitch];
@@ -48,10 +53,15 @@ gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint32_t row_bytes = uint32_t(K) * 2;
     const int blocks = K / 64 / kWaves;   // 64-element K blocks per wave
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(BM) * row_bytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(M) * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + size_t(n0) * row_bytes, uint32_t(kBN) * row_bytes);
     // lane (lr, lg): row lr of each 16-row block, bytes 64s + 16lg of the wave's block
     const uint32_t voff = uint32_t(lr) * row_bytes + uint32_t(wave) * 128 + 16 * lg;
+    // A's row (16i + lr) is in the per-lane offset, which the range check covers
+    uint32_t voff_a[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        voff_a[i] = voff + uint32_t(16 * i) * row_bytes;
 
     // fragment buffers: [buffer][16-row block][sub-step]
     u32x4 fa[2][TM][2], fb[2][TN][2];
@@ -66,7 +76,7 @@ gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                fa[buf][i][s] = buffer_load16(ra, voff + 64 * s, uint32_t(16 * i) * row_bytes + kb);
+                fa[buf][i][s] = buffer_load16(ra, voff_a[i] + 64 * s, kb);
     };
 
     f32x4 acc[TN][TM];
@@ -117,10 +127,13 @@ gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int i = 0; i < TM; ++i)
             *reinterpret_cast<f32x4 *>(mine + (16 * i + lr) * kRedPitch + 16 * j + 4 * lg) = acc[j][i];
     __syncthreads();
-    // thread t sums BM*64/512 consecutive outputs of one row, in wave order
+    // thread t sums BM*64/512 consecutive outputs of one row, in wave order;
+    // rows beyond M are not stored
     constexpr int kPer = BM * kBN / kThreads;   // 8 (BM = 64) or 4 (BM = 32)
     const int e0 = tid * kPer;
     const int m = e0 / kBN, c0 = e0 % kBN;
+    if (m >= M)
+        return;
 #pragma unroll
     for (int c = 0; c < kPer; c += 4) {
         f32x4 s = *reinterpret_cast<const f32x4 *>(red + m * kRedPitch + c0 + c);
@@ -142,10 +155,10 @@ hipError_t launch_bm(const DenseArgs &a, hipStream_t stream)
     const dim3 grid(a.N / kBN);
     if (a.beta)
         hipLaunchKernelGGL((gemm_skinny_kernel<BF16, BM, true>), grid, dim3(kThreads), 0, stream, A, B, a.D,
-                           a.N, a.K);
+                           a.M, a.N, a.K);
     else
         hipLaunchKernelGGL((gemm_skinny_kernel<BF16, BM, false>), grid, dim3(kThreads), 0, stream, A, B, a.D,
-                           a.N, a.K);
+                           a.M, a.N, a.K);
     return hipGetLastError();
 }
 
@@ -153,11 +166,11 @@ hipError_t launch_bm(const DenseArgs &a, hipStream_t stream)
 
 hipError_t launch_skinny(bool bf16, const DenseArgs &a, hipStream_t stream)
 {
-    if (a.M == 64)
+    if (a.M < 1 || a.M > 64)
+        return hipErrorInvalidValue;
+    if (a.M > 32)
         return bf16 ? launch_bm<true, 64>(a, stream) : launch_bm<false, 64>(a, stream);
-    if (a.M == 32)
-        return bf16 ? launch_bm<true, 32>(a, stream) : launch_bm<false, 32>(a, stream);
-    return hipErrorInvalidValue;
+    return bf16 ? launch_bm<true, 32>(a, stream) : launch_bm<false, 32>(a, stream);
 }
 
 }  // namespace mswz

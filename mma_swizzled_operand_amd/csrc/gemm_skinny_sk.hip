@@ -1,5 +1,5 @@
 // gemm_skinny_sk.hip — weight-streaming GEMM with K split over workgroups:
-//     D[64][N] = beta*D + A[64][K] . B[N][K]^T,  fp16 / bf16, K-major A and B
+//     D[M][N] = beta*D + A[M][K] . B[N][K]^T,  1 <= M <= 64, fp16 / bf16, K-major A and B
 // (tcgen05.mma page, "Operands and repeat axes"; the weight-stationary
 // workload of "Weight-stationary and block scaling").
 //
@@ -23,6 +23,11 @@
 //     16x16x32 operand form, kAhead blocks ahead (no LDS);
 //   * the K order inside a 32-wide sub-step is kblk16 (gemm256_kernel.hpp), the same
 //     for A and B, so the LDS fragment reads are free of bank conflicts.
+//
+// M is padded to 64 rows: A's copies carry the row in the range-checked
+// per-lane offset and the buffer covers the M rows of A, so the rows beyond M
+// land in LDS as zeros without a memory access; only rows below M are
+// stored (partials and D).
 //
 // Reduction (deterministic, no waiting), two ways:
 //   * default: each workgroup stores its 64 x 256 fp32 partial into the
@@ -48,7 +53,7 @@ namespace mswz {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kBM = 64;            // rows of A (and of D)
+constexpr int kBM = 64;            // rows of the padded tile (M <= 64 rows of A and D)
 constexpr int kBN = 256;           // columns of D per workgroup
 constexpr int kSlots = 4;          // A stages and B register slots
 constexpr int kAhead = kSlots - 1; // K blocks in flight ahead of the one computed
@@ -61,7 +66,7 @@ __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 template <bool BF16, bool BETA, bool INLINE>
 __global__ void __launch_bounds__(kThreads)
 gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, float *__restrict__ D,
-                      float *__restrict__ part_ws, uint32_t *__restrict__ counters, int N, int K, int S)
+                      float *__restrict__ part_ws, uint32_t *__restrict__ counters, int M, int N, int K, int S)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
@@ -84,7 +89,7 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
     const int kb0 = part * T;
 
     // ---- A: direct copy of one K block per step, wave w fills tile rows 8w .. 8w+7
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(kBM) * row_bytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(M) * row_bytes);
     const int arow = 8 * wave + (lane >> 3);
     const uint32_t a_voff = uint32_t(arow) * row_bytes + 16u * uint32_t((lane & 7) ^ tile_key(arow));
     auto issue_a = [&](int slot, int t) {
@@ -166,13 +171,16 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
     // no copy may still be writing LDS when the workgroup ends
     lds_barrier_keep_vm<0>();
 
-    // ---- partial -> workspace; lane holds row 16i + r16, columns 32w + 16jb + 4g .. +3
-    const size_t MN = size_t(kBM) * N;
+    // ---- partial -> workspace ([part][M][N]); lane holds row 16i + r16,
+    // columns 32w + 16jb + 4g .. +3
+    const size_t MN = size_t(M) * N;
     float *mine = part_ws + size_t(part) * MN;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (16 * i + r16 >= M)
+                continue;
             const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
             *reinterpret_cast<f32x4 *>(mine + idx) = acc[jb][i];
         }
@@ -203,8 +211,9 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
-                v[jb][i] = p == part ? acc[jb][i]
-                                     : *reinterpret_cast<const f32x4 *>(part_ws + size_t(p) * MN + idx);
+                v[jb][i] = p == part || 16 * i + r16 >= M
+                               ? acc[jb][i]
+                               : *reinterpret_cast<const f32x4 *>(part_ws + size_t(p) * MN + idx);
             }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
@@ -216,6 +225,8 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            if (16 * i + r16 >= M)
+                continue;
             const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
             f32x4 *dp = reinterpret_cast<f32x4 *>(D + idx);
             f32x4 out = sum[jb][i];
@@ -266,11 +277,11 @@ hipError_t launch_bb(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
     const dim3 grid(a.N / kBN * sk.parts);
     if (reduce_inline()) {
         hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, true>), grid, dim3(kThreads), 0, stream, A, B,
-                           a.D, sk.partials, sk.counters, a.N, a.K, sk.parts);
+                           a.D, sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, false>), grid, dim3(kThreads), 0, stream, A, B, a.D,
-                       sk.partials, sk.counters, a.N, a.K, sk.parts);
+                       sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -293,7 +304,7 @@ hipError_t launch_bf(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
 // multiple of kSlots 64-element K blocks.
 int skinny_split_parts(int64_t M, int64_t N, int64_t K)
 {
-    if (M != kBM || N % kBN != 0)
+    if (M < 1 || M > kBM || N % kBN != 0)
         return 0;
     const int64_t n_cb = N / kBN;
     int best = 0;

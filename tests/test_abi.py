@@ -159,6 +159,12 @@ def test_tile_choice():
     assert (d["tile_m"], d["tile_k"], d["blocks"]) == (256, 128, 1024)
     d = mswz.gemm_plan_create(128, 256, 64, "f16", "f16").describe()
     assert d["tile_m"] * d["tile_n"] * d["blocks"] == 128 * 256
+    # weight streaming for any M up to 64 (padded to 32 or 64 rows)
+    for M, pad in ((1, 32), (17, 32), (32, 32), (33, 64), (64, 64)):
+        d = mswz.gemm_plan_create(M, 2048, 1024, "bf16", "bf16").describe()
+        assert (d["variant"], d["tile_m"], d["blocks"]) == (21, pad, 2048 // 64), (M, d)
+    assert mswz.gemm_plan_create(65, 2048, 1024, "bf16", "bf16").describe()["variant"] != 21
+    assert mswz.gemm_plan_create(16, 2048, 1024, "bf16", "bf16", "bf16").describe()["variant"] != 21
 
 
 # ---- run-time rejections (fake pointers: never dereferenced) -------------------
@@ -217,7 +223,11 @@ def test_workspace_size_query():
     # of counters, then 4 fp32 partials of 64 x 16384
     assert mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16").workspace_bytes() == 256 + 4 * 64 * 16384 * 4
     assert mswz.gemm_plan_create(64, 2048, 4096, "f16", "f16").workspace_bytes() == 256 + 16 * 64 * 2048 * 4
-    assert mswz.gemm_plan_create(32, 16384, 8192, "bf16", "bf16").workspace_bytes() == 0   # M = 32
+    assert mswz.gemm_plan_create(32, 16384, 8192, "bf16", "bf16").workspace_bytes() == 256 + 4 * 32 * 16384 * 4
+    assert mswz.gemm_plan_create(1, 4096, 4096, "bf16", "bf16").workspace_bytes() == 256 + 16 * 1 * 4096 * 4
+    assert mswz.gemm_plan_create(17, 16384, 8192, "f16", "f16").workspace_bytes() == 256 + 4 * 17 * 16384 * 4
+    assert mswz.gemm_plan_create(48, 1024 + 64, 8192, "bf16", "bf16").workspace_bytes() == 0   # N % 256
+    assert mswz.gemm_plan_create(65, 16384, 8192, "bf16", "bf16").workspace_bytes() == 0       # M > 64
     assert mswz.gemm_plan_create(4096, 4096, 4096, "bf16", "bf16").workspace_bytes() == 0
     assert mswz.gemm_plan_create(256, 256, 128, "e4m3", "e4m3", scale_vec_len=32).workspace_bytes() == 0
 

@@ -25,6 +25,22 @@ SMALL = {
     "ws-f16-1024x2048-beta": wl.custom(64, 1024, 2048, "f16", beta=1, name="ws-f16-1024x2048-beta"),
     "ws-bf16-256x1024": wl.custom(64, 256, 1024, "bf16", name="ws-bf16-256x1024"),
     "ws-f16-4096x1024": wl.custom(64, 4096, 1024, "f16", name="ws-f16-4096x1024"),
+    # M below 64 (decode-style batches): padded rows are never read nor stored
+    "ws-bf16-m1": wl.custom(1, 2048, 4096, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                            name="ws-bf16-m1"),
+    "ws-f16-m17-beta": wl.custom(17, 1024, 2048, "f16", beta=1, name="ws-f16-m17-beta"),
+    "ws-bf16-m32": wl.custom(32, 4096, 2048, "bf16", name="ws-bf16-m32"),
+    "ws-bf16-m48-beta": wl.custom(48, 2048, 1024, "bf16", beta=1, a_dist=("normal", 1.0),
+                                  b_dist=("normal", 0.02), name="ws-bf16-m48-beta"),
+}
+
+# the same kernels without a workspace (K not split), ragged M
+UNSPLIT = {
+    "skinny-f16-m1": wl.custom(1, 1024, 1024, "f16", name="skinny-f16-m1"),
+    "skinny-bf16-m20-beta": wl.custom(20, 2048, 2048, "bf16", beta=1, name="skinny-bf16-m20-beta"),
+    "skinny-bf16-m33": wl.custom(33, 1024, 3072, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                                 name="skinny-bf16-m33"),
+    "skinny-f16-m63-n1088": wl.custom(63, 1088, 1024, "f16", name="skinny-f16-m63-n1088"),
 }
 
 
@@ -80,3 +96,57 @@ def test_split_full_size_c4_sampled():
     ref_c, mag_c = reference(w, x, cols=cols)
     print("c4 ws", compare(w, got[rows], ref_r, mag_r), compare(w, got[:, cols], ref_c, mag_c))
     assert not ws[:256].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("name", list(UNSPLIT))
+def test_unsplit_ragged_m(name):
+    w = UNSPLIT[name]
+    plan = plan_for(w)
+    assert plan.describe()["variant"] == 21
+    say(f"[skinny] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta}")
+    x = wl.generate(w, seed=14)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+    xq = wl.generate(w, seed=15, values="quarter")
+    assert np.array_equal(run_gpu(w, xq, plan), reference(w, xq, with_mag=False).astype(np.float32))
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_ragged_m_stores_stay_inside_d_and_workspace(split):
+    """M = 17: canaries after D (and after the workspace) are unchanged."""
+    import mma_swizzled_operand_amd as mswz
+    w = SMALL["ws-f16-m17-beta"]
+    plan = plan_for(w)
+    x = wl.generate(w, seed=16)
+    A, B = (torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).cuda() for k in ("A", "B"))
+    n = w.M * w.N
+    dbuf = torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda")
+    dbuf[:n] = torch.from_numpy(x["D0"].reshape(-1)).cuda()
+    need = plan.workspace_bytes()
+    wbuf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    wbuf[need:] = 0xA5
+    say(f"[skinny] canaries split={split}")
+    if split:
+        mswz.gemm_run_ws(plan, A, B, dbuf[:n], wbuf[:need], 1)
+    else:
+        mswz.gemm_run(plan, A, B, dbuf[:n], 1)
+    torch.cuda.synchronize()
+    assert torch.all(dbuf[n:] == 7.0)
+    assert torch.all(wbuf[need:] == 0xA5)
+    ref, mag = reference(w, x)
+    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, mag, x.get("D0"))
+
+
+def test_decode_m16_full_size_sampled():
+    """16 x 16384 x 8192 bf16 (the weight-streaming workload with a 16-row
+    batch) through the workspace path, on sampled rows and columns."""
+    w = wl.custom(16, 16384, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02), name="decode-m16")
+    plan = plan_for(w)
+    ws = zero_workspace(plan)
+    say("[splitk] 16x16384x8192")
+    x = wl.generate(w, seed=17)
+    got = run_gpu(w, x, plan, workspace=ws)
+    cols = wl.sample_points(w, 8, 16)[1]
+    ref, mag = reference(w, x, cols=cols)
+    print("decode-m16", compare(w, got[:, cols], ref, mag))
