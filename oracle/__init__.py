@@ -9,7 +9,8 @@ Contents
 --------
 ``oracle.c`` (built here into ``liboracle.so`` with gcc)
     * element decoders (fp16, bf16, OCP E4M3, OCP E2M1 packed two per byte,
-      OCP E8M0) from the bit fields;
+      OCP E2M3 / E3M2 in the padded sixteen-per-16-byte form of the tcgen05.cp
+      page's "Native FP4/FP6 decompression", OCP E8M0) from the bit fields;
     * ``gemm``: D = beta*D0 + A.B^T with B held as (N,K), in fp64, for dense
       and block-scaled operands, K-major or MN-major
       (tcgen05.mma page: "Operands and repeat axes", "Shared descriptors are
@@ -33,12 +34,15 @@ Parity pins (tests/test_oracle_*.py, tests/test_walk.py, run with -m "not gpu")
 * decoders: all 65,536 fp16 and bf16 patterns against numpy / torch, all 256
   e4m3 patterns against torch.float8_e4m3fn, e8m0 against the definition,
   the 16 e2m1 patterns against the format's table of values and their nibble
-  order within a byte;
+  order within a byte; the 64 e2m3 and e3m2 codes against the formats'
+  definitions in exact rationals, their largest and smallest values, and the
+  padded packing against a bit-by-bit writer with random padding;
 * gemm: all-ones closed form (every entry is K), identity and permutation
   operands, A = 0 with beta = 1, majors invariance, tiny shapes against exact
   rational arithmetic, the page's quarter-integer example, block-scale closed
   forms, numpy float64 matmul on medium shapes; e2m1 products equal to the
-  e4m3 products of the same values (every e2m1 value is an e4m3 value);
+  e4m3 products of the same values (every e2m1, e2m3 and e3m2 value is an
+  e4m3 value, so the same holds for the 6-bit kinds);
 * walk: the page's printed descriptor examples and the printed mode-4
   permutation; modes 1..3 are pinned only through the properties the page
   states (periods, 16-byte atoms) — "parity unpinned" beyond those.
@@ -57,9 +61,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own element-kind and major numbering (independent of the GPU ABI).
-DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5}
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7}
 MAJORS = {"k": 0, "mn": 1}
-_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 1}
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 1, "e2m3": 1, "e3m2": 1}
 # elements per stored item: e2m1 packs two per byte (element 2j in the low nibble)
 _PER_ITEM = {"e2m1": 2}
 
@@ -126,10 +130,16 @@ def _raw(a: np.ndarray, kind: str) -> np.ndarray:
     return a
 
 
+_FP6 = ("e2m3", "e3m2")
+
+
 def decode(kind: str, stored: np.ndarray) -> np.ndarray:
     """Exact fp64 value of every stored element (bit patterns -> reals).  For
-    e2m1 the last axis of the result is twice as long (two per byte)."""
+    e2m1 the last axis of the result is twice as long (two per byte); e2m3 and
+    e3m2 arrays hold whole 16-byte blocks of sixteen values per row."""
     s = _raw(stored, kind)
+    if kind in _FP6 and (s.ndim == 0 or s.shape[-1] % 16):
+        raise ValueError("6-bit rows must hold whole 16-byte blocks")
     per = _PER_ITEM.get(kind, 1)
     shape = s.shape[:-1] + (s.shape[-1] * per,) if s.ndim else (per,)
     out = np.empty(shape, dtype=np.float64)
@@ -162,6 +172,9 @@ def gemm(M, N, K, a_kind, a_major, A, b_kind, b_major, B, *, V=0, SFA=None, SFB=
     B = _raw(B, b_kind)
     if A.size * _PER_ITEM.get(a_kind, 1) != M * K or B.size * _PER_ITEM.get(b_kind, 1) != N * K:
         raise ValueError("operand sizes do not match M, N, K")
+    for kind, major, rows_mn in ((a_kind, a_major, M), (b_kind, b_major, N)):
+        if kind in _FP6 and (K if major == "k" else rows_mn) % 16:
+            raise ValueError("6-bit operands need stored rows of whole 16-byte blocks")
     sfa = sfb = None
     if V:
         sfa = np.ascontiguousarray(SFA, dtype=np.uint8)

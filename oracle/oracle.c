@@ -21,13 +21,19 @@
  *                 + sum_k (2^(SFA[m][k/V]-127) a(m,k)) * (2^(SFB[n][k/V]-127) b(n,k))
  *
  * Every stored element is first decoded to the exact real number its bit
- * pattern encodes (fp64 holds every fp16, bf16, e4m3, e2m1 and e8m0 value exactly),
+ * pattern encodes (fp64 holds every fp16, bf16, e4m3, e2m3, e3m2, e2m1 and e8m0
+ * value exactly),
  * then the K products are summed in fp64 in increasing k.  The componentwise
  * magnitude S[m][n] = sum_k |a*b| is returned beside D for error bounds.
  *
  * Readings taken where the pages are silent: the 8-bit element format is OCP
  * E4M3 (bias 7, no infinities, S.1111.111 is NaN); the 4-bit one (the pages'
  * FP4, "four-bit values") is OCP E2M1, packed two per byte, low nibble first;
+ * the 6-bit ones (the pages' FP6, "six-bit values") are OCP E2M3 and E3M2,
+ * stored in the pages' padded form of the decompression copy (tcgen05.cp page,
+ * "Native FP4/FP6 decompression": each 16-byte block holds sixteen packed
+ * values followed by four bytes of padding), read as value j of a block in
+ * bits 6j .. 6j+5 of its first twelve bytes taken little-endian;
  * a scale byte E means 2^(E-127) (OCP E8M0, 255 is NaN); scale blocks start
  * at k = 0, V, 2V, ...; beta is 0 or 1 and beta = 0 never reads D0.
  *
@@ -43,8 +49,11 @@
 
 /* Element kinds understood by the oracle (its own numbering).  ORC_E2M1
  * elements are packed two per byte: element 2j in bits 0..3 of byte j,
- * element 2j+1 in bits 4..7. */
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4, ORC_E2M1 = 5 };
+ * element 2j+1 in bits 4..7.  ORC_E2M3 / ORC_E3M2 elements are packed sixteen
+ * per 16-byte block: element 16b + j in bits 6j .. 6j+5 of bytes 16b .. 16b+11
+ * read as one little-endian number; bytes 16b+12 .. 16b+15 are padding and
+ * never read. */
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4, ORC_E2M1 = 5, ORC_E2M3 = 6, ORC_E3M2 = 7 };
 /* Operand majors (its own numbering). */
 enum { ORC_KMAJOR = 0, ORC_MNMAJOR = 1 };
 /* Return codes. */
@@ -105,6 +114,38 @@ double orc_decode_e2m1(uint8_t nibble)
     return s ? -v : v;
 }
 
+/* OCP E2M3 (6-bit): 1 sign, 2 exponent (bias 1), 3 fraction bits; no
+ * infinities or NaN.  Exponent 0 is subnormal: f/8; otherwise
+ * (1 + f/8) * 2^(e-1); the largest magnitude is 7.5. */
+double orc_decode_e2m3(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 3) & 3, f = code & 7;
+    double v = e == 0 ? ldexp((double)f, -3) : ldexp((double)(8 + f), e - 4);
+    return s ? -v : v;
+}
+
+/* OCP E3M2 (6-bit): 1 sign, 3 exponent (bias 3), 2 fraction bits; no
+ * infinities or NaN.  Exponent 0 is subnormal: f/4 * 2^-2; otherwise
+ * (1 + f/4) * 2^(e-3); the largest magnitude is 28. */
+double orc_decode_e3m2(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 2) & 7, f = code & 3;
+    double v = e == 0 ? ldexp((double)f, -4) : ldexp((double)(4 + f), e - 5);
+    return s ? -v : v;
+}
+
+/* The 6-bit code of element idx of a padded FP6 array (see ORC_E2M3). */
+static uint8_t fp6_code(const uint8_t *base, int64_t idx)
+{
+    const uint8_t *blk = base + (idx / 16) * 16;
+    const int bit = 6 * (int)(idx % 16);               /* 0 .. 90 */
+    const int byte = bit / 8, sh = bit % 8;            /* byte <= 11 */
+    unsigned v = blk[byte];
+    if (sh > 2)                                        /* the code spills into the next byte (<= 11) */
+        v |= (unsigned)blk[byte + 1] << 8;
+    return (uint8_t)((v >> sh) & 0x3f);
+}
+
 /* OCP E8M0 scale: 2^(E-127); E = 255 is NaN. */
 double orc_decode_e8m0(uint8_t b)
 {
@@ -118,6 +159,7 @@ static int elem_size(int dt)
     case ORC_E4M3: return 1;
     case ORC_F32: return 4;
     case ORC_E2M1: return 1;   /* storage byte (two elements) */
+    case ORC_E2M3: case ORC_E3M2: return 1;   /* 16 bytes per 16 elements */
     default: return 0;
     }
 }
@@ -133,6 +175,8 @@ static double decode_one(int dt, const void *base, int64_t idx)
         const uint8_t byte = ((const uint8_t *)base)[idx >> 1];
         return orc_decode_e2m1((idx & 1) ? byte >> 4 : byte & 0xf);
     }
+    case ORC_E2M3: return orc_decode_e2m3(fp6_code((const uint8_t *)base, idx));
+    case ORC_E3M2: return orc_decode_e3m2(fp6_code((const uint8_t *)base, idx));
     default: return NAN;
     }
 }

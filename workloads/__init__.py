@@ -13,7 +13,11 @@ draws in the order A, B, D0, SFA, SFB, each in the C order of its stored
 layout; fp64 samples are rounded to nearest-even into the storage type
 (fp16 by numpy; bf16 and e4m3 through an fp32 intermediate by torch; e2m1 to
 the nearest of its 16 values, ties to the even code, magnitudes above 6
-saturating to 6, then packed two per byte, element 2j in the low nibble);
+saturating to 6, then packed two per byte, element 2j in the low nibble;
+e2m3 and e3m2 to the nearest of their 64 values, ties to the even code,
+saturating at 7.5 and 28, then packed sixteen per 16-byte block in bits
+6j .. 6j+5 of the block's first twelve bytes, little-endian, the last four
+bytes zero);
 e8m0 scale bytes are 127 + u with u a uniform integer in [-4, 4].
 The quarter-integer variant (the tcgen05.mma page's example test draws
 integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
@@ -30,7 +34,7 @@ import numpy as np
 import torch
 
 #: Stored element kinds, named as in the oracle and the binding.
-KINDS = ("f16", "bf16", "e4m3", "e2m1")
+KINDS = ("f16", "bf16", "e4m3", "e2m1", "e2m3", "e3m2")
 
 
 @dataclass(frozen=True)
@@ -100,6 +104,8 @@ def to_stored(x: np.ndarray, kind: str) -> np.ndarray:
     """Round fp64 values into the stored bit patterns of ``kind``."""
     if kind == "e2m1":
         return _to_e2m1_packed(x)
+    if kind in _FP6_MAG:
+        return _to_fp6_padded(x, kind)
     if kind == "f16":
         return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
@@ -128,6 +134,42 @@ def _to_e2m1_packed(x: np.ndarray) -> np.ndarray:
     code = np.where((lo != hi) & (lo % 2 == 1), hi, lo).astype(np.uint8)   # exact tie: even code
     code |= (np.signbit(x).astype(np.uint8) << 3)
     return np.ascontiguousarray(code[..., 0::2] | (code[..., 1::2] << 4))
+
+
+# E2M3 / E3M2 magnitudes by code 0..31 (the OCP MX formats' value lists:
+# E2M3 subnormals 0.125 apart up to 0.875, then 1 .. 1.875, 2 .. 3.75,
+# 4 .. 7.5; E3M2 subnormals 0.0625 apart up to 0.1875, then four values per
+# binade from 0.25 up to 28)
+_FP6_MAG = {
+    "e2m3": np.array([i / 8 for i in range(8)] + [1 + i / 8 for i in range(8)] +
+                     [2 + i / 4 for i in range(8)] + [4 + i / 2 for i in range(8)]),
+    "e3m2": np.array([i / 16 for i in range(4)] +
+                     [2.0 ** (e - 3) * (1 + i / 4) for e in range(1, 8) for i in range(4)]),
+}
+
+
+def _to_fp6_padded(x: np.ndarray, kind: str) -> np.ndarray:
+    """Nearest code (ties to the even code, saturating at the largest value),
+    packed sixteen per 16-byte block along the last axis: value j of a block
+    in bits 6j .. 6j+5 of its first twelve bytes (little-endian), the last
+    four bytes zero."""
+    if x.shape[-1] % 16:
+        raise ValueError("6-bit rows need a multiple of 16 elements")
+    mag = _FP6_MAG[kind]
+    mid = (mag[1:] + mag[:-1]) / 2
+    a = np.abs(x)
+    lo = np.searchsorted(mid, a, side="left")
+    hi = np.searchsorted(mid, a, side="right")
+    code = np.where((lo != hi) & (lo % 2 == 1), hi, lo).astype(np.uint64)   # exact tie: even code
+    code |= np.signbit(x).astype(np.uint64) << np.uint64(5)
+    c = code.reshape(x.shape[:-1] + (x.shape[-1] // 16, 2, 8))
+    sh = np.arange(8, dtype=np.uint64) * np.uint64(6)
+    half = np.bitwise_or.reduce(c << sh, axis=-1)          # two 48-bit halves per block
+    le = half[..., None] >> (np.arange(6, dtype=np.uint64) * np.uint64(8))
+    payload = (le & np.uint64(0xFF)).astype(np.uint8).reshape(x.shape[:-1] + (x.shape[-1] // 16, 12))
+    out = np.zeros(x.shape[:-1] + (x.shape[-1] // 16, 16), dtype=np.uint8)
+    out[..., :12] = payload
+    return np.ascontiguousarray(out.reshape(x.shape))
 
 
 def _draw(rng, dist, size):
