@@ -67,6 +67,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 
 bool is_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+mswz::MxKind mx_kind(int dt)
+{
+    return dt == MSWZ_DT_E2M1 ? mswz::kMxE2m1 : dt == MSWZ_DT_E2M3 ? mswz::kMxE2m3
+                                              : dt == MSWZ_DT_E3M2 ? mswz::kMxE3m2 : mswz::kMxE4m3;
+}
+
 int out_kind(int d_dt)
 {
     return d_dt == MSWZ_DT_BF16 ? mswz::kOutBf16 : d_dt == MSWZ_DT_F16 ? mswz::kOutF16 : mswz::kOutF32;
@@ -113,7 +119,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     *out = nullptr;
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MSWZ_ERR_INVALID;
-    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_E2M1; };
+    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_E3M2; };
     if (!known_dt(a_dt) || !known_dt(b_dt) || !known_dt(d_dt))
         return MSWZ_ERR_INVALID;
     if ((a_major != MSWZ_MAJOR_K && a_major != MSWZ_MAJOR_MN) ||
@@ -128,9 +134,10 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     const bool narrow_d = d_dt != MSWZ_DT_F32;
     const bool fp4 = a_dt == MSWZ_DT_E2M1;
-    const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4;   // block-scaled formats
+    const bool fp6 = a_dt == MSWZ_DT_E2M3 || a_dt == MSWZ_DT_E3M2;
+    const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4 || fp6;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
-        return MSWZ_ERR_UNSUPPORTED;     // E4M3 / E2M1 are block-scaled only; 16-bit is dense only
+        return MSWZ_ERR_UNSUPPORTED;     // 8-, 6- and 4-bit kinds are block-scaled only; 16-bit is dense only
     if (fp8 && scale_vec_len != 32)
         return MSWZ_ERR_UNSUPPORTED;
     if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
@@ -178,7 +185,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     const bool skinny = !fp8 && !narrow_d && !strided && a_major == MSWZ_MAJOR_K &&
                         b_major == MSWZ_MAJOR_K && M <= 64 && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : (tail || ktail || fp4 || narrow_d || strided) ? 256 : pick_tile(M, N);
+    const int tile = skinny ? 64 : (tail || ktail || fp4 || fp6 || narrow_d || strided) ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -287,7 +294,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                    p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd)};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st)
+    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, mx_kind(p->a_dt), st)
                                                   : mswz::launch_mx(p->variant, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
@@ -323,7 +330,7 @@ int gemm_run_opts(const gemm_plan *p, const void *A, const void *B, const uint8_
     if (mx) {
         mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                        p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};
-        err = mswz::launch_mx256(a, p->a_dt == MSWZ_DT_E2M1, st);
+        err = mswz::launch_mx256(a, mx_kind(p->a_dt), st);
     } else {
         mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                           p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};

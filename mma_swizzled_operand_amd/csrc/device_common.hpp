@@ -78,6 +78,17 @@ __device__ __forceinline__ f32x4 mfma_scale_16x16x128_e2m1(i32x8 a, i32x8 b, f32
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, scale_a, 0, scale_b);
 }
 
+// The same MFMA with OCP 6-bit operands, E2M3 (format code 2) or E3M2 (code
+// 3): lane l holds 32 values of row l % 16, value j in bits 6j .. 6j+5 of
+// registers 0..5 (registers 6 and 7 unused), all in scale block l/16, and lane
+// i + 16b supplies row i's scale for block b.
+template <bool E3M2>
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fp6(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b)
+{
+    constexpr int kFmt = E3M2 ? 3 : 2;
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmt, kFmt, 0, scale_a, 0, scale_b);
+}
+
 // Workgroup -> output tile.  The hardware hands consecutive workgroups to the
 // eight XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has its own
 // L2.  Tile ids are therefore re-ordered so that each XCD receives one

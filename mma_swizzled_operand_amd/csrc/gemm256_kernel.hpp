@@ -49,7 +49,7 @@ constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K s
 
 constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
 
-enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3 };
+enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3, kE2m3 = 4, kE3m2 = 5 };
 
 // Direct-to-LDS copy of one K-major operand tile (256 rows x 128 bytes per K
 // step) through a buffer resource on the workgroup's 256-row panel.  With W
@@ -244,6 +244,19 @@ __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 // the grouping by lane bits 3 and 4.
 __device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
 
+// First-half chunk of lane group g for the block-scaled 16x16x128 MFMA on
+// 6-bit operands in the padded layout (sixteen values per 16-byte chunk, so
+// the 128-byte row of a K step holds 128 values, four 32-value scale blocks
+// of two chunks each).  A probe pinned the operand image: lane (row i, group
+// g) holds 32 values (value j in bits 6j .. 6j+5 of registers 0..5) all in
+// scale block g, and lane i + 16b supplies row i's scale for block b.  Group
+// g therefore reads the two chunks 2g and 2g+1 of its rows and keeps the
+// first twelve bytes of each; with the E4M3 fragments' rows (two runs of 8
+// rows 16 apart) groups 0 and 2 take the two chunks in the other order
+// (chunk 2g+1 first), which keeps the reads free of bank conflicts.  A and B
+// use the same order, so each value still meets its partner.
+__device__ __forceinline__ int fp6_chunk16(int g) { return 2 * g + ((g & 1) ^ 1); }
+
 // Compile-time loop: fn(std::integral_constant<int, F>), ..., up to L - 1.
 template <int F, int L, class Fn>
 __device__ __forceinline__ void static_for(Fn &&fn)
@@ -435,17 +448,20 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                void *__restrict__ D, int M, int N, int K, int lda, int ldb, int ldd, int tiles_m,
                int tiles_n, int group_m, EpiOpts opts)
 {
-    static_assert(!((A_MN || B_MN) && (KIND == kE4m3 || KIND == kE2m1)),
-                  "MN-major operands are built for 16-bit only");
+    static_assert(!((A_MN || B_MN) && KIND != kBf16 && KIND != kF16), "MN-major operands are built for 16-bit only");
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
-    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1;
-    constexpr bool kMx = kFp8 || kFp4;
+    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1, kFp6 = KIND == kE2m3 || KIND == kE3m2;
+    constexpr bool kMx = kFp8 || kFp4 || kFp6;
+    // E4M3 and padded 6-bit operands share the byte layout (128 values per
+    // 128-byte row step) and the split-row fragments
+    constexpr bool kByteRows = kFp8 || kFp6;
     static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
+    static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "FP6 is built for the eight-wave 16x16 path");
     // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
     // E2M1 (packed two per byte) K elements
-    constexpr int kStepK = kFp4 ? 256 : kFp8 ? 128 : 64;
+    constexpr int kStepK = kFp4 ? 256 : kByteRows ? 128 : 64;
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
@@ -512,7 +528,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kFp8 && (REG & 8) != 0 && W == 8;   // the 16x16 E4M3 path
+    constexpr bool kScaleGroups = kByteRows && (REG & 8) != 0 && W == 8;   // the 16x16 E4M3 / FP6 path
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / 32;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -615,15 +631,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < TM16; ++i) {
-            const uint32_t row = wm + row16<kFp8>(i, r16);
-            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
+            const uint32_t row = wm + row16<kByteRows>(i, r16);
+            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
             abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
                               : row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < TN16; ++j) {
-            const uint32_t row = wn + row16<kFp8>(j, r16);
-            const int c = kFp8 ? mx_chunk16(g) : kblk16(g);
+            const uint32_t row = wn + row16<kByteRows>(j, r16);
+            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
             bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
                               : kATile + row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
@@ -782,9 +798,13 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
+        // E4M3: chunks c and c + 4; FP6: chunks c and c ^ 1, of which the
+        // first twelve bytes each form registers 0..2 and 3..5
         auto frag = [&](uint32_t base) {
             const u32x4 lo = lds_read16(s, base);
-            const u32x4 hi = lds_read16(s, base ^ 64u);
+            const u32x4 hi = lds_read16(s, base ^ (kFp6 ? 16u : 64u));
+            if constexpr (kFp6)
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 4, 5, 6, 3, 7));
             return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         // MFMA m = TN16 * i + j; each block's fragment and scale are read two
@@ -811,7 +831,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             if constexpr (c1 > c0)
                 __builtin_amdgcn_sched_group_barrier(0x100, 3 * (c1 - c0), 0);   // DS reads
             constexpr int i = m / TN16, j = m % TN16;
-            acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
+            if constexpr (kFp6)
+                acc4[j][i] = mfma_scale_16x16x128_fp6<KIND == kE3m2>(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
+            else
+                acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
         });
     };
@@ -996,8 +1019,8 @@ epilogue:
         for (int j = 0; j < TN16; ++j)
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
-                const int m = m0 + wm + row16<kFp8>(i, lane & 15);
-                const int n = n0 + wn + row16<kFp8>(j, 4 * (lane >> 4));
+                const int m = m0 + wm + row16<kByteRows>(i, lane & 15);
+                const int n = n0 + wn + row16<kByteRows>(j, 4 * (lane >> 4));
                 if (m >= M || n >= N)
                     continue;
                 f32x4 v = acc4[j][i];
@@ -1060,7 +1083,7 @@ hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
     if (a.out != kOutF32)
         return launch_out<KIND, A_MN, B_MN>(a, stream);
     // a K that is not a multiple of the step takes the default pipeline
-    if (KIND != kE4m3 && KIND != kE2m1 && a.K % 64 != 0)
+    if ((KIND == kBf16 || KIND == kF16) && a.K % 64 != 0)
         return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
     switch (config256()) {
     case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);

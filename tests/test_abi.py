@@ -64,7 +64,7 @@ def _create(*args):
     return rc
 
 
-F16, BF16, E4M3, F32, E2M1 = 1, 2, 3, 4, 5
+F16, BF16, E4M3, F32, E2M1, E2M3, E3M2 = 1, 2, 3, 4, 5, 6, 7
 K_, MN = 0, 1
 
 
@@ -78,11 +78,18 @@ K_, MN = 0, 1
     ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 0), -2),       # fp4 needs scales
     ((256, 256, 512, E2M1, E2M1, F32, MN, K_, 32), -2),      # MN-major fp4 not built
     ((256, 256, 512, E2M1, E4M3, F32, K_, K_, 32), -2),      # mixed formats
+    ((256, 256, 128, E2M3, E2M3, F32, K_, K_, 32), 0),       # MX-fp6 (padded, sixteen per 16 bytes)
+    ((300, 260, 384, E3M2, E3M2, BF16, K_, K_, 32), 0),      # ragged, bf16 output
+    ((256, 256, 64, E2M3, E2M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
+    ((256, 256, 128, E3M2, E3M2, F32, K_, K_, 0), -2),       # fp6 needs scales
+    ((256, 256, 128, E2M3, E2M3, F32, K_, MN, 32), -2),      # MN-major fp6 not built
+    ((256, 256, 128, E2M3, E3M2, F32, K_, K_, 32), -2),      # mixed formats
+    ((256, 256, 128, E2M3, E4M3, F32, K_, K_, 32), -2),
+    ((256, 256, 128, 8, 8, F32, K_, K_, 32), -1),            # unknown dtype
     ((0, 256, 64, F16, F16, F32, K_, K_, 0), -1),            # empty M
     ((256, -1, 64, F16, F16, F32, K_, K_, 0), -1),
     ((256, 256, 0, F16, F16, F32, K_, K_, 0), -1),           # empty K
     ((256, 256, 64, 9, F16, F32, K_, K_, 0), -1),            # unknown dtype
-    ((256, 256, 64, 6, 6, F32, K_, K_, 0), -1),
     ((256, 256, 64, F16, F16, F32, 2, K_, 0), -1),           # unknown major
     ((256, 256, 64, F16, F16, F32, K_, K_, -32), -1),
     ((256, 256, 64, F16, BF16, F32, K_, K_, 0), -2),         # mixed 16-bit kinds

@@ -30,6 +30,8 @@ CASES = {
                                 name="e4m3-bf16-out"), "bf16"),
     "e2m1-f16-out-beta": (wl.custom(256, 256, 512, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
                                     b_dist=("normal", 1.0), name="e2m1-f16-out-beta"), "f16"),
+    "e2m3-bf16-out": (wl.custom(256, 512, 1024, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="e2m3-bf16-out"), "bf16"),
 }
 
 

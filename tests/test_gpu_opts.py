@@ -110,6 +110,8 @@ CASES = {
                                    name="e4m3-neg_a-masks"), "f32", dict(neg_a=True)),
     "e2m1-neg_b-beta": (wl.custom(256, 512, 512, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
                                   b_dist=("normal", 1.0), name="e2m1-neg_b-beta"), "f32", dict(neg_b=True)),
+    "e3m2-neg_a-masks": (wl.custom(256, 256, 1024, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                   name="e3m2-neg_a-masks"), "f32", dict(neg_a=True)),
 }
 
 

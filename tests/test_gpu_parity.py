@@ -285,6 +285,78 @@ def test_fp4_scale_bytes_select_the_right_block():
     assert np.array_equal(got.astype(np.float64), expect)
 
 
+# MX-fp6 (OCP E2M3 / E3M2, sixteen per 16-byte block with four bytes of
+# padding; the 256 tile only): per-step and grouped scale copies (K a multiple
+# of 1024), ragged M and N, beta = 1
+FP6 = {
+    "e2m3-mx": wl.custom(512, 768, 512, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                         name="e2m3-mx"),
+    "e3m2-mx-k1024-beta": wl.custom(256, 512, 1024, "e3m2", V=32, beta=1, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="e3m2-mx-k1024-beta"),
+    "e2m3-mx-tail": wl.custom(300, 292, 384, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                              name="e2m3-mx-tail"),
+    "e3m2-mx-k2048": wl.custom(512, 512, 2048, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e3m2-mx-k2048"),
+}
+
+
+@pytest.mark.parametrize("name", list(FP6))
+def test_fp6_full_compare(name):
+    w = FP6[name]
+    plan = plan_for(w)
+    say(f"[fp6] {name} {w.M}x{w.N}x{w.K} beta={w.beta} {plan.describe()}")
+    x = wl.generate(w, seed=41)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(FP6))
+def test_fp6_quarter_integers_bit_exact(name):
+    w = FP6[name]
+    say(f"[fp6-exact] {name}")
+    x = wl.generate(w, seed=42, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    ref = reference(w, x, with_mag=False)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("name", ["e2m3-mx", "e3m2-mx-k1024-beta"])
+def test_fp6_padding_bytes_are_never_read(name):
+    """Random bytes in every block's four padding bytes give the same bits."""
+    w = FP6[name]
+    say(f"[fp6-pad] {name}")
+    x = wl.generate(w, seed=43)
+    base = run_gpu(w, x)
+    rng = np.random.default_rng(44)
+    y = dict(x)
+    for k in ("A", "B"):
+        a = x[k].copy().reshape(-1, 16)
+        a[:, 12:] = rng.integers(0, 256, (a.shape[0], 4), dtype=np.uint8)
+        y[k] = a.reshape(x[k].shape)
+    assert np.array_equal(run_gpu(w, y), base)
+
+
+@pytest.mark.parametrize("kind,one", [("e2m3", 8), ("e3m2", 12)])
+def test_fp6_scale_bytes_select_the_right_block(kind, one):
+    """Scales only: every element 1.0, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
+    exactly; a wrong scale byte or lane for any block changes the value."""
+    M, N, K = 256, 512, 1024
+    w = wl.custom(M, N, K, kind, V=32, name=f"{kind}-scale-only")
+    rng = np.random.default_rng(9)
+    ones = wl.to_stored(np.ones((1, 16)), kind)[0]
+    assert ones[0] == one
+    x = {"A": np.tile(ones, (M, K // 16)), "B": np.tile(ones, (N, K // 16)),
+         "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
+         "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
+    say(f"[fp6] scale closed form {kind}")
+    got = run_gpu(w, x)
+    ua = x["SFA"].astype(np.int64) - 127
+    ub = x["SFB"].astype(np.int64) - 127
+    expect = 32.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
+    assert np.array_equal(got.astype(np.float64), expect)
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
@@ -301,7 +373,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c3b", *EXTRA_FULL])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c3b", *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""

@@ -20,9 +20,10 @@ from gpu_util import compare, plan_for, reference, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 # stored element -> (torch storage dtype, elements per storage element)
-STORE = {"f16": (torch.int16, 1), "bf16": (torch.int16, 1), "e4m3": (torch.uint8, 1), "e2m1": (torch.uint8, 2)}
+STORE = {"f16": (torch.int16, 1), "bf16": (torch.int16, 1), "e4m3": (torch.uint8, 1), "e2m1": (torch.uint8, 2),
+         "e2m3": (torch.uint8, 1), "e3m2": (torch.uint8, 1)}
 # padding that would poison any output it entered
-POISON = {"f16": 0x7C00, "bf16": 0x7F80, "e4m3": 0x7F, "e2m1": 0x77}
+POISON = {"f16": 0x7C00, "bf16": 0x7F80, "e4m3": 0x7F, "e2m1": 0x77, "e2m3": 0xFF, "e3m2": 0xFF}
 D_SENTINEL = {"f32": -12345.5, "bf16": -123.5, "f16": -123.5}
 D_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -44,6 +45,8 @@ CASES = {
                             b_dist=("normal", 1.0), name="e2m1-beta"), 544, 576, 388, "f32"),
     "bf16-out-tail": (wl.custom(264, 300, 192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                 name="bf16-out-tail"), 256, 200, 304, "bf16"),
+    "e3m2-beta": (wl.custom(256, 264, 512, "e3m2", V=32, beta=1, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                            name="e3m2-beta"), 544, 528, 268, "f32"),
     # K tails: the poisoned storage between K and the pitch must never reach the sums
     "bf16-ktail": (wl.custom(256, 256, 72, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                              name="bf16-ktail"), 136, 80, 0, "f32"),
@@ -147,7 +150,7 @@ def test_strided_against_oracle(case):
         assert np.array_equal(got, pk), "strided and packed results differ"
 
 
-@pytest.mark.parametrize("case", ["bf16-k", "f16-amn-tail-beta", "bf16-both-mn", "e4m3-mx", "e2m1-beta"])
+@pytest.mark.parametrize("case", ["bf16-k", "f16-amn-tail-beta", "bf16-both-mn", "e4m3-mx", "e2m1-beta", "e3m2-beta"])
 def test_strided_quarter_integers_exact(case):
     w, lda, ldb, ldd, d_fmt = CASES[case]
     say(f"[strided-exact] {case}")

@@ -82,6 +82,10 @@ WORKLOADS = {
                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
     "c6": Workload("c6", "MX-fp4 8192^3 e2m1 K-major, N(0,1) rounded to e2m1, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
                    8192, 8192, 8192, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c7": Workload("c7", "MX-fp6 8192^3 e2m3 K-major (padded, sixteen per 16 bytes), N(0,1) rounded to e2m3, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                   8192, 8192, 8192, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c8": Workload("c8", "MX-fp6 8192^3 e3m2 K-major (padded, sixteen per 16 bytes), N(0,1) rounded to e3m2, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                   8192, 8192, 8192, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
     "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
                     8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
 }
@@ -156,20 +160,22 @@ def _to_fp6_padded(x: np.ndarray, kind: str) -> np.ndarray:
     if x.shape[-1] % 16:
         raise ValueError("6-bit rows need a multiple of 16 elements")
     mag = _FP6_MAG[kind]
-    mid = (mag[1:] + mag[:-1]) / 2
-    a = np.abs(x)
-    lo = np.searchsorted(mid, a, side="left")
-    hi = np.searchsorted(mid, a, side="right")
-    code = np.where((lo != hi) & (lo % 2 == 1), hi, lo).astype(np.uint64)   # exact tie: even code
-    code |= np.signbit(x).astype(np.uint64) << np.uint64(5)
-    c = code.reshape(x.shape[:-1] + (x.shape[-1] // 16, 2, 8))
-    sh = np.arange(8, dtype=np.uint64) * np.uint64(6)
-    half = np.bitwise_or.reduce(c << sh, axis=-1)          # two 48-bit halves per block
-    le = half[..., None] >> (np.arange(6, dtype=np.uint64) * np.uint64(8))
-    payload = (le & np.uint64(0xFF)).astype(np.uint8).reshape(x.shape[:-1] + (x.shape[-1] // 16, 12))
-    out = np.zeros(x.shape[:-1] + (x.shape[-1] // 16, 16), dtype=np.uint8)
-    out[..., :12] = payload
-    return np.ascontiguousarray(out.reshape(x.shape))
+    mid = torch.from_numpy((mag[1:] + mag[:-1]) / 2)
+    flat = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64).reshape(-1, 16))
+    out = torch.zeros((flat.shape[0], 16), dtype=torch.uint8)
+    step = 1 << 20   # blocks per chunk (bounded temporaries)
+    for b0 in range(0, flat.shape[0], step):
+        xb = flat[b0:b0 + step]
+        a = xb.abs()
+        lo = torch.bucketize(a, mid)                                   # first midpoint >= a
+        tie = (lo < mid.numel()) & (mid[lo.clamp(max=mid.numel() - 1)] == a)
+        code = (lo + (tie & (lo % 2 == 1))).to(torch.int32)           # exact tie: even code
+        code |= torch.signbit(xb).to(torch.int32) << 5
+        # four values = 24 bits = three bytes; value 4q + t at bits 6t of group q
+        g = code.reshape(-1, 4, 4)
+        v = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)
+        out[b0:b0 + step, :12] = torch.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], dim=-1).reshape(-1, 12).to(torch.uint8)
+    return np.ascontiguousarray(out.numpy().reshape(x.shape))
 
 
 def _draw(rng, dist, size):
