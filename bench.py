@@ -6,8 +6,8 @@ for the workload on inputs already resident in HBM.  Default workload: the
 square dense 4096^3 bf16 GEMM with both operands K-major (N(0,1) inputs,
 seed 0).  The other full-size workloads (8192^3 fp16 MN-major A with beta=1,
 8192^3 bf16, the skinny 64x16384x8192 weight-streaming shape, 8192^3 MX-fp8,
-8192^3 MX-fp4 and 8192^3 MX-fp6 in both 6-bit formats) are timed in the same
-run and reported under "also".
+8192^3 MX-fp4, 8192^3 MX-fp6 in both 6-bit formats and 8192^3 with E4M3 A
+and E2M3 B) are timed in the same run and reported under "also".
 
 Prints ONE JSON line (rank 0).  ``roofline`` reports the dominant kernel
 against the MI355X dense MFMA peak (or HBM peak for the skinny shape), using
@@ -32,6 +32,12 @@ METRIC = "GEMM TFLOP/s on 1 MI355X (bf16 8192³, MX-fp8 8192³) and % of MFMA pe
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4, "e2m3": 10066.4, "e3m2": 10066.4}
 HBM_PEAK = 8000.0
+
+
+def mfma_peak(w) -> float:
+    """Dense MFMA peak of the workload's operand kinds (the slower one when A
+    and B differ: a mixed MFMA runs at the wider format's rate)."""
+    return min(MFMA_PEAK[w.kind], MFMA_PEAK[w.kind_b])
 
 
 def log(msg):
@@ -76,7 +82,7 @@ def setup(w, seed=0):
             a = a.view(np.int16)
         return torch.from_numpy(a).cuda()
 
-    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, "f32", w.a_major, w.b_major, w.V)
+    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind_b, "f32", w.a_major, w.b_major, w.V)
     A, B = dev(x["A"]), dev(x["B"])
     D = dev(x["D0"]) if w.beta else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
     if w.V:
@@ -148,7 +154,7 @@ def cpu_baseline(w, x, target_s):
 
     def run(r):
         t0 = time.perf_counter()
-        oracle.gemm(w.M, w.N, w.K, w.kind, w.a_major, x["A"], w.kind, w.b_major, x["B"],
+        oracle.gemm(w.M, w.N, w.K, w.kind, w.a_major, x["A"], w.kind_b, w.b_major, x["B"],
                     V=w.V, SFA=x.get("SFA"), SFB=x.get("SFB"), beta=w.beta, D0=x.get("D0"),
                     rows=list(range(r)))
         return time.perf_counter() - t0
@@ -176,7 +182,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8",
+    ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8,c9",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -218,7 +224,7 @@ def main():
     if hbm:
         achieved, peak, unit = head["kernel_gbs"], HBM_PEAK, "GB/s"
     else:
-        achieved, peak, unit = head["kernel_tflops"], MFMA_PEAK[w.kind], "TFLOP/s"
+        achieved, peak, unit = head["kernel_tflops"], mfma_peak(w), "TFLOP/s"
     roofline = {"bound": "hbm" if hbm else "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(w.name)}
@@ -229,7 +235,7 @@ def main():
         ow = r["workload"]
         entry = {"title": ow.title, "us_per_call": round(r["kernel_avg_ms"] * 1e3, 2),
                  "TFLOP/s": round(r["kernel_tflops"], 1),
-                 "frac_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK[ow.kind], 4),
+                 "frac_mfma_peak": round(r["kernel_tflops"] / mfma_peak(ow), 4),
                  "GB/s_algorithmic": round(r["kernel_gbs"], 1),
                  "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"], r["plan"]["tile_k"]]}
         if ow.name == "c4":
@@ -258,7 +264,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.title}", "M": w.M, "N": w.N, "K": w.K,
                    "a_major": w.a_major, "b_major": w.b_major, "beta": w.beta,
                    "scale_vec_len": w.V, "tile": head["plan"], "frac_mfma_peak":
-                   round(head["kernel_tflops"] / MFMA_PEAK[w.kind], 4)},
+                   round(head["kernel_tflops"] / mfma_peak(w), 4)},
         "roofline": roofline,
         "kernel_avg_us": round(head["kernel_avg_ms"] * 1e3, 2),
         "cpu_baseline": cpu,

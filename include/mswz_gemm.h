@@ -95,7 +95,9 @@ typedef struct gemm_plan gemm_plan;
  *                 reads D in that format and adds it in fp32 before
  *                 rounding); narrow D always uses the 256 tile
  *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) and
- *                 (E2M1,E2M1), (E2M3,E2M3), (E3M2,E3M2) block-scaled.
+ *                 (E2M1,E2M1), (E2M3,E2M3), (E3M2,E3M2) block-scaled, and any
+ *                 mix of E4M3, E2M3 and E3M2 for A and B (the pages' mixed
+ *                 f8f6f4 kind; each operand decoded in its own format, 256 tile).
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3, E2M1,

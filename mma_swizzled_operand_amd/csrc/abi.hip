@@ -127,8 +127,11 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_INVALID;
     if (scale_vec_len < 0)
         return MSWZ_ERR_INVALID;
-    if (a_dt != b_dt || a_dt == MSWZ_DT_F32)
+    // A and B share a kind, except that E4M3, E2M3 and E3M2 mix freely
+    auto byte_mx = [](int d) { return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2; };
+    if ((a_dt != b_dt && !(byte_mx(a_dt) && byte_mx(b_dt))) || a_dt == MSWZ_DT_F32)
         return MSWZ_ERR_UNSUPPORTED;
+    const bool mixed = a_dt != b_dt;
     // D: fp32, or the fp32 result rounded to bf16 / fp16 (the 256 tile only)
     if (d_dt != MSWZ_DT_F32 && d_dt != MSWZ_DT_BF16 && d_dt != MSWZ_DT_F16)
         return MSWZ_ERR_UNSUPPORTED;
@@ -185,7 +188,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     const bool skinny = !fp8 && !narrow_d && !strided && a_major == MSWZ_MAJOR_K &&
                         b_major == MSWZ_MAJOR_K && M <= 64 && N % 64 == 0 &&
                         K % 1024 == 0 && !getenv("MSWZ_TILE");
-    const int tile = skinny ? 64 : (tail || ktail || fp4 || fp6 || narrow_d || strided) ? 256 : pick_tile(M, N);
+    const int tile = skinny ? 64 : (tail || ktail || fp4 || fp6 || mixed || narrow_d || strided) ? 256 : pick_tile(M, N);
     if (!tile)
         return MSWZ_ERR_UNSUPPORTED;
 
@@ -294,7 +297,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                    p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd)};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, mx_kind(p->a_dt), st)
+    hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st)
                                                   : mswz::launch_mx(p->variant, a, st);
     return e == hipSuccess ? MSWZ_OK : MSWZ_ERR_HIP;
 }
@@ -330,7 +333,7 @@ int gemm_run_opts(const gemm_plan *p, const void *A, const void *B, const uint8_
     if (mx) {
         mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                        p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};
-        err = mswz::launch_mx256(a, mx_kind(p->a_dt), st);
+        err = mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st);
     } else {
         mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                           p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};

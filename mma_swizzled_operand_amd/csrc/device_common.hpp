@@ -89,6 +89,14 @@ __device__ __forceinline__ f32x4 mfma_scale_16x16x128_fp6(i32x8 a, i32x8 b, f32x
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmt, kFmt, 0, scale_a, 0, scale_b);
 }
 
+// The same MFMA with the first and second operands in formats F1 and F2
+// (E4M3 0, E2M3 2, E3M2 3); lane images as in the single-format forms above.
+template <int F1, int F2>
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fmt(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F1, F2, 0, scale_a, 0, scale_b);
+}
+
 // Workgroup -> output tile.  The hardware hands consecutive workgroups to the
 // eight XCDs in turn (workgroup b runs on XCD b % 8), and each XCD has its own
 // L2.  Tile ids are therefore re-ordered so that each XCD receives one

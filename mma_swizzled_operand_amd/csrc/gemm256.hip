@@ -1,7 +1,8 @@
 // gemm256.hip — run-time dispatch of the 256x256-tile GEMM (gemm256_kernel.hpp)
 // to its instantiations, one translation unit per operand kind and A major
 // (gemm256_bf16_ak.hip, gemm256_bf16_amn.hip, gemm256_f16_ak.hip,
-// gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e2m1.hip, gemm256_fp6.hip),
+// gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e2m1.hip, gemm256_fp6.hip,
+// gemm256_mixed.hip),
 // so that they
 // compile in parallel.
 #include <hip/hip_runtime.h>
@@ -39,8 +40,10 @@ hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, 
     return a_mn ? launch256_f16_amn(b_mn, a, stream) : launch256_f16_ak(b_mn, a, stream);
 }
 
-hipError_t launch_mx256(const MxArgs &a, MxKind kind, hipStream_t stream)
+hipError_t launch_mx256(const MxArgs &a, MxKind kind, MxKind kind_b, hipStream_t stream)
 {
+    if (kind_b != kind)
+        return launch256_mixed(a, kind, kind_b, stream);
     switch (kind) {
     case kMxE2m1: return launch256_e2m1(a, stream);
     case kMxE2m3: return launch256_fp6(a, false, stream);

@@ -257,6 +257,25 @@ __device__ __forceinline__ int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1
 // use the same order, so each value still meets its partner.
 __device__ __forceinline__ int fp6_chunk16(int g) { return 2 * g + ((g & 1) ^ 1); }
 
+// Mixed formats (one operand E4M3, the other 6-bit).  A probe of the scaled
+// MFMA with one-hot operands of different formats showed that values meet by
+// an internal K index: 32g + j for value j of lane group g of a 6-bit (or
+// 4-bit) operand, and 32(g/2) + 16(g%2) + j for byte j < 16 of an E4M3 lane
+// (64 more for bytes 16..31).  With the 6-bit operand's chunk order
+// fp6_chunk16, the E4M3 operand's lane group g must read chunk
+// mx_chunk16_mixed(g) for bytes 0..15 (and that chunk + 4 for bytes 16..31)
+// so that partners share their K position in memory; this order, like
+// fp6_chunk16, is free of bank conflicts with the split-row fragments, and
+// each group still reads the 32-element scale blocks g/2 and 2 + g/2.
+__device__ __forceinline__ int mx_chunk16_mixed(int g) { return (g >> 1) ? g : g ^ 1; }
+
+// MFMA format code of a block-scaled element kind (E4M3 0, E2M3 2, E3M2 3).
+template <int KIND_>
+constexpr int mx_format()
+{
+    return KIND_ == kE3m2 ? 3 : KIND_ == kE2m3 ? 2 : 0;
+}
+
 // Compile-time loop: fn(std::integral_constant<int, F>), ..., up to L - 1.
 template <int F, int L, class Fn>
 __device__ __forceinline__ void static_for(Fn &&fn)
@@ -441,7 +460,9 @@ __device__ __forceinline__ bool apply_opts(const EpiOpts &o, int m, int n, f32x4
     return true;
 }
 
-template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32>
+// KIND: element kind of A (and of B unless KB >= 0); KB: B's kind when it
+// differs (block-scaled E4M3 / E2M3 / E3M2 only).
+template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32, int KB = -1>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -452,6 +473,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
+    constexpr int kKindB = KB < 0 ? KIND : KB;
+    constexpr bool kMixed = kKindB != KIND;
+    static_assert(!kMixed || ((KIND == kE4m3 || KIND == kE2m3 || KIND == kE3m2) &&
+                              (kKindB == kE4m3 || kKindB == kE2m3 || kKindB == kE3m2)),
+                  "mixed operand kinds are built for E4M3 / E2M3 / E3M2");
+    constexpr bool kFp6B = kKindB == kE2m3 || kKindB == kE3m2;
+    constexpr bool kFp8B = kKindB == kE4m3;
+    // A's kind below; B's differs only in the fragment reads and the MFMA format
     constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1, kFp6 = KIND == kE2m3 || KIND == kE3m2;
     constexpr bool kMx = kFp8 || kFp4 || kFp6;
     // E4M3 and padded 6-bit operands share the byte layout (128 values per
@@ -459,6 +488,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr bool kByteRows = kFp8 || kFp6;
     static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
     static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "FP6 is built for the eight-wave 16x16 path");
+    static_assert(!kMixed || ((REG & 8) != 0 && W == 8), "mixed kinds are built for the eight-wave 16x16 path");
     // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
     // E2M1 (packed two per byte) K elements
     constexpr int kStepK = kFp4 ? 256 : kByteRows ? 128 : 64;
@@ -632,14 +662,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
         for (int i = 0; i < TM16; ++i) {
             const uint32_t row = wm + row16<kByteRows>(i, r16);
-            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
+            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? (kMixed ? mx_chunk16_mixed(g) : mx_chunk16(g)) : kblk16(g);
             abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane)
                               : row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
 #pragma unroll
         for (int j = 0; j < TN16; ++j) {
             const uint32_t row = wn + row16<kByteRows>(j, r16);
-            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
+            const int c = kMixed ? (kFp6B ? fp6_chunk16(g) : mx_chunk16_mixed(g))
+                                 : kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
             bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane)
                               : kATile + row * kTileRowBytes + ((c ^ tile_key(row)) << 4);
         }
@@ -800,13 +831,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
         // E4M3: chunks c and c + 4; FP6: chunks c and c ^ 1, of which the
         // first twelve bytes each form registers 0..2 and 3..5
-        auto frag = [&](uint32_t base) {
+        auto frag_of = [&](uint32_t base, auto six) {
+            constexpr bool k6 = decltype(six)::value;
             const u32x4 lo = lds_read16(s, base);
-            const u32x4 hi = lds_read16(s, base ^ (kFp6 ? 16u : 64u));
-            if constexpr (kFp6)
+            const u32x4 hi = lds_read16(s, base ^ (k6 ? 16u : 64u));
+            if constexpr (k6)
                 return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 4, 5, 6, 3, 7));
             return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
+        auto frag = [&](uint32_t base) { return frag_of(base, std::integral_constant<bool, kFp6>{}); };
+        auto frag_b = [&](uint32_t base) { return frag_of(base, std::integral_constant<bool, kFp6B>{}); };
         // MFMA m = TN16 * i + j; each block's fragment and scale are read two
         // MFMAs ahead of first use, in that order (FragSchedule), so that a
         // wave's first MFMA waits for a few reads rather than for the whole
@@ -825,13 +859,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                     af[it - 1] = frag(ab[it - 1]);
                 } else {
                     sb[-it - 1] = ss[sfb + sf_off(-it - 1) + 4 * widx];
-                    bf[-it - 1] = frag(bb[-it - 1]);
+                    bf[-it - 1] = frag_b(bb[-it - 1]);
                 }
             });
             if constexpr (c1 > c0)
                 __builtin_amdgcn_sched_group_barrier(0x100, 3 * (c1 - c0), 0);   // DS reads
             constexpr int i = m / TN16, j = m % TN16;
-            if constexpr (kFp6)
+            if constexpr (kMixed)
+                acc4[j][i] = mfma_scale_16x16x128_fmt<mx_format<kKindB>(), mx_format<KIND>()>(bf[j], af[i], acc4[j][i],
+                                                                                              sb[j], sa[i]);
+            else if constexpr (kFp6)
                 acc4[j][i] = mfma_scale_16x16x128_fp6<KIND == kE3m2>(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
             else
                 acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
@@ -1049,7 +1086,7 @@ epilogue:
         }
 }
 
-template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32>
+template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32, int KB = -1>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
@@ -1057,23 +1094,23 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT, KB>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT, KB>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
 }
 
 // bf16 / fp16 output: the default pipeline only
-template <int KIND, bool A_MN, bool B_MN>
+template <int KIND, bool A_MN, bool B_MN, int KB = -1>
 hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 {
     constexpr int kReg = (A_MN && B_MN) ? 0 : 8;
-    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16>(a, stream)
-                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16>(a, stream);
+    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16, KB>(a, stream)
+                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16, KB>(a, stream);
 }
 
 

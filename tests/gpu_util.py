@@ -36,7 +36,7 @@ def to_device(arr: np.ndarray) -> torch.Tensor:
 
 
 def plan_for(w: wl.Workload) -> mswz.Plan:
-    return mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, "f32", w.a_major, w.b_major, w.V)
+    return mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind_b, "f32", w.a_major, w.b_major, w.V)
 
 
 def run_gpu(w: wl.Workload, x: dict, plan=None, D_init=None, workspace=None) -> np.ndarray:
@@ -68,7 +68,7 @@ def zero_workspace(plan):
 
 
 def reference(w: wl.Workload, x: dict, rows=None, cols=None, with_mag=True):
-    return oracle.gemm(w.M, w.N, w.K, w.kind, w.a_major, x["A"], w.kind, w.b_major, x["B"],
+    return oracle.gemm(w.M, w.N, w.K, w.kind, w.a_major, x["A"], w.kind_b, w.b_major, x["B"],
                        V=w.V, SFA=x.get("SFA"), SFB=x.get("SFB"), beta=w.beta, D0=x.get("D0"),
                        rows=rows, cols=cols, with_mag=with_mag)
 

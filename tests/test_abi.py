@@ -83,8 +83,12 @@ K_, MN = 0, 1
     ((256, 256, 64, E2M3, E2M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
     ((256, 256, 128, E3M2, E3M2, F32, K_, K_, 0), -2),       # fp6 needs scales
     ((256, 256, 128, E2M3, E2M3, F32, K_, MN, 32), -2),      # MN-major fp6 not built
-    ((256, 256, 128, E2M3, E3M2, F32, K_, K_, 32), -2),      # mixed formats
-    ((256, 256, 128, E2M3, E4M3, F32, K_, K_, 32), -2),
+    ((256, 256, 128, E2M3, E3M2, F32, K_, K_, 32), 0),       # mixed 8- and 6-bit kinds
+    ((256, 256, 128, E2M3, E4M3, F32, K_, K_, 32), 0),
+    ((300, 260, 256, E4M3, E3M2, F16, K_, K_, 32), 0),
+    ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), -2),      # FP4 does not mix
+    ((256, 256, 256, E2M1, E2M3, F32, K_, K_, 32), -2),
+    ((256, 256, 128, E4M3, BF16, F32, K_, K_, 32), -2),      # dense with block-scaled
     ((256, 256, 128, 8, 8, F32, K_, K_, 32), -1),            # unknown dtype
     ((0, 256, 64, F16, F16, F32, K_, K_, 0), -1),            # empty M
     ((256, -1, 64, F16, F16, F32, K_, K_, 0), -1),

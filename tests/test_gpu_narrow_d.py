@@ -36,7 +36,7 @@ CASES = {
 
 
 def run_narrow(w, x, d_kind):
-    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, d_kind, w.a_major, w.b_major, w.V)
+    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind_b, d_kind, w.a_major, w.b_major, w.V)
     assert plan.describe()["tile_m"] == 256
     A, B = to_device(x["A"]), to_device(x["B"])
     if w.beta:

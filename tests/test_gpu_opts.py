@@ -47,7 +47,7 @@ def masks(w, seed, rows=True, cols=True):
 
 def run_opts(w, x, d_kind="f32", D_before=None, row_mask=None, col_zero=None, **kw):
     """One gemm_run_opts call on device copies; returns D (fp64 numpy)."""
-    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, d_kind, w.a_major, w.b_major, w.V)
+    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind_b, d_kind, w.a_major, w.b_major, w.V)
     A, B = to_device(x["A"]), to_device(x["B"])
     D = torch.from_numpy(np.ascontiguousarray(D_before)).to(TORCH_D[d_kind]).cuda()
     sf = {}

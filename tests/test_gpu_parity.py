@@ -357,6 +357,83 @@ def test_fp6_scale_bytes_select_the_right_block(kind, one):
     assert np.array_equal(got.astype(np.float64), expect)
 
 
+# mixed block-scaled kinds (E4M3, E2M3, E3M2 for A and B independently): each
+# E4M3 / 6-bit pairing in both orders and the two 6-bit formats together,
+# grouped and per-step scale copies, ragged M and N, beta = 1
+MIXED = {
+    "e4m3xe2m3": wl.custom(512, 768, 1024, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e4m3xe2m3", b_kind="e2m3"),
+    "e2m3xe4m3-beta": wl.custom(256, 512, 512, "e2m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                b_dist=("normal", 1.0), name="e2m3xe4m3-beta", b_kind="e4m3"),
+    "e4m3xe3m2-tail": wl.custom(300, 292, 384, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="e4m3xe3m2-tail", b_kind="e3m2"),
+    "e3m2xe4m3-k2048": wl.custom(512, 256, 2048, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                 name="e3m2xe4m3-k2048", b_kind="e4m3"),
+    "e2m3xe3m2": wl.custom(256, 256, 1024, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e2m3xe3m2", b_kind="e3m2"),
+    "e3m2xe2m3-beta": wl.custom(264, 256, 640, "e3m2", V=32, beta=1, a_dist=("normal", 1.0),
+                                b_dist=("normal", 1.0), name="e3m2xe2m3-beta", b_kind="e2m3"),
+}
+
+
+@pytest.mark.parametrize("name", list(MIXED))
+def test_mixed_full_compare(name):
+    w = MIXED[name]
+    plan = plan_for(w)
+    assert plan.describe()["tile_m"] == 256
+    say(f"[mixed] {name} {w.M}x{w.N}x{w.K} {w.kind} x {w.kind_b} beta={w.beta}")
+    x = wl.generate(w, seed=51)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(MIXED))
+def test_mixed_quarter_integers_bit_exact(name):
+    w = MIXED[name]
+    say(f"[mixed-exact] {name}")
+    x = wl.generate(w, seed=52, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
+
+
+@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3")])
+def test_mixed_scale_bytes_select_the_right_block(ka, kb):
+    """Scales only, every element 1.0 in its own format: D[m,n] =
+    32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a value meeting a partner from
+    another K block, or a wrong scale byte, changes the value."""
+    M, N, K = 256, 512, 1024
+    w = wl.custom(M, N, K, ka, V=32, name=f"{ka}x{kb}-scale-only", b_kind=kb)
+    rng = np.random.default_rng(10)
+    x = {"A": wl.to_stored(np.ones((M, K)), ka), "B": wl.to_stored(np.ones((N, K)), kb),
+         "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
+         "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
+    say(f"[mixed] scale closed form {ka} x {kb}")
+    got = run_gpu(w, x)
+    ua = x["SFA"].astype(np.int64) - 127
+    ub = x["SFB"].astype(np.int64) - 127
+    expect = 32.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
+    assert np.array_equal(got.astype(np.float64), expect)
+
+
+def test_mixed_k_positions_meet():
+    """A one-hot in K per row of A against B rows holding k at position k:
+    D[m,n] = value of B[n] at A's hot position, so any K-order mismatch between
+    the E4M3 and E2M3 fragments shows (every k in 0..127 of several steps)."""
+    M, N, K = 256, 256, 512
+    w = wl.custom(M, N, K, "e4m3", V=32, name="mixed-one-hot", b_kind="e2m3")
+    rng = np.random.default_rng(11)
+    hot = rng.integers(0, K, M)
+    a = np.zeros((M, K))
+    a[np.arange(M), hot] = 1.0
+    b = rng.integers(-7, 8, (N, K)) / 2.0          # half-integers, exact in E2M3
+    x = {"A": wl.to_stored(a, "e4m3"), "B": wl.to_stored(b, "e2m3"),
+         "SFA": np.full((M, K // 32), 127, np.uint8), "SFB": np.full((N, K // 32), 127, np.uint8)}
+    say("[mixed] one-hot K positions")
+    got = run_gpu(w, x)
+    assert np.array_equal(got.astype(np.float64), b[:, hot].T)
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
@@ -373,7 +450,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c3b", *EXTRA_FULL])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c3b", *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""

@@ -86,11 +86,11 @@ def d_storage(w, d_fmt, ldd, d0=None):
 
 
 def run_strided(w, x, lda, ldb, ldd, d_fmt):
-    plan = mswz.gemm_plan_create_ld(w.M, w.N, w.K, w.kind, w.kind, d_fmt, w.a_major, w.b_major, w.V,
+    plan = mswz.gemm_plan_create_ld(w.M, w.N, w.K, w.kind, w.kind_b, d_fmt, w.a_major, w.b_major, w.V,
                                     lda=lda, ldb=ldb, ldd=ldd)
     assert plan.describe()["tile_m"] == 256
     _, A = embed(x["A"], w.kind, lda)
-    _, B = embed(x["B"], w.kind, ldb)
+    _, B = embed(x["B"], w.kind_b, ldb)
     Dbig, D = d_storage(w, d_fmt, ldd, x.get("D0") if w.beta else None)
     if w.V:
         sfa = torch.from_numpy(np.ascontiguousarray(x["SFA"])).cuda()
@@ -110,11 +110,11 @@ def run_strided(w, x, lda, ldb, ldd, d_fmt):
 
 def packed_run(w, x, d_fmt):
     """The same problem with packed storage; None unless it also takes the 256 tile."""
-    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind, d_fmt, w.a_major, w.b_major, w.V)
+    plan = mswz.gemm_plan_create(w.M, w.N, w.K, w.kind, w.kind_b, d_fmt, w.a_major, w.b_major, w.V)
     if plan.describe()["tile_m"] != 256:
         return None
     _, A = embed(x["A"], w.kind, 0)
-    _, B = embed(x["B"], w.kind, 0)
+    _, B = embed(x["B"], w.kind_b, 0)
     _, D = d_storage(w, d_fmt, 0, x.get("D0") if w.beta else None)
     if w.V:
         sfa = torch.from_numpy(np.ascontiguousarray(x["SFA"])).cuda()

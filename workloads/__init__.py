@@ -44,7 +44,7 @@ class Workload:
     M: int
     N: int
     K: int
-    kind: str                 # operand element kind for A and B
+    kind: str                 # operand element kind for A (and B unless b_kind is set)
     a_major: str = "k"        # "k" or "mn"
     b_major: str = "k"
     beta: int = 0
@@ -52,6 +52,11 @@ class Workload:
     a_dist: tuple = ("uniform", 1.0)   # ("uniform", half-width) or ("normal", sigma)
     b_dist: tuple = ("uniform", 1.0)
     tags: tuple = field(default=())
+    b_kind: str = ""          # B's element kind when it differs from A's
+
+    @property
+    def kind_b(self) -> str:
+        return self.b_kind or self.kind
 
     @property
     def flops(self) -> int:
@@ -60,8 +65,10 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Minimal HBM traffic of one call: A + B (+ scales) + D write
         (+ D read when beta = 1)."""
-        num, den = {"e4m3": (1, 1), "e2m1": (1, 2)}.get(self.kind, (2, 1))
-        b = (self.M + self.N) * self.K * num // den + self.M * self.N * 4
+        def per(kind):   # stored bytes per element (6-bit kinds: sixteen per 16 bytes)
+            return {"e4m3": (1, 1), "e2m1": (1, 2), "e2m3": (1, 1), "e3m2": (1, 1)}.get(kind, (2, 1))
+        (na, da), (nb, db) = per(self.kind), per(self.kind_b)
+        b = self.M * self.K * na // da + self.N * self.K * nb // db + self.M * self.N * 4
         if self.V:
             b += (self.M + self.N) * (self.K // self.V)
         if self.beta:
@@ -86,15 +93,18 @@ WORKLOADS = {
                    8192, 8192, 8192, "e2m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
     "c8": Workload("c8", "MX-fp6 8192^3 e3m2 K-major (padded, sixteen per 16 bytes), N(0,1) rounded to e3m2, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
                    8192, 8192, 8192, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c9": Workload("c9", "MX mixed 8192^3: A e4m3, B e2m3 (padded), K-major, N(0,1) rounded to each format, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                   8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m3"),
     "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
                     8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
 }
 
 
 def custom(M, N, K, kind, a_major="k", b_major="k", beta=0, V=0,
-           a_dist=("uniform", 1.0), b_dist=("uniform", 1.0), name="custom") -> Workload:
-    return Workload(name, f"{name} {M}x{N}x{K} {kind} A:{a_major} B:{b_major} beta={beta} V={V}",
-                    M, N, K, kind, a_major, b_major, beta, V, a_dist, b_dist)
+           a_dist=("uniform", 1.0), b_dist=("uniform", 1.0), name="custom", b_kind="") -> Workload:
+    kinds = kind if not b_kind or b_kind == kind else f"{kind}x{b_kind}"
+    return Workload(name, f"{name} {M}x{N}x{K} {kinds} A:{a_major} B:{b_major} beta={beta} V={V}",
+                    M, N, K, kind, a_major, b_major, beta, V, a_dist, b_dist, b_kind=b_kind if b_kind != kind else "")
 
 
 def scaled(w: Workload, M=None, N=None, K=None, name=None) -> Workload:
@@ -210,8 +220,8 @@ def value_shapes(w: Workload) -> dict:
 def stored_shapes(w: Workload) -> dict:
     """Shapes of the stored arrays (e2m1 rows hold two elements per byte)."""
     s = value_shapes(w)
-    if w.kind == "e2m1":
-        for name in ("A", "B"):
+    for name, kind in (("A", w.kind), ("B", w.kind_b)):
+        if kind == "e2m1":
             r, c = s[name]
             s[name] = (r, c // 2)
     return s
@@ -228,9 +238,9 @@ def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
     rng = np.random.default_rng(seed)
     shapes = value_shapes(w)
     out = {}
-    for name, dist in (("A", w.a_dist), ("B", w.b_dist)):
-        x = _quarter(rng, shapes[name], w.kind) if values == "quarter" else _draw(rng, dist, shapes[name])
-        out[name] = to_stored(x, w.kind)
+    for name, dist, kind in (("A", w.a_dist, w.kind), ("B", w.b_dist, w.kind_b)):
+        x = _quarter(rng, shapes[name], kind) if values == "quarter" else _draw(rng, dist, shapes[name])
+        out[name] = to_stored(x, kind)
     if w.beta:
         out["D0"] = rng.uniform(-1.0, 1.0, shapes["D0"]).astype(np.float32)
     if w.V:
