@@ -9,8 +9,9 @@ Contents
 --------
 ``oracle.c`` (built here into ``liboracle.so`` with gcc)
     * element decoders (fp16, bf16, OCP E4M3, OCP E2M1 packed two per byte,
-      OCP E2M3 / E3M2 in the padded sixteen-per-16-byte form of the tcgen05.cp
-      page's "Native FP4/FP6 decompression", OCP E8M0) from the bit fields;
+      OCP E2M3 / E3M2 and E2M1 ("e2m1p") in the padded sixteen-per-16-byte
+      forms of the tcgen05.cp page's "Native FP4/FP6 decompression", OCP
+      E8M0) from the bit fields;
     * ``gemm``: D = beta*D0 + A.B^T with B held as (N,K), in fp64, for dense
       and block-scaled operands, K-major or MN-major
       (tcgen05.mma page: "Operands and repeat axes", "Shared descriptors are
@@ -61,9 +62,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own element-kind and major numbering (independent of the GPU ABI).
-DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7}
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7, "e2m1p": 8}
 MAJORS = {"k": 0, "mn": 1}
-_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 1, "e2m3": 1, "e3m2": 1}
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 1, "e2m3": 1, "e3m2": 1, "e2m1p": 1}
 # elements per stored item: e2m1 packs two per byte (element 2j in the low nibble)
 _PER_ITEM = {"e2m1": 2}
 
@@ -130,7 +131,9 @@ def _raw(a: np.ndarray, kind: str) -> np.ndarray:
     return a
 
 
-_FP6 = ("e2m3", "e3m2")
+# kinds stored sixteen per 16-byte block with padding (the pages' padded
+# FP6 and FP4 forms)
+_FP6 = ("e2m3", "e3m2", "e2m1p")
 
 
 def decode(kind: str, stored: np.ndarray) -> np.ndarray:

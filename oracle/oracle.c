@@ -33,7 +33,10 @@
  * stored in the pages' padded form of the decompression copy (tcgen05.cp page,
  * "Native FP4/FP6 decompression": each 16-byte block holds sixteen packed
  * values followed by four bytes of padding), read as value j of a block in
- * bits 6j .. 6j+5 of its first twelve bytes taken little-endian;
+ * bits 6j .. 6j+5 of its first twelve bytes taken little-endian; the padded
+ * 4-bit form of the same section (sixteen values followed by eight bytes of
+ * padding) holds value j in bits 4j .. 4j+3 of the block's first eight bytes
+ * (low nibble first);
  * a scale byte E means 2^(E-127) (OCP E8M0, 255 is NaN); scale blocks start
  * at k = 0, V, 2V, ...; beta is 0 or 1 and beta = 0 never reads D0.
  *
@@ -53,7 +56,9 @@
  * per 16-byte block: element 16b + j in bits 6j .. 6j+5 of bytes 16b .. 16b+11
  * read as one little-endian number; bytes 16b+12 .. 16b+15 are padding and
  * never read. */
-enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4, ORC_E2M1 = 5, ORC_E2M3 = 6, ORC_E3M2 = 7 };
+enum { ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F32 = 4, ORC_E2M1 = 5, ORC_E2M3 = 6, ORC_E3M2 = 7,
+       ORC_E2M1_P64 = 8 };   /* E2M1 sixteen per 16-byte block: value 16b + j in the low (j even) or
+                                high (j odd) nibble of byte 16b + j/2; bytes 16b+8 .. 16b+15 padding */
 /* Operand majors (its own numbering). */
 enum { ORC_KMAJOR = 0, ORC_MNMAJOR = 1 };
 /* Return codes. */
@@ -159,7 +164,7 @@ static int elem_size(int dt)
     case ORC_E4M3: return 1;
     case ORC_F32: return 4;
     case ORC_E2M1: return 1;   /* storage byte (two elements) */
-    case ORC_E2M3: case ORC_E3M2: return 1;   /* 16 bytes per 16 elements */
+    case ORC_E2M3: case ORC_E3M2: case ORC_E2M1_P64: return 1;   /* 16 bytes per 16 elements */
     default: return 0;
     }
 }
@@ -177,6 +182,10 @@ static double decode_one(int dt, const void *base, int64_t idx)
     }
     case ORC_E2M3: return orc_decode_e2m3(fp6_code((const uint8_t *)base, idx));
     case ORC_E3M2: return orc_decode_e3m2(fp6_code((const uint8_t *)base, idx));
+    case ORC_E2M1_P64: {
+        const uint8_t byte = ((const uint8_t *)base)[(idx / 16) * 16 + (idx % 16) / 2];
+        return orc_decode_e2m1((idx & 1) ? byte >> 4 : byte & 0xf);
+    }
     default: return NAN;
     }
 }

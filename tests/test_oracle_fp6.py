@@ -1,4 +1,4 @@
-"""Pins for the oracle's 6-bit element kinds (CPU only).
+"""Pins for the oracle's 6-bit element kinds and the padded 4-bit form (CPU only).
 
 The pages name FP6 ("six-bit values") only in the tcgen05.cp page's "Native
 FP4/FP6 decompression" section, which fixes the storage: each 16-byte block
@@ -149,3 +149,69 @@ def test_fp6_rows_must_be_whole_blocks():
     with pytest.raises(ValueError):
         oracle.gemm(2, 2, 24, "e3m2", "k", np.zeros((2, 24), np.uint8), "e3m2", "k",
                     np.zeros((2, 24), np.uint8))
+
+
+# ---- the padded 4-bit form ("e2m1p": sixteen E2M1 values, then eight bytes
+# of padding, per 16-byte block; same section of the tcgen05.cp page) ----------
+
+def pack_e2m1_padded(codes: np.ndarray, pad: np.ndarray) -> np.ndarray:
+    """Nibble writer: value j of a block in the low (even j) or high (odd j)
+    nibble of byte j // 2; bytes 8..15 take `pad`."""
+    rows, n = codes.shape
+    out = np.zeros((rows, n), dtype=np.uint8)
+    for r in range(rows):
+        for blk in range(n // 16):
+            for j in range(16):
+                out[r, 16 * blk + j // 2] |= int(codes[r, 16 * blk + j]) << (4 * (j % 2))
+            out[r, 16 * blk + 8:16 * blk + 16] = pad[r, 8 * blk:8 * blk + 8]
+    return out
+
+
+def test_e2m1_padded_codes_and_padding():
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 16, (4, 64), dtype=np.uint8)
+    a = pack_e2m1_padded(codes, rng.integers(0, 256, (4, 32), dtype=np.uint8))
+    b = pack_e2m1_padded(codes, rng.integers(0, 256, (4, 32), dtype=np.uint8))
+    # the same codes in the dense two-per-byte form (pinned against the format table)
+    dense = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    want = oracle.decode("e2m1", dense)
+    assert np.array_equal(oracle.decode("e2m1p", a), want)
+    assert np.array_equal(oracle.decode("e2m1p", b), want)
+
+
+def test_e2m1_padded_generator_matches_dense_form():
+    rng = np.random.default_rng(13)
+    x = rng.normal(0, 2, (3, 64))
+    padded = wl.to_stored(x, "e2m1p").reshape(3, 4, 16)
+    dense = wl.to_stored(x, "e2m1").reshape(3, 4, 8)
+    assert np.array_equal(padded[..., :8], dense) and not padded[..., 8:].any()
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 64), (16, 9, 256)])
+def test_e2m1_padded_gemm_equals_dense_e2m1_gemm(M, N, K):
+    rng = np.random.default_rng(14)
+    ca = rng.integers(0, 16, (M, K), dtype=np.uint8)
+    cb = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    A = pack_e2m1_padded(ca, rng.integers(0, 256, (M, K // 2), dtype=np.uint8))
+    B = pack_e2m1_padded(cb, rng.integers(0, 256, (N, K // 2), dtype=np.uint8))
+    Ad = (ca[:, 0::2] | (ca[:, 1::2] << 4)).astype(np.uint8)
+    Bd = (cb[:, 0::2] | (cb[:, 1::2] << 4)).astype(np.uint8)
+    SFA = (127 + rng.integers(-3, 4, (M, K // 32))).astype(np.uint8)
+    SFB = (127 + rng.integers(-3, 4, (N, K // 32))).astype(np.uint8)
+    got = oracle.gemm(M, N, K, "e2m1p", "k", A, "e2m1p", "k", B, V=32, SFA=SFA, SFB=SFB)
+    ref = oracle.gemm(M, N, K, "e2m1", "k", Ad, "e2m1", "k", Bd, V=32, SFA=SFA, SFB=SFB)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m1p"), ("e2m3", "e3m2"), ("e2m1p", "e2m3")])
+def test_mixed_kinds_equal_e4m3_of_the_same_values(ka, kb):
+    """Operands of two kinds: the same as both re-encoded as E4M3."""
+    M, N, K = 7, 5, 128
+    rng = np.random.default_rng(15)
+    x = {"A": wl.to_stored(rng.normal(0, 2, (M, K)), ka), "B": wl.to_stored(rng.normal(0, 2, (N, K)), kb)}
+    SFA = (127 + rng.integers(-3, 4, (M, K // 32))).astype(np.uint8)
+    SFB = (127 + rng.integers(-3, 4, (N, K // 32))).astype(np.uint8)
+    got = oracle.gemm(M, N, K, ka, "k", x["A"], kb, "k", x["B"], V=32, SFA=SFA, SFB=SFB)
+    ref = oracle.gemm(M, N, K, "e4m3", "k", _as_e4m3(ka, x["A"]), "e4m3", "k", _as_e4m3(kb, x["B"]),
+                      V=32, SFA=SFA, SFB=SFB)
+    assert np.array_equal(got, ref)

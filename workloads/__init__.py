@@ -17,7 +17,8 @@ saturating to 6, then packed two per byte, element 2j in the low nibble;
 e2m3 and e3m2 to the nearest of their 64 values, ties to the even code,
 saturating at 7.5 and 28, then packed sixteen per 16-byte block in bits
 6j .. 6j+5 of the block's first twelve bytes, little-endian, the last four
-bytes zero);
+bytes zero; "e2m1p" rounds like e2m1 and stores sixteen per 16-byte block,
+eight bytes of nibbles then eight zero bytes);
 e8m0 scale bytes are 127 + u with u a uniform integer in [-4, 4].
 The quarter-integer variant (the tcgen05.mma page's example test draws
 integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
@@ -34,7 +35,7 @@ import numpy as np
 import torch
 
 #: Stored element kinds, named as in the oracle and the binding.
-KINDS = ("f16", "bf16", "e4m3", "e2m1", "e2m3", "e3m2")
+KINDS = ("f16", "bf16", "e4m3", "e2m1", "e2m3", "e3m2", "e2m1p")
 
 
 @dataclass(frozen=True)
@@ -66,7 +67,7 @@ class Workload:
         """Minimal HBM traffic of one call: A + B (+ scales) + D write
         (+ D read when beta = 1)."""
         def per(kind):   # stored bytes per element (6-bit kinds: sixteen per 16 bytes)
-            return {"e4m3": (1, 1), "e2m1": (1, 2), "e2m3": (1, 1), "e3m2": (1, 1)}.get(kind, (2, 1))
+            return {"e4m3": (1, 1), "e2m1": (1, 2), "e2m3": (1, 1), "e3m2": (1, 1), "e2m1p": (1, 1)}.get(kind, (2, 1))
         (na, da), (nb, db) = per(self.kind), per(self.kind_b)
         b = self.M * self.K * na // da + self.N * self.K * nb // db + self.M * self.N * 4
         if self.V:
@@ -120,6 +121,8 @@ def to_stored(x: np.ndarray, kind: str) -> np.ndarray:
         return _to_e2m1_packed(x)
     if kind in _FP6_MAG:
         return _to_fp6_padded(x, kind)
+    if kind == "e2m1p":
+        return _to_e2m1_padded(x)
     if kind == "f16":
         return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
@@ -188,6 +191,18 @@ def _to_fp6_padded(x: np.ndarray, kind: str) -> np.ndarray:
     return np.ascontiguousarray(out.numpy().reshape(x.shape))
 
 
+def _to_e2m1_padded(x: np.ndarray) -> np.ndarray:
+    """E2M1 codes (as for the packed form) stored sixteen per 16-byte block:
+    eight bytes of nibbles (value 2i in the low nibble of byte i), then eight
+    zero bytes of padding."""
+    if x.shape[-1] % 16:
+        raise ValueError("padded e2m1 rows need a multiple of 16 elements")
+    packed = _to_e2m1_packed(x).reshape(x.shape[:-1] + (x.shape[-1] // 16, 8))
+    out = np.zeros(x.shape[:-1] + (x.shape[-1] // 16, 16), dtype=np.uint8)
+    out[..., :8] = packed
+    return np.ascontiguousarray(out.reshape(x.shape))
+
+
 def _draw(rng, dist, size):
     kind, p = dist
     if kind == "uniform":
@@ -198,7 +213,7 @@ def _draw(rng, dist, size):
 
 
 def _quarter(rng, size, kind="f16"):
-    if kind == "e2m1":
+    if kind in ("e2m1", "e2m1p"):
         return rng.integers(-2, 3, size) / 2.0
     return rng.integers(-4, 5, size) / 4.0
 
