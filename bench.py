@@ -6,8 +6,9 @@ for the workload on inputs already resident in HBM.  Default workload: the
 square dense 4096^3 bf16 GEMM with both operands K-major (N(0,1) inputs,
 seed 0).  The other full-size workloads (8192^3 fp16 MN-major A with beta=1,
 8192^3 bf16, the skinny 64x16384x8192 weight-streaming shape, 8192^3 MX-fp8,
-8192^3 MX-fp4, 8192^3 MX-fp6 in both 6-bit formats and 8192^3 with E4M3 A
-and E2M3 B) are timed in the same run and reported under "also".
+8192^3 MX-fp4, 8192^3 MX-fp6 in both 6-bit formats, and 8192^3 with E4M3 A
+against E2M3 or padded E2M1 B) are timed in the same run and reported under
+"also".
 
 Prints ONE JSON line (rank 0).  ``roofline`` reports the dominant kernel
 against the MI355X dense MFMA peak (or HBM peak for the skinny shape), using
@@ -30,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s on 1 MI355X (bf16 8192³, MX-fp8 8192³) and % of MFMA peak"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
-MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4, "e2m3": 10066.4, "e3m2": 10066.4}
+MFMA_PEAK = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.4, "e2m3": 10066.4, "e3m2": 10066.4, "e2m1p": 10066.4}
 HBM_PEAK = 8000.0
 
 
@@ -182,7 +183,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8,c9",
+    ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8,c9,c10",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -26,7 +26,10 @@
  *      holding sixteen 6-bit values, value j in bits 6j .. 6j+5 of the block's
  *      first twelve bytes taken little-endian, the last four bytes padding
  *      that is never read: the padded FP6 form of the tcgen05.cp page's
- *      "Native FP4/FP6 decompression")
+ *      "Native FP4/FP6 decompression"; E2M1_P64: the padded FP4 form of the
+ *      same section, [M][K] and [N][K] bytes, each 16-byte block holding
+ *      sixteen 4-bit values in its first eight bytes, value j in the low
+ *      (j even) or high (j odd) nibble of byte j/2, then eight padding bytes)
  *     D  [M][N] in the plan's d_dt (fp32, bf16 or fp16)
  *     SFA uint8 [M][K/V], SFB uint8 [N][K/V]: OCP E8M0 exponents, value 2^(E-127)
  * Element formats: fp16 (IEEE binary16), bf16, fp8 = OCP E4M3 (bias 7, no
@@ -75,7 +78,8 @@ typedef enum {
     MSWZ_DT_F32 = 4,
     MSWZ_DT_E2M1 = 5,           /* OCP FP4, two per byte, element 2j in the low nibble of byte j */
     MSWZ_DT_E2M3 = 6,           /* OCP FP6 E2M3, sixteen per 16-byte block (see Storage) */
-    MSWZ_DT_E3M2 = 7            /* OCP FP6 E3M2, sixteen per 16-byte block (see Storage) */
+    MSWZ_DT_E3M2 = 7,           /* OCP FP6 E3M2, sixteen per 16-byte block (see Storage) */
+    MSWZ_DT_E2M1_P64 = 8        /* OCP FP4 E2M1, sixteen per 16-byte block (see Storage) */
 } mswz_dtype;
 
 typedef enum {
@@ -95,15 +99,16 @@ typedef struct gemm_plan gemm_plan;
  *                 reads D in that format and adds it in fp32 before
  *                 rounding); narrow D always uses the 256 tile
  *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) and
- *                 (E2M1,E2M1), (E2M3,E2M3), (E3M2,E3M2) block-scaled, and any
- *                 mix of E4M3, E2M3 and E3M2 for A and B (the pages' mixed
- *                 f8f6f4 kind; each operand decoded in its own format, 256 tile).
+ *                 (E2M1,E2M1), (E2M3,E2M3), (E3M2,E3M2), (E2M1_P64,E2M1_P64)
+ *                 block-scaled, and any mix of E4M3, E2M3, E3M2 and E2M1_P64
+ *                 for A and B (the pages' mixed f8f6f4 kind; each operand
+ *                 decoded in its own format, 256 tile).
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3, E2M1,
- *                 E2M3 and E3M2
- * Shape rules: K % 128 == 0 (E4M3; E2M3 and E3M2, which always use the 256
- * tile) or K % 256 == 0 (E2M1, which always uses the 256 tile).  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
+ *                 E2M3, E3M2 and E2M1_P64
+ * Shape rules: K % 128 == 0 (E4M3; E2M3, E3M2 and E2M1_P64, which always use
+ * the 256 tile) or K % 256 == 0 (E2M1, which always uses the 256 tile).  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
  * K when both operands are MN-major); a K that is not a multiple of 64 uses
  * the 256 tile, whose last K step reads the values beyond K as zeros.  M and N
  * multiples of 64 choose among 256, 128 and 64 square tiles; otherwise (tails)
@@ -130,8 +135,8 @@ int gemm_plan_create(gemm_plan **out, int64_t M, int64_t N, int64_t K,
  *   ldd   elements from one row of D to the next, ldd >= N
  * 0 for any of them means packed (K, M / N, N).  A plan with any pitch other
  * than packed uses the 256 tile and needs every stored row 16-byte aligned:
- * lda and ldb multiples of 8 (16-bit), 16 (E4M3, E2M3, E3M2: whole 16-byte
- * blocks) or 32 (E2M1), ldd a multiple
+ * lda and ldb multiples of 8 (16-bit), 16 (E4M3, E2M3, E3M2, E2M1_P64: whole
+ * 16-byte blocks) or 32 (E2M1), ldd a multiple
  * of 4; pitches are at most 2^22, and an MN-major operand's span
  * ((K - 1) * ld + M or N elements) must stay below 4 GiB.  The elements
  * between a row's end and the next row's start are neither read (operands)

@@ -28,11 +28,11 @@ __all__ = [
     "desc_address", "desc_check", "tile_offset", "library_path", "load",
 ]
 
-DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7}
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7, "e2m1p": 8}
 MAJORS = {"k": 0, "mn": 1}
 STATUS = {"ok": 0, "invalid": -1, "unsupported": -2, "align": -3, "hip": -4, "kind": -5}
-# bytes per element (the 6-bit kinds: sixteen per 16-byte block, padding included)
-_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 0.5, "e2m3": 1, "e3m2": 1}
+# bytes per element (the padded 6- and 4-bit kinds: sixteen per 16-byte block, padding included)
+_ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 0.5, "e2m3": 1, "e3m2": 1, "e2m1p": 1}
 _DESCRIBE_KEYS = ("variant", "tile_m", "tile_n", "tile_k", "threads", "blocks", "lds_bytes", "group_m")
 
 _lock = threading.Lock()

@@ -70,7 +70,8 @@ bool is_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u)
 mswz::MxKind mx_kind(int dt)
 {
     return dt == MSWZ_DT_E2M1 ? mswz::kMxE2m1 : dt == MSWZ_DT_E2M3 ? mswz::kMxE2m3
-                                              : dt == MSWZ_DT_E3M2 ? mswz::kMxE3m2 : mswz::kMxE4m3;
+                                              : dt == MSWZ_DT_E3M2 ? mswz::kMxE3m2
+                                              : dt == MSWZ_DT_E2M1_P64 ? mswz::kMxE2m1p : mswz::kMxE4m3;
 }
 
 int out_kind(int d_dt)
@@ -119,7 +120,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     *out = nullptr;
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MSWZ_ERR_INVALID;
-    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_E3M2; };
+    auto known_dt = [](int d) { return d >= MSWZ_DT_F16 && d <= MSWZ_DT_E2M1_P64; };
     if (!known_dt(a_dt) || !known_dt(b_dt) || !known_dt(d_dt))
         return MSWZ_ERR_INVALID;
     if ((a_major != MSWZ_MAJOR_K && a_major != MSWZ_MAJOR_MN) ||
@@ -128,7 +129,9 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     if (scale_vec_len < 0)
         return MSWZ_ERR_INVALID;
     // A and B share a kind, except that E4M3, E2M3 and E3M2 mix freely
-    auto byte_mx = [](int d) { return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2; };
+    auto byte_mx = [](int d) {
+        return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2 || d == MSWZ_DT_E2M1_P64;
+    };
     if ((a_dt != b_dt && !(byte_mx(a_dt) && byte_mx(b_dt))) || a_dt == MSWZ_DT_F32)
         return MSWZ_ERR_UNSUPPORTED;
     const bool mixed = a_dt != b_dt;
@@ -137,7 +140,8 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     const bool narrow_d = d_dt != MSWZ_DT_F32;
     const bool fp4 = a_dt == MSWZ_DT_E2M1;
-    const bool fp6 = a_dt == MSWZ_DT_E2M3 || a_dt == MSWZ_DT_E3M2;
+    // padded sub-byte kinds (sixteen values per 16-byte block)
+    const bool fp6 = a_dt == MSWZ_DT_E2M3 || a_dt == MSWZ_DT_E3M2 || a_dt == MSWZ_DT_E2M1_P64;
     const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4 || fp6;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
         return MSWZ_ERR_UNSUPPORTED;     // 8-, 6- and 4-bit kinds are block-scaled only; 16-bit is dense only

@@ -58,14 +58,23 @@ __device__ __forceinline__ f32x16 mfma_scale_32x32x64_e4m3(i32x8 a, i32x8 b, f32
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, scale_a, SEL, scale_b);
 }
 
-// Block-scaled 16x16x128 MFMA, E4M3 operands, scale byte 0 of each scale
-// register.  Lane l holds 32 bytes of row l % 16: bytes 0..15 lie in 32-wide
-// scale block (l/16)/2 and bytes 16..31 in block 2 + (l/16)/2, and lane
-// i + 16b supplies row i's scale for block b.
-__device__ __forceinline__ f32x4 mfma_scale_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c, int scale_a,
-                                                           int scale_b)
+// Block-scaled 16x16x128 MFMA, scale byte 0 of each scale register, the
+// first and second operands in formats F1 and F2 (E4M3 0, E2M3 2, E3M2 3,
+// E2M1 4).  Lane images (each pinned by a one-wave probe):
+//   E4M3: lane l holds 32 bytes of row l % 16: bytes 0..15 lie in 32-wide
+//         scale block (l/16)/2 and bytes 16..31 in block 2 + (l/16)/2;
+//   E2M3 / E3M2: 32 values of row l % 16, value j in bits 6j .. 6j+5 of
+//         registers 0..5, all in scale block l/16;
+//   E2M1: 32 values, value j in bits 4j .. 4j+3 of registers 0..3, all in
+//         scale block l/16;
+// and in every case lane i + 16b supplies row i's scale for block b.  Across
+// formats, values meet by an internal K index: 32g + j for value j of lane
+// group g of a 6- or 4-bit operand, 32(g/2) + 16(g%2) + j (plus 64 for bytes
+// 16..31) for byte j of an E4M3 lane.
+template <int F1, int F2>
+__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fmt(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b)
 {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F1, F2, 0, scale_a, 0, scale_b);
 }
 
 // The same MFMA with OCP E2M1 (FP4) operands (format code 4): lane l holds
@@ -76,25 +85,6 @@ __device__ __forceinline__ f32x4 mfma_scale_16x16x128_e2m1(i32x8 a, i32x8 b, f32
                                                            int scale_b)
 {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, scale_a, 0, scale_b);
-}
-
-// The same MFMA with OCP 6-bit operands, E2M3 (format code 2) or E3M2 (code
-// 3): lane l holds 32 values of row l % 16, value j in bits 6j .. 6j+5 of
-// registers 0..5 (registers 6 and 7 unused), all in scale block l/16, and lane
-// i + 16b supplies row i's scale for block b.
-template <bool E3M2>
-__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fp6(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b)
-{
-    constexpr int kFmt = E3M2 ? 3 : 2;
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmt, kFmt, 0, scale_a, 0, scale_b);
-}
-
-// The same MFMA with the first and second operands in formats F1 and F2
-// (E4M3 0, E2M3 2, E3M2 3); lane images as in the single-format forms above.
-template <int F1, int F2>
-__device__ __forceinline__ f32x4 mfma_scale_16x16x128_fmt(i32x8 a, i32x8 b, f32x4 c, int scale_a, int scale_b)
-{
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, F1, F2, 0, scale_a, 0, scale_b);
 }
 
 // Workgroup -> output tile.  The hardware hands consecutive workgroups to the

@@ -46,8 +46,7 @@ hipError_t launch_mx256(const MxArgs &a, MxKind kind, MxKind kind_b, hipStream_t
         return launch256_mixed(a, kind, kind_b, stream);
     switch (kind) {
     case kMxE2m1: return launch256_e2m1(a, stream);
-    case kMxE2m3: return launch256_fp6(a, false, stream);
-    case kMxE3m2: return launch256_fp6(a, true, stream);
+    case kMxE2m3: case kMxE3m2: case kMxE2m1p: return launch256_padded(a, kind, stream);
     default: return launch256_e4m3(a, stream);
     }
 }

@@ -1,17 +1,29 @@
 // gemm256_fp6.hip — instantiations of the 256x256-tile GEMM for block-scaled
-// 6-bit operands, OCP E2M3 and E3M2 in the padded sixteen-per-16-byte form
-// (both K-major; the eight-wave 16x16 pipeline only).
+// padded sub-byte operands: OCP E2M3 and E3M2 (sixteen 6-bit values and four
+// bytes of padding per 16-byte block) and E2M1 in the padded form (sixteen
+// 4-bit values and eight bytes of padding); both K-major, the eight-wave
+// 16x16 pipeline only.
 #include "gemm256_kernel.hpp"
 
 namespace mswz {
+namespace {
 
-hipError_t launch256_fp6(const MxArgs &a, bool e3m2, hipStream_t stream)
+template <int K>
+hipError_t launch_padded(const MxArgs &a, hipStream_t stream)
 {
-    if (e3m2)
-        return a.out == kOutF32 ? launch_kind<kE3m2, false, false, 8, 8>(a, stream)
-                                : launch_out<kE3m2, false, false>(a, stream);
-    return a.out == kOutF32 ? launch_kind<kE2m3, false, false, 8, 8>(a, stream)
-                            : launch_out<kE2m3, false, false>(a, stream);
+    return a.out == kOutF32 ? launch_kind<K, false, false, 8, 8>(a, stream) : launch_out<K, false, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch256_padded(const MxArgs &a, MxKind kind, hipStream_t stream)
+{
+    switch (kind) {
+    case kMxE2m3: return launch_padded<kE2m3>(a, stream);
+    case kMxE3m2: return launch_padded<kE3m2>(a, stream);
+    case kMxE2m1p: return launch_padded<kE2m1p>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mswz

@@ -49,7 +49,9 @@ constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K s
 
 constexpr uint32_t kMnRowBytes = 512;           // one K row of an MN-major tile (256 values)
 
-enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3, kE2m3 = 4, kE3m2 = 5 };
+// kE2m1p: E2M1 in the padded sixteen-per-16-byte form (eight bytes of nibbles,
+// eight of padding), with the byte layout of E4M3 and the 6-bit kinds
+enum Kind { kBf16 = 0, kF16 = 1, kE4m3 = 2, kE2m1 = 3, kE2m3 = 4, kE3m2 = 5, kE2m1p = 6 };
 
 // Direct-to-LDS copy of one K-major operand tile (256 rows x 128 bytes per K
 // step) through a buffer resource on the workgroup's 256-row panel.  With W
@@ -269,12 +271,20 @@ __device__ __forceinline__ int fp6_chunk16(int g) { return 2 * g + ((g & 1) ^ 1)
 // each group still reads the 32-element scale blocks g/2 and 2 + g/2.
 __device__ __forceinline__ int mx_chunk16_mixed(int g) { return (g >> 1) ? g : g ^ 1; }
 
-// MFMA format code of a block-scaled element kind (E4M3 0, E2M3 2, E3M2 3).
+// MFMA format code of a block-scaled element kind (E4M3 0, E2M3 2, E3M2 3,
+// E2M1 4).
 template <int KIND_>
 constexpr int mx_format()
 {
-    return KIND_ == kE3m2 ? 3 : KIND_ == kE2m3 ? 2 : 0;
+    return KIND_ == kE3m2 ? 3 : KIND_ == kE2m3 ? 2 : (KIND_ == kE2m1 || KIND_ == kE2m1p) ? 4 : 0;
 }
+
+// Padded sub-byte kinds (6-bit, and 4-bit in the padded form): sixteen values
+// per 16-byte chunk, a lane's 32 values all in one scale block (the FP4
+// operand image has the block structure of the FP6 one: lane (row i, group g)
+// holds values j at bits 4j of registers 0..3, all in block g).
+constexpr bool padded_kind(int k) { return k == kE2m3 || k == kE3m2 || k == kE2m1p; }
+constexpr bool byte_row_kind(int k) { return k == kE4m3 || padded_kind(k); }
 
 // Compile-time loop: fn(std::integral_constant<int, F>), ..., up to L - 1.
 template <int F, int L, class Fn>
@@ -475,19 +485,18 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
     constexpr int kKindB = KB < 0 ? KIND : KB;
     constexpr bool kMixed = kKindB != KIND;
-    static_assert(!kMixed || ((KIND == kE4m3 || KIND == kE2m3 || KIND == kE3m2) &&
-                              (kKindB == kE4m3 || kKindB == kE2m3 || kKindB == kE3m2)),
-                  "mixed operand kinds are built for E4M3 / E2M3 / E3M2");
-    constexpr bool kFp6B = kKindB == kE2m3 || kKindB == kE3m2;
-    constexpr bool kFp8B = kKindB == kE4m3;
-    // A's kind below; B's differs only in the fragment reads and the MFMA format
-    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1, kFp6 = KIND == kE2m3 || KIND == kE3m2;
+    static_assert(!kMixed || (byte_row_kind(KIND) && byte_row_kind(kKindB)),
+                  "mixed operand kinds are built for E4M3 and the padded 6- and 4-bit kinds");
+    constexpr bool kFp6B = padded_kind(kKindB);
+    // A's kind below; B's differs only in the fragment reads and the MFMA format.
+    // kFp6: a padded sub-byte kind (E2M3, E3M2 or padded E2M1).
+    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1, kFp6 = padded_kind(KIND);
     constexpr bool kMx = kFp8 || kFp4 || kFp6;
     // E4M3 and padded 6-bit operands share the byte layout (128 values per
     // 128-byte row step) and the split-row fragments
     constexpr bool kByteRows = kFp8 || kFp6;
     static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
-    static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "FP6 is built for the eight-wave 16x16 path");
+    static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "padded 6- and 4-bit kinds are built for the eight-wave 16x16 path");
     static_assert(!kMixed || ((REG & 8) != 0 && W == 8), "mixed kinds are built for the eight-wave 16x16 path");
     // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
     // E2M1 (packed two per byte) K elements
@@ -829,18 +838,22 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
-        // E4M3: chunks c and c + 4; FP6: chunks c and c ^ 1, of which the
-        // first twelve bytes each form registers 0..2 and 3..5
-        auto frag_of = [&](uint32_t base, auto six) {
-            constexpr bool k6 = decltype(six)::value;
+        // E4M3: chunks c and c + 4.  Padded kinds: chunks c and c ^ 1, of
+        // which the first twelve (6-bit) or eight (4-bit) bytes each form
+        // registers 0..2 and 3..5 (0..1 and 2..3)
+        auto frag_of = [&](uint32_t base, auto kind) {
+            constexpr int k = decltype(kind)::value;
             const u32x4 lo = lds_read16(s, base);
-            const u32x4 hi = lds_read16(s, base ^ (k6 ? 16u : 64u));
-            if constexpr (k6)
+            const u32x4 hi = lds_read16(s, base ^ (padded_kind(k) ? 16u : 64u));
+            if constexpr (k == kE2m1p)
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 4, 5, 2, 3, 6, 7));
+            else if constexpr (padded_kind(k))
                 return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 4, 5, 6, 3, 7));
-            return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            else
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        auto frag = [&](uint32_t base) { return frag_of(base, std::integral_constant<bool, kFp6>{}); };
-        auto frag_b = [&](uint32_t base) { return frag_of(base, std::integral_constant<bool, kFp6B>{}); };
+        auto frag = [&](uint32_t base) { return frag_of(base, std::integral_constant<int, KIND>{}); };
+        auto frag_b = [&](uint32_t base) { return frag_of(base, std::integral_constant<int, kKindB>{}); };
         // MFMA m = TN16 * i + j; each block's fragment and scale are read two
         // MFMAs ahead of first use, in that order (FragSchedule), so that a
         // wave's first MFMA waits for a few reads rather than for the whole
@@ -865,13 +878,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             if constexpr (c1 > c0)
                 __builtin_amdgcn_sched_group_barrier(0x100, 3 * (c1 - c0), 0);   // DS reads
             constexpr int i = m / TN16, j = m % TN16;
-            if constexpr (kMixed)
-                acc4[j][i] = mfma_scale_16x16x128_fmt<mx_format<kKindB>(), mx_format<KIND>()>(bf[j], af[i], acc4[j][i],
-                                                                                              sb[j], sa[i]);
-            else if constexpr (kFp6)
-                acc4[j][i] = mfma_scale_16x16x128_fp6<KIND == kE3m2>(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
-            else
-                acc4[j][i] = mfma_scale_16x16x128_e4m3(bf[j], af[i], acc4[j][i], sb[j], sa[i]);
+            acc4[j][i] = mfma_scale_16x16x128_fmt<mx_format<kKindB>(), mx_format<KIND>()>(bf[j], af[i], acc4[j][i],
+                                                                                          sb[j], sa[i]);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
         });
     };

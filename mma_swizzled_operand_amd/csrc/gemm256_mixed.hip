@@ -1,6 +1,6 @@
 // gemm256_mixed.hip — instantiations of the 256x256-tile GEMM for block-scaled
-// operands of two different kinds among OCP E4M3, E2M3 and E3M2 (both
-// K-major; the eight-wave 16x16 pipeline only).
+// operands of two different kinds among OCP E4M3, E2M3, E3M2 and padded E2M1
+// (both K-major; the eight-wave 16x16 pipeline only).
 #include "gemm256_kernel.hpp"
 
 namespace mswz {
@@ -13,17 +13,29 @@ hipError_t launch_pair(const MxArgs &a, hipStream_t stream)
                             : launch_out<KA, false, false, KB>(a, stream);
 }
 
+template <int KA>
+hipError_t launch_b(const MxArgs &a, MxKind kb, hipStream_t stream)
+{
+    switch (kb) {
+    case kMxE4m3: return KA == kE4m3 ? hipErrorInvalidValue : launch_pair<KA, kE4m3>(a, stream);
+    case kMxE2m3: return KA == kE2m3 ? hipErrorInvalidValue : launch_pair<KA, kE2m3>(a, stream);
+    case kMxE3m2: return KA == kE3m2 ? hipErrorInvalidValue : launch_pair<KA, kE3m2>(a, stream);
+    case kMxE2m1p: return KA == kE2m1p ? hipErrorInvalidValue : launch_pair<KA, kE2m1p>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch256_mixed(const MxArgs &a, MxKind ka, MxKind kb, hipStream_t stream)
 {
-    if (ka == kMxE4m3 && kb == kMxE2m3) return launch_pair<kE4m3, kE2m3>(a, stream);
-    if (ka == kMxE4m3 && kb == kMxE3m2) return launch_pair<kE4m3, kE3m2>(a, stream);
-    if (ka == kMxE2m3 && kb == kMxE4m3) return launch_pair<kE2m3, kE4m3>(a, stream);
-    if (ka == kMxE3m2 && kb == kMxE4m3) return launch_pair<kE3m2, kE4m3>(a, stream);
-    if (ka == kMxE2m3 && kb == kMxE3m2) return launch_pair<kE2m3, kE3m2>(a, stream);
-    if (ka == kMxE3m2 && kb == kMxE2m3) return launch_pair<kE3m2, kE2m3>(a, stream);
-    return hipErrorInvalidValue;
+    switch (ka) {
+    case kMxE4m3: return launch_b<kE4m3>(a, kb, stream);
+    case kMxE2m3: return launch_b<kE2m3>(a, kb, stream);
+    case kMxE3m2: return launch_b<kE3m2>(a, kb, stream);
+    case kMxE2m1p: return launch_b<kE2m1p>(a, kb, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mswz

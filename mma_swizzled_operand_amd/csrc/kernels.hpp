@@ -71,7 +71,7 @@ hipError_t launch_dense(int variant, bool bf16, bool a_mn, bool b_mn, const Dens
                         hipStream_t stream);
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &args, hipStream_t stream);
 // block-scaled element kinds of the 256x256 tile
-enum MxKind { kMxE4m3 = 0, kMxE2m1 = 1, kMxE2m3 = 2, kMxE3m2 = 3 };
+enum MxKind { kMxE4m3 = 0, kMxE2m1 = 1, kMxE2m3 = 2, kMxE3m2 = 3, kMxE2m1p = 4 };
 hipError_t launch_mx256(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
 // the 256x256-tile instantiations, one translation unit each (gemm256_*.hip)
 hipError_t launch256_bf16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
@@ -80,7 +80,7 @@ hipError_t launch256_f16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_f16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
-hipError_t launch256_fp6(const MxArgs &args, bool e3m2, hipStream_t stream);
+hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
 hipError_t launch_dense256pp(bool bf16, const DenseArgs &args, hipStream_t stream);
 int config256();

@@ -64,7 +64,7 @@ def _create(*args):
     return rc
 
 
-F16, BF16, E4M3, F32, E2M1, E2M3, E3M2 = 1, 2, 3, 4, 5, 6, 7
+F16, BF16, E4M3, F32, E2M1, E2M3, E3M2, E2M1P = 1, 2, 3, 4, 5, 6, 7, 8
 K_, MN = 0, 1
 
 
@@ -89,7 +89,11 @@ K_, MN = 0, 1
     ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), -2),      # FP4 does not mix
     ((256, 256, 256, E2M1, E2M3, F32, K_, K_, 32), -2),
     ((256, 256, 128, E4M3, BF16, F32, K_, K_, 32), -2),      # dense with block-scaled
-    ((256, 256, 128, 8, 8, F32, K_, K_, 32), -1),            # unknown dtype
+    ((256, 256, 128, 9, 9, F32, K_, K_, 32), -1),            # unknown dtype
+    ((256, 256, 128, E2M1P, E2M1P, F32, K_, K_, 32), 0),     # padded FP4 (sixteen per 16 bytes)
+    ((256, 256, 128, E4M3, E2M1P, F32, K_, K_, 32), 0),      # mixed fp8 x padded fp4
+    ((256, 256, 128, E2M1P, E2M1, F32, K_, K_, 32), -2),     # the dense FP4 form does not mix
+    ((256, 256, 64, E2M1P, E2M1P, F32, K_, K_, 32), -2),     # K not a multiple of 128
     ((0, 256, 64, F16, F16, F32, K_, K_, 0), -1),            # empty M
     ((256, -1, 64, F16, F16, F32, K_, K_, 0), -1),
     ((256, 256, 0, F16, F16, F32, K_, K_, 0), -1),           # empty K

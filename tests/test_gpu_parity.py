@@ -321,18 +321,22 @@ def test_fp6_quarter_integers_bit_exact(name):
     assert np.array_equal(got, ref.astype(np.float32))
 
 
-@pytest.mark.parametrize("name", ["e2m3-mx", "e3m2-mx-k1024-beta"])
-def test_fp6_padding_bytes_are_never_read(name):
-    """Random bytes in every block's four padding bytes give the same bits."""
-    w = FP6[name]
-    say(f"[fp6-pad] {name}")
+@pytest.mark.parametrize("name", ["e2m3-mx", "e3m2-mx-k1024-beta", "e2m1p", "e4m3xe2m1p"])
+def test_padding_bytes_are_never_read(name):
+    """Random bytes in every block's padding (the last four bytes of a 6-bit
+    block, the last eight of a padded 4-bit one) give the same bits."""
+    w = FP6[name] if name in FP6 else MIXED[name]
+    say(f"[pad] {name}")
     x = wl.generate(w, seed=43)
     base = run_gpu(w, x)
     rng = np.random.default_rng(44)
     y = dict(x)
-    for k in ("A", "B"):
+    for k, kind in (("A", w.kind), ("B", w.kind_b)):
+        first = {"e2m3": 12, "e3m2": 12, "e2m1p": 8}.get(kind)
+        if first is None:
+            continue
         a = x[k].copy().reshape(-1, 16)
-        a[:, 12:] = rng.integers(0, 256, (a.shape[0], 4), dtype=np.uint8)
+        a[:, first:] = rng.integers(0, 256, (a.shape[0], 16 - first), dtype=np.uint8)
         y[k] = a.reshape(x[k].shape)
     assert np.array_equal(run_gpu(w, y), base)
 
@@ -373,6 +377,17 @@ MIXED = {
                            name="e2m3xe3m2", b_kind="e3m2"),
     "e3m2xe2m3-beta": wl.custom(264, 256, 640, "e3m2", V=32, beta=1, a_dist=("normal", 1.0),
                                 b_dist=("normal", 1.0), name="e3m2xe2m3-beta", b_kind="e2m3"),
+    # E2M1 in the pages' padded form, alone and mixed
+    "e2m1p": wl.custom(512, 512, 1024, "e2m1p", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                       name="e2m1p"),
+    "e2m1p-tail-beta": wl.custom(300, 292, 384, "e2m1p", V=32, beta=1, a_dist=("normal", 1.0),
+                                 b_dist=("normal", 1.0), name="e2m1p-tail-beta"),
+    "e4m3xe2m1p": wl.custom(512, 768, 1024, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                            name="e4m3xe2m1p", b_kind="e2m1p"),
+    "e2m1pxe4m3-beta": wl.custom(256, 512, 512, "e2m1p", V=32, beta=1, a_dist=("normal", 1.0),
+                                 b_dist=("normal", 1.0), name="e2m1pxe4m3-beta", b_kind="e4m3"),
+    "e2m1pxe2m3": wl.custom(256, 256, 640, "e2m1p", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                            name="e2m1pxe2m3", b_kind="e2m3"),
 }
 
 
@@ -397,7 +412,7 @@ def test_mixed_quarter_integers_bit_exact(name):
     assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
 
 
-@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3")])
+@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3"), ("e2m1p", "e2m1p"), ("e2m1p", "e4m3")])
 def test_mixed_scale_bytes_select_the_right_block(ka, kb):
     """Scales only, every element 1.0 in its own format: D[m,n] =
     32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a value meeting a partner from
@@ -416,20 +431,22 @@ def test_mixed_scale_bytes_select_the_right_block(ka, kb):
     assert np.array_equal(got.astype(np.float64), expect)
 
 
-def test_mixed_k_positions_meet():
-    """A one-hot in K per row of A against B rows holding k at position k:
-    D[m,n] = value of B[n] at A's hot position, so any K-order mismatch between
-    the E4M3 and E2M3 fragments shows (every k in 0..127 of several steps)."""
+@pytest.mark.parametrize("kb", ["e2m3", "e2m1p"])
+def test_mixed_k_positions_meet(kb):
+    """A one-hot in K per row of A against random B rows: D[m,n] = B[n] at
+    A's hot position, so any K-order mismatch between the E4M3 fragments and
+    the 6- or 4-bit ones shows (hot positions cover every k of a step)."""
     M, N, K = 256, 256, 512
-    w = wl.custom(M, N, K, "e4m3", V=32, name="mixed-one-hot", b_kind="e2m3")
+    w = wl.custom(M, N, K, "e4m3", V=32, name="mixed-one-hot", b_kind=kb)
     rng = np.random.default_rng(11)
-    hot = rng.integers(0, K, M)
+    hot = np.arange(M) % 128 + 128 * rng.integers(0, K // 128, M)   # every position of a step, random steps
     a = np.zeros((M, K))
     a[np.arange(M), hot] = 1.0
-    b = rng.integers(-7, 8, (N, K)) / 2.0          # half-integers, exact in E2M3
-    x = {"A": wl.to_stored(a, "e4m3"), "B": wl.to_stored(b, "e2m3"),
+    b = rng.integers(-3, 4, (N, K)) / 2.0          # half-integers in [-1.5, 1.5]: exact in E2M3 and E2M1
+    x = {"A": wl.to_stored(a, "e4m3"), "B": wl.to_stored(b, kb),
          "SFA": np.full((M, K // 32), 127, np.uint8), "SFB": np.full((N, K // 32), 127, np.uint8)}
-    say("[mixed] one-hot K positions")
+    assert len(set(hot % 128)) == 128
+    say(f"[mixed] one-hot K positions e4m3 x {kb}")
     got = run_gpu(w, x)
     assert np.array_equal(got.astype(np.float64), b[:, hot].T)
 
@@ -450,7 +467,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c3b", *EXTRA_FULL])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""

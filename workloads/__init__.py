@@ -96,6 +96,8 @@ WORKLOADS = {
                    8192, 8192, 8192, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
     "c9": Workload("c9", "MX mixed 8192^3: A e4m3, B e2m3 (padded), K-major, N(0,1) rounded to each format, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m3"),
+    "c10": Workload("c10", "MX mixed 8192^3: A e4m3, B e2m1 padded (sixteen per 16 bytes), K-major, N(0,1) rounded to each format, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m1p"),
     "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
                     8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
 }
