@@ -305,3 +305,39 @@ def test_e2m1_all_ones_closed_form():
     got = oracle.gemm(M, N, K, "e2m1", "k", A, "e2m1", "k", B, V=32, SFA=one,
                       SFB=np.full((N, K // 32), 127, np.uint8))
     assert np.array_equal(got, np.full((M, N), float(K)))
+
+
+# ---- 16-element scale blocks (the pages' scale_vec::4X for 4-bit operands) ---
+
+@pytest.mark.parametrize("kind", ["e2m1", "e2m1p", "e2m3"])
+def test_sixteen_element_blocks(kind):
+    """V = 16: every pair of 16-blocks sharing a scale equals V = 32 with that
+    scale; all-ones values give D[m,n] = 16 * sum_q 2^(uA[m,q] + uB[n,q]); and
+    the exact rational sum on a tiny shape."""
+    import workloads as wl
+    M, N, K = 5, 6, 256
+    rng = np.random.default_rng(21)
+    A = wl.to_stored(rng.normal(0, 2, (M, K)), kind)
+    B = wl.to_stored(rng.normal(0, 2, (N, K)), kind)
+    s32a = (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8)
+    s32b = (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)
+    d32 = oracle.gemm(M, N, K, kind, "k", A, kind, "k", B, V=32, SFA=s32a, SFB=s32b)
+    d16 = oracle.gemm(M, N, K, kind, "k", A, kind, "k", B, V=16, SFA=np.repeat(s32a, 2, axis=1),
+                      SFB=np.repeat(s32b, 2, axis=1))
+    assert np.array_equal(d16, d32)
+    ones_a = wl.to_stored(np.ones((M, K)), kind)
+    ones_b = wl.to_stored(np.ones((N, K)), kind)
+    sa = (127 + rng.integers(-4, 5, (M, K // 16))).astype(np.uint8)
+    sb = (127 + rng.integers(-4, 5, (N, K // 16))).astype(np.uint8)
+    D = oracle.gemm(M, N, K, kind, "k", ones_a, kind, "k", ones_b, V=16, SFA=sa, SFB=sb)
+    ua, ub = sa.astype(np.int64) - 127, sb.astype(np.int64) - 127
+    want = 16.0 * np.exp2(ua[:, None, :] + ub[None, :, :]).sum(-1)
+    assert np.array_equal(D, want)
+    # exact rationals: every product and scale is a dyadic rational
+    vals_a, vals_b = oracle.decode(kind, A), oracle.decode(kind, B)
+    got = oracle.gemm(M, N, K, kind, "k", A, kind, "k", B, V=16, SFA=sa, SFB=sb)
+    for m in range(M):
+        for n in range(N):
+            ex = sum(Fraction(vals_a[m, k]) * Fraction(vals_b[n, k]) * Fraction(2) ** int(ua[m, k // 16] + ub[n, k // 16])
+                     for k in range(K))
+            assert Fraction(got[m, n]) == ex
