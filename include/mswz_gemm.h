@@ -106,7 +106,9 @@ typedef struct gemm_plan gemm_plan;
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3, E2M1,
- *                 E2M3, E3M2 and E2M1_P64
+ *                 E2M3, E3M2 and E2M1_P64; or 16 (one scale per 16 K
+ *                 elements: the pages' scale_vec::4X) for E2M1, E2M1_P64,
+ *                 E2M3 and E3M2 with A and B of the same kind
  * Shape rules: K % 128 == 0 (E4M3; E2M3, E3M2 and E2M1_P64, which always use
  * the 256 tile) or K % 256 == 0 (E2M1, which always uses the 256 tile).  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
  * K when both operands are MN-major); a K that is not a multiple of 64 uses

@@ -145,7 +145,10 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4 || fp6;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
         return MSWZ_ERR_UNSUPPORTED;     // 8-, 6- and 4-bit kinds are block-scaled only; 16-bit is dense only
-    if (fp8 && scale_vec_len != 32)
+    // 32 K elements per scale byte; 16 (the pages' scale_vec::4X for 4-bit
+    // operands) for E2M1 and the padded kinds, A and B of one kind
+    if (fp8 && scale_vec_len != 32 &&
+        !(scale_vec_len == 16 && (fp4 || fp6) && a_dt == b_dt))
         return MSWZ_ERR_UNSUPPORTED;
     if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
@@ -299,7 +302,7 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
         !is_aligned16(SFB))
         return MSWZ_ERR_ALIGN;
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                   p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd)};
+                   p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), {}, p->scale_vec_len};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st)
                                                   : mswz::launch_mx(p->variant, a, st);
@@ -336,7 +339,8 @@ int gemm_run_opts(const gemm_plan *p, const void *A, const void *B, const uint8_
     hipError_t err;
     if (mx) {
         mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                       p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e};
+                       p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e,
+                       p->scale_vec_len};
         err = mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st);
     } else {
         mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // 32x32x16 MFMA on 16-bit operands, fp32 accumulate.  Operand lane l holds
 // 8 consecutive K elements of row l % 32 (K half l / 32); both operands use
@@ -215,6 +216,14 @@ __device__ __forceinline__ void lds_write16(uint8_t *lds, uint32_t off, u32x4 v)
 // (v_0[t], v_1[t], v_2[t], v_3[t]).  So four lanes per row pointing at 16
 // consecutive values of rows r0 .. r0+3 give lane t the column t of that 4x16
 // block.
+__device__ __forceinline__ u32x2 lds_read8(const uint8_t *lds, uint32_t off)
+{
+    return *reinterpret_cast<const u32x2 *>(lds + off);
+}
+__device__ __forceinline__ u32x3 lds_read12(const uint8_t *lds, uint32_t off)
+{
+    return *reinterpret_cast<const u32x3 *>(lds + off);
+}
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t *lds, uint32_t off)
 {
     auto *p = (__attribute__((address_space(3))) i16x4 *)(lds + off);

@@ -2,7 +2,7 @@
 // to its instantiations, one translation unit per operand kind and A major
 // (gemm256_bf16_ak.hip, gemm256_bf16_amn.hip, gemm256_f16_ak.hip,
 // gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e2m1.hip, gemm256_fp6.hip,
-// gemm256_mixed.hip),
+// gemm256_mixed.hip, gemm256_v16.hip),
 // so that they
 // compile in parallel.
 #include <hip/hip_runtime.h>
@@ -42,6 +42,8 @@ hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, 
 
 hipError_t launch_mx256(const MxArgs &a, MxKind kind, MxKind kind_b, hipStream_t stream)
 {
+    if (a.sv == 16)
+        return kind_b == kind ? launch256_v16(a, kind, stream) : hipErrorInvalidValue;
     if (kind_b != kind)
         return launch256_mixed(a, kind, kind_b, stream);
     switch (kind) {

@@ -471,8 +471,9 @@ __device__ __forceinline__ bool apply_opts(const EpiOpts &o, int m, int n, f32x4
 }
 
 // KIND: element kind of A (and of B unless KB >= 0); KB: B's kind when it
-// differs (block-scaled E4M3 / E2M3 / E3M2 only).
-template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32, int KB = -1>
+// differs (block-scaled E4M3 / E2M3 / E3M2 / padded E2M1 only); SV: K
+// elements per scale byte (32, or 16 for E2M1 and the padded kinds).
+template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32, int KB = -1, int SV = 32>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -498,6 +499,12 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
     static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "padded 6- and 4-bit kinds are built for the eight-wave 16x16 path");
     static_assert(!kMixed || ((REG & 8) != 0 && W == 8), "mixed kinds are built for the eight-wave 16x16 path");
+    // 16-element scale blocks: a lane's 32 values of a 32-block are two
+    // 16-element halves (one 16-byte chunk of a padded kind, or the two 8-byte
+    // halves of a dense E2M1 chunk), so each 16x16 block takes two MFMAs, each
+    // with one half (the other zero) and that half's scales
+    constexpr bool kV16 = SV == 16;
+    static_assert(SV == 32 || (kV16 && (kFp4 || kFp6) && !kMixed), "16-element blocks: E2M1 and padded kinds");
     // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
     // E2M1 (packed two per byte) K elements
     constexpr int kStepK = kFp4 ? 256 : kByteRows ? 128 : 64;
@@ -567,9 +574,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kByteRows && (REG & 8) != 0 && W == 8;   // the 16x16 E4M3 / FP6 path
+    constexpr bool kScaleGroups = kByteRows && (REG & 8) != 0 && W == 8 && !kV16;   // the 16x16 E4M3 / FP6 path
     constexpr int kSfInstr = 8 / W;
-    const uint32_t sf_row = uint32_t(K) / 32;
+    const uint32_t sf_row = uint32_t(K) / SV;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
     uint32_t sf_voff = 0;
     if constexpr (kMx) {
@@ -613,10 +620,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         if constexpr (kDmaB)
             db.issue(stage, kt);
         if constexpr (kMx) {
-            // scale words per row per step: one (E4M3, four 32-element blocks)
-            // or two (E2M1, eight blocks); word w of 64-row group g lands at
-            // stage byte 2048w + 256g + 4*(row in group)
-            constexpr int kWords = kFp4 ? 2 : 1;
+            // scale words per row per step: one (E4M3 and padded kinds, four
+            // 32-element blocks), two (E2M1, eight blocks), twice that with
+            // 16-element blocks; word w of 64-row group g lands at stage byte
+            // 2048w + 256g + 4*(row in group)
+            constexpr int kWords = (kFp4 ? 2 : 1) * (kV16 ? 2 : 1);
 #pragma unroll
             for (int q = 0; q < kSfInstr; ++q)
 #pragma unroll
@@ -897,19 +905,34 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < TN16; ++j)
             bb[j] = opaque(bbase16[j]);
         // lane group g supplies the scale of block kblk16(g): that byte of its
-        // row's scale word, read as one byte
-        const int r16 = lane & 15, sbyte = kblk16(lane >> 4);
-        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16) + sbyte));
-        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16) + sbyte));
+        // row's scale word, read as one byte.  With 16-element blocks the
+        // chunk's two halves are 16-blocks 2c and 2c + 1 of the step (c =
+        // 4ks + kblk16(g)): word 2ks + kblk16(g)/2, bytes 2 (kblk16(g) % 2) and
+        // that + 1.
+        const int r16 = lane & 15, kb = kblk16(lane >> 4);
+        const uint32_t sb16 = kV16 ? uint32_t(2048 * (kb >> 1) + 2 * (kb & 1)) : uint32_t(kb);
+        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16)) + sb16);
+        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16)) + sb16);
         const u32x4 zero = {0, 0, 0, 0};
-        auto frag = [&](uint32_t base, int ks) {
-            const u32x4 v = lds_read16(s, base ^ uint32_t(ks << 6));
-            return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
+        // sub-step u: K elements 128 u' .. of the step (u' = ks), and with
+        // 16-element blocks each chunk in two halves h
+        auto frag = [&](uint32_t base, int ks, int h) {
+            if constexpr (kV16) {
+                // registers 0..1 the half, 2..3 zero, 4..7 not read by the FP4 MFMA
+                const u32x2 d = lds_read8(s, (base ^ uint32_t(ks << 6)) + 8u * uint32_t(h));
+                const u32x2 z = {0, 0};
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(d, z, 0, 1, 2, 3, -1, -1, -1, -1));
+            } else {
+                const u32x4 v = lds_read16(s, base ^ uint32_t(ks << 6));
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
         };
         // reads two MFMAs ahead of first use, as in compute_mx16
         using Sched = FragSchedule<TM16, TN16, 2>;
-        static_for<0, 2>([&](auto ksc) {
-            constexpr int ks = decltype(ksc)::value;
+        static_for<0, kV16 ? 4 : 2>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            constexpr int ks = kV16 ? u >> 1 : u, h = kV16 ? u & 1 : 0;
+            constexpr int sw = kV16 ? 2048 * 2 * ks + h : 2048 * ks;   // scale byte offset of the sub-step
             uint32_t sa[TM16], sb[TN16];
             i32x8 bf[TN16], af[TM16];
             static_for<0, TM16 * TN16>([&](auto mc) {
@@ -918,11 +941,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 static_for<c0, c1>([&](auto rc) {
                     constexpr int it = Sched::item(decltype(rc)::value);
                     if constexpr (it > 0) {
-                        sa[it - 1] = ss[2048 * ks + sfa + 64 * (it - 1)];
-                        af[it - 1] = frag(ab[it - 1], ks);
+                        sa[it - 1] = ss[sw + sfa + 64 * (it - 1)];
+                        af[it - 1] = frag(ab[it - 1], ks, h);
                     } else {
-                        sb[-it - 1] = ss[2048 * ks + sfb + 64 * (-it - 1)];
-                        bf[-it - 1] = frag(bb[-it - 1], ks);
+                        sb[-it - 1] = ss[sw + sfb + 64 * (-it - 1)];
+                        bf[-it - 1] = frag(bb[-it - 1], ks, h);
                     }
                 });
                 if constexpr (c1 > c0)
@@ -934,9 +957,74 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         });
     };
 
+    // Padded kinds with 16-element scale blocks: lane group g's two chunks
+    // (fp6_chunk16(g) and that ^ 1) are one 16-block each, taken one per
+    // sub-step h into the low registers (twelve bytes for 6-bit, eight for
+    // 4-bit values; the rest zero).  Chunk c of the step is 16-block c: word
+    // c / 4 = g / 2 of the row's two per-step words, byte c % 4.
+    auto compute_pad16 = [&](const uint8_t *s, const uint8_t *ss) {
+        uint32_t ab[TM16], bb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            ab[i] = opaque(abase16[i]);
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bb[j] = opaque(bbase16[j]);
+        const int r16 = lane & 15, g = lane >> 4;
+        const uint32_t sg = uint32_t(2048 * (g >> 1) + (fp6_chunk16(g) & 3));
+        const uint32_t sfa = opaque(uint32_t(4 * (wm + row16<true>(0, r16))) + sg);
+        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + row16<true>(0, r16))) + sg);
+        auto sf_off = [&](int b) { return 4 * (32 * (b >> 1) + 8 * (b & 1)); };
+        auto frag = [&](uint32_t base, int h) {
+            const uint32_t a = base ^ uint32_t(16 * h);
+            // the half in the low registers, zeros for the other half, the
+            // registers the format does not read left undefined
+            if constexpr (KIND == kE2m1p) {
+                const u32x2 d = lds_read8(s, a);
+                const u32x2 z = {0, 0};
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(d, z, 0, 1, 2, 3, -1, -1, -1, -1));
+            } else {
+                const u32x4 d = lds_read16(s, a);            // the last word is padding
+                const u32x4 z = {0, 0, 0, 0};
+                return __builtin_bit_cast(i32x8, __builtin_shufflevector(d, z, 0, 1, 2, 4, 5, 6, -1, -1));
+            }
+        };
+        using Sched = FragSchedule<TM16, TN16, 2>;
+        static_for<0, 2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            // the two halves' fragments are not interleaved (register pressure)
+            if constexpr (h == 1)
+                __builtin_amdgcn_sched_barrier(0);
+            uint32_t sa[TM16], sb[TN16];
+            i32x8 bf[TN16], af[TM16];
+            static_for<0, TM16 * TN16>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
+                static_for<c0, c1>([&](auto rc) {
+                    constexpr int it = Sched::item(decltype(rc)::value);
+                    if constexpr (it > 0) {
+                        sa[it - 1] = ss[(sfa ^ uint32_t(h)) + sf_off(it - 1)];
+                        af[it - 1] = frag(ab[it - 1], h);
+                    } else {
+                        sb[-it - 1] = ss[(sfb ^ uint32_t(h)) + sf_off(-it - 1)];
+                        bf[-it - 1] = frag(bb[-it - 1], h);
+                    }
+                });
+                if constexpr (c1 > c0)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (c1 - c0), 0);   // DS reads
+                constexpr int i = m / TN16, j = m % TN16;
+                acc4[j][i] = mfma_scale_16x16x128_fmt<mx_format<KIND>(), mx_format<KIND>()>(bf[j], af[i], acc4[j][i],
+                                                                                            sb[j], sa[i]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+            });
+        });
+    };
+
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kFp4)
             compute_fp4(s, ss);
+        else if constexpr (kFp6 && kV16)
+            compute_pad16(s, ss);
         else if constexpr (kMx && kMf16)
             compute_mx16(s, ss, 4, 0);
         else if constexpr (kMx)
@@ -1094,7 +1182,7 @@ epilogue:
         }
 }
 
-template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32, int KB = -1>
+template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32, int KB = -1, int SV = 32>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
@@ -1102,23 +1190,23 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT, KB>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT, KB, SV>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT, KB>), dim3(blocks), dim3(64 * W), 0,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT, KB, SV>), dim3(blocks), dim3(64 * W), 0,
                            stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
 }
 
 // bf16 / fp16 output: the default pipeline only
-template <int KIND, bool A_MN, bool B_MN, int KB = -1>
+template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32>
 hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 {
     constexpr int kReg = (A_MN && B_MN) ? 0 : 8;
-    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16, KB>(a, stream)
-                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16, KB>(a, stream);
+    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16, KB, SV>(a, stream)
+                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16, KB, SV>(a, stream);
 }
 
 

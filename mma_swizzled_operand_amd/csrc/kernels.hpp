@@ -59,6 +59,7 @@ struct MxArgs {
     int out = kOutF32;
     int lda = 0, ldb = 0, ldd = 0;   // as in DenseArgs (scale arrays are packed)
     EpiOpts opts = {};
+    int sv = 32;                     // K elements per scale byte (32, or 16)
 };
 
 struct VariantInfo {
@@ -82,6 +83,7 @@ hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
+hipError_t launch256_v16(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch_dense256pp(bool bf16, const DenseArgs &args, hipStream_t stream);
 int config256();
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);

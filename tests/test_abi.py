@@ -107,7 +107,12 @@ K_, MN = 0, 1
     ((256, 256, 64, F16, F16, E4M3, K_, K_, 0), -2),         # e4m3 output
     ((256, 256, 64, F32, F32, F32, K_, K_, 0), -2),
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 0), -2),       # e4m3 needs scales
-    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 16), -2),      # only 32-element blocks
+    ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 16), -2),      # E4M3: only 32-element blocks
+    ((256, 256, 256, E2M1, E2M1, F32, K_, K_, 16), 0),       # 16-element blocks (scale_vec::4X)
+    ((256, 256, 128, E2M1P, E2M1P, F32, K_, K_, 16), 0),
+    ((256, 256, 128, E3M2, E3M2, BF16, K_, K_, 16), 0),
+    ((256, 256, 128, E4M3, E2M3, F32, K_, K_, 16), -2),      # not for mixed kinds
+    ((256, 256, 256, E2M1, E2M1, F32, K_, K_, 8), -2),
     ((256, 256, 64, F16, F16, F32, K_, K_, 32), -2),         # 16-bit is dense only
     ((256, 256, 64, F16, F16, F32, K_, MN, 0), 0),           # B MN-major (16-bit)
     ((256, 256, 64, BF16, BF16, F32, MN, MN, 0), 0),         # both MN-major

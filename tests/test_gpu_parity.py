@@ -451,6 +451,71 @@ def test_mixed_k_positions_meet(kb):
     assert np.array_equal(got.astype(np.float64), b[:, hot].T)
 
 
+# 16-element scale blocks (scale_vec_len 16: the pages' scale_vec::4X) for
+# E2M1 (dense and padded) and the 6-bit kinds
+V16 = {
+    "e2m1-v16": wl.custom(512, 512, 1024, "e2m1", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                          name="e2m1-v16"),
+    "e2m1-v16-tail-beta": wl.custom(300, 292, 768, "e2m1", V=16, beta=1, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="e2m1-v16-tail-beta"),
+    "e2m1p-v16": wl.custom(512, 256, 1024, "e2m1p", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e2m1p-v16"),
+    "e2m3-v16-beta": wl.custom(256, 512, 512, "e2m3", V=16, beta=1, a_dist=("normal", 1.0),
+                               b_dist=("normal", 1.0), name="e2m3-v16-beta"),
+    "e3m2-v16-tail": wl.custom(264, 300, 384, "e3m2", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e3m2-v16-tail"),
+}
+
+
+@pytest.mark.parametrize("name", list(V16))
+def test_v16_full_compare(name):
+    w = V16[name]
+    plan = plan_for(w)
+    say(f"[v16] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta}")
+    x = wl.generate(w, seed=61)
+    got = run_gpu(w, x, plan)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(V16))
+def test_v16_quarter_integers_bit_exact(name):
+    w = V16[name]
+    say(f"[v16-exact] {name}")
+    x = wl.generate(w, seed=62, values="quarter")
+    got = run_gpu(w, x, plan_for(w))
+    assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["e2m1", "e2m1p", "e3m2"])
+def test_v16_scale_bytes_select_the_right_block(kind):
+    """Scales only: every element 1.0, D[m,n] = 16 sum_q 2^(uA[m,q]+uB[n,q])
+    exactly; a wrong scale byte, word or half for any 16-block changes it."""
+    M, N, K = 256, 512, 1024
+    w = wl.custom(M, N, K, kind, V=16, name=f"{kind}-v16-scale-only")
+    rng = np.random.default_rng(12)
+    x = {"A": wl.to_stored(np.ones((M, K)), kind), "B": wl.to_stored(np.ones((N, K)), kind),
+         "SFA": (127 + rng.integers(-4, 5, (M, K // 16))).astype(np.uint8),
+         "SFB": (127 + rng.integers(-4, 5, (N, K // 16))).astype(np.uint8)}
+    say(f"[v16] scale closed form {kind}")
+    got = run_gpu(w, x)
+    ua = x["SFA"].astype(np.int64) - 127
+    ub = x["SFB"].astype(np.int64) - 127
+    expect = 16.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
+    assert np.array_equal(got.astype(np.float64), expect)
+
+
+def test_v16_full_size_sampled():
+    """4096^3 E2M1 with 16-element blocks, sampled rows and columns."""
+    w = wl.custom(4096, 4096, 4096, "e2m1", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0), name="e2m1-v16-4096")
+    say("[v16 full] 4096^3 e2m1")
+    x = wl.generate(w, seed=63)
+    got = run_gpu(w, x)
+    rows, cols = wl.sample_points(w, 8, 8, seed=64)
+    ref_r, mag_r = reference(w, x, rows=rows)
+    print(compare(w, got[rows], ref_r, mag_r))
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
