@@ -516,6 +516,28 @@ def test_v16_full_size_sampled():
     print(compare(w, got[rows], ref_r, mag_r))
 
 
+# long K: large per-step offsets, long fp32 accumulation chains
+LONGK = {
+    "bf16-k65536": wl.custom(256, 512, 65536, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                             name="bf16-k65536"),
+    "f16-amn-k16384-beta": wl.custom(256, 256, 16384, "f16", a_major="mn", beta=1, name="f16-amn-k16384-beta"),
+    "e4m3-k32768": wl.custom(256, 256, 32768, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                             name="e4m3-k32768"),
+}
+
+
+@pytest.mark.parametrize("name", list(LONGK))
+def test_long_k(name):
+    w = LONGK[name]
+    say(f"[long-k] {name} {w.M}x{w.N}x{w.K}")
+    x = wl.generate(w, seed=71)
+    got = run_gpu(w, x)
+    ref, mag = reference(w, x)
+    print(name, compare(w, got, ref, mag, x.get("D0")))
+    xq = wl.generate(w, seed=72, values="quarter")
+    assert np.array_equal(run_gpu(w, xq), reference(w, xq, with_mag=False).astype(np.float32))
+
+
 # the remaining dense operand layouts at full size (fp16 K-major, bf16 with
 # MN-major A, MN-major B alone, both MN-major with beta)
 EXTRA_FULL = {
