@@ -15,6 +15,13 @@ against the MI355X dense MFMA peak (or HBM peak for the skinny shape), using
 the average kernel duration from HIP events recorded on the launch stream
 over the timed region.  ``cpu_baseline`` times the fp64 oracle, as it stands,
 on a bounded sample of the same workload on this host's cores.
+
+``value`` and ``roofline`` come from back-to-back launches, where operands of
+256 MiB or less can stay partly resident in the 256 MiB MALL between calls.
+``caches_flushed`` therefore reports each workload once more: single calls,
+each preceded by an untimed read of another 512 MiB buffer that evicts the
+operands from the L2s and the MALL, with the median and minimum per-call time and, for
+comparison, the median of the same per-call timing without the flush.
 """
 from __future__ import annotations
 
@@ -124,7 +131,58 @@ def time_steps(step, steps, warmup):
     return wall, ev0.elapsed_time(ev1) / steps
 
 
-def measure(name, steps, warmup):
+# Bytes of the buffer copied between calls to empty the caches: twice the
+# 256 MiB MALL (Infinity Cache) and far beyond the 8 x 4 MiB of L2.
+FLUSH_BYTES = 512 << 20
+
+
+def make_flush():
+    """A callable that reads FLUSH_BYTES of another buffer (a sum into one
+    scalar), which evicts every line of the operands from the L2s and the MALL
+    and leaves them holding clean lines.  A flush that writes (a copy, a fill)
+    leaves dirty lines whose write-back then lands inside the next timed call:
+    measured on the skinny shape, a copy flush makes the call 1.36x and a fill
+    1.7x slower than this read-only flush does."""
+    import torch
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    acc = torch.zeros((), dtype=torch.float32, device="cuda")
+    return lambda: torch.sum(buf, dim=0, out=acc)
+
+
+def per_call_ms(step, calls, flush=None):
+    """Duration of each of `calls` library calls, from one HIP event pair per
+    call on the launch stream; with `flush`, the (untimed) cache flush runs
+    before every call.  Sorted ascending."""
+    import torch
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def cold_entry(w, warm_ms, cold_ms):
+    """Median and minimum per-call time with and without the flush, and the
+    rates at the flushed median."""
+    med = cold_ms[len(cold_ms) // 2]
+    out = {"calls": len(cold_ms), "flushed_us_median": round(med * 1e3, 2),
+           "flushed_us_min": round(cold_ms[0] * 1e3, 2),
+           "unflushed_us_median": round(warm_ms[len(warm_ms) // 2] * 1e3, 2),
+           "TFLOP/s": round(w.flops / (med * 1e-3) / 1e12, 1),
+           "frac_mfma_peak": round(w.flops / (med * 1e-3) / 1e12 / mfma_peak(w), 4),
+           "GB/s_algorithmic": round(w.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}
+    if w.name == "c4":
+        out["frac_hbm_peak"] = round(out["GB/s_algorithmic"] / HBM_PEAK, 4)
+    return out
+
+
+def measure(name, steps, warmup, cold=0, flush=None):
     import workloads as wl
     w = wl.WORKLOADS[name]
     log(f"{name}: generating inputs ({w.title})")
@@ -144,6 +202,11 @@ def measure(name, steps, warmup):
     }
     log(f"{name}: {r['kernel_avg_ms'] * 1e3:.1f} us/launch, {r['kernel_tflops']:.1f} TFLOP/s, "
         f"{r['kernel_gbs']:.0f} GB/s algorithmic")
+    if cold:
+        # after the timed region, so that its dispatches stay contiguous
+        r["cold"] = cold_entry(w, per_call_ms(step, cold), per_call_ms(step, cold, flush))
+        log(f"{name}: caches flushed before each call: {r['cold']['flushed_us_median']:.1f} us "
+            f"median ({r['cold']['unflushed_us_median']:.1f} us unflushed, one event pair per call)")
     return r
 
 
@@ -185,6 +248,9 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8,c9,c10",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
+    ap.add_argument("--cold-calls", type=int, default=50,
+                    help="after the timed steps, time this many single calls of each workload "
+                         "with the L2s and the MALL flushed before every call (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -218,7 +284,8 @@ def main():
 
     if args.workload not in wl.WORKLOADS:
         raise SystemExit(f"unknown workload {args.workload}")
-    head = measure(args.workload, args.steps, args.warmup)
+    flush = make_flush() if args.cold_calls else None
+    head = measure(args.workload, args.steps, args.warmup, args.cold_calls, flush)
     w = head["workload"]
 
     hbm = w.name == "c4"
@@ -232,7 +299,7 @@ def main():
 
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = measure(name, args.steps, args.warmup)
+        r = measure(name, args.steps, args.warmup, args.cold_calls, flush)
         ow = r["workload"]
         entry = {"title": ow.title, "us_per_call": round(r["kernel_avg_ms"] * 1e3, 2),
                  "TFLOP/s": round(r["kernel_tflops"], 1),
@@ -241,6 +308,8 @@ def main():
                  "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"], r["plan"]["tile_k"]]}
         if ow.name == "c4":
             entry["frac_hbm_peak"] = round(r["kernel_gbs"] / HBM_PEAK, 4)
+        if "cold" in r:
+            entry["caches_flushed"] = r["cold"]
         also[name] = entry
         del r
 
@@ -268,6 +337,7 @@ def main():
                    round(head["kernel_tflops"] / mfma_peak(w), 4)},
         "roofline": roofline,
         "kernel_avg_us": round(head["kernel_avg_ms"] * 1e3, 2),
+        "caches_flushed": head.get("cold"),
         "cpu_baseline": cpu,
         "also": also,
         "kernel_source_hash": kernel_source_hash(),

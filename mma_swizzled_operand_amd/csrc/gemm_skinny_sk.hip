@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -238,6 +240,135 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
         __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// K-sliced variant, used where a part holds 8 x KS K elements (KS = 128 or
+// 256).  The workgroup covers the same 256 columns x K part as above, but its
+// 8 waves split the part's K range instead of its columns: wave w owns the
+// KS-element slice [w KS, (w+1) KS) of the part, keeps A's slice (MT 16-row
+// blocks x KS) in registers for the whole kernel, and streams B in groups of
+// 16 rows: group G is rows 16G .. 16G+15 of the 256, of which the wave loads
+// its slice (16 rows x 2 KS bytes, one 16x16x32 operand fragment per load, K
+// in natural order).  All 8 waves load group G at the same time, so each
+// B row's whole K-part segment is requested together, which is what makes
+// the streaming efficient from DRAM (the column-split kernel requests 128
+// bytes of each of 256 rows per step, and from cold memory streams about 25 %
+// slower).  Each load slot is reissued for group G+1 as soon as the MFMAs of
+// group G have read it, so one group per wave stays in flight throughout.
+// The 8 waves' 64 x 16 partials of group G are summed through LDS in wave
+// order (double-buffered, one barrier per group; waves 0-3 reduce the even
+// groups and 4-7 the odd ones); the sums are stored to the part's fp32
+// partial after the last group, and splitk_reduce_kernel adds the parts as
+// for the column-split kernel.
+template <bool BF16, int MT, int KS>
+__global__ void __launch_bounds__(kThreads)
+gemm_skinny_ks_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                      float *__restrict__ part_ws, int M, int N, int K)
+{
+    static_assert(MT == 1 || MT == 2 || MT == 4, "16, 32 or 64 padded rows");
+    static_assert(KS % 32 == 0 && KS <= 256, "whole 16x16x32 steps, A slice in registers");
+    constexpr int kSteps = KS / 32;
+    constexpr int kGroups = kBN / 16;
+    constexpr int kRedBytes = 8 * MT * 64 * 16;   // one group: [wave][mt][lane] f32x4
+    __shared__ __attribute__((aligned(16))) uint8_t red0[kRedBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t red1[kRedBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_cb = N / kBN;
+    const int cb = blockIdx.x % n_cb, part = blockIdx.x / n_cb;
+    const int n0 = cb * kBN;
+    const uint32_t row_bytes = uint32_t(K) * 2;
+    // byte offset of this wave's K slice within a row
+    const uint32_t k_off = (uint32_t(part) * 8u + uint32_t(wave)) * uint32_t(KS) * 2u;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    // B: lane (r16, g) of step s loads row 16G + r16, K elements 32s + 8g .. +7 of the slice
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + size_t(n0) * row_bytes, uint32_t(kBN) * row_bytes);
+    const uint32_t b_voff = uint32_t(r16) * row_bytes + 16u * uint32_t(g);
+    u32x4 bf[kSteps];
+    auto issue_b = [&](int G, int s) {
+        bf[s] = buffer_load16(rb, b_voff + 64u * uint32_t(s), k_off + uint32_t(16 * G) * row_bytes);
+    };
+    // A: row 16 mt + r16 (rows >= M lie beyond the buffer's range and read as
+    // zeros).  Loaded step by step with group 0's B fragments, in the order the
+    // first group's MFMAs use them, so that they start before all of A is in.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, uint32_t(M) * row_bytes);
+    u32x4 af[MT][kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        issue_b(0, s);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            af[mt][s] = buffer_load16(ra, uint32_t(16 * mt + r16) * row_bytes + 16u * uint32_t(g) + 64u * uint32_t(s),
+                                      k_off);
+    }
+    sched_fence();
+
+    // The reducing waves keep their groups' sums in registers and store them
+    // after the last group: stores issued during the streaming cost more than
+    // their bytes (each one is waited for at the next barrier, and the writes
+    // interleave with the stream's reads in DRAM).
+    f32x4 sums[kGroups / 2];
+    // One group: MFMAs step by step, each step's load slot reissued for group
+    // G+1 right after its MFMAs (NEXT), partials to LDS, barrier, and the
+    // reducing waves' fixed-order sum.
+    auto group = [&](int G, uint8_t *red, int red_wave0, auto next) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = mfma_16x16x32<BF16>(bf[s], af[mt][s], acc[mt]);
+            if constexpr (decltype(next)::value)
+                issue_b(G + 1, s);
+            sched_fence();
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<f32x4 *>(red + ((wave * MT + mt) * 64 + lane) * 16) = acc[mt];
+        // the partials are in LDS; the next group's loads stay in flight
+        lds_barrier_keep_vm<decltype(next)::value ? kSteps : 0>();
+        const int mt = wave - red_wave0;
+        if (mt >= 0 && mt < MT) {
+            f32x4 v[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+                v[w] = *reinterpret_cast<const f32x4 *>(red + ((w * MT + mt) * 64 + lane) * 16);
+            sched_fence();
+            f32x4 sum = v[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w)
+                sum += v[w];
+            sums[G >> 1] = sum;
+        }
+    };
+    // Group G's LDS buffer is rewritten by group G+2 only after the barrier of
+    // group G+1, which every wave reaches after its reads of group G.
+    // (unrolled in full, so that every index into sums is a constant)
+    using yes = std::true_type;
+#pragma unroll
+    for (int G = 0; G < kGroups - 2; G += 2) {
+        group(G, red0, 0, yes{});
+        group(G + 1, red1, 4, yes{});
+    }
+    group(kGroups - 2, red0, 0, yes{});
+    group(kGroups - 1, red1, 4, std::false_type{});
+
+    // wave w reduced the groups of parity w / 4 for 16-row block w % 4: lane
+    // holds row 16 mt + r16, columns 16G + 4g .. +3 of the workgroup's block
+    const int mt = wave & 3, odd = wave >> 2;
+    const int m = 16 * mt + r16;
+    if (mt < MT && m < M) {
+        float *const mine = part_ws + size_t(part) * size_t(M) * N + size_t(m) * N + n0 + 4 * g;
+#pragma unroll
+        for (int h = 0; h < kGroups / 2; ++h)
+            *reinterpret_cast<f32x4 *>(mine + 16 * (2 * h + odd)) = sums[h];
+    }
+}
+
 // Second pass of the two-kernel reduction: D = sum_p partial[p] (+ D), the S
 // partials added in part order, one 16-byte group of outputs per thread.
 template <bool BETA>
@@ -269,19 +400,54 @@ bool reduce_inline()
     return v;
 }
 
+// Streaming kernel, selected at run time by MSWZ_SPLITK_KERNEL (tuning only):
+// "cols" = the column-split kernel everywhere; otherwise the K-sliced kernel
+// wherever a part holds 1024 or 2048 K elements.
+bool kslice_allowed()
+{
+    static const bool v = [] {
+        const char *e = getenv("MSWZ_SPLITK_KERNEL");
+        return !(e && e[0] == 'c');
+    }();
+    return v;
+}
+
+template <bool BF16, int MT>
+void launch_ks(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
+{
+    const uint8_t *A = static_cast<const uint8_t *>(a.A);
+    const uint8_t *B = static_cast<const uint8_t *>(a.B);
+    const dim3 grid(a.N / kBN * sk.parts);
+    if (a.K / sk.parts == 8 * 256)
+        hipLaunchKernelGGL((gemm_skinny_ks_kernel<BF16, MT, 256>), grid, dim3(kThreads), 0, stream, A, B,
+                           sk.partials, a.M, a.N, a.K);
+    else
+        hipLaunchKernelGGL((gemm_skinny_ks_kernel<BF16, MT, 128>), grid, dim3(kThreads), 0, stream, A, B,
+                           sk.partials, a.M, a.N, a.K);
+}
+
 template <bool BF16, bool BETA>
 hipError_t launch_bb(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
 {
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     const dim3 grid(a.N / kBN * sk.parts);
-    if (reduce_inline()) {
+    const int kpart = a.K / sk.parts;
+    if (!reduce_inline() && kslice_allowed() && (kpart == 8 * 256 || kpart == 8 * 128)) {
+        if (a.M <= 16)
+            launch_ks<BF16, 1>(a, sk, stream);
+        else if (a.M <= 32)
+            launch_ks<BF16, 2>(a, sk, stream);
+        else
+            launch_ks<BF16, 4>(a, sk, stream);
+    } else if (reduce_inline()) {
         hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, true>), grid, dim3(kThreads), 0, stream, A, B,
                            a.D, sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
         return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, false>), grid, dim3(kThreads), 0, stream, A, B,
+                           a.D, sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
     }
-    hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, false>), grid, dim3(kThreads), 0, stream, A, B, a.D,
-                       sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

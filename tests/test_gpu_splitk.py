@@ -34,6 +34,18 @@ SMALL = {
                                   b_dist=("normal", 0.02), name="ws-bf16-m48-beta"),
 }
 
+# parts of 2048 or 1024 K elements: the K-sliced streaming kernel (each wave
+# keeps a 256- or 128-element slice of A in registers), M padded to 16, 32 or 64
+KSLICE = {
+    "ks-bf16-m64-k32768": wl.custom(64, 256, 32768, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                                    name="ks-bf16-m64-k32768"),      # S = 16, slices of 256
+    "ks-f16-m20-k16384-beta": wl.custom(20, 512, 16384, "f16", beta=1, name="ks-f16-m20-k16384-beta"),  # S = 16, 128
+    "ks-bf16-m1-k32768": wl.custom(1, 1024, 32768, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                                   name="ks-bf16-m1-k32768"),        # S = 16, 256
+    "ks-bf16-m48-k16384-beta": wl.custom(48, 4096, 16384, "bf16", beta=1, name="ks-bf16-m48-k16384-beta"),  # 128
+    "ks-f16-m64-n16384-k4096": wl.custom(64, 16384, 4096, "f16", name="ks-f16-m64-n16384-k4096"),  # S = 4, 128
+}
+
 # the same kernels without a workspace (K not split), ragged M
 UNSPLIT = {
     "skinny-f16-m1": wl.custom(1, 1024, 1024, "f16", name="skinny-f16-m1"),
@@ -56,6 +68,73 @@ def test_split_small_full_compare(name):
     print(name, compare(w, got, ref, mag, x.get("D0")))
     counters = ws[:256].cpu().numpy()
     assert not counters.any(), "counters not reset"
+
+
+def ks_parts(w):
+    """K parts the plan picks (the smallest power of two up to 16 giving at
+    least 256 workgroups of 256 columns, else the largest that fits K)."""
+    best = 0
+    for s in (2, 4, 8, 16):
+        if w.K % (256 * s):
+            continue
+        best = s
+        if w.N // 256 * s >= 256:
+            break
+    return best
+
+
+@pytest.mark.parametrize("name", list(KSLICE))
+def test_kslice_full_compare(name):
+    w = KSLICE[name]
+    assert w.K // ks_parts(w) in (1024, 2048), "case must reach the K-sliced kernel"
+    plan = plan_for(w)
+    ws = zero_workspace(plan)
+    say(f"[splitk-ks] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta} parts={ks_parts(w)}")
+    x = wl.generate(w, seed=21)
+    got = run_gpu(w, x, plan, workspace=ws)
+    if w.M * w.N * w.K <= (1 << 30):
+        ref, mag = reference(w, x)
+        print(name, compare(w, got, ref, mag, x.get("D0")))
+    else:
+        cols = wl.sample_points(w, 8, 64)[1]
+        ref, mag = reference(w, x, cols=cols)
+        print(name, compare(w, got[:, cols], ref, mag, None if x.get("D0") is None else x["D0"][:, cols]))
+    again = run_gpu(w, x, plan, workspace=ws)
+    assert np.array_equal(got, again), "not bit-identical run to run"
+
+
+@pytest.mark.parametrize("name", ["ks-bf16-m64-k32768", "ks-bf16-m1-k32768"])
+def test_kslice_quarter_exact(name):
+    """Quarter-integer operands: every product, per-wave partial and sum is
+    exact in fp32, so the result equals the exact product bit for bit."""
+    w = KSLICE[name]
+    plan = plan_for(w)
+    x = wl.generate(w, seed=22, values="quarter")
+    say(f"[splitk-ks] quarter exact {name}")
+    got = run_gpu(w, x, plan, workspace=zero_workspace(plan))
+    assert np.array_equal(got.astype(np.float64), reference(w, x, with_mag=False))
+
+
+def test_kslice_stores_stay_inside_d_and_workspace():
+    """M = 20 (padded to 32): canaries after D and after the workspace."""
+    import mma_swizzled_operand_amd as mswz
+    w = KSLICE["ks-f16-m20-k16384-beta"]
+    plan = plan_for(w)
+    x = wl.generate(w, seed=23)
+    A, B = (torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).cuda() for k in ("A", "B"))
+    n = w.M * w.N
+    dbuf = torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda")
+    dbuf[:n] = torch.from_numpy(x["D0"].reshape(-1)).cuda()
+    need = plan.workspace_bytes()
+    wbuf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    wbuf[need:] = 0xA5
+    say("[splitk-ks] canaries")
+    mswz.gemm_run_ws(plan, A, B, dbuf[:n], wbuf[:need], 1)
+    torch.cuda.synchronize()
+    assert torch.all(dbuf[n:] == 7.0)
+    assert torch.all(wbuf[need:] == 0xA5)
+    ref, mag = reference(w, x)
+    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, mag, x.get("D0"))
 
 
 def test_split_repeatable_and_counters_reset():
