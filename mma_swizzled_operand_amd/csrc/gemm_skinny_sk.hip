@@ -385,7 +385,10 @@ splitk_reduce_kernel(const float *__restrict__ part_ws, float *__restrict__ D, i
     f32x4 *d = reinterpret_cast<f32x4 *>(D) + i;
     if constexpr (BETA)
         sum += *d;
-    *d = sum;
+    // streamed to memory (consecutive threads write whole lines): 1 us less
+    // per 64 x 16384 call than plain stores; the partials, read again right
+    // after, are stored plainly
+    __builtin_nontemporal_store(sum, d);
 }
 
 // Reduction mode, selected at run time by the environment variable
