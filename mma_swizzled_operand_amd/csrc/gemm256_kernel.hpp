@@ -1159,6 +1159,50 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // ---- epilogue -------------------------------------------------------------
 epilogue:
     const bool opts_on = opts.neg || opts.row_mask || opts.col_zero;
+    // (6-bit operand pairs only: with E4M3 operands, whose main loops sit
+    // at the 256-VGPR limit, this epilogue made the compiler spill inside
+    // the loop)
+    constexpr bool kSix = (KIND == kE2m3 || KIND == kE3m2) && (kKindB == kE2m3 || kKindB == kE3m2);
+    if constexpr (kMf16 && kSix && OUT == kOutF32) {
+        // Byte-row blocks give each row's lanes two runs of 8 columns, too
+        // small a piece for non-temporal stores, so the tile goes through
+        // the (now idle) operand stages: each wave writes a quarter of its
+        // 128 x 64 tile (32 rows, fragment blocks 2q and 2q+1) into its own
+        // 32-row area (waves 0-3 in lds0, 4-7 in lds1; rows 272 bytes apart,
+        // so the 16 rows of a fragment write fall on distinct banks), reads
+        // it back as 4 rows x 256 bytes per instruction and stores those
+        // non-temporally.  One wave's writes and reads are ordered by the
+        // LDS itself; the barrier keeps the last K step's reads of the
+        // stages before the first write.
+        constexpr uint32_t kPitch = 272;
+        __syncthreads();
+        uint8_t *area = (wave < 4 ? lds0 : lds1) + (wave & 3) * 32 * kPitch;
+        const int rd_row = lane >> 4, rd_col = 4 * (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int j = 0; j < TN16; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * q + ii;
+                    const int r = row16<true>(i, lane & 15) - 32 * q;      // 0 .. 31
+                    const int c = row16<true>(j, 4 * (lane >> 4));        // 0 .. 63
+                    *reinterpret_cast<f32x4 *>(area + r * kPitch + c * 4) = acc4[j][i];
+                }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = 4 * k + rd_row;
+                f32x4 v = *reinterpret_cast<const f32x4 *>(area + r * kPitch + rd_col * 4);
+                const int m = m0 + wm + 32 * q + r, n = n0 + wn + rd_col;
+                if (m >= M || n >= N)
+                    continue;
+                if (opts_on && !apply_opts(opts, m, n, v))
+                    continue;
+                store_d4<OUT, BETA, true>(D, size_t(m) * ldd + n, v, opts.sat);
+            }
+        }
+        return;
+    }
     if constexpr (kMf16) {
         // 16x16 block (j, i): lane l holds fragment row l % 16 of A block i
         // and fragment rows 4(l/16) .. +3 of B block j
