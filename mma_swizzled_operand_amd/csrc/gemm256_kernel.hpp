@@ -1159,13 +1159,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // ---- epilogue -------------------------------------------------------------
 epilogue:
     const bool opts_on = opts.neg || opts.row_mask || opts.col_zero;
-    // (6-bit operand pairs only: with E4M3 operands, whose main loops sit
-    // at the 256-VGPR limit, this epilogue made the compiler spill inside
-    // the loop)
+    // (16-bit, E2M1 and 6-bit operand pairs: with E4M3 operands, whose main
+    // loops sit at the 256-VGPR limit, this epilogue made the compiler spill
+    // inside the loop, and it added spills to the 16-bit kernel with both
+    // operands MN-major)
     constexpr bool kSix = (KIND == kE2m3 || KIND == kE3m2) && (kKindB == kE2m3 || kKindB == kE3m2);
-    if constexpr (kMf16 && kSix && OUT == kOutF32) {
+    if constexpr (kMf16 && (kSix || !kByteRows) && !(A_MN && B_MN) && OUT == kOutF32) {
         // Byte-row blocks give each row's lanes two runs of 8 columns, too
-        // small a piece for non-temporal stores, so the tile goes through
+        // small a piece for non-temporal stores, and the other blocks 16
+        // columns (64 bytes), so the tile goes through
         // the (now idle) operand stages: each wave writes a quarter of its
         // 128 x 64 tile (32 rows, fragment blocks 2q and 2q+1) into its own
         // 32-row area (waves 0-3 in lds0, 4-7 in lds1; rows 272 bytes apart,
@@ -1185,8 +1187,8 @@ epilogue:
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
                     const int i = 2 * q + ii;
-                    const int r = row16<true>(i, lane & 15) - 32 * q;      // 0 .. 31
-                    const int c = row16<true>(j, 4 * (lane >> 4));        // 0 .. 63
+                    const int r = row16<kByteRows>(i, lane & 15) - 32 * q;      // 0 .. 31
+                    const int c = row16<kByteRows>(j, 4 * (lane >> 4));        // 0 .. 63
                     *reinterpret_cast<f32x4 *>(area + r * kPitch + c * 4) = acc4[j][i];
                 }
 #pragma unroll
