@@ -955,8 +955,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         };
-        // reads two MFMAs ahead of first use, as in compute_mx16
-        using Sched = FragSchedule<TM16, TN16, 2>;
+        // reads three MFMAs ahead of first use (two with 16-element blocks,
+        // whose kernels have no registers to spare), as in compute_mx16; three
+        // ran 8192^3 MX-fp4 1.6 % faster than two
+        using Sched = FragSchedule<TM16, TN16, kV16 ? 2 : 3>;
         static_for<0, kV16 ? 4 : 2>([&](auto uc) {
             constexpr int u = decltype(uc)::value;
             constexpr int ks = kV16 ? u >> 1 : u, h = kV16 ? u & 1 : 0;
