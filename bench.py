@@ -1,20 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the swizzled-operand GEMM on one MI355X.
 
-One step = one library call (one kernel launch) computing the whole product
-for the workload on inputs already resident in HBM.  Default workload: the
-square dense 4096^3 bf16 GEMM with both operands K-major (N(0,1) inputs,
-seed 0).  The other full-size workloads (8192^3 fp16 MN-major A with beta=1,
-8192^3 bf16, the skinny 64x16384x8192 weight-streaming shape, 8192^3 MX-fp8,
-8192^3 MX-fp4, 8192^3 MX-fp6 in both 6-bit formats, and 8192^3 with E4M3 A
-against E2M3 or padded E2M1 B) are timed in the same run and reported under
-"also".
+One step = one library call (one kernel launch; two for the split weight-
+streaming path) computing the whole product for the workload on inputs
+already resident in HBM.  Default workload: the square dense 8192^3 bf16
+GEMM with both operands K-major (N(0,1) inputs, seed 0), the metric's "bf16
+8192^3".  The other workloads (the single 128x256x64 tile, 4096^3 bf16,
+8192^3 fp16 MN-major A with beta=1, the skinny 64x16384x8192 weight-streaming
+shape, 8192^3 MX-fp8 -- the metric's second configuration --, 8192^3 MX-fp4,
+MX-fp6 in both 6-bit formats, E4M3 A against E2M3 or padded E2M1 B, and bf16
+8192^3 with B MN-major or both operands MN-major) are timed in the same run
+and reported under "also", each with its own roofline and sampled oracle
+baseline.
 
 Prints ONE JSON line (rank 0).  ``roofline`` reports the dominant kernel
 against the MI355X dense MFMA peak (or HBM peak for the skinny shape), using
 the average kernel duration from HIP events recorded on the launch stream
 over the timed region.  ``cpu_baseline`` times the fp64 oracle, as it stands,
 on a bounded sample of the same workload on this host's cores.
+
+Warm-up: after the requested warm-up launches, launches continue until at
+least ``--settle-ms`` (default 250 ms) of back-to-back work has passed since
+the first one.  The chip's power management needs about 40-60 ms of
+sustained MFMA load after an idle start to settle; launches before that run
+up to 20 % slower, which would put a short timed region on the transient
+rather than on the steady state of a loaded GPU.  The extra warm-up launches
+are reported (``warmup_settle``); the timed region is exactly ``--steps``
+launches.
 
 ``value`` and ``roofline`` come from back-to-back launches, where operands of
 256 MiB or less can stay partly resident in the 256 MiB MALL between calls.
@@ -100,8 +112,8 @@ def setup(w, seed=0):
             mswz.gemm_run_blockscaled(plan, A, B, SFA, SFB, D, w.beta)
     elif plan.workspace_bytes() > 0:
         # weight streaming with K split over workgroups: the library's
-        # workspace path (zero-filled once; every call leaves it so)
-        ws = torch.zeros(plan.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        # workspace path (the caller's workspace holds the fp32 partials)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device="cuda")
 
         def step():
             mswz.gemm_run_ws(plan, A, B, D, ws, w.beta)
@@ -111,14 +123,34 @@ def setup(w, seed=0):
     return x, plan, step
 
 
-def time_steps(step, steps, warmup):
-    """Wall time of `steps` launches, and their mean duration from two HIP
-    events on the launch stream bracketing the timed region (events between
-    launches would each add a few microseconds of idle GPU time)."""
+def warm_up(step, warmup, settle_ms):
+    """`warmup` launches, then more until at least settle_ms of back-to-back
+    launches have passed since the first (batches sized from the measured
+    rate, about 20 ms each).  Returns (extra launches, total ms)."""
     import torch
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    done, extra = warmup, 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        per = max((time.perf_counter() - t0) * 1e3 / max(done, 1), 1e-3)
+        n = max(1, min(int(20.0 / per), 100000))
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        done += n
+        extra += n
+    return extra, (time.perf_counter() - t0) * 1e3
+
+
+def time_steps(step, steps, warmup, settle_ms=0.0):
+    """Wall time of `steps` launches, and their mean duration from two HIP
+    events on the launch stream bracketing the timed region (events between
+    launches would each add a few microseconds of idle GPU time); also the
+    warm-up's extra launches and length."""
+    import torch
+    settle = warm_up(step, warmup, settle_ms)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -128,7 +160,7 @@ def time_steps(step, steps, warmup):
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, ev0.elapsed_time(ev1) / steps
+    return wall, ev0.elapsed_time(ev1) / steps, settle
 
 
 # Bytes of the buffer copied between calls to empty the caches: twice the
@@ -182,14 +214,16 @@ def cold_entry(w, warm_ms, cold_ms):
     return out
 
 
-def measure(name, steps, warmup, cold=0, flush=None):
+def measure(name, steps, warmup, cold=0, flush=None, settle_ms=0.0):
     import workloads as wl
     w = wl.WORKLOADS[name]
     log(f"{name}: generating inputs ({w.title})")
     x, plan, step = setup(w)
-    log(f"{name}: plan {plan.describe()}; timing {steps} steps after {warmup} warm-up")
-    wall, avg_ms = time_steps(step, steps, warmup)
+    log(f"{name}: plan {plan.describe()}; timing {steps} steps after {warmup} warm-up "
+        f"(and at least {settle_ms:.0f} ms of warm-up launches)")
+    wall, avg_ms, (extra, settle_total) = time_steps(step, steps, warmup, settle_ms)
     r = {
+        "warmup_settle": {"extra_launches": extra, "warmup_ms": round(settle_total, 1)},
         "workload": w,
         "inputs": x,
         "plan": plan.describe(),
@@ -230,29 +264,47 @@ def cpu_baseline(w, x, target_s):
         r *= grow
         t = run(r)
     flops = 2.0 * r * w.N * w.K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {r} of {w.M} output rows (all {w.N} columns, K={w.K}) of the "
-                      f"same workload in fp64: {flops / 1e9:.1f} GFLOP in {t:.1f} s"}
+                      f"same workload in fp64: {flops / 1e9:.2f} GFLOP in {t:.2f} s"}
+
+
+# One compute unit's share of the bf16 / fp16 dense peak (256 CUs): the bound
+# of a one-workgroup launch such as the single 128x256 tile.
+ONE_CU_PEAK = MFMA_PEAK["bf16"] / 256
+
+
+def roofline_of(r):
+    """The roofline object of one measured workload: HBM-bound for the skinny
+    weight-streaming shape, MFMA-bound (the operand kinds' dense peak)
+    otherwise, from the launch-averaged kernel duration."""
+    w = r["workload"]
+    if w.name == "c4":
+        achieved, peak, unit, bound = r["kernel_gbs"], HBM_PEAK, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = r["kernel_tflops"], mfma_peak(w), "TFLOP/s", "mfma"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(w.name)}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # The default warm-up (400 launches, 45 ms to 0.4 s of back-to-back work
-    # depending on the workload) outlasts the chip's power-management settling
-    # after an idle start, about the first 40 ms of sustained MFMA load,
-    # during which launches run up to 20 % slower; the timed steps then see
-    # the steady clock that a continuously loaded GPU runs at.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="c2")
-    ap.add_argument("--also", default="c3,c3b,c4,c5,c6,c7,c8,c9,c10",
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="keep warming up until this many ms of back-to-back launches have passed")
+    ap.add_argument("--workload", default="c3b")
+    ap.add_argument("--also", default="c5,c1,c2,c3,c4,c6,c7,c8,c9,c10,c11,c12",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--cold-calls", type=int, default=50,
                     help="after the timed steps, time this many single calls of each workload "
                          "with the L2s and the MALL flushed before every call (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle sample length for the headline workload")
+    ap.add_argument("--cpu-seconds-also", type=float, default=2.0,
+                    help="oracle sample length for each 'also' workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the GEMM, time a plain device-to-device copy of this many "
                          "bytes (used to calibrate the HBM byte counters)")
@@ -276,40 +328,42 @@ def main():
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").random_(0, 255)
         dst = torch.empty_like(src)
-        wall, avg_ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        wall, avg_ms, _ = time_steps(lambda: dst.copy_(src), args.steps, args.warmup, args.settle_ms)
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps,
                           "avg_ms": round(avg_ms, 5),
                           "GB/s": round(2 * args.copy_bytes / (avg_ms * 1e-3) / 1e9, 1)}), flush=True)
         return
 
-    if args.workload not in wl.WORKLOADS:
-        raise SystemExit(f"unknown workload {args.workload}")
+    names = [args.workload] + [s for s in args.also.split(",") if s and s != args.workload]
+    for n in names:
+        if n not in wl.WORKLOADS:
+            raise SystemExit(f"unknown workload {n}")
     flush = make_flush() if args.cold_calls else None
-    head = measure(args.workload, args.steps, args.warmup, args.cold_calls, flush)
+    head = measure(args.workload, args.steps, args.warmup, args.cold_calls, flush, args.settle_ms)
     w = head["workload"]
-
-    hbm = w.name == "c4"
-    if hbm:
-        achieved, peak, unit = head["kernel_gbs"], HBM_PEAK, "GB/s"
-    else:
-        achieved, peak, unit = head["kernel_tflops"], mfma_peak(w), "TFLOP/s"
-    roofline = {"bound": "hbm" if hbm else "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic_for(w.name)}
+    roofline = roofline_of(head)
 
     also = {}
-    for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = measure(name, args.steps, args.warmup, args.cold_calls, flush)
+    for name in names[1:]:
+        r = measure(name, args.steps, args.warmup, args.cold_calls, flush, args.settle_ms)
         ow = r["workload"]
         entry = {"title": ow.title, "us_per_call": round(r["kernel_avg_ms"] * 1e3, 2),
                  "TFLOP/s": round(r["kernel_tflops"], 1),
                  "frac_mfma_peak": round(r["kernel_tflops"] / mfma_peak(ow), 4),
                  "GB/s_algorithmic": round(r["kernel_gbs"], 1),
-                 "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"], r["plan"]["tile_k"]]}
+                 "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"], r["plan"]["tile_k"]],
+                 "roofline": roofline_of(r),
+                 "warmup_settle": r["warmup_settle"]}
         if ow.name == "c4":
             entry["frac_hbm_peak"] = round(r["kernel_gbs"] / HBM_PEAK, 4)
+        if ow.name == "c1":
+            # one workgroup: the bound is one compute unit's share of the peak
+            entry["frac_one_cu_peak"] = round(r["kernel_tflops"] / ONE_CU_PEAK, 4)
         if "cold" in r:
             entry["caches_flushed"] = r["cold"]
+        if not args.no_cpu_baseline:
+            log(f"cpu baseline: oracle on a sample of {name} (~{args.cpu_seconds_also:.0f} s)")
+            entry["cpu_baseline"] = cpu_baseline(ow, r["inputs"], args.cpu_seconds_also)
         also[name] = entry
         del r
 
@@ -337,6 +391,7 @@ def main():
                    round(head["kernel_tflops"] / mfma_peak(w), 4)},
         "roofline": roofline,
         "kernel_avg_us": round(head["kernel_avg_ms"] * 1e3, 2),
+        "warmup_settle": head["warmup_settle"],
         "caches_flushed": head.get("cold"),
         "cpu_baseline": cpu,
         "also": also,

@@ -153,9 +153,15 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
 
 /*
  * Enqueue D = beta*D + A.B^T for a dense plan on `stream` (a hipStream_t;
- * NULL is the default stream).  A, B, D are device pointers, 16-byte aligned.
- * Returns MSWZ_OK, MSWZ_ERR_INVALID, MSWZ_ERR_ALIGN, MSWZ_ERR_KIND or
- * MSWZ_ERR_HIP.
+ * NULL is the default stream): the product of the tcgen05.mma page's
+ * "Operands and repeat axes" and "Example: four K16 issues for a 128x64x64
+ * product" (B held as (N,K), fp32 accumulation, `accum` as beta), with the
+ * operand majors of its "Shared descriptors are byte-stride contracts".
+ * A, B, D are device pointers, 16-byte aligned, in the layouts above; the
+ * caller owns them and keeps them alive until the stream passes the kernel.
+ * Returns MSWZ_OK, MSWZ_ERR_INVALID (null pointer, beta not 0 or 1),
+ * MSWZ_ERR_ALIGN, MSWZ_ERR_KIND (a block-scaled plan) or MSWZ_ERR_HIP (launch
+ * error); on any error other than MSWZ_ERR_HIP nothing was enqueued.
  */
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *D,
              int beta, void *stream);
@@ -164,30 +170,28 @@ int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *D,
  * Device workspace, in bytes, that gemm_run_ws can use for this plan: > 0 for
  * weight-streaming plans (the skinny kernel above) with N % 256 == 0 (K split
  * into S parts, each a multiple of 256: the smallest power of two up to 16
- * giving N/256 * S >= 256 workgroups, else the largest that fits): 256 bytes
- * of counters (rounded up from 4 per 256 columns) plus S * M * N * 4 bytes of
- * fp32 partials; 0 otherwise.
+ * giving N/256 * S >= 256 workgroups, else the largest that fits): S * M * N * 4
+ * bytes of fp32 partials; 0 otherwise.
  * MSWZ_ERR_INVALID for a NULL plan.
  */
 int64_t gemm_plan_workspace_size(const gemm_plan *plan);
 
 /*
  * gemm_run with a caller-provided device workspace (tcgen05.mma page,
- * "Weight-stationary and block scaling": the weight-streaming workload).  For
- * a plan with gemm_plan_workspace_size(plan) > 0 it splits K over S
- * workgroups per 256 output columns, each storing an fp32 partial in the
- * workspace, and enqueues a second kernel that sums the S partials of every
- * output in a fixed order and applies beta; results are bit-identical run to
- * run (not necessarily to gemm_run's, whose summation order differs).  For
- * other plans it is gemm_run and ignores the workspace.
+ * "Weight-stationary and block scaling": the weight-stationary workload,
+ * read here as a few rows of activations against a large weight matrix that
+ * is streamed once).  For a plan with gemm_plan_workspace_size(plan) > 0 it
+ * splits K over S workgroups per 256 output columns, each storing an fp32
+ * partial in the workspace, and enqueues a second kernel that sums the S
+ * partials of every output in a fixed order and applies beta; results are
+ * bit-identical run to run (not necessarily to gemm_run's, whose summation
+ * order differs).  For other plans it is gemm_run and ignores the workspace.
  *   workspace        device pointer, 16-byte aligned, at least
  *                    gemm_plan_workspace_size(plan) bytes; the caller owns it.
- *                    Its first 256 * ceil(N/256 * 4 / 256) bytes are counters
- *                    for the in-kernel reduction (selectable for tuning); they
- *                    must be zero before the first call (fill the whole
- *                    workspace with zero bytes once) and every call leaves
- *                    them zero again.  Two calls that may run at the same time
- *                    must not share a workspace.
+ *                    Its contents before the call do not matter (every byte
+ *                    the reduction reads is written first by the same call).
+ *                    Two calls that may run at the same time must not share
+ *                    a workspace.
  *   workspace_bytes  its size.
  * Returns as gemm_run; MSWZ_ERR_INVALID also for a NULL or too small workspace.
  */
@@ -195,9 +199,13 @@ int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *D,
                 int beta, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * Enqueue the block-scaled product for a plan created with scale_vec_len > 0.
- * SFA [M][K/V] and SFB [N][K/V] are device pointers to E8M0 bytes, 16-byte
- * aligned.  Same returns as gemm_run.
+ * Enqueue the block-scaled product for a plan created with scale_vec_len > 0
+ * (tcgen05.mma page, "Weight-stationary and block scaling": one scale vector
+ * per row of A and of B, each scale covering scale_vec_len consecutive K
+ * elements; every element is multiplied by 2^(E-127) of its block before the
+ * products are summed).  SFA [M][K/V] and SFB [N][K/V] are device pointers to
+ * E8M0 bytes, 16-byte aligned, owned by the caller.  Same returns as
+ * gemm_run, with MSWZ_ERR_KIND for a dense plan.
  */
 int gemm_run_blockscaled(const gemm_plan *plan, const void *A, const void *B,
                          const uint8_t *SFA, const uint8_t *SFB, void *D,

@@ -222,11 +222,6 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         p->variant = tile == 256 ? mswz::kVarDense256 : tile == 128 ? mswz::kVarDense128
                                                                      : mswz::kVarDense64;
     p->group_m = -4;   // 2-D XCD regions, groups of 4 tile rows (device_common.hpp)
-    if (const char *env = getenv("MSWZ_GROUP_M")) {   // tuning override
-        const int g = atoi(env);
-        if ((g >= 1 && g <= 64) || (g <= -1 && g >= -64))
-            p->group_m = g;
-    }
     mswz::variant_info(p->variant, fp8, &p->info);
     if (fp4)
         p->info.tile_k = 256;                              // K elements per 128-byte row step

@@ -172,6 +172,18 @@ __device__ __forceinline__ void lds_barrier_keep_vm()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Orders one wave's LDS accesses across its lanes: every lane's LDS writes
+// before the call are visible to every lane's LDS reads after it (and reads
+// before it are done before writes after it).  Needed where lanes of one wave
+// exchange data through LDS, since from one lane's point of view its own
+// accesses to different addresses are independent and could be reordered.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Scheduling fence: no instruction is moved across it by the compiler.
 __device__ __forceinline__ void sched_fence()
 {

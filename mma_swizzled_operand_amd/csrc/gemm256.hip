@@ -6,33 +6,13 @@
 // so that they
 // compile in parallel.
 #include <hip/hip_runtime.h>
-#include <stdlib.h>
 
 #include "kernels.hpp"
 
 namespace mswz {
 
-// Pipeline configuration of the 256x256 tile, selected at run time by the
-// environment variable MSWZ_TILE256 (tuning only): 1 = four waves (else
-// eight); 4 / 8 / 12 = K-major A / B / both staged through registers;
-// 16 = the ping-pong kernel for 16-bit K-major operands with K % 128 == 0;
-// 32 = MN-major operands through register transposes; 64 = 16x16x32 MFMAs
-// in every case; 128 = 32x32x16 MFMAs in every case.
-int config256()
-{
-    static int cfg = [] {
-        const char *e = getenv("MSWZ_TILE256");
-        return e ? atoi(e) : 0;
-    }();
-    return cfg;
-}
-
 hipError_t launch_dense256(bool bf16, bool a_mn, bool b_mn, const DenseArgs &d, hipStream_t stream)
 {
-    if (config256() == 16 && !a_mn && !b_mn && d.K % 128 == 0 && d.M % 256 == 0 && d.N % 256 == 0 &&
-        d.out == kOutF32 && d.lda == d.K && d.ldb == d.K && d.ldd == d.N && !d.opts.neg && !d.opts.sat &&
-        !d.opts.row_mask && !d.opts.col_zero)
-        return launch_dense256pp(bf16, d, stream);
     const MxArgs a{d.A, d.B, nullptr, nullptr, d.D, d.M, d.N, d.K, d.beta, d.group_m, d.out,
                    d.lda, d.ldb, d.ldd, d.opts};
     if (bf16)

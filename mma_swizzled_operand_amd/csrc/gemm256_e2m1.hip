@@ -6,8 +6,7 @@ namespace mswz {
 
 hipError_t launch256_e2m1(const MxArgs &a, hipStream_t stream)
 {
-    return a.out == kOutF32 ? launch_kind<kE2m1, false, false, 8, 8>(a, stream)
-                            : launch_out<kE2m1, false, false>(a, stream);
+    return launch_cfg<kE2m1, false, false>(a, stream);
 }
 
 }  // namespace mswz

@@ -11,7 +11,7 @@ namespace {
 template <int K>
 hipError_t launch_padded(const MxArgs &a, hipStream_t stream)
 {
-    return a.out == kOutF32 ? launch_kind<K, false, false, 8, 8>(a, stream) : launch_out<K, false, false>(a, stream);
+    return launch_cfg<K, false, false>(a, stream);
 }
 
 }  // namespace

@@ -25,7 +25,8 @@
 // Compute.  Wave w owns output rows 128*(w/4) .. +127 and columns 64*(w%4)
 // .. +63, 128 fp32 accumulators per lane: 8 x 4 blocks of 16x16x32 MFMA
 // output for 16-bit operands (4 x 2 blocks of 32x32x16 when both are
-// MN-major), 4 x 2 blocks of the 32x32x64 block-scaled MFMA for E4M3.  The
+// MN-major), 8 x 4 blocks of the scaled 16x16x128 MFMA for the block-scaled
+// kinds.  The
 // 16x16 shape moves fewer register bytes per flop than the 32x32 one; under
 // the chip's power limit it runs at a higher clock and is faster overall.
 // The MFMA's first operand is the B fragment and its second the A fragment,
@@ -33,7 +34,6 @@
 // of one M row and the epilogue stores 16 bytes per lane.
 #pragma once
 #include <hip/hip_runtime.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -107,44 +107,6 @@ struct DmaOperand {
             const uint32_t off = 16 * chunk < lim ? voff[i] + uint32_t(kt) * 128 : nbytes;
             buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, off, 0);
         }
-    }
-};
-
-// Register-staged copy of one K-major operand tile (eight waves): the 512
-// threads each load four 16-byte chunks per step into registers (thread t:
-// rows t/8 + 64i, chunk t % 8; the row in the range-checked per-lane offset,
-// as in DmaOperand) and, after the step's MFMAs, store them to the other
-// stage at row*128 + ((chunk ^ key) << 4).  Eight consecutive lanes cover one
-// 128-byte row, so each wave-wide load reads eight whole rows and each
-// wave-wide store fills 1 KiB of LDS.
-template <int W>
-struct RegOperand {
-    static constexpr int kN = 2048 / (64 * W);
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff[kN], lds0;
-    u32x4 r[kN];
-
-    __device__ void init(const uint8_t *X, int row0, int rows, uint32_t rb, int tid, uint32_t tile_off)
-    {
-        static_assert(W == 8, "register staging is built for eight waves");
-        rsrc = make_rsrc(X + size_t(row0) * rb, uint32_t(rows) * rb);
-        const int row = tid >> 3, chunk = tid & 7;
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            voff[i] = uint32_t(row + 8 * W * i) * rb + chunk * 16;
-        lds0 = tile_off + tile_offset(row, chunk);   // key(row + 64i) == key(row): period 64
-    }
-    __device__ void load(int kt)
-    {
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            r[i] = buffer_load16(rsrc, voff[i], uint32_t(kt) * 128);
-    }
-    __device__ void store(uint8_t *stage) const
-    {
-#pragma unroll
-        for (int i = 0; i < kN; ++i)
-            lds_write16(stage, lds0 + i * 8 * W * kTileRowBytes, r[i]);
     }
 };
 
@@ -363,54 +325,6 @@ __device__ __forceinline__ uint32_t mn_frag_base16(uint32_t tile_off, int rbase,
     return tile_off + uint32_t(8 * kblk16(g) + j) * kMnRowBytes + (uint32_t(chunk) << 4) + 8 * (a & 1);
 }
 
-// Register-staged copy of one MN-major 16-bit operand ([K][R] storage, R = M
-// or N) for a 256-row tile: block `blk` (0..255) is tile rows 8*(blk % 32)
-// .. +7 and K rows 8*(blk / 32) .. +7 of the step; the active thread loads
-// its eight 16-byte K-row pieces, transposes the 8x8 block in registers and
-// stores eight K-contiguous 16-byte chunks.
-struct MnOperand {
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t voff, kstride, lds_base;
-    int mb, kc;
-    bool active;
-    u32x4 r[8];
-
-    __device__ void init(const uint8_t *X, int R, int ld, int row0, int K, int blk, bool act,
-                         uint32_t tile_off)
-    {
-        active = act;
-        mb = blk & 31;
-        kc = (blk >> 5) & 7;
-        kstride = uint32_t(ld) * 2;
-        rsrc = make_rsrc(X + size_t(row0) * 2, uint32_t(K - 1) * kstride + uint32_t(R - row0) * 2);
-        // columns beyond the operand (tail tile): fetch the tile's first columns
-        // instead, as in DmaMnOperand
-        voff = uint32_t(8 * kc) * kstride + 16 * (row0 + 8 * mb < R ? mb : 0);
-        lds_base = tile_off;
-    }
-    __device__ void load(int kt)
-    {
-        if (active) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r[j] = buffer_load16(rsrc, voff, (uint32_t(kt) * 64 + j) * kstride);
-        }
-    }
-    __device__ void store(uint8_t *stage) const
-    {
-        if (active) {
-            u32x4 t[8];
-            transpose8x8_b16(r, t);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                lds_write16(stage, lds_base + tile_offset(8 * mb + i, kc), t[i]);
-        }
-    }
-};
-
-// W waves per workgroup: W = 8 gives each wave a 128 x 64 output sub-tile
-// (two waves per SIMD), W = 4 a 128 x 128 sub-tile (one wave per SIMD,
-// accumulators in AGPRs, a third fewer LDS bytes read per MFMA).
 // Four consecutive outputs of one row of D, as fp32 or rounded to nearest
 // even into bf16 / fp16 (OUT, see OutKind); with BETA the old values, read in
 // the same kind, are added first.
@@ -484,10 +398,15 @@ __device__ __forceinline__ bool apply_opts(const EpiOpts &o, int m, int n, f32x4
     return true;
 }
 
+// Eight waves per workgroup, each owning a 128 x 64 output sub-tile (two
+// waves per SIMD).
+constexpr int W = 8;
+
 // KIND: element kind of A (and of B unless KB >= 0); KB: B's kind when it
 // differs (block-scaled E4M3 / E2M3 / E3M2 / padded E2M1 only); SV: K
-// elements per scale byte (32, or 16 for E2M1 and the padded kinds).
-template <int KIND, bool A_MN, bool B_MN, bool BETA, int W, int REG, int OUT = kOutF32, int KB = -1, int SV = 32>
+// elements per scale byte (32, or 16 for E2M1 and the padded kinds); MF16:
+// 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major).
+template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -495,8 +414,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                int tiles_n, int group_m, EpiOpts opts)
 {
     static_assert(!((A_MN || B_MN) && KIND != kBf16 && KIND != kF16), "MN-major operands are built for 16-bit only");
-    static_assert(W == 4 || W == 8, "4 or 8 waves");
-    constexpr int TM = 4, TN = W == 8 ? 2 : 4;   // 32x32 blocks per wave along M and N
+    constexpr int TM = 4, TN = 2;                // 32x32 blocks per wave along M and N
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
     constexpr int kKindB = KB < 0 ? KIND : KB;
     constexpr bool kMixed = kKindB != KIND;
@@ -510,9 +428,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // E4M3 and padded 6-bit operands share the byte layout (128 values per
     // 128-byte row step) and the split-row fragments
     constexpr bool kByteRows = kFp8 || kFp6;
-    static_assert(!kFp4 || ((REG & 8) != 0 && W == 8), "FP4 is built for the eight-wave 16x16 path");
-    static_assert(!kFp6 || ((REG & 8) != 0 && W == 8), "padded 6- and 4-bit kinds are built for the eight-wave 16x16 path");
-    static_assert(!kMixed || ((REG & 8) != 0 && W == 8), "mixed kinds are built for the eight-wave 16x16 path");
+    static_assert(!kMx || MF16, "block-scaled kinds are built for the 16x16 MFMA");
     // 16-element scale blocks: a lane's 32 values of a 32-block are two
     // 16-element halves (one 16-byte chunk of a padded kind, or the two 8-byte
     // halves of a dense E2M1 chunk), so each 16x16 block takes two MFMAs, each
@@ -546,36 +462,21 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const int rows_a = min(kBM, M - m0), rows_b = min(kBN, N - n0);
 
     // ---- operand copies ---------------------------------------------------------
-    // K-major operands: copied straight into LDS, or through registers when
-    // REG bit 0 (A) / bit 1 (B) is set.  MN-major operands: copied straight
-    // into an MN-major LDS tile and read with transposing LDS reads, or, when
-    // REG bit 2 is set, 8x8 register transposes into the K-contiguous layout
-    // (A by threads 0..255 and B by threads 256..511 with eight waves, both
-    // by every thread with four).
-    constexpr bool kRegA = (REG & 1) && !A_MN, kRegB = (REG & 2) && !B_MN;
-    constexpr bool kDmaA = !A_MN && !kRegA, kDmaB = !B_MN && !kRegB;
-    constexpr bool kMnReg = (REG & 4) != 0;
-    constexpr bool kTrA = A_MN && !kMnReg, kTrB = B_MN && !kMnReg;
+    // K-major operands are copied straight into the K-major LDS tile;
+    // MN-major operands straight into an MN-major LDS tile, read back with
+    // transposing LDS reads.
+    constexpr bool kDmaA = !A_MN, kDmaB = !B_MN;
+    constexpr bool kTrA = A_MN, kTrB = B_MN;
     DmaOperand<W> da, db;
     if constexpr (kDmaA)
         da.init(A, m0, rows_a, a_row_bytes, wave, lane, 0);
     if constexpr (kDmaB)
         db.init(B, n0, rows_b, b_row_bytes, wave, lane, kATile);
-    RegOperand<W> rga, rgb;
-    if constexpr (kRegA)
-        rga.init(A, m0, rows_a, a_row_bytes, tid, 0);
-    if constexpr (kRegB)
-        rgb.init(B, n0, rows_b, b_row_bytes, tid, kATile);
     DmaMnOperand<W> dma_mna, dma_mnb;
     if constexpr (kTrA)
         dma_mna.init(A, M, lda, m0, K, wave, lane, 0);
     if constexpr (kTrB)
         dma_mnb.init(B, N, ldb, n0, K, wave, lane, kATile);
-    MnOperand mna, mnb;
-    if constexpr (A_MN && kMnReg)
-        mna.init(A, M, lda, m0, K, tid & 255, W == 4 || tid < 256, 0);
-    if constexpr (B_MN && kMnReg)
-        mnb.init(B, N, ldb, n0, K, tid & 255, W == 4 || (A_MN ? tid >= 256 : tid < 256), kATile);
 
     // ---- scale copies (MX): 64-row group g = 0..7 (A rows for g < 4, B rows
     // for g >= 4) is copied by wave g % W.  Per K step (kScaleGroups false):
@@ -588,7 +489,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kByteRows && (REG & 8) != 0 && W == 8 && !kV16;   // the 16x16 E4M3 / FP6 path
+    constexpr bool kScaleGroups = kByteRows && !kV16;   // E4M3 and the padded kinds, 32-element blocks
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / SV;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -605,32 +506,13 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
 
-    auto store_regs = [&](uint8_t *stage) {
-        if constexpr (A_MN && kMnReg)
-            mna.store(stage);
-        if constexpr (B_MN && kMnReg)
-            mnb.store(stage);
-        if constexpr (kRegA)
-            rga.store(stage);
-        if constexpr (kRegB)
-            rgb.store(stage);
-    };
-
     auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
-        if constexpr (A_MN && kMnReg)
-            mna.load(kt);
-        if constexpr (kRegA)
-            rga.load(kt);
         if constexpr (kDmaA)
             da.issue(stage, kt);
         if constexpr (kTrA)
             dma_mna.issue(stage, kt);
-        if constexpr (B_MN && kMnReg)
-            mnb.load(kt);
         if constexpr (kTrB)
             dma_mnb.issue(stage, kt);
-        if constexpr (kRegB)
-            rgb.load(kt);
         if constexpr (kDmaB)
             db.issue(stage, kt);
         if constexpr (kMx) {
@@ -681,11 +563,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                         : kATile + row * kTileRowBytes + ((lh ^ tile_key(row)) << 4);
     }
 
-    // 16x16 MFMAs (REG bit 3): the same wave tile as 2TM x 2TN blocks of
+    // 16x16 MFMAs (MF16): the same wave tile as 2TM x 2TN blocks of
     // 16 x 16.  16-bit: fragment rows l % 16, 16-byte chunk 4s + kblk16(l/16)
     // for the 32-wide sub-step s, i.e. base XOR (s << 6).  E4M3: one 16x16x128
     // MFMA per K step, chunks mx_chunk16(l/16) and that + 4 (base XOR 64).
-    constexpr bool kMf16 = (REG & 8) != 0;
+    constexpr bool kMf16 = MF16;
     // Epilogue through LDS with non-temporal 256-byte row pieces (see the
     // epilogue), except where it made the compiler spill inside the main loop
     // (it shares the register allocation): dense E2M1 with 16-element scale
@@ -767,50 +649,6 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
                     acc[j][i] = mfma_32x32x16<KIND == kBf16>(bf[ks & 1][j], af[ks & 1][i], acc[j][i]);
-        }
-    };
-
-    auto compute_mx = [&](const uint8_t *s, const uint8_t *ss) {
-        uint32_t ab[TM], bb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            ab[i] = opaque(abase[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bb[j] = opaque(bbase[j]);
-        // lane half lh supplies the scale of K block lh of its row: byte lh (sub-step 0)
-        // and byte 2 + lh (sub-step 1) of the row's scale word
-        uint32_t sa[TM], sb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            sa[i] = *reinterpret_cast<const uint32_t *>(ss + 4 * (wm + 32 * i + lr)) >> (8 * lh);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            sb[j] = *reinterpret_cast<const uint32_t *>(ss + kBM * 4 + 4 * (wn + 32 * j + lr)) >> (8 * lh);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            i32x8 af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const u32x4 lo = lds_read16(s, ab[i] ^ (ks << 6));
-                const u32x4 hi = lds_read16(s, ab[i] ^ (ks << 6) ^ 32u);
-                af[i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const u32x4 lo = lds_read16(s, bb[j] ^ (ks << 6));
-                const u32x4 hi = lds_read16(s, bb[j] ^ (ks << 6) ^ 32u);
-                bf[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    if (ks == 0)
-                        acc[j][i] = mfma_scale_32x32x64_e4m3<0>(bf[j], af[i], acc[j][i], sb[j], sa[i]);
-                    else
-                        acc[j][i] = mfma_scale_32x32x64_e4m3<2>(bf[j], af[i], acc[j][i], sb[j], sa[i]);
-                }
         }
     };
 
@@ -1055,10 +893,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             compute_fp4(s, ss);
         else if constexpr (kFp6 && kV16)
             compute_pad16(s, ss);
-        else if constexpr (kMx && kMf16)
-            compute_mx16(s, ss, 4, 0);
         else if constexpr (kMx)
-            compute_mx(s, ss);
+            compute_mx16(s, ss, 4, 0);
         else if constexpr (kMf16)
             compute16x16(s);
         else
@@ -1133,18 +969,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
     if (KT > 0) {
     issue_step(lds0, scl0, 0);
-    store_regs(lds0);
     __syncthreads();
 
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
         issue_step(lds1, scl1, kt + 1);
         compute(lds0, scl0);
-        store_regs(lds1);
         lds_barrier_keep_vm<0>();
         issue_step(lds0, scl0, min(kt + 2, KT - 1));
         compute(lds1, scl1);
-        store_regs(lds0);
         lds_barrier_keep_vm<0>();
     }
     if (kt < KT)
@@ -1155,7 +988,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // the host launches no other configuration for it): one more step after
     // the loop whose K values beyond K are copied as zeros into both
     // operands, so they add nothing.
-    if constexpr (!kMx && !kRegA && !kRegB && !kMnReg) {
+    if constexpr (!kMx) {
         if (K % kStepK) {
             lds_barrier_keep_vm<0>();   // every copy landed, every wave done reading lds0
             const uint32_t lim = uint32_t(K % kStepK) * 2;   // bytes of each K-major row slice inside K
@@ -1184,9 +1017,10 @@ epilogue:
         // 32-row area (waves 0-3 in lds0, 4-7 in lds1; rows 272 bytes apart,
         // so the 16 rows of a fragment write fall on distinct banks), reads
         // it back as 4 rows x 256 bytes per instruction and stores those
-        // non-temporally.  One wave's writes and reads are ordered by the
-        // LDS itself; the barrier keeps the last K step's reads of the
-        // stages before the first write.
+        // non-temporally.  The lanes of one wave exchange values through
+        // its area, so each quarter's writes and reads are separated by a
+        // wave-level LDS fence (wave_lds_sync); the workgroup barrier keeps
+        // the last K step's reads of the stages before the first write.
         constexpr uint32_t kPitch = 272;
         __syncthreads();
         uint8_t *area = (wave < 4 ? lds0 : lds1) + (wave & 3) * 32 * kPitch;
@@ -1202,10 +1036,16 @@ epilogue:
                     const int c = row16<kByteRows>(j, 4 * (lane >> 4));        // 0 .. 63
                     *reinterpret_cast<f32x4 *>(area + r * kPitch + c * 4) = acc4[j][i];
                 }
+            wave_lds_sync();
+            f32x4 vals[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                vals[k] = *reinterpret_cast<const f32x4 *>(area + (4 * k + rd_row) * kPitch + rd_col * 4);
+            wave_lds_sync();   // the next quarter's writes come after these reads
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int r = 4 * k + rd_row;
-                f32x4 v = *reinterpret_cast<const f32x4 *>(area + r * kPitch + rd_col * 4);
+                f32x4 v = vals[k];
                 const int m = m0 + wm + 32 * q + r, n = n0 + wn + rd_col;
                 if (m >= M || n >= N)
                     continue;
@@ -1256,53 +1096,36 @@ epilogue:
         }
 }
 
-template <int KIND, bool A_MN, bool B_MN, int W, int REG, int OUT = kOutF32, int KB = -1, int SV = 32>
+// 16x16 MFMAs for every operand kind, except 16-bit operands that are both
+// MN-major, which take 32x32x16 (their 16x16 fragment reads would need more
+// than 256 VGPRs).
+template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
+    constexpr bool kMf16 = !(A_MN && B_MN);
     const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
     const int blocks = tiles_m * tiles_n;
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, W, REG, OUT, KB, SV>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV>), dim3(blocks), dim3(64 * W),
+                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, W, REG, OUT, KB, SV>), dim3(blocks), dim3(64 * W), 0,
-                           stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV>), dim3(blocks), dim3(64 * W),
+                           0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
 }
 
-// bf16 / fp16 output: the default pipeline only
+// D's element kind chosen at run time
 template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32>
-hipError_t launch_out(const MxArgs &a, hipStream_t stream)
-{
-    constexpr int kReg = (A_MN && B_MN) ? 0 : 8;
-    return a.out == kOutBf16 ? launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutBf16, KB, SV>(a, stream)
-                             : launch_kind<KIND, A_MN, B_MN, 8, kReg, kOutF16, KB, SV>(a, stream);
-}
-
-
-template <int KIND, bool A_MN, bool B_MN>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
-    if (a.out != kOutF32)
-        return launch_out<KIND, A_MN, B_MN>(a, stream);
-    // a K that is not a multiple of the step takes the default pipeline
-    if ((KIND == kBf16 || KIND == kF16) && a.K % 64 != 0)
-        return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
-    switch (config256()) {
-    case 1: return launch_kind<KIND, A_MN, B_MN, 4, 0>(a, stream);
-    case 4: return launch_kind<KIND, A_MN, B_MN, 8, 1>(a, stream);
-    case 8: return launch_kind<KIND, A_MN, B_MN, 8, 2>(a, stream);
-    case 12: return launch_kind<KIND, A_MN, B_MN, 8, 3>(a, stream);
-    case 32: return launch_kind<KIND, A_MN, B_MN, 8, 4>(a, stream);
-    case 64: return launch_kind<KIND, A_MN, B_MN, 8, 8>(a, stream);
-    case 128: return launch_kind<KIND, A_MN, B_MN, 8, 0>(a, stream);
-    // 16x16x32 MFMAs for 16-bit operands, except with both operands MN-major,
-    // where they would need more than 256 VGPRs
-    default: return launch_kind<KIND, A_MN, B_MN, 8, (A_MN && B_MN) ? 0 : 8>(a, stream);
+    switch (a.out) {
+    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV>(a, stream);
+    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV>(a, stream);
+    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV>(a, stream);
     }
 }
 

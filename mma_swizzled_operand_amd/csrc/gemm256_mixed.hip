@@ -9,8 +9,7 @@ namespace {
 template <int KA, int KB>
 hipError_t launch_pair(const MxArgs &a, hipStream_t stream)
 {
-    return a.out == kOutF32 ? launch_kind<KA, false, false, 8, 8, kOutF32, KB>(a, stream)
-                            : launch_out<KA, false, false, KB>(a, stream);
+    return launch_cfg<KA, false, false, KB>(a, stream);
 }
 
 template <int KA>

@@ -10,8 +10,7 @@ namespace {
 template <int K>
 hipError_t launch16(const MxArgs &a, hipStream_t stream)
 {
-    return a.out == kOutF32 ? launch_kind<K, false, false, 8, 8, kOutF32, -1, 16>(a, stream)
-                            : launch_out<K, false, false, -1, 16>(a, stream);
+    return launch_cfg<K, false, false, -1, 16>(a, stream);
 }
 
 }  // namespace

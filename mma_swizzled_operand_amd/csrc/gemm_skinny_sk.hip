@@ -29,23 +29,15 @@
 // land in LDS as zeros without a memory access; only rows below M are
 // stored (partials and D).
 //
-// Reduction (deterministic, no waiting), two ways:
-//   * default: each workgroup stores its 64 x 256 fp32 partial into the
-//     caller's workspace; a second kernel (splitk_reduce_kernel) sums the S
-//     partials of every output in part order 0 .. S-1 and adds beta*D;
-//   * inline (selectable): after storing its partial, each workgroup
-//     increments its column block's counter (agent-scope release); the one
-//     that sees the count S-1 is the last: it acquires, sums the S partials
-//     in part order (its own from registers), adds beta*D, writes D and
-//     resets the counter, so the counters are zero again after every call.
-// Both give the same bits.  All workgroups finish streaming at about the same
-// time, so the inline reduction's store acknowledgements, L2 write-backs,
-// atomic round trip and partial reads form an exposed tail of ~16 us on
-// 64 x 16384 x 8192, against ~6 us for the second kernel (including its
-// launch): the second kernel is the default.
+// Reduction (deterministic, no waiting): each workgroup stores its 64 x 256
+// fp32 partial into the caller's workspace; a second kernel
+// (splitk_reduce_kernel) sums the S partials of every output in part order
+// 0 .. S-1 and adds beta*D.  (An in-kernel reduction by the last workgroup of
+// each column block, behind a counter, was measured: all workgroups finish
+// streaming at about the same time, so its store acknowledgements, L2
+// write-backs, atomic round trip and partial reads formed an exposed tail of
+// ~16 us on 64 x 16384 x 8192, against ~6 us for the second kernel.)
 #include <hip/hip_runtime.h>
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -63,18 +55,17 @@ constexpr int kStageBytes = kBM * 128;
 
 __device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 
-// INLINE: reduce inside the kernel (counters, last workgroup); otherwise only
-// store the partials, which splitk_reduce_kernel then sums.
-template <bool BF16, bool BETA, bool INLINE>
+// The column-split streaming kernel: stores the workgroup's partial, which
+// splitk_reduce_kernel then sums with the others.
+template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
-gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, float *__restrict__ D,
-                      float *__restrict__ part_ws, uint32_t *__restrict__ counters, int M, int N, int K, int S)
+gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                      float *__restrict__ part_ws, int M, int N, int K, int S)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
-    __shared__ uint32_t last_flag;
     static_assert(kSlots == 4, "one named LDS array per stage");
     auto stage = [&](int u) { return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3; };
 
@@ -186,58 +177,6 @@ gemm_skinny_sk_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
             const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
             *reinterpret_cast<f32x4 *>(mine + idx) = acc[jb][i];
         }
-    if constexpr (!INLINE)
-        return;
-    // every wave's stores are complete before the barrier; thread 0's
-    // agent-scope release then publishes them with the count.  Only the last
-    // workgroup acquires: an acquire invalidates the XCD's L2, which would
-    // cost the workgroups still streaming their cached A and half-read B lines.
-    lds_barrier_keep_vm<0>();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&counters[cb], 1u, __ATOMIC_RELEASE,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = old == uint32_t(S - 1);
-    }
-    __syncthreads();
-    if (!last_flag)
-        return;
-
-    // ---- last workgroup of the column block: fixed-order sum of the S partials
-    // (part by part, the eight loads of one part in flight together)
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    f32x4 sum[2][4];
-    for (int p = 0; p < S; ++p) {
-        f32x4 v[2][4];
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
-                v[jb][i] = p == part || 16 * i + r16 >= M
-                               ? acc[jb][i]
-                               : *reinterpret_cast<const f32x4 *>(part_ws + size_t(p) * MN + idx);
-            }
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sum[jb][i] = p == 0 ? v[jb][i] : sum[jb][i] + v[jb][i];
-    }
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (16 * i + r16 >= M)
-                continue;
-            const size_t idx = size_t(16 * i + r16) * N + n0 + 32 * wave + 16 * jb + 4 * g;
-            f32x4 *dp = reinterpret_cast<f32x4 *>(D + idx);
-            f32x4 out = sum[jb][i];
-            if constexpr (BETA)
-                out += *dp;
-            *dp = out;
-        }
-    if (tid == 0)
-        __hip_atomic_store(&counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // K-sliced variant, used where a part holds 8 x KS K elements (KS = 128 or
@@ -391,30 +330,6 @@ splitk_reduce_kernel(const float *__restrict__ part_ws, float *__restrict__ D, i
     __builtin_nontemporal_store(sum, d);
 }
 
-// Reduction mode, selected at run time by the environment variable
-// MSWZ_SPLITK_REDUCE (tuning only): "inline" = in the streaming kernel
-// (counters), anything else = a second kernel.
-bool reduce_inline()
-{
-    static const bool v = [] {
-        const char *e = getenv("MSWZ_SPLITK_REDUCE");
-        return e && e[0] == 'i';
-    }();
-    return v;
-}
-
-// Streaming kernel, selected at run time by MSWZ_SPLITK_KERNEL (tuning only):
-// "cols" = the column-split kernel everywhere; otherwise the K-sliced kernel
-// wherever a part holds 1024 or 2048 K elements.
-bool kslice_allowed()
-{
-    static const bool v = [] {
-        const char *e = getenv("MSWZ_SPLITK_KERNEL");
-        return !(e && e[0] == 'c');
-    }();
-    return v;
-}
-
 template <bool BF16, int MT>
 void launch_ks(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
 {
@@ -429,6 +344,8 @@ void launch_ks(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
                            sk.partials, a.M, a.N, a.K);
 }
 
+// The K-sliced kernel wherever a part holds 2048 or 1024 K elements, the
+// column-split kernel elsewhere; then the reduction.
 template <bool BF16, bool BETA>
 hipError_t launch_bb(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
 {
@@ -436,20 +353,16 @@ hipError_t launch_bb(const DenseArgs &a, const SplitK &sk, hipStream_t stream)
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     const dim3 grid(a.N / kBN * sk.parts);
     const int kpart = a.K / sk.parts;
-    if (!reduce_inline() && kslice_allowed() && (kpart == 8 * 256 || kpart == 8 * 128)) {
+    if (kpart == 8 * 256 || kpart == 8 * 128) {
         if (a.M <= 16)
             launch_ks<BF16, 1>(a, sk, stream);
         else if (a.M <= 32)
             launch_ks<BF16, 2>(a, sk, stream);
         else
             launch_ks<BF16, 4>(a, sk, stream);
-    } else if (reduce_inline()) {
-        hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, true>), grid, dim3(kThreads), 0, stream, A, B,
-                           a.D, sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
-        return hipGetLastError();
     } else {
-        hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16, BETA, false>), grid, dim3(kThreads), 0, stream, A, B,
-                           a.D, sk.partials, sk.counters, a.M, a.N, a.K, sk.parts);
+        hipLaunchKernelGGL((gemm_skinny_sk_kernel<BF16>), grid, dim3(kThreads), 0, stream, A, B, sk.partials,
+                           a.M, a.N, a.K, sk.parts);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -489,9 +402,7 @@ int skinny_split_parts(int64_t M, int64_t N, int64_t K)
 
 int64_t skinny_split_workspace_bytes(int64_t M, int64_t N, int parts)
 {
-    // counters (one per 256-column block) first, padded to 256 bytes, then the partials
-    const int64_t counter_bytes = ((N / kBN) * 4 + 255) / 256 * 256;
-    return counter_bytes + int64_t(parts) * M * N * 4;
+    return int64_t(parts) * M * N * 4;   // the fp32 partials
 }
 
 hipError_t launch_skinny_split(bool bf16, const DenseArgs &a, void *workspace, hipStream_t stream)
@@ -500,9 +411,7 @@ hipError_t launch_skinny_split(bool bf16, const DenseArgs &a, void *workspace, h
     sk.parts = skinny_split_parts(a.M, a.N, a.K);
     if (!sk.parts)
         return hipErrorInvalidValue;
-    const int64_t counter_bytes = ((a.N / kBN) * 4 + 255) / 256 * 256;
-    sk.counters = static_cast<uint32_t *>(workspace);
-    sk.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + counter_bytes);
+    sk.partials = static_cast<float *>(workspace);
     return bf16 ? launch_bf<true>(a, sk, stream) : launch_bf<false>(a, sk, stream);
 }
 

@@ -84,8 +84,6 @@ hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
 hipError_t launch256_v16(const MxArgs &args, MxKind kind, hipStream_t stream);
-hipError_t launch_dense256pp(bool bf16, const DenseArgs &args, hipStream_t stream);
-int config256();
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);
 hipError_t launch_skinny(bool bf16, const DenseArgs &args, hipStream_t stream);
 
@@ -94,7 +92,6 @@ hipError_t launch_skinny(bool bf16, const DenseArgs &args, hipStream_t stream);
 // apply), the workspace it needs, and the launch on a caller's workspace.
 struct SplitK {
     int parts;
-    uint32_t *counters;   // one per 256-column block, zero between calls
     float *partials;      // parts x M x N fp32
 };
 int skinny_split_parts(int64_t M, int64_t N, int64_t K);

@@ -24,7 +24,11 @@ The quarter-integer variant (the tcgen05.mma page's example test draws
 integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
 recipe and sets every scale byte to 127, so every product and partial sum is
 exact in fp32; for e2m1, which has no 0.25 or 0.75, it draws integers in
-[-2, 2] divided by 2 instead.
+[-2, 2] divided by 2 instead.  The "quarter_scaled" variant draws the same
+values but keeps random scale bytes, 127 + u with u uniform in [-2, 2]: each
+scaled product is then a multiple of 2^-8 of magnitude at most 16, so for
+K <= 4096 every partial sum is a multiple of 2^-8 of magnitude at most 2^16,
+i.e. an integer multiple of 2^-8 below 2^24 units, and still exact in fp32.
 """
 from __future__ import annotations
 
@@ -100,6 +104,12 @@ WORKLOADS = {
                     8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m1p"),
     "c3b": Workload("c3b", "square dense 8192^3 bf16, A and B K-major, N(0,1)",
                     8192, 8192, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    # the remaining operand layouts at the square size
+    "c11": Workload("c11", "8192^3 bf16, A K-major [M,K], B MN-major [K,N], N(0,1)",
+                    8192, 8192, 8192, "bf16", b_major="mn", a_dist=("normal", 1.0), b_dist=("normal", 1.0)),
+    "c12": Workload("c12", "8192^3 bf16, A MN-major [K,M], B MN-major [K,N], N(0,1)",
+                    8192, 8192, 8192, "bf16", a_major="mn", b_major="mn", a_dist=("normal", 1.0),
+                    b_dist=("normal", 1.0)),
 }
 
 
@@ -248,15 +258,19 @@ def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
     """Stored inputs of workload ``w`` (numpy arrays, raw bit patterns).
 
     values = "config": the config's distributions; "quarter": quarter-integer
-    operands in [-1, 1] with unit scales (exact in fp32 in any summation order).
+    operands in [-1, 1] with unit scales (exact in fp32 in any summation order);
+    "quarter_scaled": the same operands with scale bytes 127 + u, u uniform in
+    [-2, 2] (still exact for K <= 4096).
     """
-    if values not in ("config", "quarter"):
+    if values not in ("config", "quarter", "quarter_scaled"):
         raise ValueError(values)
+    if values == "quarter_scaled" and w.K > 4096:
+        raise ValueError("quarter_scaled inputs are exact in fp32 only for K <= 4096")
     rng = np.random.default_rng(seed)
     shapes = value_shapes(w)
     out = {}
     for name, dist, kind in (("A", w.a_dist, w.kind), ("B", w.b_dist, w.kind_b)):
-        x = _quarter(rng, shapes[name], kind) if values == "quarter" else _draw(rng, dist, shapes[name])
+        x = _quarter(rng, shapes[name], kind) if values != "config" else _draw(rng, dist, shapes[name])
         out[name] = to_stored(x, kind)
     if w.beta:
         out["D0"] = rng.uniform(-1.0, 1.0, shapes["D0"]).astype(np.float32)
@@ -265,6 +279,8 @@ def generate(w: Workload, seed: int = 0, values: str = "config") -> dict:
             u = rng.integers(-4, 5, shapes[name])
             if values == "quarter":
                 u = np.zeros_like(u)
+            elif values == "quarter_scaled":
+                u = rng.integers(-2, 3, shapes[name])
             out[name] = (127 + u).astype(np.uint8)
     return out
 
