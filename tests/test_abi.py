@@ -239,13 +239,13 @@ def test_run_opts_rejections_before_gpu_work():
 def test_workspace_size_query():
     lib = mswz.load()
     assert lib.gemm_plan_workspace_size(None) == -1
-    # weight streaming 64 x 16384 x 8192: 64 column blocks x 4 K parts; 256 bytes
-    # of counters, then 4 fp32 partials of 64 x 16384
-    assert mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16").workspace_bytes() == 256 + 4 * 64 * 16384 * 4
-    assert mswz.gemm_plan_create(64, 2048, 4096, "f16", "f16").workspace_bytes() == 256 + 16 * 64 * 2048 * 4
-    assert mswz.gemm_plan_create(32, 16384, 8192, "bf16", "bf16").workspace_bytes() == 256 + 4 * 32 * 16384 * 4
-    assert mswz.gemm_plan_create(1, 4096, 4096, "bf16", "bf16").workspace_bytes() == 256 + 16 * 1 * 4096 * 4
-    assert mswz.gemm_plan_create(17, 16384, 8192, "f16", "f16").workspace_bytes() == 256 + 4 * 17 * 16384 * 4
+    # weight streaming 64 x 16384 x 8192: 64 column blocks x 4 K parts, so 4
+    # fp32 partials of 64 x 16384
+    assert mswz.gemm_plan_create(64, 16384, 8192, "bf16", "bf16").workspace_bytes() == 4 * 64 * 16384 * 4
+    assert mswz.gemm_plan_create(64, 2048, 4096, "f16", "f16").workspace_bytes() == 16 * 64 * 2048 * 4
+    assert mswz.gemm_plan_create(32, 16384, 8192, "bf16", "bf16").workspace_bytes() == 4 * 32 * 16384 * 4
+    assert mswz.gemm_plan_create(1, 4096, 4096, "bf16", "bf16").workspace_bytes() == 16 * 1 * 4096 * 4
+    assert mswz.gemm_plan_create(17, 16384, 8192, "f16", "f16").workspace_bytes() == 4 * 17 * 16384 * 4
     assert mswz.gemm_plan_create(48, 1024 + 64, 8192, "bf16", "bf16").workspace_bytes() == 0   # N % 256
     assert mswz.gemm_plan_create(65, 16384, 8192, "bf16", "bf16").workspace_bytes() == 0       # M > 64
     assert mswz.gemm_plan_create(4096, 4096, 4096, "bf16", "bf16").workspace_bytes() == 0
@@ -368,3 +368,4 @@ def test_plan_create_ld_chooses_the_256_tile():
     assert (p.a_rows, p.a_cols, p.lda) == (128, 256, 264)
     assert (p.b_rows, p.b_cols, p.ldb) == (512, 128, 128)
     assert p.ldd == 512
+
