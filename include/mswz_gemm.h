@@ -68,7 +68,8 @@ typedef enum {
     MSWZ_ERR_UNSUPPORTED = -2,  /* valid request this library has no kernel for (shape not a tile multiple, dtype/major combination) */
     MSWZ_ERR_ALIGN = -3,        /* pointer not 16-byte aligned */
     MSWZ_ERR_HIP = -4,          /* the HIP runtime reported an error on launch */
-    MSWZ_ERR_KIND = -5          /* dense plan passed to gemm_run_blockscaled or the reverse */
+    MSWZ_ERR_KIND = -5,         /* dense plan passed to gemm_run_blockscaled or the reverse */
+    MSWZ_ERR_SCRATCH = -6       /* gemm_run_ws_noalloc: the plan needs more than the library's scratch */
 } mswz_status;
 
 typedef enum {
@@ -197,6 +198,28 @@ int64_t gemm_plan_workspace_size(const gemm_plan *plan);
  */
 int gemm_run_ws(const gemm_plan *plan, const void *A, const void *B, void *D,
                 int beta, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * gemm_run_ws for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results as gemm_run_ws, bit for bit, with the fp32
+ * partials in a scratch array the library owns, gemm_noalloc_scratch_bytes()
+ * bytes (16 MiB, enough for the 64 x 16384 x 8192 weight-streaming shape) per
+ * GPU, held until the process ends.  It calls no hipMalloc, hipFree or other
+ * allocating routine; the first call on a device looks the array's device
+ * address up (hipGetSymbolAddress) with that device current, so `stream` must
+ * belong to the current device.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must not be issued.  Plans without a split path run as
+ * gemm_run and use no scratch.
+ * Returns as gemm_run_ws, and MSWZ_ERR_SCRATCH (before any GPU work) when
+ * gemm_plan_workspace_size(plan) exceeds the scratch size.
+ */
+int gemm_run_ws_noalloc(const gemm_plan *plan, const void *A, const void *B, void *D,
+                        int beta, void *stream);
+
+/* Bytes of the scratch array gemm_run_ws_noalloc uses per GPU. */
+int64_t gemm_noalloc_scratch_bytes(void);
 
 /*
  * Enqueue the block-scaled product for a plan created with scale_vec_len > 0

@@ -24,13 +24,13 @@ from . import _build
 
 __all__ = [
     "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_plan_create_ld", "gemm_run",
-    "gemm_run_blockscaled", "gemm_run_opts", "GemmOpts", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
+    "gemm_run_blockscaled", "gemm_run_opts", "gemm_run_ws", "gemm_run_ws_noalloc", "gemm_noalloc_scratch_bytes", "GemmOpts", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
     "desc_address", "desc_check", "tile_offset", "library_path", "load",
 ]
 
 DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7, "e2m1p": 8}
 MAJORS = {"k": 0, "mn": 1}
-STATUS = {"ok": 0, "invalid": -1, "unsupported": -2, "align": -3, "hip": -4, "kind": -5}
+STATUS = {"ok": 0, "invalid": -1, "unsupported": -2, "align": -3, "hip": -4, "kind": -5, "scratch": -6}
 # bytes per element (the padded 6- and 4-bit kinds: sixteen per 16-byte block, padding included)
 _ITEMSIZE = {"f16": 2, "bf16": 2, "e4m3": 1, "f32": 4, "e2m1": 0.5, "e2m3": 1, "e3m2": 1, "e2m1p": 1}
 _DESCRIBE_KEYS = ("variant", "tile_m", "tile_n", "tile_k", "threads", "blocks", "lds_bytes", "group_m")
@@ -78,6 +78,10 @@ def load():
         h.gemm_plan_workspace_size.restype = i64
         h.gemm_run_ws.argtypes = [vp, vp, vp, vp, c_int, vp, i64, vp]
         h.gemm_run_ws.restype = c_int
+        h.gemm_run_ws_noalloc.argtypes = [vp, vp, vp, vp, c_int, vp]
+        h.gemm_run_ws_noalloc.restype = c_int
+        h.gemm_noalloc_scratch_bytes.argtypes = []
+        h.gemm_noalloc_scratch_bytes.restype = i64
         h.gemm_run_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, c_int, vp]
         h.gemm_run_blockscaled.restype = c_int
         h.gemm_run_opts.argtypes = [vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(GemmOpts), vp]
@@ -273,9 +277,8 @@ def gemm_run(plan: Plan, A, B, D, beta: int = 0, stream=None) -> None:
 
 def gemm_run_ws(plan: Plan, A, B, D, workspace, beta: int = 0, stream=None) -> None:
     """gemm_run with a device workspace (a contiguous GPU tensor of at least
-    ``plan.workspace_bytes()`` bytes, zero-filled before its first use; every
-    call leaves its counters zero again).  Plans without a workspace path run
-    as gemm_run."""
+    ``plan.workspace_bytes()`` bytes; its prior contents do not matter).
+    Plans without a workspace path run as gemm_run."""
     a, b, d = _operands(plan, A, B, D)
     need = plan.workspace_bytes()
     if isinstance(workspace, int):
@@ -290,6 +293,21 @@ def gemm_run_ws(plan: Plan, A, B, D, workspace, beta: int = 0, stream=None) -> N
     rc = load().gemm_run_ws(plan.handle, a, b, d, int(beta), w, int(wb), _stream_ptr(stream))
     if rc != 0:
         raise MswzError(rc, "gemm_run_ws")
+
+
+def gemm_run_ws_noalloc(plan: Plan, A, B, D, beta: int = 0, stream=None) -> None:
+    """gemm_run_ws with the library's own static scratch instead of a caller
+    workspace (for callers that cannot allocate); calls that overlap on one
+    GPU race on that scratch."""
+    a, b, d = _operands(plan, A, B, D)
+    rc = load().gemm_run_ws_noalloc(plan.handle, a, b, d, int(beta), _stream_ptr(stream))
+    if rc != 0:
+        raise MswzError(rc, "gemm_run_ws_noalloc")
+
+
+def gemm_noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch gemm_run_ws_noalloc uses."""
+    return int(load().gemm_noalloc_scratch_bytes())
 
 
 def gemm_run_blockscaled(plan: Plan, A, B, SFA, SFB, D, beta: int = 0, stream=None) -> None:

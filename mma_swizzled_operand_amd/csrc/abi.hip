@@ -356,6 +356,7 @@ const char *gemm_status_str(int status)
     case MSWZ_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MSWZ_ERR_HIP: return "HIP runtime error on launch";
     case MSWZ_ERR_KIND: return "plan kind does not match the run function (dense vs block-scaled)";
+    case MSWZ_ERR_SCRATCH: return "the plan's workspace exceeds the library's static scratch (gemm_noalloc_scratch_bytes)";
     default: return "unknown status";
     }
 }

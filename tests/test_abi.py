@@ -369,3 +369,16 @@ def test_plan_create_ld_chooses_the_256_tile():
     assert (p.b_rows, p.b_cols, p.ldb) == (512, 128, 128)
     assert p.ldd == 512
 
+
+def test_run_ws_noalloc_rejections_before_gpu_work():
+    """Plans whose partials exceed the static scratch are refused with
+    MSWZ_ERR_SCRATCH before any HIP call; a NULL plan is invalid."""
+    lib = mswz.load()
+    assert lib.gemm_noalloc_scratch_bytes() == 16 << 20
+    assert mswz.STATUS["scratch"] == -6
+    big = mswz.gemm_plan_create(64, 65536, 8192, "bf16", "bf16")      # 2 parts x 64 x 65536 fp32 = 32 MiB
+    assert big.workspace_bytes() == 2 * 64 * 65536 * 4
+    P = 0x10000
+    assert lib.gemm_run_ws_noalloc(big.handle, P, P, P, 0, None) == -6
+    assert lib.gemm_run_ws_noalloc(None, P, P, P, 0, None) == -1
+    assert "scratch" in mswz.gemm_status_str(-6)
