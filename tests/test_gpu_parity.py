@@ -73,8 +73,8 @@ def test_small_full_compare(case, tile, tile_env):
     say(f"[parity] {case} tile={tile} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} beta={w.beta}")
     x = wl.generate(w, seed=0)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(case, tile, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(case, tile, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -114,8 +114,8 @@ def test_beta_zero_ignores_nan_in_D():
     x = wl.generate(w, seed=3)
     say("[edge] beta=0 over NaN-filled D")
     got = run_gpu(w, x, D_init=np.full((w.M, w.N), np.nan, dtype=np.float32))
-    ref, mag = reference(w, x)
-    compare(w, got, ref, mag)
+    ref = reference(w, x)
+    compare(w, got, ref)
 
 
 def test_single_k_step_single_tile():
@@ -123,8 +123,8 @@ def test_single_k_step_single_tile():
     x = wl.generate(w, seed=4)
     say("[edge] 64x64x64")
     got = run_gpu(w, x)
-    ref, mag = reference(w, x)
-    compare(w, got, ref, mag)
+    ref = reference(w, x)
+    compare(w, got, ref)
 
 
 def test_deterministic_bits():
@@ -158,8 +158,8 @@ def test_tail_shapes_full_compare(name):
     say(f"[tail] {name} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} B:{w.b_major} beta={w.beta} {plan.describe()}")
     x = wl.generate(w, seed=21)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 def test_tail_output_untouched_outside_d():
@@ -206,8 +206,8 @@ def test_k_tail_full_compare(name):
     say(f"[k-tail] {name} {w.M}x{w.N}x{w.K} {w.kind} A:{w.a_major} B:{w.b_major} beta={w.beta}")
     x = wl.generate(w, seed=31)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("name", list(KTAILS))
@@ -228,8 +228,8 @@ def test_k_tail_full_size_sampled():
     x = wl.generate(w, seed=33)
     got = run_gpu(w, x)
     rows, cols = wl.sample_points(w, 12, 12, seed=34)
-    ref, mag = reference(w, x, rows=rows, cols=cols)
-    print(compare(w, got[np.ix_(rows, cols)], ref, mag))
+    ref = reference(w, x, rows=rows, cols=cols)
+    print(compare(w, got[np.ix_(rows, cols)], ref))
 
 
 # MX-fp4 (OCP E2M1, two per byte; the 256 tile only): several tiles and K
@@ -251,8 +251,8 @@ def test_fp4_full_compare(name):
     say(f"[fp4] {name} {w.M}x{w.N}x{w.K} beta={w.beta} {plan.describe()}")
     x = wl.generate(w, seed=31)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("name", list(FP4))
@@ -307,8 +307,8 @@ def test_fp6_full_compare(name):
     say(f"[fp6] {name} {w.M}x{w.N}x{w.K} beta={w.beta} {plan.describe()}")
     x = wl.generate(w, seed=41)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("name", list(FP6))
@@ -399,8 +399,8 @@ def test_mixed_full_compare(name):
     say(f"[mixed] {name} {w.M}x{w.N}x{w.K} {w.kind} x {w.kind_b} beta={w.beta}")
     x = wl.generate(w, seed=51)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("name", list(MIXED))
@@ -474,8 +474,8 @@ def test_v16_full_compare(name):
     say(f"[v16] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta}")
     x = wl.generate(w, seed=61)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 @pytest.mark.parametrize("name", list(V16))
@@ -512,8 +512,8 @@ def test_v16_full_size_sampled():
     x = wl.generate(w, seed=63)
     got = run_gpu(w, x)
     rows, cols = wl.sample_points(w, 8, 8, seed=64)
-    ref_r, mag_r = reference(w, x, rows=rows)
-    print(compare(w, got[rows], ref_r, mag_r))
+    ref_r = reference(w, x, rows=rows)
+    print(compare(w, got[rows], ref_r))
 
 
 # long K: large per-step offsets, long fp32 accumulation chains
@@ -532,8 +532,8 @@ def test_long_k(name):
     say(f"[long-k] {name} {w.M}x{w.N}x{w.K}")
     x = wl.generate(w, seed=71)
     got = run_gpu(w, x)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
     xq = wl.generate(w, seed=72, values="quarter")
     assert np.array_equal(run_gpu(w, xq), reference(w, xq, with_mag=False).astype(np.float32))
 
@@ -554,7 +554,8 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", *EXTRA_FULL])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", "c11", "c12",
+                                  *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
     sampled rows and columns are compared with the oracle."""
@@ -565,11 +566,11 @@ def test_full_size_sampled(name):
     say(f"[full] {name} plan {plan.describe()}")
     got = run_gpu(w, x, plan)
     rows, cols = wl.sample_points(w, 8, 8)
-    ref_r, mag_r = reference(w, x, rows=rows)
-    ref_c, mag_c = reference(w, x, cols=cols)
+    ref_r = reference(w, x, rows=rows)
+    ref_c = reference(w, x, cols=cols)
     d0 = x.get("D0")
-    r1 = compare(w, got[rows], ref_r, mag_r, None if d0 is None else d0[rows])
-    r2 = compare(w, got[:, cols], ref_c, mag_c, None if d0 is None else d0[:, cols])
+    r1 = compare(w, got[rows], ref_r, None if d0 is None else d0[rows])
+    r2 = compare(w, got[:, cols], ref_c, None if d0 is None else d0[:, cols])
     print(name, r1, r2)
 
 
@@ -601,3 +602,31 @@ def test_scale_bytes_select_the_right_block(M, N, K):
     ub = x["SFB"].astype(np.int64) - 127
     expect = 32.0 * (np.exp2(ua[:, None, :] + ub[None, :, :])).sum(-1)
     assert np.array_equal(got.astype(np.float64), expect)
+
+
+def _block_scaled_cases():
+    out = {}
+    for group in (SMALL, TAILS, FP4, FP6, MIXED, V16):
+        for name, w in group.items():
+            if w.V and w.K <= 4096:
+                out[name] = w
+    return out
+
+
+MX_RANDOM_SCALES = _block_scaled_cases()
+
+
+@pytest.mark.parametrize("name", sorted(MX_RANDOM_SCALES))
+def test_mx_random_scales_bit_exact(name):
+    """Quarter-integer values (half-integers for E2M1) with random scale bytes
+    127 + u, u in [-2, 2], for both operands: every scaled product and partial
+    sum is exact in fp32 (K <= 4096), so the result must equal the oracle bit
+    for bit, element by element.  A value meeting the wrong scale byte, or a
+    scale byte applied to the wrong block or row, changes the output."""
+    w = MX_RANDOM_SCALES[name]
+    say(f"[mx-exact-scaled] {name} {w.M}x{w.N}x{w.K} {w.kind} x {w.kind_b} V={w.V} beta={w.beta}")
+    x = wl.generate(w, seed=81, values="quarter_scaled")
+    assert len(np.unique(x["SFA"])) == 5 and len(np.unique(x["SFB"])) == 5
+    got = run_gpu(w, x, plan_for(w))
+    ref = reference(w, x, with_mag=False)
+    assert np.array_equal(got, ref.astype(np.float32))

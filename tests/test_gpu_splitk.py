@@ -1,20 +1,20 @@
 """Weight streaming with K split over workgroups (gemm_run_ws) against the
 oracle, through the C ABI.
 
-The split kernel sums S fp32 partials per output in a fixed part order inside
-the kernel (the last workgroup of a column block does it), so besides parity
-with the oracle these tests check that results are bit-identical run to run
-on one workspace, that every call leaves the workspace's counters at zero,
-and beta = 1.  Tolerances are those of the dense cases (tests/gpu_util.py):
-any fp32 summation order of the exact 16-bit products stays within the
-componentwise bound.
+The streaming kernel stores S fp32 partials per output in the workspace and a
+second kernel sums them in a fixed part order and applies beta, so besides
+parity with the oracle these tests check that results are bit-identical run to
+run on one workspace, that the workspace's prior contents (filled with NaNs
+here) do not matter, and beta = 1.  Tolerances are those of the dense cases
+(tests/gpu_util.py): any fp32 summation order of the exact 16-bit products
+stays within the componentwise bound.
 """
 import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from gpu_util import compare, plan_for, reference, run_gpu, say, zero_workspace
+from gpu_util import compare, plan_for, reference, run_gpu, say, poisoned_workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -60,14 +60,12 @@ UNSPLIT = {
 def test_split_small_full_compare(name):
     w = SMALL[name]
     plan = plan_for(w)
-    ws = zero_workspace(plan)
+    ws = poisoned_workspace(plan)
     say(f"[splitk] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta} ws={ws.numel()} B")
     x = wl.generate(w, seed=11)
     got = run_gpu(w, x, plan, workspace=ws)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
-    counters = ws[:256].cpu().numpy()
-    assert not counters.any(), "counters not reset"
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
 
 
 def ks_parts(w):
@@ -88,17 +86,17 @@ def test_kslice_full_compare(name):
     w = KSLICE[name]
     assert w.K // ks_parts(w) in (1024, 2048), "case must reach the K-sliced kernel"
     plan = plan_for(w)
-    ws = zero_workspace(plan)
+    ws = poisoned_workspace(plan)
     say(f"[splitk-ks] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta} parts={ks_parts(w)}")
     x = wl.generate(w, seed=21)
     got = run_gpu(w, x, plan, workspace=ws)
     if w.M * w.N * w.K <= (1 << 30):
-        ref, mag = reference(w, x)
-        print(name, compare(w, got, ref, mag, x.get("D0")))
+        ref = reference(w, x)
+        print(name, compare(w, got, ref, x.get("D0")))
     else:
         cols = wl.sample_points(w, 8, 64)[1]
-        ref, mag = reference(w, x, cols=cols)
-        print(name, compare(w, got[:, cols], ref, mag, None if x.get("D0") is None else x["D0"][:, cols]))
+        ref = reference(w, x, cols=cols)
+        print(name, compare(w, got[:, cols], ref, None if x.get("D0") is None else x["D0"][:, cols]))
     again = run_gpu(w, x, plan, workspace=ws)
     assert np.array_equal(got, again), "not bit-identical run to run"
 
@@ -111,7 +109,7 @@ def test_kslice_quarter_exact(name):
     plan = plan_for(w)
     x = wl.generate(w, seed=22, values="quarter")
     say(f"[splitk-ks] quarter exact {name}")
-    got = run_gpu(w, x, plan, workspace=zero_workspace(plan))
+    got = run_gpu(w, x, plan, workspace=poisoned_workspace(plan))
     assert np.array_equal(got.astype(np.float64), reference(w, x, with_mag=False))
 
 
@@ -126,28 +124,25 @@ def test_kslice_stores_stay_inside_d_and_workspace():
     dbuf = torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda")
     dbuf[:n] = torch.from_numpy(x["D0"].reshape(-1)).cuda()
     need = plan.workspace_bytes()
-    wbuf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    wbuf = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
     wbuf[need:] = 0xA5
     say("[splitk-ks] canaries")
     mswz.gemm_run_ws(plan, A, B, dbuf[:n], wbuf[:need], 1)
     torch.cuda.synchronize()
     assert torch.all(dbuf[n:] == 7.0)
     assert torch.all(wbuf[need:] == 0xA5)
-    ref, mag = reference(w, x)
-    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, mag, x.get("D0"))
+    ref = reference(w, x)
+    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, x.get("D0"))
 
 
-def test_split_repeatable_and_counters_reset():
-    """Three calls on one workspace: identical bits, counters zero after each."""
+def test_split_repeatable():
+    """Three calls on one workspace: identical bits."""
     w = SMALL["ws-bf16-2048x4096"]
     plan = plan_for(w)
-    ws = zero_workspace(plan)
+    ws = poisoned_workspace(plan)
     x = wl.generate(w, seed=12)
     say("[splitk] repeat x3")
-    outs = []
-    for _ in range(3):
-        outs.append(run_gpu(w, x, plan, workspace=ws))
-        assert not ws[:256].cpu().numpy().any()
+    outs = [run_gpu(w, x, plan, workspace=ws) for _ in range(3)]
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
@@ -158,7 +153,7 @@ def test_split_quarter_exact():
     plan = plan_for(w)
     x = wl.generate(w, seed=13, values="quarter")
     say("[splitk] quarter exact")
-    got = run_gpu(w, x, plan, workspace=zero_workspace(plan))
+    got = run_gpu(w, x, plan, workspace=poisoned_workspace(plan))
     assert np.array_equal(got.astype(np.float64), reference(w, x, with_mag=False))
 
 
@@ -166,15 +161,14 @@ def test_split_full_size_c4_sampled():
     """The weight-streaming workload at full size through the workspace path."""
     w = wl.WORKLOADS["c4"]
     plan = plan_for(w)
-    ws = zero_workspace(plan)
+    ws = poisoned_workspace(plan)
     say(f"[splitk] c4 full size, workspace {ws.numel()} B")
     x = wl.generate(w, seed=0)
     got = run_gpu(w, x, plan, workspace=ws)
     rows, cols = wl.sample_points(w, 8, 8)
-    ref_r, mag_r = reference(w, x, rows=rows)
-    ref_c, mag_c = reference(w, x, cols=cols)
-    print("c4 ws", compare(w, got[rows], ref_r, mag_r), compare(w, got[:, cols], ref_c, mag_c))
-    assert not ws[:256].cpu().numpy().any()
+    ref_r = reference(w, x, rows=rows)
+    ref_c = reference(w, x, cols=cols)
+    print("c4 ws", compare(w, got[rows], ref_r), compare(w, got[:, cols], ref_c))
 
 
 @pytest.mark.parametrize("name", list(UNSPLIT))
@@ -185,8 +179,8 @@ def test_unsplit_ragged_m(name):
     say(f"[skinny] {name} {w.M}x{w.N}x{w.K} {w.kind} beta={w.beta}")
     x = wl.generate(w, seed=14)
     got = run_gpu(w, x, plan)
-    ref, mag = reference(w, x)
-    print(name, compare(w, got, ref, mag, x.get("D0")))
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
     xq = wl.generate(w, seed=15, values="quarter")
     assert np.array_equal(run_gpu(w, xq, plan), reference(w, xq, with_mag=False).astype(np.float32))
 
@@ -203,7 +197,7 @@ def test_ragged_m_stores_stay_inside_d_and_workspace(split):
     dbuf = torch.full((n + 4096,), 7.0, dtype=torch.float32, device="cuda")
     dbuf[:n] = torch.from_numpy(x["D0"].reshape(-1)).cuda()
     need = plan.workspace_bytes()
-    wbuf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    wbuf = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
     wbuf[need:] = 0xA5
     say(f"[skinny] canaries split={split}")
     if split:
@@ -213,8 +207,8 @@ def test_ragged_m_stores_stay_inside_d_and_workspace(split):
     torch.cuda.synchronize()
     assert torch.all(dbuf[n:] == 7.0)
     assert torch.all(wbuf[need:] == 0xA5)
-    ref, mag = reference(w, x)
-    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, mag, x.get("D0"))
+    ref = reference(w, x)
+    compare(w, dbuf[:n].cpu().numpy().reshape(w.M, w.N), ref, x.get("D0"))
 
 
 def test_decode_m16_full_size_sampled():
@@ -222,10 +216,10 @@ def test_decode_m16_full_size_sampled():
     batch) through the workspace path, on sampled rows and columns."""
     w = wl.custom(16, 16384, 8192, "bf16", a_dist=("normal", 1.0), b_dist=("normal", 0.02), name="decode-m16")
     plan = plan_for(w)
-    ws = zero_workspace(plan)
+    ws = poisoned_workspace(plan)
     say("[splitk] 16x16384x8192")
     x = wl.generate(w, seed=17)
     got = run_gpu(w, x, plan, workspace=ws)
     cols = wl.sample_points(w, 8, 16)[1]
-    ref, mag = reference(w, x, cols=cols)
-    print("decode-m16", compare(w, got[:, cols], ref, mag))
+    ref = reference(w, x, cols=cols)
+    print("decode-m16", compare(w, got[:, cols], ref))

@@ -341,3 +341,20 @@ def test_sixteen_element_blocks(kind):
             ex = sum(Fraction(vals_a[m, k]) * Fraction(vals_b[n, k]) * Fraction(2) ** int(ua[m, k // 16] + ub[n, k // 16])
                      for k in range(K))
             assert Fraction(got[m, n]) == ex
+
+
+@pytest.mark.parametrize("kind,kind_b,V,beta", [("e4m3", "", 32, 0), ("e2m1", "", 16, 1), ("e2m3", "", 32, 0),
+                                                 ("e3m2", "e4m3", 32, 1), ("e2m1p", "", 16, 0)])
+def test_quarter_scaled_inputs_give_fp32_exact_products(kind, kind_b, V, beta):
+    """The exactness argument behind the GPU's bit-exact random-scale tests:
+    with quarter-integer (E2M1: half-integer) values and scales 2^u, u in
+    [-2, 2], at K = 4096 the exact product A.B^T is a multiple of 2^-8 of
+    magnitude at most 2^16, so it is representable in fp32; checked here on
+    the oracle's fp64 result."""
+    w = wl.custom(32, 48, 4096, kind, V=V, b_kind=kind_b, beta=beta)
+    x = wl.generate(w, seed=5, values="quarter_scaled")
+    assert set(np.unique(x["SFA"])) == set(range(125, 130))
+    P = oracle.gemm(w.M, w.N, w.K, w.kind, "k", x["A"], w.kind_b, "k", x["B"], V=w.V, SFA=x["SFA"], SFB=x["SFB"])
+    assert np.all(np.abs(P) <= 2.0 ** 16)
+    assert np.array_equal(np.round(P * 256), P * 256)
+    assert np.array_equal(P.astype(np.float32).astype(np.float64), P)
