@@ -110,8 +110,13 @@ typedef struct gemm_plan gemm_plan;
  *                 E2M3, E3M2 and E2M1_P64; or 16 (one scale per 16 K
  *                 elements: the pages' scale_vec::4X) for E2M1, E2M1_P64,
  *                 E2M3 and E3M2 with A and B of the same kind
- * Shape rules: K % 128 == 0 (E4M3; E2M3, E3M2 and E2M1_P64, which always use
- * the 256 tile) or K % 256 == 0 (E2M1, which always uses the 256 tile).  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
+ * Shape rules: block-scaled K: any multiple of scale_vec_len (E2M1: of 32 as
+ * well, so that rows of K/2 bytes stay 16-byte aligned); a K that is not a
+ * multiple of the kernel's K step (128 elements; E2M1 256) uses the 256 tile,
+ * whose last K step reads the values beyond K as zeros and gives their scale
+ * blocks the exponent 127 (the scale array itself holds K/V bytes per row,
+ * nothing beyond them is read).  E2M1, E2M3, E3M2, E2M1_P64 and mixed kinds
+ * always use the 256 tile.  16-bit K: any K with K % 8 == 0 (16-byte K-major rows; any
  * K when both operands are MN-major); a K that is not a multiple of 64 uses
  * the 256 tile, whose last K step reads the values beyond K as zeros.  M and N
  * multiples of 64 choose among 256, 128 and 64 square tiles; otherwise (tails)

@@ -152,13 +152,16 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_UNSUPPORTED;
     if (fp8 && (a_major != MSWZ_MAJOR_K || b_major != MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;     // MN-major operands are built for 16-bit formats
-    // block-scaled: K a multiple of the K step (scale rows stay 4-byte words
-    // per step).  16-bit: any K whose K-major rows keep 16-byte alignment
+    // block-scaled: any K that is a multiple of the scale block and keeps
+    // stored rows 16-byte aligned (E2M1: K % 32 == 0, two elements a byte);
+    // a K that is not a multiple of the K step (128, E2M1 256) takes the
+    // 256x256 tile with a zero-padded last step and scale words assembled in
+    // registers.  16-bit: any K whose K-major rows keep 16-byte alignment
     // (K % 8 == 0 unless both operands are MN-major); a K that is not a
     // multiple of 64 takes the 256x256 tile with a zero-padded last step.
-    if (fp8 && K % (fp4 ? 256 : 128) != 0)
+    if (fp8 && (K % scale_vec_len != 0 || (fp4 && K % 32 != 0)))
         return MSWZ_ERR_UNSUPPORTED;
-    const bool ktail = !fp8 && K % 64 != 0;
+    const bool ktail = fp8 ? K % (fp4 ? 256 : 128) != 0 : K % 64 != 0;
     if (ktail && K % 8 != 0 && (a_major == MSWZ_MAJOR_K || b_major == MSWZ_MAJOR_K))
         return MSWZ_ERR_UNSUPPORTED;
     // M or N not a multiple of 64: the 256x256 tile with masked stores; D rows

@@ -405,8 +405,11 @@ constexpr int W = 8;
 // KIND: element kind of A (and of B unless KB >= 0); KB: B's kind when it
 // differs (block-scaled E4M3 / E2M3 / E3M2 / padded E2M1 only); SV: K
 // elements per scale byte (32, or 16 for E2M1 and the padded kinds); MF16:
-// 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major).
-template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32>
+// 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major);
+// SB: block-scaled K that is not a multiple of the K step (scale bytes
+// assembled in registers, see below).
+template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32,
+          bool SB = false>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -489,7 +492,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kByteRows && !kV16;   // E4M3 and the padded kinds, 32-element blocks
+    constexpr bool kScaleGroups = kByteRows && !kV16 && !SB;   // E4M3 and the padded kinds, 32-element blocks
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / SV;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -505,6 +508,46 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
+    static_assert(!SB || (kMx && W == 8), "register-assembled scales: block-scaled kinds, eight waves");
+    // scale words per row per step: one (E4M3 and padded kinds, four
+    // 32-element blocks), two (E2M1, eight blocks), twice that with
+    // 16-element blocks; word w of 64-row group g sits at stage byte
+    // 2048w + 256g + 4*(row in group)
+    constexpr int kWords = (kFp4 ? 2 : 1) * (kV16 ? 2 : 1);
+    // SB (K not a multiple of the K step): a row's K/SV scale bytes are then
+    // not a whole number of 4-byte words, so the words cannot be copied
+    // straight into LDS.  Each step, lane l of wave g loads the step's scale
+    // bytes of row 64*(g%4) + l of its group one by one (range-checked: rows
+    // beyond the operand read zero), assembles the words in registers and
+    // stores them into the scale stage in the layout above.  A block at or
+    // beyond K gets the byte 127 (2^0): its values are zeros, and no byte of
+    // a neighbouring row (255 would be NaN) is read for it.
+    uint32_t sbyte[SB ? 4 * kWords : 1];
+    const uint32_t sf_range = kMx ? uint32_t(wave < 4 ? rows_a : rows_b) * sf_row : 0;
+    auto load_scale_bytes = [&](int kt) {
+        if constexpr (SB) {
+#pragma unroll
+            for (int w = 0; w < kWords; ++w)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t j = 4u * uint32_t(kWords * kt + w) + uint32_t(b);   // block index in the row
+                    const uint32_t off = j < sf_row ? sf_voff + j : sf_range;
+                    sbyte[4 * w + b] = j < sf_row ? uint32_t(__builtin_amdgcn_raw_buffer_load_b8(sf_rsrc[0], off, 0, 0))
+                                                  : 127u;
+                }
+        }
+    };
+    auto put_scales = [&](uint8_t *sstage) {
+        if constexpr (SB) {
+            sched_fence();   // after the step's MFMAs: the loads' wait must not block them
+#pragma unroll
+            for (int w = 0; w < kWords; ++w) {
+                const uint32_t word = sbyte[4 * w] | (sbyte[4 * w + 1] << 8) | (sbyte[4 * w + 2] << 16) |
+                                      (sbyte[4 * w + 3] << 24);
+                *reinterpret_cast<uint32_t *>(sstage + 2048 * w + 256 * wave + 4 * lane) = word;
+            }
+        }
+    };
 
     auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
         if constexpr (kDmaA)
@@ -515,12 +558,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             dma_mnb.issue(stage, kt);
         if constexpr (kDmaB)
             db.issue(stage, kt);
-        if constexpr (kMx) {
-            // scale words per row per step: one (E4M3 and padded kinds, four
-            // 32-element blocks), two (E2M1, eight blocks), twice that with
-            // 16-element blocks; word w of 64-row group g lands at stage byte
-            // 2048w + 256g + 4*(row in group)
-            constexpr int kWords = (kFp4 ? 2 : 1) * (kV16 ? 2 : 1);
+        if constexpr (SB) {
+            load_scale_bytes(kt);
+        } else if constexpr (kMx) {
 #pragma unroll
             for (int q = 0; q < kSfInstr; ++q)
 #pragma unroll
@@ -969,29 +1009,33 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
     if (KT > 0) {
     issue_step(lds0, scl0, 0);
+    put_scales(scl0);
     __syncthreads();
 
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
         issue_step(lds1, scl1, kt + 1);
         compute(lds0, scl0);
+        put_scales(scl1);
         lds_barrier_keep_vm<0>();
         issue_step(lds0, scl0, min(kt + 2, KT - 1));
         compute(lds1, scl1);
+        put_scales(scl0);
         lds_barrier_keep_vm<0>();
     }
     if (kt < KT)
         compute(lds0, scl0);
     __syncthreads();   // no copy may still be writing LDS when the workgroup ends
     }
-    // K not a multiple of the step (16-bit operands copied straight into LDS;
-    // the host launches no other configuration for it): one more step after
-    // the loop whose K values beyond K are copied as zeros into both
-    // operands, so they add nothing.
-    if constexpr (!kMx) {
+    // K not a multiple of the step (operands copied straight into LDS, and
+    // for block-scaled kinds the SB scale path; the host launches no other
+    // configuration for it): one more step after the loop whose K values
+    // beyond K are copied as zeros into both operands, so they add nothing.
+    if constexpr (!kMx || SB) {
         if (K % kStepK) {
             lds_barrier_keep_vm<0>();   // every copy landed, every wave done reading lds0
-            const uint32_t lim = uint32_t(K % kStepK) * 2;   // bytes of each K-major row slice inside K
+            // bytes of each K-major row's step slice inside K (whole 16-byte chunks)
+            const uint32_t lim = uint32_t(K % kStepK) * 128 / kStepK;
             if constexpr (kDmaA)
                 da.issue_tail(lds0, KT, lim, wave, lane);
             if constexpr (kTrA)
@@ -1000,6 +1044,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 db.issue_tail(lds0, KT, lim, wave, lane);
             if constexpr (kTrB)
                 dma_mnb.issue_tail(lds0, KT, K, wave, lane);
+            load_scale_bytes(KT);
+            put_scales(scl0);
             lds_barrier_keep_vm<0>();
             compute(lds0, scl0);
         }
@@ -1037,15 +1083,10 @@ epilogue:
                     *reinterpret_cast<f32x4 *>(area + r * kPitch + c * 4) = acc4[j][i];
                 }
             wave_lds_sync();
-            f32x4 vals[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                vals[k] = *reinterpret_cast<const f32x4 *>(area + (4 * k + rd_row) * kPitch + rd_col * 4);
-            wave_lds_sync();   // the next quarter's writes come after these reads
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int r = 4 * k + rd_row;
-                f32x4 v = vals[k];
+                f32x4 v = *reinterpret_cast<const f32x4 *>(area + r * kPitch + rd_col * 4);
                 const int m = m0 + wm + 32 * q + r, n = n0 + wn + rd_col;
                 if (m >= M || n >= N)
                     continue;
@@ -1053,6 +1094,7 @@ epilogue:
                     continue;
                 store_d4<OUT, BETA, true>(D, size_t(m) * ldd + n, v, opts.sat);
             }
+            wave_lds_sync();   // the next quarter's writes come after these reads
         }
         return;
     }
@@ -1099,7 +1141,7 @@ epilogue:
 // 16x16 MFMAs for every operand kind, except 16-bit operands that are both
 // MN-major, which take 32x32x16 (their 16x16 fragment reads would need more
 // than 256 VGPRs).
-template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32>
+template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32, bool SB = false>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     constexpr bool kMf16 = !(A_MN && B_MN);
@@ -1108,25 +1150,38 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV, SB>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV, SB>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
 }
 
 // D's element kind chosen at run time
+template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32, bool SB = false>
+hipError_t launch_out(const MxArgs &a, hipStream_t stream)
+{
+    switch (a.out) {
+    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV, SB>(a, stream);
+    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV, SB>(a, stream);
+    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV, SB>(a, stream);
+    }
+}
+
+// Block-scaled kinds with a K that is not a multiple of their K step take
+// the SB variant (scale words assembled in registers).
 template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
-    switch (a.out) {
-    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV>(a, stream);
-    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV>(a, stream);
-    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV>(a, stream);
+    if constexpr (KIND != kBf16 && KIND != kF16) {
+        constexpr int kStep = KIND == kE2m1 ? 256 : 128;
+        if (a.K % kStep != 0)
+            return launch_out<KIND, A_MN, B_MN, KB, SV, true>(a, stream);
     }
+    return launch_out<KIND, A_MN, B_MN, KB, SV, false>(a, stream);
 }
 
 }  // namespace

@@ -74,13 +74,15 @@ K_, MN = 0, 1
     ((256, 256, 128, E4M3, E4M3, F32, K_, K_, 32), 0),
     ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 32), 0),       # MX-fp4
     ((300, 260, 256, E2M1, E2M1, F32, K_, K_, 32), 0),       # ragged MX-fp4
-    ((256, 256, 384, E2M1, E2M1, F32, K_, K_, 32), -2),      # K not a multiple of 256
+    ((256, 256, 384, E2M1, E2M1, F32, K_, K_, 32), 0),       # K tail (1.5 steps of 256)
+    ((256, 256, 400, E2M1, E2M1, F32, K_, K_, 16), -2),      # rows of K/2 bytes not 16-byte aligned
     ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 0), -2),       # fp4 needs scales
     ((256, 256, 512, E2M1, E2M1, F32, MN, K_, 32), -2),      # MN-major fp4 not built
     ((256, 256, 512, E2M1, E4M3, F32, K_, K_, 32), -2),      # mixed formats
     ((256, 256, 128, E2M3, E2M3, F32, K_, K_, 32), 0),       # MX-fp6 (padded, sixteen per 16 bytes)
     ((300, 260, 384, E3M2, E3M2, BF16, K_, K_, 32), 0),      # ragged, bf16 output
-    ((256, 256, 64, E2M3, E2M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
+    ((256, 256, 64, E2M3, E2M3, F32, K_, K_, 32), 0),        # K tail (half a 128-element step)
+    ((256, 256, 40, E2M3, E2M3, F32, K_, K_, 32), -2),       # K not a multiple of the scale block
     ((256, 256, 128, E3M2, E3M2, F32, K_, K_, 0), -2),       # fp6 needs scales
     ((256, 256, 128, E2M3, E2M3, F32, K_, MN, 32), -2),      # MN-major fp6 not built
     ((256, 256, 128, E2M3, E3M2, F32, K_, K_, 32), 0),       # mixed 8- and 6-bit kinds
@@ -93,7 +95,12 @@ K_, MN = 0, 1
     ((256, 256, 128, E2M1P, E2M1P, F32, K_, K_, 32), 0),     # padded FP4 (sixteen per 16 bytes)
     ((256, 256, 128, E4M3, E2M1P, F32, K_, K_, 32), 0),      # mixed fp8 x padded fp4
     ((256, 256, 128, E2M1P, E2M1, F32, K_, K_, 32), -2),     # the dense FP4 form does not mix
-    ((256, 256, 64, E2M1P, E2M1P, F32, K_, K_, 32), -2),     # K not a multiple of 128
+    ((256, 256, 64, E2M1P, E2M1P, F32, K_, K_, 32), 0),      # K tail: half a 128-element step
+    ((256, 256, 48, E2M1P, E2M1P, F32, K_, K_, 32), -2),     # K not a multiple of the scale block
+    ((256, 256, 48, E2M1P, E2M1P, F32, K_, K_, 16), 0),      # ... of 16-element blocks it is
+    ((256, 256, 48, E2M1, E2M1, F32, K_, K_, 16), -2),       # E2M1 rows of K/2 bytes need K % 32
+    ((256, 256, 96, E2M1, E2M1, F32, K_, K_, 16), 0),
+    ((256, 256, 160, E4M3, E2M3, F32, K_, K_, 32), 0),       # mixed kinds, K tail
     ((0, 256, 64, F16, F16, F32, K_, K_, 0), -1),            # empty M
     ((256, -1, 64, F16, F16, F32, K_, K_, 0), -1),
     ((256, 256, 0, F16, F16, F32, K_, K_, 0), -1),           # empty K
@@ -124,7 +131,8 @@ K_, MN = 0, 1
     ((256, 256, 100, F16, F16, F32, MN, K_, 0), -2),         # (B is K-major)
     ((256, 256, 100, F16, F16, F32, MN, MN, 0), 0),          # both MN-major: any K
     ((256, 256, 1, BF16, BF16, F32, MN, MN, 0), 0),
-    ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 128
+    ((256, 256, 64, E4M3, E4M3, F32, K_, K_, 32), 0),        # K below one 128-element step
+    ((256, 256, 80, E4M3, E4M3, F32, K_, K_, 32), -2),       # K not a multiple of 32
     ((100, 256, 64, F16, F16, F32, K_, K_, 0), 0),           # ragged M: 256 tile, masked stores
     ((256, 96, 64, F16, F16, F32, K_, K_, 0), 0),            # ragged N
     ((100, 260, 128, E4M3, E4M3, F32, K_, K_, 32), 0),       # ragged MX

@@ -13,7 +13,7 @@ import pytest
 
 import mma_swizzled_operand_amd as mswz
 import workloads as wl
-from gpu_util import compare, plan_for, reference, run_gpu, say
+from gpu_util import compare, plan_for, reference, run_gpu, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -630,3 +630,81 @@ def test_mx_random_scales_bit_exact(name):
     got = run_gpu(w, x, plan_for(w))
     ref = reference(w, x, with_mag=False)
     assert np.array_equal(got, ref.astype(np.float32))
+
+
+# Block-scaled K that is not a multiple of the kernel's K step (128 elements,
+# E2M1 256): the last step is zero-padded and the scale words are assembled
+# in registers (a row's K/V scale bytes are not whole 4-byte words)
+MXKTAILS = {
+    "e4m3-k160": wl.custom(512, 256, 160, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e4m3-k160"),
+    "e4m3-k96-tail-beta": wl.custom(300, 292, 96, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="e4m3-k96-tail-beta"),
+    "e4m3-k4000": wl.custom(256, 256, 4000, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                            name="e4m3-k4000"),
+    "e2m1-k288": wl.custom(256, 512, 288, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e2m1-k288"),
+    "e2m1-v16-k96-beta": wl.custom(264, 256, 96, "e2m1", V=16, beta=1, a_dist=("normal", 1.0),
+                                   b_dist=("normal", 1.0), name="e2m1-v16-k96-beta"),
+    "e2m3-v16-k176": wl.custom(256, 256, 176, "e2m3", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e2m3-v16-k176"),
+    "e3m2-k224-beta": wl.custom(256, 264, 224, "e3m2", V=32, beta=1, a_dist=("normal", 1.0),
+                                b_dist=("normal", 1.0), name="e3m2-k224-beta"),
+    "e2m1p-v16-k80": wl.custom(256, 256, 80, "e2m1p", V=16, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e2m1p-v16-k80"),
+    "e4m3xe2m3-k160": wl.custom(512, 256, 160, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="e4m3xe2m3-k160", b_kind="e2m3"),
+    "e4m3xe2m1p-k352-beta": wl.custom(256, 512, 352, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                      b_dist=("normal", 1.0), name="e4m3xe2m1p-k352-beta", b_kind="e2m1p"),
+}
+
+
+@pytest.mark.parametrize("name", list(MXKTAILS))
+def test_mx_k_tail_full_compare(name):
+    w = MXKTAILS[name]
+    plan = plan_for(w)
+    assert plan.describe()["tile_m"] == 256
+    say(f"[mx-k-tail] {name} {w.M}x{w.N}x{w.K} {w.kind} x {w.kind_b} V={w.V} beta={w.beta}")
+    x = wl.generate(w, seed=91)
+    got = run_gpu(w, x, plan)
+    ref = reference(w, x)
+    print(name, compare(w, got, ref, x.get("D0")))
+
+
+@pytest.mark.parametrize("name", list(MXKTAILS))
+def test_mx_k_tail_random_scales_bit_exact(name):
+    w = MXKTAILS[name]
+    say(f"[mx-k-tail exact] {name}")
+    x = wl.generate(w, seed=92, values="quarter_scaled")
+    got = run_gpu(w, x, plan_for(w))
+    assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
+
+
+@pytest.mark.parametrize("name", ["e4m3-k160", "e2m1-v16-k96-beta", "e3m2-k224-beta"])
+def test_mx_k_tail_reads_no_scale_byte_beyond_the_array(name):
+    """SFA and SFB are views at the very end of larger buffers whose following
+    bytes are 255 (the NaN code): the result is still finite and exact for
+    quarter-integer values, so no scale byte past the last row's K/V was
+    used (blocks beyond K take 2^0 without a read)."""
+    import torch
+    w = MXKTAILS[name]
+    x = wl.generate(w, seed=93, values="quarter_scaled")
+    plan = plan_for(w)
+    A, B = to_device(x["A"]), to_device(x["B"])
+
+    def at_end(sf):
+        """The scale bytes followed by 256 bytes of 255 in one allocation."""
+        n = sf.size
+        buf = torch.full((n + 256,), 255, dtype=torch.uint8, device="cuda")
+        view = buf[:n]
+        view.copy_(torch.from_numpy(np.ascontiguousarray(sf).reshape(-1)).cuda())
+        return view
+
+    SFA, SFB = at_end(x["SFA"]), at_end(x["SFB"])
+    D = to_device(x["D0"]) if w.beta else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
+    say(f"[mx-k-tail nan-guard] {name}")
+    mswz.gemm_run_blockscaled(plan, A, B, SFA, SFB, D, w.beta)
+    torch.cuda.synchronize()
+    got = D.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))

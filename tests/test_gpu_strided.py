@@ -54,6 +54,12 @@ CASES = {
                            272, 264, 268, "f32"),
     "bf16-bmn-ktail-out": (wl.custom(256, 264, 24, "bf16", b_major="mn", name="bf16-bmn-ktail-out"),
                            32, 272, 0, "bf16"),
+    # block-scaled K tails: the poisoned storage (NaN codes) between K and the
+    # pitch must never reach the sums
+    "e4m3-ktail-beta": (wl.custom(264, 256, 160, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                  b_dist=("normal", 1.0), name="e4m3-ktail-beta"), 192, 176, 260, "f32"),
+    "e3m2-ktail": (wl.custom(256, 256, 96, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                             name="e3m2-ktail"), 128, 112, 0, "f32"),
 }
 
 
@@ -150,7 +156,8 @@ def test_strided_against_oracle(case):
         assert np.array_equal(got, pk), "strided and packed results differ"
 
 
-@pytest.mark.parametrize("case", ["bf16-k", "f16-amn-tail-beta", "bf16-both-mn", "e4m3-mx", "e2m1-beta", "e3m2-beta"])
+@pytest.mark.parametrize("case", ["bf16-k", "f16-amn-tail-beta", "bf16-both-mn", "e4m3-mx", "e2m1-beta", "e3m2-beta",
+                                  "e4m3-ktail-beta"])
 def test_strided_quarter_integers_exact(case):
     w, lda, ldb, ldd, d_fmt = CASES[case]
     say(f"[strided-exact] {case}")
