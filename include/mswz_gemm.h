@@ -312,6 +312,46 @@ int gemm_plan_describe(const gemm_plan *plan, int64_t *info, int n);
 int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m,
                        int *tile_m, int *tile_n);
 
+/*
+ * The 256x256 kernel's per-lane LDS addresses for one wave-wide access, from
+ * the same address functions the kernel uses (no GPU work), so that host
+ * tests can check the staging layouts and fragment maps bit for bit.
+ * Offsets are bytes from the start of the operand tile (or of the scale
+ * stage, or of a wave's epilogue area).  Writes `count` values to out (at
+ * most n) and returns count, or MSWZ_ERR_INVALID.
+ *   MSWZ_LDS_DMA_K      p0 = copy instruction q (0..31): out[2l] = LDS offset
+ *                       lane l writes (16 bytes), out[2l+1] = the source
+ *                       offset row * 128 + 16 * chunk in the step's [256][128 B]
+ *                       slice of the operand                   (count 128)
+ *   MSWZ_LDS_DMA_MN     p0 = q (0..31): the same for an MN-major operand, source
+ *                       k * 512 + 16 * chunk in the step's [64][512 B] slice
+ *   MSWZ_LDS_FRAG_K16   p0 = 16-row block b (0..15), p1 = sub-step (0..1): the
+ *                       16-byte read of a 16-bit K-major 16x16x32 fragment (64)
+ *   MSWZ_LDS_FRAG_MN16  p0 = b, p1 = sub-step: the two 8-byte transposing
+ *                       reads (ds_read_b64_tr_b16) of an MN-major fragment (128)
+ *   MSWZ_LDS_FRAG_E4M3  p0 = b (0..15): the two 16-byte reads (bytes 0..15 and
+ *                       16..31) of an E4M3 fragment                     (128)
+ *   MSWZ_LDS_FRAG_PAD   p0 = b: the two 16-byte reads of a padded 6- or
+ *                       4-bit fragment                                   (128)
+ *   MSWZ_LDS_FRAG_E4M3_MIXED  p0 = b: E4M3 paired with a padded kind     (128)
+ *   MSWZ_LDS_FRAG_E2M1  p0 = b, p1 = sub-step (0..1): the 16-byte read of a
+ *                       dense E2M1 fragment                               (64)
+ *   MSWZ_LDS_SCALE_GRP  p0 = b (0..7), p1 = step in its group of four (0..3):
+ *                       the scale byte each lane reads (A side, wave rows 0..127)
+ *   MSWZ_LDS_SCALE_DMA  p0 = wave (0..7): out[2l] = stage offset lane l writes
+ *                       (16 bytes), out[2l+1] = the row of its 64-row group
+ *                       whose four steps' scale bytes it copies        (128)
+ *   MSWZ_LDS_EPI_WRITE  p0 = quarter q (0..3), p1 = 16*byte_rows + 4*ii + j:
+ *                       the 16-byte write of 16x16 block (2q + ii, j)    (64)
+ *   MSWZ_LDS_EPI_READ   p0 = read-back instruction k (0..7)              (64)
+ */
+enum {
+    MSWZ_LDS_DMA_K = 1, MSWZ_LDS_DMA_MN = 2, MSWZ_LDS_FRAG_K16 = 3, MSWZ_LDS_FRAG_MN16 = 4,
+    MSWZ_LDS_FRAG_E4M3 = 5, MSWZ_LDS_FRAG_PAD = 6, MSWZ_LDS_FRAG_E4M3_MIXED = 7, MSWZ_LDS_FRAG_E2M1 = 8,
+    MSWZ_LDS_SCALE_GRP = 9, MSWZ_LDS_SCALE_DMA = 10, MSWZ_LDS_EPI_WRITE = 11, MSWZ_LDS_EPI_READ = 12
+};
+int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n);
+
 int64_t mswz_desc_address(int64_t r, int64_t w, int64_t ldo, int64_t sdo,
                           int mode, int major, int64_t origin);
 int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin);

@@ -25,7 +25,7 @@ from . import _build
 __all__ = [
     "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_plan_create_ld", "gemm_run",
     "gemm_run_blockscaled", "gemm_run_opts", "gemm_run_ws", "gemm_run_ws_noalloc", "gemm_noalloc_scratch_bytes", "GemmOpts", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
-    "desc_address", "desc_check", "tile_offset", "library_path", "load",
+    "desc_address", "desc_check", "tile_offset", "lds_lanes", "library_path", "load",
 ]
 
 DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "f32": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7, "e2m1p": 8}
@@ -98,6 +98,8 @@ def load():
         h.mswz_desc_check.restype = c_int
         h.mswz_tile_offset.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
         h.mswz_tile_offset.restype = ctypes.c_uint32
+        h.mswz_lds_lanes.argtypes = [c_int, c_int, c_int, ctypes.POINTER(ctypes.c_uint32), c_int]
+        h.mswz_lds_lanes.restype = c_int
         _lib = h
         return _lib
 
@@ -363,3 +365,19 @@ def desc_check(ldo, sdo, mode, origin=0) -> int:
 def tile_offset(row, chunk) -> int:
     """Byte offset of 16-byte chunk ``chunk`` of row ``row`` in the kernels' LDS tile."""
     return int(load().mswz_tile_offset(int(row), int(chunk)))
+
+
+#: access patterns of lds_lanes (include/mswz_gemm.h, MSWZ_LDS_*)
+LDS_PATTERNS = {"dma_k": 1, "dma_mn": 2, "frag_k16": 3, "frag_mn16": 4, "frag_e4m3": 5, "frag_pad": 6,
+                "frag_e4m3_mixed": 7, "frag_e2m1": 8, "scale_grp": 9, "scale_dma": 10, "epi_write": 11,
+                "epi_read": 12}
+
+
+def lds_lanes(pattern: str, p0: int = 0, p1: int = 0) -> list[int]:
+    """The 256x256 kernel's per-lane LDS offsets for one access pattern (see
+    mswz_lds_lanes in include/mswz_gemm.h); 64 or 128 values."""
+    buf = (ctypes.c_uint32 * 128)()
+    n = load().mswz_lds_lanes(LDS_PATTERNS[pattern], int(p0), int(p1), buf, 128)
+    if n < 0:
+        raise MswzError(n, "mswz_lds_lanes")
+    return list(buf[:n])

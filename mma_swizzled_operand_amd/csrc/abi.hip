@@ -389,6 +389,89 @@ int mswz_desc_check(int64_t ldo, int64_t sdo, int mode, int64_t origin)
 
 uint32_t mswz_tile_offset(uint32_t row, uint32_t chunk) { return mswz::tile_offset(row, chunk); }
 
+int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
+{
+    using namespace mswz;
+    constexpr int W = 8;   // waves of the 256x256 kernel
+    auto in = [](int v, int lo, int hi) { return v >= lo && v < hi; };
+    const int count = (pattern == MSWZ_LDS_DMA_K || pattern == MSWZ_LDS_DMA_MN || pattern == MSWZ_LDS_FRAG_MN16 ||
+                       pattern == MSWZ_LDS_FRAG_E4M3 || pattern == MSWZ_LDS_FRAG_PAD ||
+                       pattern == MSWZ_LDS_FRAG_E4M3_MIXED || pattern == MSWZ_LDS_SCALE_DMA)
+                          ? 128 : 64;
+    if (!out || n < count)
+        return MSWZ_ERR_INVALID;
+    for (int l = 0; l < 64; ++l) {
+        const int g = l >> 4;
+        switch (pattern) {
+        case MSWZ_LDS_DMA_K:
+            if (!in(p0, 0, 32))
+                return MSWZ_ERR_INVALID;
+            out[2 * l] = uint32_t(1024 * p0 + 16 * l);
+            out[2 * l + 1] = dma_row(p0, l) * kTileRowBytes + 16 * dma_chunk(p0, l);
+            break;
+        case MSWZ_LDS_DMA_MN:
+            if (!in(p0, 0, 32))
+                return MSWZ_ERR_INVALID;
+            out[2 * l] = uint32_t(1024 * p0 + 16 * l);
+            out[2 * l + 1] = dma_mn_krow(p0, l) * kMnRowBytes + 16 * dma_mn_chunk(p0, l);
+            break;
+        case MSWZ_LDS_FRAG_K16:
+        case MSWZ_LDS_FRAG_E2M1:
+            if (!in(p0, 0, 16) || !in(p1, 0, 2))
+                return MSWZ_ERR_INVALID;
+            out[l] = kfrag_base<false>(0, 0, p0, kblk16(g), l) ^ uint32_t(p1 << 6);
+            break;
+        case MSWZ_LDS_FRAG_MN16: {
+            if (!in(p0, 0, 16) || !in(p1, 0, 2))
+                return MSWZ_ERR_INVALID;
+            const uint32_t base = mn_frag_base16(0, 16 * p0, l);
+            out[2 * l] = base + uint32_t(32 * p1) * kMnRowBytes;
+            out[2 * l + 1] = base + uint32_t(32 * p1 + 4) * kMnRowBytes;
+            break;
+        }
+        case MSWZ_LDS_FRAG_E4M3:
+        case MSWZ_LDS_FRAG_E4M3_MIXED:
+        case MSWZ_LDS_FRAG_PAD: {
+            if (!in(p0, 0, 16))
+                return MSWZ_ERR_INVALID;
+            const int c = pattern == MSWZ_LDS_FRAG_E4M3 ? mx_chunk16(g)
+                          : pattern == MSWZ_LDS_FRAG_PAD ? fp6_chunk16(g) : mx_chunk16_mixed(g);
+            const uint32_t base = kfrag_base<true>(0, 0, p0, c, l);
+            out[2 * l] = base;
+            out[2 * l + 1] = base ^ (pattern == MSWZ_LDS_FRAG_PAD ? 16u : 64u);
+            break;
+        }
+        case MSWZ_LDS_SCALE_GRP:
+            // grouped scale stage: 16 bytes per row slot, block b of row x in slot 16b + x
+            if (!in(p0, 0, 8) || !in(p1, 0, 4))
+                return MSWZ_ERR_INVALID;
+            out[l] = uint32_t(16 * ((l & 15) + 16 * p0) + g + 4 * p1);
+            break;
+        case MSWZ_LDS_SCALE_DMA:
+            if (!in(p0, 0, W))
+                return MSWZ_ERR_INVALID;
+            out[2 * l] = uint32_t(1024 * p0 + 16 * l);
+            out[2 * l + 1] = uint32_t(sf_slot_row(l));
+            break;
+        case MSWZ_LDS_EPI_WRITE: {
+            const int mx = p1 >> 4, ii = (p1 >> 2) & 3, j = p1 & 3;
+            if (!in(p0, 0, 4) || mx > 1 || ii > 1 || p1 < 0)
+                return MSWZ_ERR_INVALID;
+            out[l] = mx ? epi_write_offset<true>(p0, ii, j, l) : epi_write_offset<false>(p0, ii, j, l);
+            break;
+        }
+        case MSWZ_LDS_EPI_READ:
+            if (!in(p0, 0, 8))
+                return MSWZ_ERR_INVALID;
+            out[l] = epi_read_offset(p0, l);
+            break;
+        default:
+            return MSWZ_ERR_INVALID;
+        }
+    }
+    return count;
+}
+
 int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m, int *tile_m, int *tile_n)
 {
     if (!tile_m || !tile_n || tiles_m <= 0 || tiles_n <= 0 || block < 0 || block >= tiles_m * tiles_n ||

@@ -53,7 +53,6 @@ constexpr int kSlots = 4;          // A stages and B register slots
 constexpr int kAhead = kSlots - 1; // K blocks in flight ahead of the one computed
 constexpr int kStageBytes = kBM * 128;
 
-__device__ __forceinline__ int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
 
 // The column-split streaming kernel: stores the workgroup's partial, which
 // splitk_reduce_kernel then sums with the others.

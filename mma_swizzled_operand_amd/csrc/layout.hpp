@@ -103,4 +103,149 @@ MSWZ_HD constexpr uint32_t tile_offset(uint32_t row, uint32_t chunk)
     return row * kTileRowBytes + ((chunk ^ tile_key(row)) << 4);
 }
 
+// Direct global -> LDS copy of a K-major tile: wave instruction q (of any
+// wave) fills LDS bytes [1024 q, 1024 q + 1024) contiguously, lane l writing
+// 16 bytes at 1024 q + 16 l, i.e. position l % 8 of tile row 8 q + l / 8.
+// The lane therefore fetches the source chunk that the layout puts there
+// (the permutation is its own inverse).
+MSWZ_HD constexpr uint32_t dma_row(int q, int lane) { return uint32_t(8 * q + (lane >> 3)); }
+MSWZ_HD constexpr uint32_t dma_chunk(int q, int lane) { return uint32_t((lane & 7) ^ (((lane >> 3) ^ q) & 7)); }
+
+// ---- MN-major operand tile ([K][R] storage, R = M or N) ----------------------
+// One K step is 64 K rows of 512 bytes (256 16-bit values); 16-byte chunk c of
+// K row k (values 8c .. 8c+7) sits at position c ^ mn_key(k).  A wave
+// instruction fills two K rows (1 KiB) contiguously: instruction q, lane l
+// writes position l % 32 of K row 2q + l / 32.
+constexpr uint32_t kMnRowBytes = 512;
+MSWZ_HD constexpr uint32_t mn_key(uint32_t k) { return (4u * (k & 3u)) ^ (2u * ((k >> 4) & 1u)); }
+MSWZ_HD constexpr uint32_t mn_tile_offset(uint32_t k, uint32_t chunk)
+{
+    return k * kMnRowBytes + ((chunk ^ mn_key(k)) << 4);
+}
+MSWZ_HD constexpr uint32_t dma_mn_krow(int q, int lane) { return uint32_t(2 * q + (lane >> 5)); }
+MSWZ_HD constexpr uint32_t dma_mn_chunk(int q, int lane)
+{
+    return uint32_t(lane & 31) ^ mn_key(dma_mn_krow(q, lane));
+}
+
+// ---- MFMA fragment maps of the 256x256 kernel ----------------------------------
+// K-block order of the 16x16x32 fragments: lane group g = l/16 of that MFMA
+// supplies 8 K values of its row, the 8-value block kblk16(g) = 2*(g%2) + g/2
+// of the 32-wide sub-step, the same for A and B (a sum over K does not depend
+// on the order of its terms).  With the natural order the 16-byte reads of
+// lanes 8p .. 8p+7 and 32+8p .. 32+8p+7, which are served together, would hit
+// the same banks; with this order the two chunks differ in their lowest bit.
+MSWZ_HD constexpr int kblk16(int g) { return 2 * (g & 1) + (g >> 1); }
+
+// First-half chunk of lane group g for the block-scaled 16x16x128 MFMA on
+// E4M3 (second half: chunk + 4).  The chunk must lie in scale block g/2, so
+// groups 0 and 1 (2 and 3) read chunks that differ only in their lowest bit;
+// E4M3 fragments therefore take their 16 rows from two runs of 8 rows 16
+// apart (row16) and groups g and g + 2 take chunks of different parity.
+MSWZ_HD constexpr int mx_chunk16(int g) { return 2 * (g >> 1) + ((g & 1) ^ (g >> 1)); }
+
+// First chunk of lane group g for the block-scaled MFMA on the padded kinds
+// (sixteen values per 16-byte chunk; the second chunk is this one ^ 1): lane
+// (row i, group g) holds the 32 values of scale block g, chunks 2g and 2g+1,
+// taken in the other order for g = 0 and 2, which keeps the reads of the
+// split-row fragments free of bank conflicts.
+MSWZ_HD constexpr int fp6_chunk16(int g) { return 2 * g + ((g & 1) ^ 1); }
+
+// First-half chunk of lane group g of an E4M3 operand paired with a padded
+// kind (second half: chunk + 4).  Values meet by an internal K index: 32g + j
+// for value j of lane group g of a 6- or 4-bit operand, 32(g/2) + 16(g%2) + j
+// for byte j < 16 of an E4M3 lane (64 more for bytes 16..31); with the padded
+// operand in fp6_chunk16 order this order makes partners share their memory
+// K position, and is free of bank conflicts with the split-row fragments.
+MSWZ_HD constexpr int mx_chunk16_mixed(int g) { return (g >> 1) ? g : g ^ 1; }
+
+// Tile row (relative to the wave's first row) of row x (0..15) of 16-row
+// fragment block b: 16-bit operands use 16 consecutive rows; the byte-row
+// (E4M3 and padded) operands rows 32*(b/2) + 8*(b%2) + {0..7, 16..23}.  Runs
+// of 4 consecutive x stay consecutive rows, so the epilogue still stores 16
+// bytes per lane.
+template <bool MX>
+MSWZ_HD constexpr int row16(int b, int x)
+{
+    return MX ? 32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3) : 16 * b + x;
+}
+
+// Scale-stage slot of row l of a 64-row group when each row's scales take 16
+// bytes (four K steps): l with bits 3 and 4 swapped (an involution).  A scale
+// read of 16-row fragment block b touches rows row16<true>(b, x), x = 0..15:
+// bits 0-2 and 4 from x, bits 3 and 5 from b; in this order they are the 16
+// consecutive slots 16 b + x.
+MSWZ_HD constexpr int sf_slot_row(int l) { return (l & ~24) | ((l & 8) << 1) | ((l & 16) >> 1); }
+
+// LDS byte offset, at sub-step 0 and first half, of this lane's piece of the
+// 32-row 32x32x16 MFMA fragment whose tile rows start at rbase (a multiple of
+// 32) in an MN-major tile, read with ds_read_b64_tr_b16.  The operand wants,
+// in lane l, row l % 32 and K values 8*(l/32) .. +7.  With lane t = l % 16 =
+// 4j + a of its group, the lane points at K row 8*(l/32) + j, values
+// rbase + 16*((l/16) % 2) + 4a .. +3; the transposing read then hands lane l
+// row rbase + l % 32 and K values 8*(l/32) .. +3.  The second half (K + 4)
+// is 4 rows further, sub-step ks 16*ks rows further and, as bit 4 of its K
+// rows is ks % 2, with its chunk XOR 2 (byte offset XOR 32) for odd ks.
+MSWZ_HD constexpr uint32_t mn_frag_base(uint32_t tile_off, int rbase, int lane)
+{
+    const int t = lane & 15, j = t >> 2, a = t & 3, g1 = (lane >> 4) & 1, h = lane >> 5;
+    const int chunk = rbase / 8 + 2 * g1 + (a >> 1);
+    return tile_off + uint32_t(8 * h + j) * kMnRowBytes + (uint32_t(chunk ^ (4 * j)) << 4) + 8 * (a & 1);
+}
+
+// The same for the 16-row fragment of the 16x16x32 MFMA in an MN-major tile:
+// lane t = l % 16 = 4j + a of group g points at K row 8*kblk16(g) + j (bit 4
+// of which is g % 2), values rbase + 4a .. +3; the second half is 4 K rows
+// further, sub-step s 32*s rows further.
+MSWZ_HD constexpr uint32_t mn_frag_base16(uint32_t tile_off, int rbase, int lane)
+{
+    const int t = lane & 15, j = t >> 2, a = t & 3, g = lane >> 4;
+    const int chunk = (rbase / 8 + (a >> 1)) ^ (4 * j) ^ (2 * (g & 1));
+    return tile_off + uint32_t(8 * kblk16(g) + j) * kMnRowBytes + (uint32_t(chunk) << 4) + 8 * (a & 1);
+}
+
+// K-major fragment read base of 16x16 block b: tile rows rbase +
+// row16<MX>(b, l % 16), 16-byte chunk `chunk` (the lane group's, see the
+// chunk orders above).  Sub-steps and second halves are this base XOR a
+// constant: 16-bit and E2M1 sub-step s: ^ (s << 6); E4M3 second half: ^ 64;
+// padded kinds' second chunk: ^ 16.
+template <bool MX>
+MSWZ_HD constexpr uint32_t kfrag_base(uint32_t tile_off, int rbase, int b, int chunk, int lane)
+{
+    return tile_off + tile_offset(uint32_t(rbase + row16<MX>(b, lane & 15)), uint32_t(chunk));
+}
+
+// ---- staged epilogue ------------------------------------------------------------
+// Each wave writes a quarter q of its 128 x 64 fp32 tile (32 rows) into its
+// own 8 KiB area, rows kEpiPitch = 256 bytes apart, then reads it back as 4
+// rows x 256 bytes per instruction.  16-byte chunk c of row r sits at chunk
+// c ^ epi_key(r), epi_key(r) = row bits 0 and 1 swapped, bit 2 kept.
+// Measured bank behaviour (SQ_LDS_BANK_CONFLICT on two layouts of this
+// epilogue, together with the calibrated read model): a 16-byte write is
+// served 8 consecutive lanes at a time, a 16-byte read 16 lanes at a time,
+// the lanes that agree in lane bits 1 and 5.  A write's 8 lanes hold rows
+// that differ in bits 0..2 and one chunk, so the key's bijection on those
+// bits puts them in 8 distinct 4-bank groups; a read's 16 lanes hold rows
+// that differ in bit 0 and chunks that differ in bits 0, 2 and 3, and the
+// key moves row bit 0 to chunk bit 1.
+constexpr uint32_t kEpiPitch = 256;
+MSWZ_HD constexpr uint32_t epi_key(uint32_t row)
+{
+    return ((row & 1u) << 1) | ((row >> 1) & 1u) | (row & 4u);
+}
+// the 16 bytes (4 columns) of 16x16 block (i = 2q + ii, j) that lane l holds
+template <bool MX>
+MSWZ_HD constexpr uint32_t epi_write_offset(int q, int ii, int j, int lane)
+{
+    const uint32_t row = uint32_t(row16<MX>(2 * q + ii, lane & 15) - 32 * q);
+    const uint32_t chunk = uint32_t(row16<MX>(j, 4 * (lane >> 4))) / 4;
+    return row * kEpiPitch + ((chunk ^ epi_key(row)) << 4);
+}
+// read-back instruction k: lane l reads row 4k + l/16, columns 4(l%16) .. +3
+MSWZ_HD constexpr uint32_t epi_read_offset(int k, int lane)
+{
+    const uint32_t row = uint32_t(4 * k + (lane >> 4));
+    return row * kEpiPitch + ((uint32_t(lane & 15) ^ epi_key(row)) << 4);
+}
+
 }  // namespace mswz

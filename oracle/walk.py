@@ -142,3 +142,28 @@ def bank_conflict_degree(byte_addrs, access_bytes: int, banks: int, lanes_per_cy
                 per_bank.setdefault(word % banks, set()).add(word)
         worst = max(worst, max(len(s) for s in per_bank.values()))
     return worst
+
+
+def mn_tile_key_table() -> list[int]:
+    """Chunk XOR key of each K row of the kernels' MN-major tile (64 K rows of
+    32 chunks): 4 x (k mod 4), with the bit of value 2 set for K rows 16..31
+    and 48..63 (the half of a 32-row block that the odd sub-step's fragments
+    read)."""
+    table = []
+    for k in range(64):
+        key = [0, 4, 8, 12][k % 4]
+        if (k // 16) % 2 == 1:
+            key ^= 2
+        table.append(key)
+    return table
+
+
+def mn_tile_bruteforce() -> np.ndarray:
+    """Byte offset of 16-byte chunk (k, c) of an MN-major tile of 64 K rows of
+    512 bytes: chunk c lands at chunk position c XOR key(k)."""
+    keys = mn_tile_key_table()
+    out = np.zeros((64, 32), dtype=np.int64)
+    for k in range(64):
+        for c in range(32):
+            out[k, c] = k * 512 + (c ^ keys[k]) * 16
+    return out
