@@ -257,11 +257,14 @@ def cpu_baseline(w, x, target_s):
                     rows=list(range(r)))
         return time.perf_counter() - t0
 
+    # each call also decodes all of B once, so the first small sample
+    # overstates the time per row: grow in up to three rounds
     r = min(threads, w.M)
     t = run(r)
-    grow = max(1, min(int(target_s / max(t, 1e-3)), w.M // r))
-    if grow > 1:
-        r *= grow
+    for _ in range(3):
+        if t >= 0.6 * target_s or r >= w.M:
+            break
+        r = min(w.M, max(r + threads, int(r * target_s / max(t, 1e-3)) // threads * threads))
         t = run(r)
     flops = 2.0 * r * w.N * w.K
     return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
