@@ -554,7 +554,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", "c11", "c12",
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", "c11", "c12",
                                   *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole
