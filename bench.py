@@ -8,8 +8,8 @@ GEMM with both operands K-major (N(0,1) inputs, seed 0), the metric's "bf16
 8192^3".  The other workloads (the single 128x256x64 tile, 4096^3 bf16,
 8192^3 fp16 MN-major A with beta=1, the skinny 64x16384x8192 weight-streaming
 shape, 8192^3 MX-fp8 -- the metric's second configuration --, 8192^3 MX-fp4,
-MX-fp6 in both 6-bit formats, E4M3 A against E2M3 or padded E2M1 B, and bf16
-8192^3 with B MN-major or both operands MN-major) are timed in the same run
+MX-fp6 in both 6-bit formats, E4M3 A against E2M3, padded E2M1 or dense E2M1
+B, and bf16 8192^3 with B MN-major or both operands MN-major) are timed in the same run
 and reported under "also", each with its own roofline and sampled oracle
 baseline.
 
@@ -298,7 +298,7 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=250.0,
                     help="keep warming up until this many ms of back-to-back launches have passed")
     ap.add_argument("--workload", default="c3b")
-    ap.add_argument("--also", default="c5,c1,c2,c3,c4,c6,c7,c8,c9,c10,c11,c12",
+    ap.add_argument("--also", default="c5,c1,c2,c3,c4,c6,c7,c8,c9,c10,c11,c12,c13",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--cold-calls", type=int, default=50,
                     help="after the timed steps, time this many single calls of each workload "

@@ -101,9 +101,10 @@ typedef struct gemm_plan gemm_plan;
  *                 rounding); narrow D always uses the 256 tile
  *                 Supported: (F16,F16), (BF16,BF16) dense; (E4M3,E4M3) and
  *                 (E2M1,E2M1), (E2M3,E2M3), (E3M2,E3M2), (E2M1_P64,E2M1_P64)
- *                 block-scaled, and any mix of E4M3, E2M3, E3M2 and E2M1_P64
- *                 for A and B (the pages' mixed f8f6f4 kind; each operand
- *                 decoded in its own format, 256 tile).
+ *                 block-scaled, any mix of E4M3, E2M3, E3M2 and E2M1_P64
+ *                 for A and B, and (E4M3,E2M1), (E2M1,E4M3) (the pages' mixed
+ *                 f8f6f4 kind; each operand decoded in its own format, 256
+ *                 tile).
  *   a_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   b_major       MSWZ_MAJOR_K or MSWZ_MAJOR_MN (MN only for 16-bit formats)
  *   scale_vec_len 0 for dense; 32 (one scale per 32 K elements) for E4M3, E2M1,
@@ -111,7 +112,9 @@ typedef struct gemm_plan gemm_plan;
  *                 elements: the pages' scale_vec::4X) for E2M1, E2M1_P64,
  *                 E2M3 and E3M2 with A and B of the same kind
  * Shape rules: block-scaled K: any multiple of scale_vec_len (E2M1: of 32 as
- * well, so that rows of K/2 bytes stay 16-byte aligned); a K that is not a
+ * well, so that rows of K/2 bytes stay 16-byte aligned; E4M3 with dense E2M1:
+ * a multiple of 512, as that kernel stages the E2M1 operand two of the E4M3
+ * operand's 128-element steps at a time and pipelines four); a K that is not a
  * multiple of the kernel's K step (128 elements; E2M1 256) uses the 256 tile,
  * whose last K step reads the values beyond K as zeros and gives their scale
  * blocks the exponent 127 (the scale array itself holds K/V bytes per row,
@@ -335,20 +338,27 @@ int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m,
  *                       4-bit fragment                                   (128)
  *   MSWZ_LDS_FRAG_E4M3_MIXED  p0 = b: E4M3 paired with a padded kind     (128)
  *   MSWZ_LDS_FRAG_E2M1  p0 = b, p1 = sub-step (0..1): the 16-byte read of a
- *                       dense E2M1 fragment                               (64)
+ *                       dense E2M1 fragment (paired with E4M3: p1 = the
+ *                       half of its two-step tile row)                    (64)
+ *   MSWZ_LDS_FRAG_E4M3_FP4  p0 = b: the two 16-byte reads of an E4M3
+ *                       fragment paired with dense E2M1                  (128)
  *   MSWZ_LDS_SCALE_GRP  p0 = b (0..7), p1 = step in its group of four (0..3):
  *                       the scale byte each lane reads (A side, wave rows 0..127)
  *   MSWZ_LDS_SCALE_DMA  p0 = wave (0..7): out[2l] = stage offset lane l writes
  *                       (16 bytes), out[2l+1] = the row of its 64-row group
  *                       whose four steps' scale bytes it copies        (128)
- *   MSWZ_LDS_EPI_WRITE  p0 = quarter q (0..3), p1 = 16*byte_rows + 4*ii + j:
- *                       the 16-byte write of 16x16 block (2q + ii, j)    (64)
+ *   MSWZ_LDS_EPI_WRITE  p0 = quarter q (0..3), p1 = 16*rows + 4*ii + j: the
+ *                       16-byte write of 16x16 block (2q + ii, j); rows 0:
+ *                       16-bit, 1: split-row fragments on both sides (E4M3,
+ *                       padded kinds), 2: on the M side only (E4M3 A with
+ *                       dense E2M1 B), 3: on the N side only            (64)
  *   MSWZ_LDS_EPI_READ   p0 = read-back instruction k (0..7)              (64)
  */
 enum {
     MSWZ_LDS_DMA_K = 1, MSWZ_LDS_DMA_MN = 2, MSWZ_LDS_FRAG_K16 = 3, MSWZ_LDS_FRAG_MN16 = 4,
     MSWZ_LDS_FRAG_E4M3 = 5, MSWZ_LDS_FRAG_PAD = 6, MSWZ_LDS_FRAG_E4M3_MIXED = 7, MSWZ_LDS_FRAG_E2M1 = 8,
-    MSWZ_LDS_SCALE_GRP = 9, MSWZ_LDS_SCALE_DMA = 10, MSWZ_LDS_EPI_WRITE = 11, MSWZ_LDS_EPI_READ = 12
+    MSWZ_LDS_SCALE_GRP = 9, MSWZ_LDS_SCALE_DMA = 10, MSWZ_LDS_EPI_WRITE = 11, MSWZ_LDS_EPI_READ = 12,
+    MSWZ_LDS_FRAG_E4M3_FP4 = 13
 };
 int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n);
 

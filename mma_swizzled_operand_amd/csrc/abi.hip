@@ -128,21 +128,23 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
         return MSWZ_ERR_INVALID;
     if (scale_vec_len < 0)
         return MSWZ_ERR_INVALID;
-    // A and B share a kind, except that E4M3, E2M3 and E3M2 mix freely
+    // A and B share a kind, except that E4M3, E2M3, E3M2 and padded E2M1 mix
+    // freely, and E4M3 pairs with dense E2M1
     auto byte_mx = [](int d) {
         return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2 || d == MSWZ_DT_E2M1_P64;
     };
-    if ((a_dt != b_dt && !(byte_mx(a_dt) && byte_mx(b_dt))) || a_dt == MSWZ_DT_F32)
+    const bool pair = (a_dt == MSWZ_DT_E4M3 && b_dt == MSWZ_DT_E2M1) || (a_dt == MSWZ_DT_E2M1 && b_dt == MSWZ_DT_E4M3);
+    if ((a_dt != b_dt && !(byte_mx(a_dt) && byte_mx(b_dt)) && !pair) || a_dt == MSWZ_DT_F32)
         return MSWZ_ERR_UNSUPPORTED;
     const bool mixed = a_dt != b_dt;
     // D: fp32, or the fp32 result rounded to bf16 / fp16 (the 256 tile only)
     if (d_dt != MSWZ_DT_F32 && d_dt != MSWZ_DT_BF16 && d_dt != MSWZ_DT_F16)
         return MSWZ_ERR_UNSUPPORTED;
     const bool narrow_d = d_dt != MSWZ_DT_F32;
-    const bool fp4 = a_dt == MSWZ_DT_E2M1;
+    const bool fp4 = a_dt == MSWZ_DT_E2M1 && !pair, any_fp4 = a_dt == MSWZ_DT_E2M1 || b_dt == MSWZ_DT_E2M1;
     // padded sub-byte kinds (sixteen values per 16-byte block)
     const bool fp6 = a_dt == MSWZ_DT_E2M3 || a_dt == MSWZ_DT_E3M2 || a_dt == MSWZ_DT_E2M1_P64;
-    const bool fp8 = a_dt == MSWZ_DT_E4M3 || fp4 || fp6;   // block-scaled formats
+    const bool fp8 = a_dt == MSWZ_DT_E4M3 || a_dt == MSWZ_DT_E2M1 || fp6;   // block-scaled formats
     if (fp8 != (scale_vec_len != 0))
         return MSWZ_ERR_UNSUPPORTED;     // 8-, 6- and 4-bit kinds are block-scaled only; 16-bit is dense only
     // 32 K elements per scale byte; 16 (the pages' scale_vec::4X for 4-bit
@@ -159,7 +161,11 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     // registers.  16-bit: any K whose K-major rows keep 16-byte alignment
     // (K % 8 == 0 unless both operands are MN-major); a K that is not a
     // multiple of 64 takes the 256x256 tile with a zero-padded last step.
-    if (fp8 && (K % scale_vec_len != 0 || (fp4 && K % 32 != 0)))
+    if (fp8 && (K % scale_vec_len != 0 || (any_fp4 && K % 32 != 0)))
+        return MSWZ_ERR_UNSUPPORTED;
+    // E4M3 with dense E2M1: the E2M1 operand's 128-byte rows hold two K steps
+    // of the E4M3 one, and its pipeline takes four steps at a time
+    if (pair && K % 512 != 0)
         return MSWZ_ERR_UNSUPPORTED;
     const bool ktail = fp8 ? K % (fp4 ? 256 : 128) != 0 : K % 64 != 0;
     if (ktail && K % 8 != 0 && (a_major == MSWZ_MAJOR_K || b_major == MSWZ_MAJOR_K))
@@ -182,9 +188,9 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     constexpr int64_t kMaxLd = int64_t(1) << 22;
     if (lda_v > kMaxLd || ldb_v > kMaxLd || ldd_v > kMaxLd)
         return MSWZ_ERR_UNSUPPORTED;
-    const int64_t align_elems = fp4 ? 32 : fp8 ? 16 : 8;   // elements in 16 bytes
+    auto align_elems = [&](int dt) { return dt == MSWZ_DT_E2M1 ? 32 : fp8 ? 16 : 8; };   // elements in 16 bytes
     const bool strided = lda_v != a_cols || ldb_v != b_cols || ldd_v != N;
-    if (strided && (lda_v % align_elems || ldb_v % align_elems || ldd_v % 4))
+    if (strided && (lda_v % align_elems(a_dt) || ldb_v % align_elems(b_dt) || ldd_v % 4))
         return MSWZ_ERR_UNSUPPORTED;
     // MN-major operands are addressed with 32-bit offsets from the start of
     // the [K][M] / [K][N] array
@@ -396,7 +402,8 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
     auto in = [](int v, int lo, int hi) { return v >= lo && v < hi; };
     const int count = (pattern == MSWZ_LDS_DMA_K || pattern == MSWZ_LDS_DMA_MN || pattern == MSWZ_LDS_FRAG_MN16 ||
                        pattern == MSWZ_LDS_FRAG_E4M3 || pattern == MSWZ_LDS_FRAG_PAD ||
-                       pattern == MSWZ_LDS_FRAG_E4M3_MIXED || pattern == MSWZ_LDS_SCALE_DMA)
+                       pattern == MSWZ_LDS_FRAG_E4M3_MIXED || pattern == MSWZ_LDS_FRAG_E4M3_FP4 ||
+                       pattern == MSWZ_LDS_SCALE_DMA)
                           ? 128 : 64;
     if (!out || n < count)
         return MSWZ_ERR_INVALID;
@@ -441,6 +448,14 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
             out[2 * l + 1] = base ^ (pattern == MSWZ_LDS_FRAG_PAD ? 16u : 64u);
             break;
         }
+        case MSWZ_LDS_FRAG_E4M3_FP4: {
+            if (!in(p0, 0, 16))
+                return MSWZ_ERR_INVALID;
+            const uint32_t base = kfrag_base<true>(0, 0, p0, pair_chunk16(g), l);
+            out[2 * l] = base;
+            out[2 * l + 1] = base ^ 32u;
+            break;
+        }
         case MSWZ_LDS_SCALE_GRP:
             // grouped scale stage: 16 bytes per row slot, block b of row x in slot 16b + x
             if (!in(p0, 0, 8) || !in(p1, 0, 4))
@@ -454,10 +469,13 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
             out[2 * l + 1] = uint32_t(sf_slot_row(l));
             break;
         case MSWZ_LDS_EPI_WRITE: {
-            const int mx = p1 >> 4, ii = (p1 >> 2) & 3, j = p1 & 3;
-            if (!in(p0, 0, 4) || mx > 1 || ii > 1 || p1 < 0)
+            const int rows = p1 >> 4, ii = (p1 >> 2) & 3, j = p1 & 3;
+            if (!in(p0, 0, 4) || rows > 3 || ii > 1 || p1 < 0)
                 return MSWZ_ERR_INVALID;
-            out[l] = mx ? epi_write_offset<true>(p0, ii, j, l) : epi_write_offset<false>(p0, ii, j, l);
+            out[l] = rows == 0 ? epi_write_offset<false, false>(p0, ii, j, l)
+                     : rows == 1 ? epi_write_offset<true, true>(p0, ii, j, l)
+                     : rows == 2 ? epi_write_offset<true, false>(p0, ii, j, l)
+                                 : epi_write_offset<false, true>(p0, ii, j, l);
             break;
         }
         case MSWZ_LDS_EPI_READ:

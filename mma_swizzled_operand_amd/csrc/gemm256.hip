@@ -2,7 +2,7 @@
 // to its instantiations, one translation unit per operand kind and A major
 // (gemm256_bf16_ak.hip, gemm256_bf16_amn.hip, gemm256_f16_ak.hip,
 // gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e2m1.hip, gemm256_fp6.hip,
-// gemm256_mixed.hip, gemm256_v16.hip),
+// gemm256_mixed.hip, gemm256_pair.hip, gemm256_v16.hip),
 // so that they
 // compile in parallel.
 #include <hip/hip_runtime.h>
@@ -24,8 +24,11 @@ hipError_t launch_mx256(const MxArgs &a, MxKind kind, MxKind kind_b, hipStream_t
 {
     if (a.sv == 16)
         return kind_b == kind ? launch256_v16(a, kind, stream) : hipErrorInvalidValue;
-    if (kind_b != kind)
+    if (kind_b != kind) {
+        if (kind == kMxE2m1 || kind_b == kMxE2m1)
+            return launch256_pair(a, kind, kind_b, stream);
         return launch256_mixed(a, kind, kind_b, stream);
+    }
     switch (kind) {
     case kMxE2m1: return launch256_e2m1(a, stream);
     case kMxE2m3: case kMxE3m2: case kMxE2m1p: return launch256_padded(a, kind, stream);

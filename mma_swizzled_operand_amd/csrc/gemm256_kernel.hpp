@@ -89,6 +89,16 @@ struct DmaOperand {
             buffer_load_lds16(rsrc, stage + lds_off + i * 8 * W * kTileRowBytes, voff[i], uint32_t(kt) * 128);
     }
 
+    // instructions [half * kInstr / 2, (half + 1) * kInstr / 2) of issue()
+    __device__ void issue_half(uint8_t *stage, int kt, int half) const
+    {
+#pragma unroll
+        for (int i = 0; i < kInstr / 2; ++i) {
+            const int q = half * (kInstr / 2) + i;
+            buffer_load_lds16(rsrc, stage + lds_off + q * 8 * W * kTileRowBytes, voff[q], uint32_t(kt) * 128);
+        }
+    }
+
     // The partial last K step kt of a K that is not a multiple of the step:
     // only the first `lim` bytes of each row's 128-byte slice lie inside K (a
     // multiple of 16, so chunks are whole).  The whole offset goes into the
@@ -304,7 +314,8 @@ __device__ __forceinline__ bool apply_opts(const EpiOpts &o, int m, int n, f32x4
 constexpr int W = 8;
 
 // KIND: element kind of A (and of B unless KB >= 0); KB: B's kind when it
-// differs (block-scaled E4M3 / E2M3 / E3M2 / padded E2M1 only); SV: K
+// differs (block-scaled E4M3 / E2M3 / E3M2 / padded E2M1 among themselves,
+// or E4M3 with dense E2M1 on either side); SV: K
 // elements per scale byte (32, or 16 for E2M1 and the padded kinds); MF16:
 // 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major);
 // SB: block-scaled K that is not a multiple of the K step (scale bytes
@@ -322,16 +333,23 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr int kWavesN = 256 / (32 * TN);     // waves along N
     constexpr int kKindB = KB < 0 ? KIND : KB;
     constexpr bool kMixed = kKindB != KIND;
-    static_assert(!kMixed || (byte_row_kind(KIND) && byte_row_kind(kKindB)),
-                  "mixed operand kinds are built for E4M3 and the padded 6- and 4-bit kinds");
+    // E4M3 paired with dense E2M1 (compute_pair): kPairB with E2M1 as B,
+    // kPairA with E2M1 as A
+    constexpr bool kPairB = KIND == kE4m3 && kKindB == kE2m1, kPairA = KIND == kE2m1 && kKindB == kE4m3;
+    constexpr bool kPair = kPairA || kPairB;
+    static_assert(!kMixed || kPair || (byte_row_kind(KIND) && byte_row_kind(kKindB)),
+                  "mixed operand kinds: E4M3 and the padded 6- and 4-bit kinds, or E4M3 with dense E2M1");
     constexpr bool kFp6B = padded_kind(kKindB);
     // A's kind below; B's differs only in the fragment reads and the MFMA format.
     // kFp6: a padded sub-byte kind (E2M3, E3M2 or padded E2M1).
-    constexpr bool kFp8 = KIND == kE4m3, kFp4 = KIND == kE2m1, kFp6 = padded_kind(KIND);
-    constexpr bool kMx = kFp8 || kFp4 || kFp6;
+    constexpr bool kFp8 = KIND == kE4m3 && !kPair, kFp4 = KIND == kE2m1 && !kPair, kFp6 = padded_kind(KIND);
+    constexpr bool kMx = kFp8 || kFp4 || kFp6 || kPair;
     // E4M3 and padded 6-bit operands share the byte layout (128 values per
     // 128-byte row step) and the split-row fragments
     constexpr bool kByteRows = kFp8 || kFp6;
+    // split-row fragments on A's and on B's side (row16<true>): the output
+    // rows and columns follow them
+    constexpr bool kRowsA = kPair ? kPairB : kByteRows, kRowsB = kPair ? kPairA : kByteRows;
     static_assert(!kMx || MF16, "block-scaled kinds are built for the 16x16 MFMA");
     // 16-element scale blocks: a lane's 32 values of a 32-block are two
     // 16-element halves (one 16-byte chunk of a padded kind, or the two 8-byte
@@ -341,7 +359,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     static_assert(SV == 32 || (kV16 && (kFp4 || kFp6) && !kMixed), "16-element blocks: E2M1 and padded kinds");
     // one step moves 128 bytes of every tile row: 64 16-bit, 128 E4M3 or 256
     // E2M1 (packed two per byte) K elements
-    constexpr int kStepK = kFp4 ? 256 : kByteRows ? 128 : 64;
+    // (with kPair the E4M3 operand's 128; the E2M1 operand's 128-byte rows
+    // then hold two steps)
+    constexpr int kStepK = kPair ? 128 : kFp4 ? 256 : kByteRows ? 128 : 64;
+    constexpr int kStepA = kPairA ? 256 : kStepK, kStepB = kPairB ? 256 : kStepK;
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
@@ -357,7 +378,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * TN);
     // bytes from one K-major operand row to the next (lda, ldb are in elements)
-    const uint32_t a_row_bytes = uint32_t(lda) * 128 / kStepK, b_row_bytes = uint32_t(ldb) * 128 / kStepK;
+    const uint32_t a_row_bytes = uint32_t(lda) * 128 / kStepA, b_row_bytes = uint32_t(ldb) * 128 / kStepB;
     const int KT = K / kStepK;
     // M and N need not be multiples of 256: a tail tile reads zeros (K-major
     // rows beyond the operand, through the buffer range) or values that only
@@ -393,7 +414,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
-    constexpr bool kScaleGroups = kByteRows && !kV16 && !SB;   // E4M3 and the padded kinds, 32-element blocks
+    constexpr bool kScaleGroups = kByteRows && !kV16 && !SB && !kPair;   // E4M3 and the padded kinds, 32-element blocks
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / SV;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -524,14 +545,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < TM16; ++i) {
-            const int c = kFp6 ? fp6_chunk16(g) : kFp8 ? (kMixed ? mx_chunk16_mixed(g) : mx_chunk16(g)) : kblk16(g);
-            abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane) : kfrag_base<kByteRows>(0, wm, i, c, lane);
+            const int c = kPair ? (kPairB ? pair_chunk16(g) : kblk16(g))
+                          : kFp6 ? fp6_chunk16(g) : kFp8 ? (kMixed ? mx_chunk16_mixed(g) : mx_chunk16(g)) : kblk16(g);
+            abase16[i] = kTrA ? mn_frag_base16(0, wm + 16 * i, lane) : kfrag_base<kRowsA>(0, wm, i, c, lane);
         }
 #pragma unroll
         for (int j = 0; j < TN16; ++j) {
-            const int c = kMixed ? (kFp6B ? fp6_chunk16(g) : mx_chunk16_mixed(g))
-                                 : kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
-            bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane) : kfrag_base<kByteRows>(kATile, wn, j, c, lane);
+            const int c = kPair ? (kPairA ? pair_chunk16(g) : kblk16(g))
+                          : kMixed ? (kFp6B ? fp6_chunk16(g) : mx_chunk16_mixed(g))
+                                   : kFp6 ? fp6_chunk16(g) : kFp8 ? mx_chunk16(g) : kblk16(g);
+            bbase16[j] = kTrB ? mn_frag_base16(kATile, wn + 16 * j, lane) : kfrag_base<kRowsB>(kATile, wn, j, c, lane);
         }
     }
 
@@ -825,6 +848,68 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         });
     };
 
+    // E4M3 paired with dense E2M1 (kPair), one 128-element K step: the E4M3
+    // operand's tile in stage s8 (its split-row fragments, chunks
+    // pair_chunk16(g) and that ^ 2), the E2M1 operand's in stage s4 (its
+    // 128-byte rows hold two steps; half h = the step's parity: contiguous
+    // fragment rows, chunk 4h + kblk16(g), one 32-element block per lane in
+    // the low four registers).  Both sides' lane group g supplies the scale
+    // of memory block kblk16(g) of the step: that byte of the row's per-step
+    // scale word (rows in natural order, 4 bytes apart).
+    auto compute_pair = [&](const uint8_t *s8, const uint8_t *s4, int h, const uint8_t *ss) {
+        uint32_t ab[TM16], bb[TN16];
+#pragma unroll
+        for (int i = 0; i < TM16; ++i)
+            ab[i] = opaque(abase16[i]);
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+            bb[j] = opaque(bbase16[j]);
+        const int r16 = lane & 15, kb = kblk16(lane >> 4);
+        const uint32_t sfa = opaque(uint32_t(4 * (wm + (kRowsA ? row16<true>(0, r16) : r16)) + kb));
+        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + (kRowsB ? row16<true>(0, r16) : r16)) + kb));
+        auto sf_off = [](bool split, int b) { return 4 * (split ? 32 * (b >> 1) + 8 * (b & 1) : 16 * b); };
+        const u32x4 zero = {0, 0, 0, 0};
+        auto frag8 = [&](uint32_t base) {
+            const u32x4 lo = lds_read16(s8, base), hi = lds_read16(s8, base ^ 32u);
+            return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto frag4 = [&](uint32_t base) {
+            const u32x4 v = lds_read16(s4, base ^ uint32_t(h << 6));
+            return __builtin_bit_cast(i32x8, __builtin_shufflevector(v, zero, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // reads (fragment and scale) per A and per B item of the schedule
+        constexpr int kReadsA = kRowsA ? 3 : 2, kReadsB = kRowsB ? 3 : 2;
+        using Sched = FragSchedule<TM16, TN16, 2>;
+        uint32_t sa[TM16], sb[TN16];
+        i32x8 bf[TN16], af[TM16];
+        static_for<0, TM16 * TN16>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int c0 = m == 0 ? 0 : Sched::issued(m - 1), c1 = Sched::issued(m);
+            constexpr int reads = [] {
+                int r = 0;
+                for (int c = c0; c < c1; ++c)
+                    r += Sched::item(c) > 0 ? kReadsA : kReadsB;
+                return r;
+            }();
+            static_for<c0, c1>([&](auto rc) {
+                constexpr int it = Sched::item(decltype(rc)::value);
+                if constexpr (it > 0) {
+                    sa[it - 1] = ss[sfa + sf_off(kRowsA, it - 1)];
+                    af[it - 1] = kRowsA ? frag8(ab[it - 1]) : frag4(ab[it - 1]);
+                } else {
+                    sb[-it - 1] = ss[sfb + sf_off(kRowsB, -it - 1)];
+                    bf[-it - 1] = kRowsB ? frag8(bb[-it - 1]) : frag4(bb[-it - 1]);
+                }
+            });
+            if constexpr (c1 > c0)
+                __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);   // DS reads
+            constexpr int i = m / TN16, j = m % TN16;
+            acc4[j][i] = mfma_scale_16x16x128_fmt<mx_format<kKindB>(), mx_format<KIND>()>(bf[j], af[i], acc4[j][i],
+                                                                                          sb[j], sa[i]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+        });
+    };
+
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kFp4)
             compute_fp4(s, ss);
@@ -843,6 +928,53 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // has no branches: in the last pair of an even step count the copy into
     // lds0 repeats step KT-1 into a stage nobody reads again, which keeps the
     // compiler from draining the copies in flight at a control-flow merge. ------
+    if constexpr (kPair) {
+        // E4M3 with dense E2M1 (K a multiple of 512; the host launches no
+        // other): four K steps per iteration.  The E4M3 operand's stages
+        // alternate lds0 / lds1 every step; the E2M1 operand's 128-byte tile
+        // rows hold two steps, so its tile for steps 2p and 2p+1 sits in its
+        // part of stage p % 2 and is copied half during each of the two steps
+        // before, into a stage whose last reader ended at the barrier before
+        // them.  Scale words go per step into scl0 / scl1.  Copies beyond the
+        // end repeat the last step or pair into a stage nobody reads again, so
+        // the loop has no branches.
+        DmaOperand<W> &d8 = kPairB ? da : db;
+        DmaOperand<W> &d4 = kPairB ? db : da;
+        const int NP = KT / 2;
+        auto issue_sf = [&](uint8_t *sstage, int kt) {
+            buffer_load_lds4(sf_rsrc[0], sstage + 256 * wave, sf_voff, 4u * uint32_t(kt));
+        };
+        static_assert(kSfInstr == 1 && kWords == 1, "one per-step scale word per row, one copy per wave");
+        d8.issue(lds0, 0);
+        d4.issue(lds0, 0);
+        issue_sf(scl0, 0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; kt += 4) {
+            const int p = kt / 2;
+            d8.issue(lds1, kt + 1);
+            d4.issue_half(lds1, min(p + 1, NP - 1), 0);
+            issue_sf(scl1, kt + 1);
+            compute_pair(lds0, lds0, 0, scl0);
+            lds_barrier_keep_vm<0>();
+            d8.issue(lds0, min(kt + 2, KT - 1));
+            d4.issue_half(lds1, min(p + 1, NP - 1), 1);
+            issue_sf(scl0, min(kt + 2, KT - 1));
+            compute_pair(lds1, lds0, 1, scl1);
+            lds_barrier_keep_vm<0>();
+            d8.issue(lds1, min(kt + 3, KT - 1));
+            d4.issue_half(lds0, min(p + 2, NP - 1), 0);
+            issue_sf(scl1, min(kt + 3, KT - 1));
+            compute_pair(lds0, lds1, 0, scl0);
+            lds_barrier_keep_vm<0>();
+            d8.issue(lds0, min(kt + 4, KT - 1));
+            d4.issue_half(lds0, min(p + 2, NP - 1), 1);
+            issue_sf(scl0, min(kt + 4, KT - 1));
+            compute_pair(lds1, lds1, 1, scl1);
+            lds_barrier_keep_vm<0>();
+        }
+        __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+        goto epilogue;
+    }
     if constexpr (kScaleGroups) {
         if (KT % 8 == 0) {
             // Eight K steps per iteration: operand stages alternate lds0 /
@@ -904,6 +1036,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             goto epilogue;
         }
     }
+    if constexpr (!kPair) {
     if (KT > 0) {
     issue_step(lds0, scl0, 0);
     put_scales(scl0);
@@ -923,6 +1056,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     if (kt < KT)
         compute(lds0, scl0);
     __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+    }
     }
     // K not a multiple of the step (operands copied straight into LDS, and
     // for block-scaled kinds the SB scale path; the host launches no other
@@ -974,7 +1108,7 @@ epilogue:
             for (int j = 0; j < TN16; ++j)
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii)
-                    *reinterpret_cast<f32x4 *>(area + epi_write_offset<kByteRows>(q, ii, j, lane)) = acc4[j][2 * q + ii];
+                    *reinterpret_cast<f32x4 *>(area + epi_write_offset<kRowsA, kRowsB>(q, ii, j, lane)) = acc4[j][2 * q + ii];
             wave_lds_sync();
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -998,8 +1132,8 @@ epilogue:
         for (int j = 0; j < TN16; ++j)
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
-                const int m = m0 + wm + row16<kByteRows>(i, lane & 15);
-                const int n = n0 + wn + row16<kByteRows>(j, 4 * (lane >> 4));
+                const int m = m0 + wm + row16<kRowsA>(i, lane & 15);
+                const int n = n0 + wn + row16<kRowsB>(j, 4 * (lane >> 4));
                 if (m >= M || n >= N)
                     continue;
                 f32x4 v = acc4[j][i];
@@ -1008,7 +1142,7 @@ epilogue:
                 // 16-bit and E2M1 blocks: the four lanes of a row hold 16
                 // consecutive columns (64 bytes of fp32 D); byte-row blocks:
                 // two runs of 8, and 16-bit D halves the piece
-                store_d4<OUT, BETA, !kByteRows && OUT == kOutF32>(D, size_t(m) * ldd + n, v, opts.sat);
+                store_d4<OUT, BETA, !(kRowsA || kRowsB) && OUT == kOutF32>(D, size_t(m) * ldd + n, v, opts.sat);
             }
         return;
     }
@@ -1069,7 +1203,9 @@ hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
-    if constexpr (KIND != kBf16 && KIND != kF16) {
+    // E4M3 with dense E2M1: K is a multiple of 512 (no SB variant)
+    constexpr bool kPairKinds = (KIND == kE4m3 && KB == kE2m1) || (KIND == kE2m1 && KB == kE4m3);
+    if constexpr (KIND != kBf16 && KIND != kF16 && !kPairKinds) {
         constexpr int kStep = KIND == kE2m1 ? 256 : 128;
         if (a.K % kStep != 0)
             return launch_out<KIND, A_MN, B_MN, KB, SV, true>(a, stream);

@@ -159,6 +159,15 @@ MSWZ_HD constexpr int fp6_chunk16(int g) { return 2 * g + ((g & 1) ^ 1); }
 // K position, and is free of bank conflicts with the split-row fragments.
 MSWZ_HD constexpr int mx_chunk16_mixed(int g) { return (g >> 1) ? g : g ^ 1; }
 
+// First-half chunk of lane group g of an E4M3 operand paired with dense
+// E2M1 (second half: chunk ^ 2).  The E2M1 operand's lane group g holds the
+// 32 values of its step block kblk16(g) (one 16-byte chunk) at internal K
+// index 32g + j; the E4M3 lanes' internal indices (32(g/2) + 16(g%2) + j,
+// plus 64 for bytes 16..31) then name memory K 16 * pair_chunk16(g) + j and,
+// for the second half, that + 32: groups (0, 1, 2, 3) read chunks
+// (0, 1, 4, 5) and (2, 3, 6, 7).
+MSWZ_HD constexpr int pair_chunk16(int g) { return (g & 1) + 4 * (g >> 1); }
+
 // Tile row (relative to the wave's first row) of row x (0..15) of 16-row
 // fragment block b: 16-bit operands use 16 consecutive rows; the byte-row
 // (E4M3 and padded) operands rows 32*(b/2) + 8*(b%2) + {0..7, 16..23}.  Runs
@@ -233,12 +242,13 @@ MSWZ_HD constexpr uint32_t epi_key(uint32_t row)
 {
     return ((row & 1u) << 1) | ((row >> 1) & 1u) | (row & 4u);
 }
-// the 16 bytes (4 columns) of 16x16 block (i = 2q + ii, j) that lane l holds
-template <bool MX>
+// the 16 bytes (4 columns) of 16x16 block (i = 2q + ii, j) that lane l holds;
+// MXM / MXN: split-row fragments on the M (A) / N (B) side
+template <bool MXM, bool MXN = MXM>
 MSWZ_HD constexpr uint32_t epi_write_offset(int q, int ii, int j, int lane)
 {
-    const uint32_t row = uint32_t(row16<MX>(2 * q + ii, lane & 15) - 32 * q);
-    const uint32_t chunk = uint32_t(row16<MX>(j, 4 * (lane >> 4))) / 4;
+    const uint32_t row = uint32_t(row16<MXM>(2 * q + ii, lane & 15) - 32 * q);
+    const uint32_t chunk = uint32_t(row16<MXN>(j, 4 * (lane >> 4))) / 4;
     return row * kEpiPitch + ((chunk ^ epi_key(row)) << 4);
 }
 // read-back instruction k: lane l reads row 4k + l/16, columns 4(l%16) .. +3

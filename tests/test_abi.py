@@ -78,7 +78,11 @@ K_, MN = 0, 1
     ((256, 256, 400, E2M1, E2M1, F32, K_, K_, 16), -2),      # rows of K/2 bytes not 16-byte aligned
     ((256, 256, 512, E2M1, E2M1, F32, K_, K_, 0), -2),       # fp4 needs scales
     ((256, 256, 512, E2M1, E2M1, F32, MN, K_, 32), -2),      # MN-major fp4 not built
-    ((256, 256, 512, E2M1, E4M3, F32, K_, K_, 32), -2),      # mixed formats
+    ((256, 256, 512, E2M1, E4M3, F32, K_, K_, 32), 0),       # dense fp4 x fp8
+    ((256, 256, 1536, E4M3, E2M1, F32, K_, K_, 32), 0),      # fp8 x dense fp4
+    ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), -2),      # fp8 x dense fp4: K % 512
+    ((256, 256, 512, E4M3, E2M1, F32, K_, K_, 16), -2),      # fp8 x dense fp4: 32-element blocks only
+    ((256, 256, 512, E2M1, E2M3, F32, K_, K_, 32), -2),      # dense fp4 pairs with fp8 only
     ((256, 256, 128, E2M3, E2M3, F32, K_, K_, 32), 0),       # MX-fp6 (padded, sixteen per 16 bytes)
     ((300, 260, 384, E3M2, E3M2, BF16, K_, K_, 32), 0),      # ragged, bf16 output
     ((256, 256, 64, E2M3, E2M3, F32, K_, K_, 32), 0),        # K tail (half a 128-element step)

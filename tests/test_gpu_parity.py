@@ -388,6 +388,15 @@ MIXED = {
                                  b_dist=("normal", 1.0), name="e2m1pxe4m3-beta", b_kind="e4m3"),
     "e2m1pxe2m3": wl.custom(256, 256, 640, "e2m1p", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                             name="e2m1pxe2m3", b_kind="e2m3"),
+    # E4M3 with dense E2M1 (K a multiple of 512), either side
+    "e4m3xe2m1": wl.custom(512, 768, 1024, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                           name="e4m3xe2m1", b_kind="e2m1"),
+    "e4m3xe2m1-k2560-tail": wl.custom(264, 300, 2560, "e4m3", V=32, a_dist=("normal", 1.0),
+                                      b_dist=("normal", 1.0), name="e4m3xe2m1-k2560-tail", b_kind="e2m1"),
+    "e2m1xe4m3-beta": wl.custom(512, 256, 512, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                b_dist=("normal", 1.0), name="e2m1xe4m3-beta", b_kind="e4m3"),
+    "e2m1xe4m3-tail": wl.custom(300, 292, 1536, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="e2m1xe4m3-tail", b_kind="e4m3"),
 }
 
 
@@ -412,7 +421,8 @@ def test_mixed_quarter_integers_bit_exact(name):
     assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
 
 
-@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3"), ("e2m1p", "e2m1p"), ("e2m1p", "e4m3")])
+@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3"), ("e2m1p", "e2m1p"), ("e2m1p", "e4m3"),
+                                   ("e4m3", "e2m1"), ("e2m1", "e4m3")])
 def test_mixed_scale_bytes_select_the_right_block(ka, kb):
     """Scales only, every element 1.0 in its own format: D[m,n] =
     32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a value meeting a partner from
@@ -431,22 +441,23 @@ def test_mixed_scale_bytes_select_the_right_block(ka, kb):
     assert np.array_equal(got.astype(np.float64), expect)
 
 
-@pytest.mark.parametrize("kb", ["e2m3", "e2m1p"])
-def test_mixed_k_positions_meet(kb):
+@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e4m3", "e2m1p"), ("e4m3", "e2m1"), ("e2m1", "e4m3")])
+def test_mixed_k_positions_meet(ka, kb):
     """A one-hot in K per row of A against random B rows: D[m,n] = B[n] at
     A's hot position, so any K-order mismatch between the E4M3 fragments and
-    the 6- or 4-bit ones shows (hot positions cover every k of a step)."""
-    M, N, K = 256, 256, 512
-    w = wl.custom(M, N, K, "e4m3", V=32, name="mixed-one-hot", b_kind=kb)
+    the 6- or 4-bit ones shows (hot positions cover every k of a 256-element
+    span, in random spans)."""
+    M, N, K = 512, 256, 1024
+    w = wl.custom(M, N, K, ka, V=32, name="mixed-one-hot", b_kind=kb)
     rng = np.random.default_rng(11)
-    hot = np.arange(M) % 128 + 128 * rng.integers(0, K // 128, M)   # every position of a step, random steps
+    hot = np.arange(M) % 256 + 256 * rng.integers(0, K // 256, M)
     a = np.zeros((M, K))
     a[np.arange(M), hot] = 1.0
-    b = rng.integers(-3, 4, (N, K)) / 2.0          # half-integers in [-1.5, 1.5]: exact in E2M3 and E2M1
-    x = {"A": wl.to_stored(a, "e4m3"), "B": wl.to_stored(b, kb),
+    b = rng.integers(-3, 4, (N, K)) / 2.0          # half-integers in [-1.5, 1.5]: exact in every kind here
+    x = {"A": wl.to_stored(a, ka), "B": wl.to_stored(b, kb),
          "SFA": np.full((M, K // 32), 127, np.uint8), "SFB": np.full((N, K // 32), 127, np.uint8)}
-    assert len(set(hot % 128)) == 128
-    say(f"[mixed] one-hot K positions e4m3 x {kb}")
+    assert len(set(hot % 256)) == 256
+    say(f"[mixed] one-hot K positions {ka} x {kb}")
     got = run_gpu(w, x)
     assert np.array_equal(got.astype(np.float64), b[:, hot].T)
 
@@ -554,7 +565,7 @@ EXTRA_FULL = {
 }
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", "c11", "c12",
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c6", "c7", "c8", "c9", "c10", "c3b", "c11", "c12", "c13",
                                   *EXTRA_FULL])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; whole

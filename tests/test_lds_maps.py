@@ -215,6 +215,35 @@ def test_mixed_e4m3_fragments_meet_their_padded_partners(b):
 
 
 @pytest.mark.parametrize("b", range(16))
+def test_e4m3_fragments_meet_their_dense_e2m1_partners(b):
+    """E4M3 paired with dense E2M1: the E2M1 tile row (128 bytes) holds two
+    E4M3 steps, read in halves h.  E2M1 lane (r, g) holds internal K 32g + j,
+    j < 32, in one 16-byte chunk; E4M3 byte j of lane (r, g) internal K
+    32(g/2) + 16(g%2) + j, plus 64 for the second read.  Every internal K
+    must name the same step-local memory K on both sides, the E2M1 chunk must
+    lie in half h, and both reads must be conflict-free."""
+    e = mswz.lds_lanes("frag_e4m3_fp4", b)
+    assert conflicts(e[0::2], 16, PASSES_16) == 1 and conflicts(e[1::2], 16, PASSES_16) == 1
+    for h in range(2):
+        f = mswz.lds_lanes("frag_e2m1", b, h)
+        assert conflicts(f, 16, PASSES_16) == 1
+        for r in range(16):
+            mem_e, mem_f = {}, {}
+            for g in range(4):
+                l = 16 * g + r
+                for half, a in enumerate(e[2 * l:2 * l + 2]):
+                    row, c = K_INV[a]
+                    assert row == 32 * (b >> 1) + 8 * (b & 1) + (r & 7) + 16 * (r >> 3)
+                    for j in range(16):
+                        mem_e[32 * (g >> 1) + 16 * (g & 1) + 64 * half + j] = 16 * c + j
+                row, c = K_INV[f[l]]
+                assert row == 16 * b + r and c // 4 == h
+                for j in range(32):
+                    mem_f[32 * g + j] = 32 * c + j - 128 * h
+            assert mem_e == mem_f and sorted(mem_e.values()) == list(range(128))
+
+
+@pytest.mark.parametrize("b", range(16))
 def test_e2m1_fragments(b):
     """Dense E2M1: lane (r, g) holds one 16-byte chunk = one 32-element scale
     block of row 16b + r; groups and sub-steps cover the step's 8 blocks once."""
@@ -262,24 +291,27 @@ def test_grouped_scale_reads_conflict_two_ways_under_the_byte_model():
 
 # ---- staged epilogue -------------------------------------------------------------------
 
-@pytest.mark.parametrize("mx", [False, True])
-def test_staged_epilogue_writes_every_output_of_a_quarter_once_where_it_is_read(mx):
+@pytest.mark.parametrize("rows", [0, 1, 2, 3])
+def test_staged_epilogue_writes_every_output_of_a_quarter_once_where_it_is_read(rows):
     """Register r of 16x16 block (i, j) in lane l is output row row16(i, l % 16),
     column row16(j, 4 (l/16)) + r of the wave's tile (the MFMA output image,
-    B first operand).  A quarter q's 32 x 64 outputs are written once into the
+    B first operand), row16 split or contiguous on each side (rows: 0 both
+    contiguous, 1 both split, 2 split M only, 3 split N only).  A quarter q's 32 x 64 outputs are written once into the
     wave's area and the read-back instructions return each (row, 4 columns)
     piece to the lane that stores row 4k + l/16, columns 4 (l%16) .. +3.
     Writes and reads are conflict-free under the 16-byte models."""
-    def r16(b, x):
-        return 32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3) if mx else 16 * b + x
+    split_m, split_n = rows in (1, 2), rows in (1, 3)
+
+    def r16(split, b, x):
+        return 32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3) if split else 16 * b + x
     for q in range(4):
         where = {}
         for ii, j in itertools.product(range(2), range(4)):
-            addrs = mswz.lds_lanes("epi_write", q, 16 * int(mx) + 4 * ii + j)
+            addrs = mswz.lds_lanes("epi_write", q, 16 * rows + 4 * ii + j)
             assert conflicts(addrs, 16, PASSES_W16) == 1
             for l, a in enumerate(addrs):
-                m = r16(2 * q + ii, l % 16) - 32 * q
-                n = r16(j, 4 * (l >> 4))
+                m = r16(split_m, 2 * q + ii, l % 16) - 32 * q
+                n = r16(split_n, j, 4 * (l >> 4))
                 for reg in range(4):
                     assert (a + 4 * reg) not in where
                     where[a + 4 * reg] = (m, n + reg)

@@ -110,6 +110,8 @@ WORKLOADS = {
     "c12": Workload("c12", "8192^3 bf16, A MN-major [K,M], B MN-major [K,N], N(0,1)",
                     8192, 8192, 8192, "bf16", a_major="mn", b_major="mn", a_dist=("normal", 1.0),
                     b_dist=("normal", 1.0)),
+    "c13": Workload("c13", "MX mixed 8192^3: A e4m3, B e2m1 dense (two per byte), K-major, N(0,1) rounded to each format, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
+                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m1"),
 }
 
 
