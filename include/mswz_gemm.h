@@ -113,8 +113,8 @@ typedef struct gemm_plan gemm_plan;
  *                 E2M3 and E3M2 with A and B of the same kind
  * Shape rules: block-scaled K: any multiple of scale_vec_len (E2M1: of 32 as
  * well, so that rows of K/2 bytes stay 16-byte aligned; E4M3 with dense E2M1:
- * a multiple of 512, as that kernel stages the E2M1 operand two of the E4M3
- * operand's 128-element steps at a time and pipelines four); a K that is not a
+ * a multiple of 256, as that kernel stages the E2M1 operand two of the E4M3
+ * operand's 128-element steps at a time); a K that is not a
  * multiple of the kernel's K step (128 elements; E2M1 256) uses the 256 tile,
  * whose last K step reads the values beyond K as zeros and gives their scale
  * blocks the exponent 127 (the scale array itself holds K/V bytes per row,

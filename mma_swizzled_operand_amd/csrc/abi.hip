@@ -164,8 +164,8 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     if (fp8 && (K % scale_vec_len != 0 || (any_fp4 && K % 32 != 0)))
         return MSWZ_ERR_UNSUPPORTED;
     // E4M3 with dense E2M1: the E2M1 operand's 128-byte rows hold two K steps
-    // of the E4M3 one, and its pipeline takes four steps at a time
-    if (pair && K % 512 != 0)
+    // of the E4M3 one, staged together
+    if (pair && K % 256 != 0)
         return MSWZ_ERR_UNSUPPORTED;
     const bool ktail = fp8 ? K % (fp4 ? 256 : 128) != 0 : K % 64 != 0;
     if (ktail && K % 8 != 0 && (a_major == MSWZ_MAJOR_K || b_major == MSWZ_MAJOR_K))

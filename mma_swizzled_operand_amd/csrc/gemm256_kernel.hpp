@@ -929,8 +929,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // lds0 repeats step KT-1 into a stage nobody reads again, which keeps the
     // compiler from draining the copies in flight at a control-flow merge. ------
     if constexpr (kPair) {
-        // E4M3 with dense E2M1 (K a multiple of 512; the host launches no
-        // other): four K steps per iteration.  The E4M3 operand's stages
+        // E4M3 with dense E2M1 (K a multiple of 256; the host launches no
+        // other): four K steps per iteration, then the last pair of steps
+        // when their number is not a multiple of four.  The E4M3 operand's stages
         // alternate lds0 / lds1 every step; the E2M1 operand's 128-byte tile
         // rows hold two steps, so its tile for steps 2p and 2p+1 sits in its
         // part of stage p % 2 and is copied half during each of the two steps
@@ -949,7 +950,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         d4.issue(lds0, 0);
         issue_sf(scl0, 0);
         __syncthreads();
-        for (int kt = 0; kt < KT; kt += 4) {
+        int kt = 0;
+        for (; kt + 4 <= KT; kt += 4) {
             const int p = kt / 2;
             d8.issue(lds1, kt + 1);
             d4.issue_half(lds1, min(p + 1, NP - 1), 0);
@@ -971,6 +973,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             issue_sf(scl0, min(kt + 4, KT - 1));
             compute_pair(lds1, lds1, 1, scl1);
             lds_barrier_keep_vm<0>();
+        }
+        if (kt < KT) {
+            // steps KT-2 and KT-1: their E2M1 pair, E4M3 step KT-2 and its
+            // scale words are in lds0 / scl0 (the loop's last copies, or the
+            // prologue's)
+            d8.issue(lds1, KT - 1);
+            issue_sf(scl1, KT - 1);
+            compute_pair(lds0, lds0, 0, scl0);
+            lds_barrier_keep_vm<0>();
+            compute_pair(lds1, lds0, 1, scl1);
         }
         __syncthreads();   // no copy may still be writing LDS when the workgroup ends
         goto epilogue;
@@ -1203,7 +1215,7 @@ hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32>
 hipError_t launch_cfg(const MxArgs &a, hipStream_t stream)
 {
-    // E4M3 with dense E2M1: K is a multiple of 512 (no SB variant)
+    // E4M3 with dense E2M1: K is a multiple of 256 (no SB variant)
     constexpr bool kPairKinds = (KIND == kE4m3 && KB == kE2m1) || (KIND == kE2m1 && KB == kE4m3);
     if constexpr (KIND != kBf16 && KIND != kF16 && !kPairKinds) {
         constexpr int kStep = KIND == kE2m1 ? 256 : 128;

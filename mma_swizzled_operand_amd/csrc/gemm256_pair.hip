@@ -1,6 +1,6 @@
 // gemm256_pair.hip — instantiations of the 256x256-tile GEMM for OCP E4M3
 // paired with dense (unpadded) OCP E2M1, either operand the E2M1 one (both
-// K-major, 32-element scale blocks, K a multiple of 512; compute_pair in
+// K-major, 32-element scale blocks, K a multiple of 256; compute_pair in
 // gemm256_kernel.hpp).
 #include "gemm256_kernel.hpp"
 

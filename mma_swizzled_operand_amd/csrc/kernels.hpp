@@ -83,7 +83,7 @@ hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
-// E4M3 with dense E2M1 (either side), K % 512 == 0
+// E4M3 with dense E2M1 (either side), K % 256 == 0
 hipError_t launch256_pair(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
 hipError_t launch256_v16(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch_mx(int variant, const MxArgs &args, hipStream_t stream);

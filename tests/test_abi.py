@@ -80,7 +80,8 @@ K_, MN = 0, 1
     ((256, 256, 512, E2M1, E2M1, F32, MN, K_, 32), -2),      # MN-major fp4 not built
     ((256, 256, 512, E2M1, E4M3, F32, K_, K_, 32), 0),       # dense fp4 x fp8
     ((256, 256, 1536, E4M3, E2M1, F32, K_, K_, 32), 0),      # fp8 x dense fp4
-    ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), -2),      # fp8 x dense fp4: K % 512
+    ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), 0),       # fp8 x dense fp4: one pair of steps
+    ((256, 256, 384, E4M3, E2M1, F32, K_, K_, 32), -2),      # fp8 x dense fp4: K % 256
     ((256, 256, 512, E4M3, E2M1, F32, K_, K_, 16), -2),      # fp8 x dense fp4: 32-element blocks only
     ((256, 256, 512, E2M1, E2M3, F32, K_, K_, 32), -2),      # dense fp4 pairs with fp8 only
     ((256, 256, 128, E2M3, E2M3, F32, K_, K_, 32), 0),       # MX-fp6 (padded, sixteen per 16 bytes)
@@ -92,8 +93,8 @@ K_, MN = 0, 1
     ((256, 256, 128, E2M3, E3M2, F32, K_, K_, 32), 0),       # mixed 8- and 6-bit kinds
     ((256, 256, 128, E2M3, E4M3, F32, K_, K_, 32), 0),
     ((300, 260, 256, E4M3, E3M2, F16, K_, K_, 32), 0),
-    ((256, 256, 256, E4M3, E2M1, F32, K_, K_, 32), -2),      # FP4 does not mix
-    ((256, 256, 256, E2M1, E2M3, F32, K_, K_, 32), -2),
+    ((256, 256, 256, E2M1, E2M3, F32, K_, K_, 32), -2),      # dense FP4 mixes with E4M3 only
+    ((256, 256, 256, E2M3, E2M1, F32, K_, K_, 32), -2),
     ((256, 256, 128, E4M3, BF16, F32, K_, K_, 32), -2),      # dense with block-scaled
     ((256, 256, 128, 9, 9, F32, K_, K_, 32), -1),            # unknown dtype
     ((256, 256, 128, E2M1P, E2M1P, F32, K_, K_, 32), 0),     # padded FP4 (sixteen per 16 bytes)

@@ -388,7 +388,7 @@ MIXED = {
                                  b_dist=("normal", 1.0), name="e2m1pxe4m3-beta", b_kind="e4m3"),
     "e2m1pxe2m3": wl.custom(256, 256, 640, "e2m1p", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                             name="e2m1pxe2m3", b_kind="e2m3"),
-    # E4M3 with dense E2M1 (K a multiple of 512), either side
+    # E4M3 with dense E2M1 (K a multiple of 256), either side
     "e4m3xe2m1": wl.custom(512, 768, 1024, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                            name="e4m3xe2m1", b_kind="e2m1"),
     "e4m3xe2m1-k2560-tail": wl.custom(264, 300, 2560, "e4m3", V=32, a_dist=("normal", 1.0),
@@ -397,6 +397,11 @@ MIXED = {
                                 b_dist=("normal", 1.0), name="e2m1xe4m3-beta", b_kind="e4m3"),
     "e2m1xe4m3-tail": wl.custom(300, 292, 1536, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                 name="e2m1xe4m3-tail", b_kind="e4m3"),
+    # step counts 2 and 6: the pair of steps after the four-step loop
+    "e4m3xe2m1-k256-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                     b_dist=("normal", 1.0), name="e4m3xe2m1-k256-beta", b_kind="e2m1"),
+    "e2m1xe4m3-k768": wl.custom(512, 264, 768, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                name="e2m1xe4m3-k768", b_kind="e4m3"),
 }
 
 
