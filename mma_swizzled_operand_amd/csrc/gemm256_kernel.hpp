@@ -415,6 +415,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
     constexpr bool kScaleGroups = kByteRows && !kV16 && !SB && !kPair;   // E4M3 and the padded kinds, 32-element blocks
+    // dense E2M1 with 32-element blocks: the same 16-byte copies per row,
+    // which hold two of its K steps (two scale words per row per step), in
+    // natural row order
+    constexpr bool kFp4Groups = kFp4 && !kV16 && !SB;
     constexpr int kSfInstr = 8 / W;
     const uint32_t sf_row = uint32_t(K) / SV;
     __amdgpu_buffer_rsrc_t sf_rsrc[kSfInstr];
@@ -498,9 +502,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         if constexpr (kDmaB)
             db.issue(stage, kt);
     };
-    // scale group `grp` (K steps 4grp .. 4grp+3), kScaleGroups only
+    // scale group `grp` (K steps 4grp .. 4grp+3; E2M1: 2grp, 2grp+1),
+    // kScaleGroups and kFp4Groups only
     auto issue_scales = [&](uint8_t *sstage, int grp) {
-        if constexpr (kScaleGroups)
+        if constexpr (kScaleGroups || kFp4Groups)
             buffer_load_lds16(sf_rsrc[0], sstage + 1024 * wave, sf_voff, 16u * uint32_t(grp));
     };
 
@@ -722,7 +727,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // 4ks + kblk16(g) of its row (one 32-element scale block, 16 bytes) into
     // the low half of the operand and supplies that block's scale: byte
     // kblk16(g) of the row's scale word ks.
-    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss) {
+    // sf_stride: scale-stage bytes per row (4: per-step words, the second
+    // 2048 bytes further; 16: a group of two steps, eight bytes each); widx:
+    // the step inside its group
+    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx) {
         uint32_t ab[TM16], bb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
@@ -737,8 +745,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // that + 1.
         const int r16 = lane & 15, kb = kblk16(lane >> 4);
         const uint32_t sb16 = kV16 ? uint32_t(2048 * (kb >> 1) + 2 * (kb & 1)) : uint32_t(kb);
-        const uint32_t sfa = opaque(uint32_t(4 * (wm + r16)) + sb16);
-        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + r16)) + sb16);
+        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + r16)) + sb16);
+        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + r16)) + sb16);
+        const uint32_t sf_blk = 16u * uint32_t(sf_stride);   // 16 rows further
         const u32x4 zero = {0, 0, 0, 0};
         // sub-step u: K elements 128 u' .. of the step (u' = ks), and with
         // 16-element blocks each chunk in two halves h
@@ -760,7 +769,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         static_for<0, kV16 ? 4 : 2>([&](auto uc) {
             constexpr int u = decltype(uc)::value;
             constexpr int ks = kV16 ? u >> 1 : u, h = kV16 ? u & 1 : 0;
-            constexpr int sw = kV16 ? 2048 * 2 * ks + h : 2048 * ks;   // scale byte offset of the sub-step
+            // scale byte offset of the sub-step
+            const int sw = kV16 ? 2048 * 2 * ks + h : sf_stride == 16 ? 8 * widx + 4 * ks : 2048 * ks;
             uint32_t sa[TM16], sb[TN16];
             i32x8 bf[TN16], af[TM16];
             static_for<0, TM16 * TN16>([&](auto mc) {
@@ -769,10 +779,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 static_for<c0, c1>([&](auto rc) {
                     constexpr int it = Sched::item(decltype(rc)::value);
                     if constexpr (it > 0) {
-                        sa[it - 1] = ss[sw + sfa + 64 * (it - 1)];
+                        sa[it - 1] = ss[sw + sfa + sf_blk * (it - 1)];
                         af[it - 1] = frag(ab[it - 1], ks, h);
                     } else {
-                        sb[-it - 1] = ss[sw + sfb + 64 * (-it - 1)];
+                        sb[-it - 1] = ss[sw + sfb + sf_blk * (-it - 1)];
                         bf[-it - 1] = frag(bb[-it - 1], ks, h);
                     }
                 });
@@ -912,7 +922,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kFp4)
-            compute_fp4(s, ss);
+            compute_fp4(s, ss, 4, 0);
         else if constexpr (kFp6 && kV16)
             compute_pad16(s, ss);
         else if constexpr (kMx)
@@ -986,6 +996,51 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
         __syncthreads();   // no copy may still be writing LDS when the workgroup ends
         goto epilogue;
+    }
+    if constexpr (kFp4Groups) {
+        if (KT % 4 == 0) {
+            // Dense E2M1, four K steps per iteration: operand stages alternate
+            // lds0 / lds1, scale groups (two steps each) scl0 / scl1.  A
+            // group's scales are copied during the first step of the group
+            // before it, as that step's last copy, which the step's barrier
+            // leaves in flight (completions are counted in order); the stage
+            // they overwrite was last read a step earlier.  Copies beyond
+            // the last step or group repeat the last one into a stage nobody
+            // reads again, so the loop has no branches.
+            const int NG = KT / 2;
+            auto step_end = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step_end_keep1 = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<1>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            issue_scales(scl0, 0);
+            issue_ab(lds0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 4) {
+                const int g = kt / 2;
+                issue_ab(lds1, kt + 1);
+                issue_scales(scl1, g + 1);
+                compute_fp4(lds0, scl0, 16, 0);
+                step_end_keep1();
+                issue_ab(lds0, kt + 2);
+                compute_fp4(lds1, scl0, 16, 1);
+                step_end();
+                issue_ab(lds1, kt + 3);
+                issue_scales(scl0, min(g + 2, NG - 1));
+                compute_fp4(lds0, scl1, 16, 0);
+                step_end_keep1();
+                issue_ab(lds0, min(kt + 4, KT - 1));
+                compute_fp4(lds1, scl1, 16, 1);
+                step_end();
+            }
+            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+            goto epilogue;
+        }
     }
     if constexpr (kScaleGroups) {
         if (KT % 8 == 0) {

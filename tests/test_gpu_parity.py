@@ -241,6 +241,11 @@ FP4 = {
                                     b_dist=("normal", 1.0), name="e2m1-mx-beta-k1280"),
     "e2m1-mx-tail": wl.custom(300, 292, 768, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                               name="e2m1-mx-tail"),
+    # K a multiple of 1024: scale bytes copied per group of two steps
+    "e2m1-mx-k2048": wl.custom(512, 512, 2048, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e2m1-mx-k2048"),
+    "e2m1-mx-tail-k1024-beta": wl.custom(300, 292, 1024, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="e2m1-mx-tail-k1024-beta"),
 }
 
 
