@@ -434,6 +434,13 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
+    // kPair with grouped scale copies: the E4M3 operand's rows in the slot
+    // order of sf_slot_row, the E2M1 operand's in natural order
+    uint32_t sf_voff_grp = 0;
+    if constexpr (kPair) {
+        const bool split = wave < 4 ? kRowsA : kRowsB;
+        sf_voff_grp = uint32_t(64 * (wave & 3) + (split ? sf_slot_row(lane) : lane)) * sf_row;
+    }
     static_assert(!SB || (kMx && W == 8), "register-assembled scales: block-scaled kinds, eight waves");
     // scale words per row per step: one (E4M3 and padded kinds, four
     // 32-element blocks), two (E2M1, eight blocks), twice that with
@@ -866,7 +873,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // the low four registers).  Both sides' lane group g supplies the scale
     // of memory block kblk16(g) of the step: that byte of the row's per-step
     // scale word (rows in natural order, 4 bytes apart).
-    auto compute_pair = [&](const uint8_t *s8, const uint8_t *s4, int h, const uint8_t *ss) {
+    // sf_stride 4: per-step words (rows in natural order); 16: a group of
+    // four steps per row slot (slot 16b + x holds fragment row x of block b
+    // on either side), widx the step inside the group
+    auto compute_pair = [&](const uint8_t *s8, const uint8_t *s4, int h, const uint8_t *ss, int sf_stride, int widx) {
         uint32_t ab[TM16], bb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
@@ -875,9 +885,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < TN16; ++j)
             bb[j] = opaque(bbase16[j]);
         const int r16 = lane & 15, kb = kblk16(lane >> 4);
-        const uint32_t sfa = opaque(uint32_t(4 * (wm + (kRowsA ? row16<true>(0, r16) : r16)) + kb));
-        const uint32_t sfb = opaque(uint32_t(4 * (kBM + wn + (kRowsB ? row16<true>(0, r16) : r16)) + kb));
-        auto sf_off = [](bool split, int b) { return 4 * (split ? 32 * (b >> 1) + 8 * (b & 1) : 16 * b); };
+        const bool grp = sf_stride == 16;
+        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kRowsA && !grp ? row16<true>(0, r16) : r16)) + kb +
+                                             4 * widx));
+        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kRowsB && !grp ? row16<true>(0, r16) : r16)) +
+                                             kb + 4 * widx));
+        auto sf_off = [&](bool split, int b) {
+            return sf_stride * (split && !grp ? 32 * (b >> 1) + 8 * (b & 1) : 16 * b);
+        };
         const u32x4 zero = {0, 0, 0, 0};
         auto frag8 = [&](uint32_t base) {
             const u32x4 lo = lds_read16(s8, base), hi = lds_read16(s8, base ^ 32u);
@@ -956,6 +971,70 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             buffer_load_lds4(sf_rsrc[0], sstage + 256 * wave, sf_voff, 4u * uint32_t(kt));
         };
         static_assert(kSfInstr == 1 && kWords == 1, "one per-step scale word per row, one copy per wave");
+        if (KT % 8 == 0) {
+            // K a multiple of 1024: scale words copied per group of four
+            // steps (16 bytes per row, as for E4M3 alone), into scl0 / scl1
+            // alternating every four steps, each as the last copy of the third
+            // step of the group before and left in flight by that step's
+            // barrier; eight steps per iteration
+            const int NG = KT / 4;
+            auto issue_grp = [&](uint8_t *sstage, int grp) {
+                buffer_load_lds16(sf_rsrc[0], sstage + 1024 * wave, sf_voff_grp, 16u * uint32_t(grp));
+            };
+            auto step_end = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step_end_keep1 = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<1>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            issue_grp(scl0, 0);
+            d8.issue(lds0, 0);
+            d4.issue(lds0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 8) {
+                const int g = kt / 4, p = kt / 2;
+                d8.issue(lds1, kt + 1);
+                d4.issue_half(lds1, p + 1, 0);
+                compute_pair(lds0, lds0, 0, scl0, 16, 0);
+                step_end();
+                d8.issue(lds0, kt + 2);
+                d4.issue_half(lds1, p + 1, 1);
+                compute_pair(lds1, lds0, 1, scl0, 16, 1);
+                step_end();
+                d8.issue(lds1, kt + 3);
+                d4.issue_half(lds0, p + 2, 0);
+                issue_grp(scl1, g + 1);
+                compute_pair(lds0, lds1, 0, scl0, 16, 2);
+                step_end_keep1();
+                d8.issue(lds0, kt + 4);
+                d4.issue_half(lds0, p + 2, 1);
+                compute_pair(lds1, lds1, 1, scl0, 16, 3);
+                step_end();
+                d8.issue(lds1, kt + 5);
+                d4.issue_half(lds1, p + 3, 0);
+                compute_pair(lds0, lds0, 0, scl1, 16, 0);
+                step_end();
+                d8.issue(lds0, kt + 6);
+                d4.issue_half(lds1, p + 3, 1);
+                compute_pair(lds1, lds0, 1, scl1, 16, 1);
+                step_end();
+                d8.issue(lds1, kt + 7);
+                d4.issue_half(lds0, min(p + 4, NP - 1), 0);
+                issue_grp(scl0, min(g + 2, NG - 1));
+                compute_pair(lds0, lds1, 0, scl1, 16, 2);
+                step_end_keep1();
+                d8.issue(lds0, min(kt + 8, KT - 1));
+                d4.issue_half(lds0, min(p + 4, NP - 1), 1);
+                compute_pair(lds1, lds1, 1, scl1, 16, 3);
+                step_end();
+            }
+            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+            goto epilogue;
+        }
         d8.issue(lds0, 0);
         d4.issue(lds0, 0);
         issue_sf(scl0, 0);
@@ -966,22 +1045,22 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             d8.issue(lds1, kt + 1);
             d4.issue_half(lds1, min(p + 1, NP - 1), 0);
             issue_sf(scl1, kt + 1);
-            compute_pair(lds0, lds0, 0, scl0);
+            compute_pair(lds0, lds0, 0, scl0, 4, 0);
             lds_barrier_keep_vm<0>();
             d8.issue(lds0, min(kt + 2, KT - 1));
             d4.issue_half(lds1, min(p + 1, NP - 1), 1);
             issue_sf(scl0, min(kt + 2, KT - 1));
-            compute_pair(lds1, lds0, 1, scl1);
+            compute_pair(lds1, lds0, 1, scl1, 4, 0);
             lds_barrier_keep_vm<0>();
             d8.issue(lds1, min(kt + 3, KT - 1));
             d4.issue_half(lds0, min(p + 2, NP - 1), 0);
             issue_sf(scl1, min(kt + 3, KT - 1));
-            compute_pair(lds0, lds1, 0, scl0);
+            compute_pair(lds0, lds1, 0, scl0, 4, 0);
             lds_barrier_keep_vm<0>();
             d8.issue(lds0, min(kt + 4, KT - 1));
             d4.issue_half(lds0, min(p + 2, NP - 1), 1);
             issue_sf(scl0, min(kt + 4, KT - 1));
-            compute_pair(lds1, lds1, 1, scl1);
+            compute_pair(lds1, lds1, 1, scl1, 4, 0);
             lds_barrier_keep_vm<0>();
         }
         if (kt < KT) {
@@ -990,9 +1069,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             // prologue's)
             d8.issue(lds1, KT - 1);
             issue_sf(scl1, KT - 1);
-            compute_pair(lds0, lds0, 0, scl0);
+            compute_pair(lds0, lds0, 0, scl0, 4, 0);
             lds_barrier_keep_vm<0>();
-            compute_pair(lds1, lds0, 1, scl1);
+            compute_pair(lds1, lds0, 1, scl1, 4, 0);
         }
         __syncthreads();   // no copy may still be writing LDS when the workgroup ends
         goto epilogue;

@@ -402,6 +402,9 @@ MIXED = {
                                 b_dist=("normal", 1.0), name="e2m1xe4m3-beta", b_kind="e4m3"),
     "e2m1xe4m3-tail": wl.custom(300, 292, 1536, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                 name="e2m1xe4m3-tail", b_kind="e4m3"),
+    # K a multiple of 1024 with E2M1 as A: scale words copied per group of four steps
+    "e2m1xe4m3-k2048-tail-beta": wl.custom(300, 292, 2048, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                           b_dist=("normal", 1.0), name="e2m1xe4m3-k2048-tail-beta", b_kind="e4m3"),
     # step counts 2 and 6: the pair of steps after the four-step loop
     "e4m3xe2m1-k256-beta": wl.custom(256, 512, 256, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
                                      b_dist=("normal", 1.0), name="e4m3xe2m1-k256-beta", b_kind="e2m1"),
