@@ -114,6 +114,16 @@ CASES = {
                                   b_dist=("normal", 1.0), name="e2m1-neg_b-beta"), "f32", dict(neg_b=True)),
     "e3m2-neg_a-masks": (wl.custom(256, 256, 1024, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                    name="e3m2-neg_a-masks"), "f32", dict(neg_a=True)),
+    # E4M3 with dense E2M1: split-row fragments on one side only, through the
+    # staged epilogue (fp32 D) and the direct one (fp16 / bf16 D)
+    "e4m3xe2m1-f16out-neg_a": (wl.custom(512, 256, 1024, "e4m3", V=32, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="e4m3xe2m1-f16out-neg_a", b_kind="e2m1"),
+                               "f16", dict(neg_a=True)),
+    "e2m1xe4m3-bf16out-beta-neg_b": (wl.custom(300, 264, 512, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                               b_dist=("normal", 1.0), name="e2m1xe4m3-bf16out-beta-neg_b",
+                                               b_kind="e4m3"), "bf16", dict(neg_b=True)),
+    "e2m1xe4m3-masks": (wl.custom(256, 512, 1024, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                  name="e2m1xe4m3-masks", b_kind="e4m3"), "f32", dict()),
 }
 
 
