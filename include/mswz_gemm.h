@@ -257,7 +257,7 @@ typedef struct {
                                    included; NaN is stored unchanged */
     const uint32_t *row_mask;   /* device pointer or NULL: ceil(M/32) words; bit m % 32
                                    of word m / 32 set leaves row m of D untouched
-                                   (neither read nor written) */
+                                   (not written; its old value does not enter any result) */
     const uint32_t *col_zero;   /* device pointer or NULL: ceil(N/32) words; bit n % 32
                                    of word n / 32 set makes column n of the product
                                    zero (row n of B treated as zero), so that column

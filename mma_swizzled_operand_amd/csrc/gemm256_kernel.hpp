@@ -291,6 +291,22 @@ __device__ __forceinline__ void store_d4(void *D, size_t idx, f32x4 v, bool sat 
     }
 }
 
+// Four consecutive outputs of D read in D's format, as fp32 (the old D of
+// beta = 1, loaded ahead of its store so that the loads of several pieces
+// are in flight together).
+template <int OUT>
+__device__ __forceinline__ f32x4 load_d4(const void *D, size_t idx)
+{
+    if constexpr (OUT == kOutF32) {
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(D) + idx);
+    } else {
+        using T = std::conditional_t<OUT == kOutBf16, __bf16, _Float16>;
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        const t4 old = *reinterpret_cast<const t4 *>(static_cast<const T *>(D) + idx);
+        return f32x4{float(old[0]), float(old[1]), float(old[2]), float(old[3])};
+    }
+}
+
 // The epilogue options applied to four outputs of row m, columns n .. n+3
 // before they are stored: false if row m is masked out (not stored at all).
 __device__ __forceinline__ bool apply_opts(const EpiOpts &o, int m, int n, f32x4 &v)
@@ -1248,8 +1264,29 @@ epilogue:
         static_assert(4 * 32 * kEpiPitch <= uint32_t(kStage), "four 32-row areas per stage");
         uint8_t *area = (wave < 4 ? lds0 : lds1) + (wave & 3) * 32 * kEpiPitch;
         const int rd_row = lane >> 4, rd_col = 4 * (lane & 15);
+        // With beta = 1 the quarter's eight pieces of the old D are loaded
+        // before its LDS round trip, all at once: loaded one by one next to
+        // their stores, each load's whole memory latency was waited for in
+        // turn (8192^3 fp16 with beta: 899.5 -> 884.6 us).  Outputs beyond M
+        // or N load D[0] instead (always inside D) and store nothing.
+        auto piece = [&](int q, int k) {
+            const int m = m0 + wm + 32 * q + 4 * k + rd_row, n = n0 + wn + rd_col;
+            return m < M && n < N ? size_t(m) * ldd + n : ~size_t(0);
+        };
+        // (The K-tail kernels (SB), short of registers, load each piece with
+        // its store.  Issuing quarter q + 1's loads before quarter q's round
+        // trip measured 0.6 % slower than this on 8192^3 fp16 with beta.)
+        constexpr bool kBatchOld = BETA && !SB;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            f32x4 old[kBatchOld ? 8 : 1];
+            if constexpr (kBatchOld) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const size_t idx = piece(q, k);
+                    old[k] = load_d4<OUT>(D, idx == ~size_t(0) ? 0 : idx);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < TN16; ++j)
 #pragma unroll
@@ -1258,14 +1295,16 @@ epilogue:
             wave_lds_sync();
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int r = 4 * k + rd_row;
                 f32x4 v = *reinterpret_cast<const f32x4 *>(area + epi_read_offset(k, lane));
-                const int m = m0 + wm + 32 * q + r, n = n0 + wn + rd_col;
-                if (m >= M || n >= N)
+                const size_t idx = piece(q, k);
+                if (idx == ~size_t(0))
                     continue;
+                const int m = m0 + wm + 32 * q + 4 * k + rd_row, n = n0 + wn + rd_col;
                 if (opts_on && !apply_opts(opts, m, n, v))
                     continue;
-                store_d4<OUT, BETA, true>(D, size_t(m) * ldd + n, v, opts.sat);
+                if constexpr (kBatchOld)
+                    v += old[k];
+                store_d4<OUT, BETA && !kBatchOld, true>(D, idx, v, opts.sat);
             }
             wave_lds_sync();   // the next quarter's writes come after these reads
         }
@@ -1274,8 +1313,21 @@ epilogue:
     if constexpr (kMf16) {
         // 16x16 block (j, i): lane l holds fragment row l % 16 of A block i
         // and fragment rows 4(l/16) .. +3 of B block j
+        // (with beta = 1 a block row's old D is loaded before its stores, as
+        // in the staged epilogue; outputs beyond M or N load D[0] and store
+        // nothing)
+        constexpr bool kBatchOld = BETA && !SB;
 #pragma unroll
-        for (int j = 0; j < TN16; ++j)
+        for (int j = 0; j < TN16; ++j) {
+            f32x4 old[kBatchOld ? TM16 : 1];
+            if constexpr (kBatchOld) {
+#pragma unroll
+                for (int i = 0; i < TM16; ++i) {
+                    const int m = m0 + wm + row16<kRowsA>(i, lane & 15);
+                    const int n = n0 + wn + row16<kRowsB>(j, 4 * (lane >> 4));
+                    old[i] = load_d4<OUT>(D, m < M && n < N ? size_t(m) * ldd + n : 0);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < TM16; ++i) {
                 const int m = m0 + wm + row16<kRowsA>(i, lane & 15);
@@ -1285,11 +1337,15 @@ epilogue:
                 f32x4 v = acc4[j][i];
                 if (opts_on && !apply_opts(opts, m, n, v))
                     continue;
+                if constexpr (kBatchOld)
+                    v += old[i];
                 // 16-bit and E2M1 blocks: the four lanes of a row hold 16
                 // consecutive columns (64 bytes of fp32 D); byte-row blocks:
                 // two runs of 8, and 16-bit D halves the piece
-                store_d4<OUT, BETA, !(kRowsA || kRowsB) && OUT == kOutF32>(D, size_t(m) * ldd + n, v, opts.sat);
+                store_d4<OUT, BETA && !kBatchOld, !(kRowsA || kRowsB) && OUT == kOutF32>(D, size_t(m) * ldd + n, v,
+                                                                                         opts.sat);
             }
+        }
         return;
     }
 #pragma unroll
@@ -1297,6 +1353,14 @@ epilogue:
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int m = m0 + wm + 32 * i + lr;
+            f32x4 old[BETA ? 4 : 1];
+            if constexpr (BETA) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn + 32 * j + 8 * q + 4 * lh;
+                    old[q] = load_d4<OUT>(D, m < M && n < N ? size_t(m) * ldd + n : 0);
+                }
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn + 32 * j + 8 * q + 4 * lh;
@@ -1306,7 +1370,9 @@ epilogue:
                            acc[j][i][4 * q + 3]};
                 if (opts_on && !apply_opts(opts, m, n, v))
                     continue;
-                store_d4<OUT, BETA>(D, size_t(m) * ldd + n, v, opts.sat);
+                if constexpr (BETA)
+                    v += old[q];
+                store_d4<OUT, false>(D, size_t(m) * ldd + n, v, opts.sat);
             }
         }
 }

@@ -12,14 +12,25 @@ hipError_t launch_pair(const MxArgs &a, hipStream_t stream)
     return launch_cfg<KA, false, false, KB>(a, stream);
 }
 
+// B's kind KB for A's kind KA; one kind on both sides is not a mix (those
+// plans take the single-kind kernels) and is not instantiated here
+template <int KA, int KB>
+hipError_t launch_if_mixed(const MxArgs &a, hipStream_t stream)
+{
+    if constexpr (KA == KB)
+        return hipErrorInvalidValue;
+    else
+        return launch_pair<KA, KB>(a, stream);
+}
+
 template <int KA>
 hipError_t launch_b(const MxArgs &a, MxKind kb, hipStream_t stream)
 {
     switch (kb) {
-    case kMxE4m3: return KA == kE4m3 ? hipErrorInvalidValue : launch_pair<KA, kE4m3>(a, stream);
-    case kMxE2m3: return KA == kE2m3 ? hipErrorInvalidValue : launch_pair<KA, kE2m3>(a, stream);
-    case kMxE3m2: return KA == kE3m2 ? hipErrorInvalidValue : launch_pair<KA, kE3m2>(a, stream);
-    case kMxE2m1p: return KA == kE2m1p ? hipErrorInvalidValue : launch_pair<KA, kE2m1p>(a, stream);
+    case kMxE4m3: return launch_if_mixed<KA, kE4m3>(a, stream);
+    case kMxE2m3: return launch_if_mixed<KA, kE2m3>(a, stream);
+    case kMxE3m2: return launch_if_mixed<KA, kE3m2>(a, stream);
+    case kMxE2m1p: return launch_if_mixed<KA, kE2m1p>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
