@@ -4,10 +4,11 @@ oracle, through the C ABI.
 The streaming kernel stores S fp32 partials per output in the workspace and a
 second kernel sums them in a fixed part order and applies beta, so besides
 parity with the oracle these tests check that results are bit-identical run to
-run on one workspace, that the workspace's prior contents (filled with NaNs
-here) do not matter, and beta = 1.  Tolerances are those of the dense cases
-(tests/gpu_util.py): any fp32 summation order of the exact 16-bit products
-stays within the componentwise bound.
+run on one workspace (also when a captured graph replays the call), that the
+workspace's prior contents (filled with NaNs here) do not matter, and beta =
+1.  Tolerances are those of the dense cases (tests/gpu_util.py): any fp32
+summation order of the exact 16-bit products stays within the componentwise
+bound.
 """
 import numpy as np
 import pytest
@@ -44,6 +45,10 @@ KSLICE = {
                                    name="ks-bf16-m1-k32768"),        # S = 16, 256
     "ks-bf16-m48-k16384-beta": wl.custom(48, 4096, 16384, "bf16", beta=1, name="ks-bf16-m48-k16384-beta"),  # 128
     "ks-f16-m64-n16384-k4096": wl.custom(64, 16384, 4096, "f16", name="ks-f16-m64-n16384-k4096"),  # S = 4, 128
+    "ks-bf16-m32-n8192-k16384": wl.custom(32, 8192, 16384, "bf16", a_dist=("normal", 1.0),
+                                          b_dist=("normal", 0.02), name="ks-bf16-m32-n8192-k16384"),  # S = 8, 256
+    "ks-f16-m16-n32768-k2048-beta": wl.custom(16, 32768, 2048, "f16", beta=1,
+                                              name="ks-f16-m16-n32768-k2048-beta"),  # S = 2, 128
 }
 
 # the same kernels without a workspace (K not split), ragged M
@@ -99,6 +104,46 @@ def test_kslice_full_compare(name):
         print(name, compare(w, got[:, cols], ref, None if x.get("D0") is None else x["D0"][:, cols]))
     again = run_gpu(w, x, plan, workspace=ws)
     assert np.array_equal(got, again), "not bit-identical run to run"
+
+
+def test_kslice_graph_replays():
+    """One K-sliced call (S = 4, beta = 1) captured in a graph and replayed
+    three times with other work, workspace fills and synchronisations between
+    the replays; each replay restores D0 first (inside the graph) and must
+    give the eager call's bits."""
+    import mma_swizzled_operand_amd as mswz
+    w = wl.custom(64, 16384, 4096, "bf16", beta=1, a_dist=("normal", 1.0), b_dist=("normal", 0.02),
+                  name="ks-graph")
+    plan = plan_for(w)
+    x = wl.generate(w, seed=24)
+    A, B = (torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).cuda() for k in ("A", "B"))
+    D0 = torch.from_numpy(x["D0"]).cuda()
+    ws = poisoned_workspace(plan)
+    say("[splitk-ks] graph replays")
+    D = D0.clone()
+    mswz.gemm_run_ws(plan, A, B, D, ws, 1)
+    torch.cuda.synchronize()
+    eager = D.cpu()
+    ref = reference(w, x, cols=wl.sample_points(w, 8, 16)[1])
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            D.copy_(D0)
+            mswz.gemm_run_ws(plan, A, B, D, ws, 1)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        junk = torch.randn(1 << 20, device="cuda") * 3.0
+        ws.fill_(0xFF if r == 1 else 0)   # the partials' old contents do not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(D.cpu().view(torch.int32), eager.view(torch.int32)), f"replay {r} differs"
+        del junk
+    cols = wl.sample_points(w, 8, 16)[1]
+    compare(w, eager.numpy()[:, cols], ref, x["D0"][:, cols])
 
 
 @pytest.mark.parametrize("name", ["ks-bf16-m64-k32768", "ks-bf16-m1-k32768"])
