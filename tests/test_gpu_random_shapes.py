@@ -72,3 +72,25 @@ def test_random_shape_full_compare(name):
     got = run_gpu(w, x, plan)
     ref = reference(w, x)
     print(name, compare(w, got, ref, x.get("D0")))
+
+
+# every fourth case again with bf16 or fp16 D (the fp32 result rounded once;
+# with beta = 1 the old D read in D's format), under the bound of
+# tests/test_gpu_narrow_d.py
+NARROW = {name + ("-bf16d" if i % 8 == 0 else "-f16d"): (w, "bf16" if i % 8 == 0 else "f16")
+          for i, (name, w) in enumerate(CASES.items()) if i % 4 == 0}
+
+
+@pytest.mark.parametrize("case", list(NARROW))
+def test_random_shape_narrow_d(case):
+    from test_gpu_narrow_d import FRAC_BITS, inputs, run_narrow
+    w, d_kind = NARROW[case]
+    say(f"[random] {case}")
+    x = inputs(w, d_kind, seed=int(case[1:4]) + 300)
+    got = run_narrow(w, x, d_kind)
+    r = reference(w, x)
+    ref, mag = r
+    extra = np.abs(x["D0"].astype(np.float64)) if w.beta else 0.0
+    tol = 2.0 ** -FRAC_BITS[d_kind] * np.abs(ref) + 1.01 * 2 * (w.K + 1) * 2.0 ** -24 * (mag + extra) + r.wabs
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), {"violations": int(bad.sum()), "max_err": float(np.abs(got - ref).max())}
