@@ -347,6 +347,18 @@ int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m,
  *   MSWZ_LDS_SCALE_DMA  p0 = wave (0..7): out[2l] = stage offset lane l writes
  *                       (16 bytes), out[2l+1] = the row of its 64-row group
  *                       whose four steps' scale bytes it copies        (128)
+ *   MSWZ_LDS_SCALE_GRP_WIDE  p0 = b (0..7), p1 = step in its group of eight
+ *                       (0..7): the scale byte each lane reads from the
+ *                       32-byte-per-row stage (6-bit kinds; A side)       (64)
+ *   MSWZ_LDS_SCALE_DMA_WIDE  p0 = wave (0..7), p1 = copy (0..1): out[2l] =
+ *                       stage offset lane l writes (16 bytes), out[2l+1] =
+ *                       2 x (row of the wave's 64-row group) + the half of
+ *                       its 32 scale bytes it copies (slot order of the 6-bit
+ *                       kinds)                                          (128)
+ *   MSWZ_LDS_SCALE_DMA_WIDE_NAT  the same for dense E2M1 (rows in order)  (128)
+ *   MSWZ_LDS_SCALE_FP4_WIDE  p0 = b (0..7), p1 = 2 x step in its group of
+ *                       four + sub-step (0..7): the scale byte each lane
+ *                       reads (dense E2M1, A side)                        (64)
  *   MSWZ_LDS_EPI_WRITE  p0 = quarter q (0..3), p1 = 16*rows + 4*ii + j: the
  *                       16-byte write of 16x16 block (2q + ii, j); rows 0:
  *                       16-bit, 1: split-row fragments on both sides (E4M3,
@@ -358,7 +370,8 @@ enum {
     MSWZ_LDS_DMA_K = 1, MSWZ_LDS_DMA_MN = 2, MSWZ_LDS_FRAG_K16 = 3, MSWZ_LDS_FRAG_MN16 = 4,
     MSWZ_LDS_FRAG_E4M3 = 5, MSWZ_LDS_FRAG_PAD = 6, MSWZ_LDS_FRAG_E4M3_MIXED = 7, MSWZ_LDS_FRAG_E2M1 = 8,
     MSWZ_LDS_SCALE_GRP = 9, MSWZ_LDS_SCALE_DMA = 10, MSWZ_LDS_EPI_WRITE = 11, MSWZ_LDS_EPI_READ = 12,
-    MSWZ_LDS_FRAG_E4M3_FP4 = 13
+    MSWZ_LDS_FRAG_E4M3_FP4 = 13, MSWZ_LDS_SCALE_GRP_WIDE = 14, MSWZ_LDS_SCALE_DMA_WIDE = 15,
+    MSWZ_LDS_SCALE_DMA_WIDE_NAT = 16, MSWZ_LDS_SCALE_FP4_WIDE = 17
 };
 int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n);
 

@@ -370,7 +370,8 @@ def tile_offset(row, chunk) -> int:
 #: access patterns of lds_lanes (include/mswz_gemm.h, MSWZ_LDS_*)
 LDS_PATTERNS = {"dma_k": 1, "dma_mn": 2, "frag_k16": 3, "frag_mn16": 4, "frag_e4m3": 5, "frag_pad": 6,
                 "frag_e4m3_mixed": 7, "frag_e2m1": 8, "scale_grp": 9, "scale_dma": 10, "epi_write": 11,
-                "epi_read": 12, "frag_e4m3_fp4": 13}
+                "epi_read": 12, "frag_e4m3_fp4": 13, "scale_grp_wide": 14, "scale_dma_wide": 15,
+                "scale_dma_wide_nat": 16, "scale_fp4_wide": 17}
 
 
 def lds_lanes(pattern: str, p0: int = 0, p1: int = 0) -> list[int]:

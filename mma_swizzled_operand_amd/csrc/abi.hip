@@ -234,8 +234,9 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     mswz::variant_info(p->variant, fp8, &p->info);
     if (fp4)
         p->info.tile_k = 256;                              // K elements per 128-byte row step
-    if (p->variant == mswz::kVarMx256)
-        p->info.lds_bytes += 2 * 512 * 16;                 // the two scale stages
+    if (p->variant == mswz::kVarMx256)                 // the two scale stages: 32 bytes per row for
+        p->info.lds_bytes += 2 * 512 * ((fp4 || fp6) && !mixed && scale_vec_len == 32 && K % (fp4 ? 256 : 128) == 0
+                                            ? 32 : 16);   // one 6- or 4-bit kind (wide groups)
     if (skinny) {
         p->info.tile_m = M > 32 ? 64 : 32;   // M padded to 32 or 64 rows
         p->info.lds_bytes = 8 * p->info.tile_m * 68 * 4;
@@ -403,7 +404,8 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
     const int count = (pattern == MSWZ_LDS_DMA_K || pattern == MSWZ_LDS_DMA_MN || pattern == MSWZ_LDS_FRAG_MN16 ||
                        pattern == MSWZ_LDS_FRAG_E4M3 || pattern == MSWZ_LDS_FRAG_PAD ||
                        pattern == MSWZ_LDS_FRAG_E4M3_MIXED || pattern == MSWZ_LDS_FRAG_E4M3_FP4 ||
-                       pattern == MSWZ_LDS_SCALE_DMA)
+                       pattern == MSWZ_LDS_SCALE_DMA || pattern == MSWZ_LDS_SCALE_DMA_WIDE ||
+                       pattern == MSWZ_LDS_SCALE_DMA_WIDE_NAT)
                           ? 128 : 64;
     if (!out || n < count)
         return MSWZ_ERR_INVALID;
@@ -468,6 +470,28 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
             out[2 * l] = uint32_t(1024 * p0 + 16 * l);
             out[2 * l + 1] = uint32_t(sf_slot_row(l));
             break;
+        case MSWZ_LDS_SCALE_GRP_WIDE:
+            if (!in(p0, 0, 8) || !in(p1, 0, 8))
+                return MSWZ_ERR_INVALID;
+            out[l] = sf_wide_read(0, p0, uint32_t(p1 >> 2), uint32_t(4 * (p1 & 3) + g), l);
+            break;
+        case MSWZ_LDS_SCALE_FP4_WIDE: {
+            if (!in(p0, 0, 8) || !in(p1, 0, 8))
+                return MSWZ_ERR_INVALID;
+            const int widx = p1 >> 1, ks = p1 & 1;
+            out[l] = sf_wide_read(0, p0, uint32_t(widx >> 1), uint32_t(8 * (widx & 1) + 4 * ks + kblk16(g)), l);
+            break;
+        }
+        case MSWZ_LDS_SCALE_DMA_WIDE:
+        case MSWZ_LDS_SCALE_DMA_WIDE_NAT: {
+            if (!in(p0, 0, W) || !in(p1, 0, 2))
+                return MSWZ_ERR_INVALID;
+            const int slot = l & 31;
+            const int row = 32 * p1 + (pattern == MSWZ_LDS_SCALE_DMA_WIDE ? sf_slot_row(slot) : slot);
+            out[2 * l] = uint32_t(2048 * p0 + 1024 * p1 + 16 * l);
+            out[2 * l + 1] = uint32_t(2 * row + (l >> 5));
+            break;
+        }
         case MSWZ_LDS_EPI_WRITE: {
             const int rows = p1 >> 4, ii = (p1 >> 2) & 3, j = p1 & 3;
             if (!in(p0, 0, 4) || rows > 3 || ii > 1 || p1 < 0)

@@ -46,6 +46,9 @@ namespace {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kATile = kBM * 128, kBTile = kBN * 128, kStage = kATile + kBTile;
 constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K steps) per row
+// grouped scale copies of 32 bytes per row (eight E4M3 / padded K steps or
+// four E2M1 steps; layout.hpp sf_wide_offset)
+constexpr int kScaleStageWide = (kBM + kBN) * 32;
 
 
 // kE2m1p: E2M1 in the padded sixteen-per-16-byte form (eight bytes of nibbles,
@@ -380,10 +383,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr int kStepK = kPair ? 128 : kFp4 ? 256 : kByteRows ? 128 : 64;
     constexpr int kStepA = kPairA ? 256 : kStepK, kStepB = kPairB ? 256 : kStepK;
 
+    // the grouped scale copies (below) with 32-element blocks, for one
+    // 6- or 4-bit kind on both sides: their stages hold 32 bytes per row
+    // (2 x 64 KiB of operand stages + 2 x 16 KiB).  (With an E4M3 operand, or
+    // two different kinds, the wide loop left the kernel short of registers:
+    // up to 20 spilled, reloaded every step.)
+    constexpr bool kWideStage = ((kFp6 && !kMixed) || kFp4) && !kV16 && !SB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    __shared__ __attribute__((aligned(256))) uint8_t scl0[kMx ? kScaleStage : 4];
-    __shared__ __attribute__((aligned(256))) uint8_t scl1[kMx ? kScaleStage : 4];
+    __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
+    __shared__ __attribute__((aligned(256))) uint8_t scl1[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -449,6 +458,26 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
+    }
+    // Wide groups (K a multiple of 2048 for E4M3 and the padded kinds, 1024
+    // for E2M1): 32 bytes per row and group, two copies per wave and group.
+    // Copy q of wave g fetches rows of slots 32q .. 32q+31 of its 64-row group
+    // (slot order as above), lane l the half l/32 of slot 32q + l%32, so both
+    // halves of a row come from one cache line in one instruction, and
+    // writes 1 KiB of consecutive LDS (sf_wide_offset).  A grouped copy of 16
+    // bytes per row touches a cache line per lane for 16 useful bytes; per K
+    // step the wide copies make half as many line requests, which are what
+    // the copy path's time is spent on.
+    // (sf_slot_row keeps bit 5, so copy 1's rows are copy 0's plus 32: one
+    // per-lane offset, the second copy 32 rows further through the scalar
+    // offset)
+    uint32_t sf_voff_w = 0;
+    if constexpr (kWideStage) {
+        static_assert(kSfInstr == 1, "one 64-row scale group per wave");
+        static_assert(sf_slot_row(32 + 5) == 32 + sf_slot_row(5), "slot order keeps bit 5");
+        const int slot = lane & 31;
+        sf_voff_w = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(slot) : slot)) * sf_row +
+                    16u * uint32_t(lane >> 5);
     }
     // kPair with grouped scale copies: the E4M3 operand's rows in the slot
     // order of sf_slot_row, the E2M1 operand's in natural order
@@ -530,6 +559,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     auto issue_scales = [&](uint8_t *sstage, int grp) {
         if constexpr (kScaleGroups || kFp4Groups)
             buffer_load_lds16(sf_rsrc[0], sstage + 1024 * wave, sf_voff, 16u * uint32_t(grp));
+    };
+    // wide group `grp` (K steps 8grp .. 8grp+7; E2M1: 4grp .. 4grp+3)
+    auto issue_scales_wide = [&](uint8_t *sstage, int grp) {
+        if constexpr (kWideStage) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                buffer_load_lds16(sf_rsrc[0], sstage + 2048 * wave + 1024 * q, sf_voff_w,
+                                  32u * uint32_t(grp) + uint32_t(32 * q) * sf_row);
+        }
     };
 
     // ---- MFMA operand read addresses -------------------------------------------
@@ -674,7 +712,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // sf_stride: scale-stage bytes per row (4: one step's word; 16: a group of
     // four steps); widx: which of the row's words (the step inside its group)
-    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx) {
+    // wide: the scale stage of the wide groups (32 bytes per row; widx 0..7)
+    auto compute_mx16 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx, auto wide) {
+        constexpr bool WD = decltype(wide)::value;
         uint32_t ab[TM16], bb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
@@ -692,9 +732,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // is slot (wave's first row) + 16 * b + x.
         const int r16 = lane & 15;
         static_assert(!kScaleGroups || (32 * TN) % 64 == 0, "wave rows start 64-row groups");
-        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
-        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
-        auto sf_off = [&](int b) { return sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1)); };
+        // (wide stage: sf_wide_read with the step's half widx/4 and byte
+        // 4 (widx%4) + block, split into lane, block and step parts)
+        const uint32_t sfa = opaque(WD ? sf_wide_read(wm, 0, 0, lane >> 4, lane)
+                                       : uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        const uint32_t sfb = opaque(WD ? sf_wide_read(kBM + wn, 0, 0, lane >> 4, lane)
+                                       : uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        auto sf_off = [&](int b) {
+            return WD ? int(sf_wide_read(0, b, 0, 0, 0)) : sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1));
+        };
+        const int sstep = WD ? int(sf_wide_offset(0, widx >> 2)) + 4 * (widx & 3) : 4 * widx;
         // E4M3: chunks c and c + 4.  Padded kinds: chunks c and c ^ 1, of
         // which the first twelve (6-bit) or eight (4-bit) bytes each form
         // registers 0..2 and 3..5 (0..1 and 2..3)
@@ -730,10 +777,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             static_for<c0, c1>([&](auto rc) {
                 constexpr int it = Sched::item(decltype(rc)::value);
                 if constexpr (it > 0) {
-                    sa[it - 1] = ss[sfa + sf_off(it - 1) + 4 * widx];
+                    sa[it - 1] = ss[sfa + sf_off(it - 1) + sstep];
                     af[it - 1] = frag(ab[it - 1]);
                 } else {
-                    sb[-it - 1] = ss[sfb + sf_off(-it - 1) + 4 * widx];
+                    sb[-it - 1] = ss[sfb + sf_off(-it - 1) + sstep];
                     bf[-it - 1] = frag_b(bb[-it - 1]);
                 }
             });
@@ -753,7 +800,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // sf_stride: scale-stage bytes per row (4: per-step words, the second
     // 2048 bytes further; 16: a group of two steps, eight bytes each); widx:
     // the step inside its group
-    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx) {
+    // wide: the scale stage of the wide groups (32 bytes per row, four steps;
+    // widx 0..3)
+    auto compute_fp4 = [&](const uint8_t *s, const uint8_t *ss, int sf_stride, int widx, auto wide) {
+        constexpr bool WD = decltype(wide)::value;
         uint32_t ab[TM16], bb[TN16];
 #pragma unroll
         for (int i = 0; i < TM16; ++i)
@@ -768,9 +818,13 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // that + 1.
         const int r16 = lane & 15, kb = kblk16(lane >> 4);
         const uint32_t sb16 = kV16 ? uint32_t(2048 * (kb >> 1) + 2 * (kb & 1)) : uint32_t(kb);
-        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + r16)) + sb16);
-        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + r16)) + sb16);
+        // (wide stage: rows in natural order, read as in compute_mx16 with
+        // the step's half widx/2 and byte 8 (widx%2) + 4 ks + block)
+        const uint32_t sfa = opaque(WD ? sf_wide_read(wm, 0, 0, sb16, lane) : uint32_t(sf_stride * (wm + r16)) + sb16);
+        const uint32_t sfb = opaque(WD ? sf_wide_read(kBM + wn, 0, 0, sb16, lane)
+                                       : uint32_t(sf_stride * (kBM + wn + r16)) + sb16);
         const uint32_t sf_blk = 16u * uint32_t(sf_stride);   // 16 rows further
+        auto blk_off = [&](int b) { return WD ? sf_wide_read(0, b, 0, 0, 0) : sf_blk * uint32_t(b); };
         const u32x4 zero = {0, 0, 0, 0};
         // sub-step u: K elements 128 u' .. of the step (u' = ks), and with
         // 16-element blocks each chunk in two halves h
@@ -793,7 +847,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             constexpr int u = decltype(uc)::value;
             constexpr int ks = kV16 ? u >> 1 : u, h = kV16 ? u & 1 : 0;
             // scale byte offset of the sub-step
-            const int sw = kV16 ? 2048 * 2 * ks + h : sf_stride == 16 ? 8 * widx + 4 * ks : 2048 * ks;
+            const int sw = kV16 ? 2048 * 2 * ks + h
+                           : WD ? int(sf_wide_offset(0, widx >> 1)) + 8 * (widx & 1) + 4 * ks
+                                : sf_stride == 16 ? 8 * widx + 4 * ks : 2048 * ks;
             uint32_t sa[TM16], sb[TN16];
             i32x8 bf[TN16], af[TM16];
             static_for<0, TM16 * TN16>([&](auto mc) {
@@ -802,10 +858,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 static_for<c0, c1>([&](auto rc) {
                     constexpr int it = Sched::item(decltype(rc)::value);
                     if constexpr (it > 0) {
-                        sa[it - 1] = ss[sw + sfa + sf_blk * (it - 1)];
+                        sa[it - 1] = ss[sw + sfa + blk_off(it - 1)];
                         af[it - 1] = frag(ab[it - 1], ks, h);
                     } else {
-                        sb[-it - 1] = ss[sw + sfb + sf_blk * (-it - 1)];
+                        sb[-it - 1] = ss[sw + sfb + blk_off(-it - 1)];
                         bf[-it - 1] = frag(bb[-it - 1], ks, h);
                     }
                 });
@@ -953,11 +1009,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
         if constexpr (kFp4)
-            compute_fp4(s, ss, 4, 0);
+            compute_fp4(s, ss, 4, 0, std::false_type{});
         else if constexpr (kFp6 && kV16)
             compute_pad16(s, ss);
         else if constexpr (kMx)
-            compute_mx16(s, ss, 4, 0);
+            compute_mx16(s, ss, 4, 0, std::false_type{});
         else if constexpr (kMf16)
             compute16x16(s);
         else
@@ -1093,6 +1149,62 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         goto epilogue;
     }
     if constexpr (kFp4Groups) {
+        if (KT % 8 == 0) {
+            // Dense E2M1, K a multiple of 2048: eight K steps per iteration,
+            // wide scale groups of four steps (scl0 for the first four, scl1
+            // for the next).  A group's scales (two copies per wave) are
+            // copied during the third step of the group before it, as that
+            // step's last copies, which its barrier leaves in flight; the
+            // stage they overwrite was last read three steps earlier.  Copies
+            // beyond the end repeat the last step or group into a stage nobody
+            // reads again, so the loop has no branches.
+            const int NG = KT / 4;
+            auto step_end = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step_end_keep2 = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<2>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            using wide = std::true_type;
+            issue_scales_wide(scl0, 0);
+            issue_ab(lds0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 8) {
+                const int g = kt / 4;
+                issue_ab(lds1, kt + 1);
+                compute_fp4(lds0, scl0, 16, 0, wide{});
+                step_end();
+                issue_ab(lds0, kt + 2);
+                compute_fp4(lds1, scl0, 16, 1, wide{});
+                step_end();
+                issue_ab(lds1, kt + 3);
+                issue_scales_wide(scl1, g + 1);
+                compute_fp4(lds0, scl0, 16, 2, wide{});
+                step_end_keep2();
+                issue_ab(lds0, kt + 4);
+                compute_fp4(lds1, scl0, 16, 3, wide{});
+                step_end();
+                issue_ab(lds1, kt + 5);
+                compute_fp4(lds0, scl1, 16, 0, wide{});
+                step_end();
+                issue_ab(lds0, kt + 6);
+                compute_fp4(lds1, scl1, 16, 1, wide{});
+                step_end();
+                issue_ab(lds1, kt + 7);
+                issue_scales_wide(scl0, min(g + 2, NG - 1));
+                compute_fp4(lds0, scl1, 16, 2, wide{});
+                step_end_keep2();
+                issue_ab(lds0, min(kt + 8, KT - 1));
+                compute_fp4(lds1, scl1, 16, 3, wide{});
+                step_end();
+            }
+            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+            goto epilogue;
+        }
         if (KT % 4 == 0) {
             // Dense E2M1, four K steps per iteration: operand stages alternate
             // lds0 / lds1, scale groups (two steps each) scl0 / scl1.  A
@@ -1120,17 +1232,98 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 const int g = kt / 2;
                 issue_ab(lds1, kt + 1);
                 issue_scales(scl1, g + 1);
-                compute_fp4(lds0, scl0, 16, 0);
+                compute_fp4(lds0, scl0, 16, 0, std::false_type{});
                 step_end_keep1();
                 issue_ab(lds0, kt + 2);
-                compute_fp4(lds1, scl0, 16, 1);
+                compute_fp4(lds1, scl0, 16, 1, std::false_type{});
                 step_end();
                 issue_ab(lds1, kt + 3);
                 issue_scales(scl0, min(g + 2, NG - 1));
-                compute_fp4(lds0, scl1, 16, 0);
+                compute_fp4(lds0, scl1, 16, 0, std::false_type{});
                 step_end_keep1();
                 issue_ab(lds0, min(kt + 4, KT - 1));
-                compute_fp4(lds1, scl1, 16, 1);
+                compute_fp4(lds1, scl1, 16, 1, std::false_type{});
+                step_end();
+            }
+            __syncthreads();   // no copy may still be writing LDS when the workgroup ends
+            goto epilogue;
+        }
+    }
+    if constexpr (kScaleGroups && kWideStage) {
+        if (KT % 16 == 0) {
+            // K a multiple of 2048: sixteen K steps per iteration, wide scale
+            // groups of eight steps (scl0 for the first eight, scl1 for the
+            // next), copied during the seventh step of the group before them
+            // as that step's last copies (two per wave), which its barrier
+            // leaves in flight; the stage they overwrite was last read seven
+            // steps earlier.  Copies beyond the end repeat the last step or
+            // group into a stage nobody reads again: no branches.
+            const int NG = KT / 8;
+            auto step_end = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto step_end_keep2 = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier_keep_vm<2>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            using wide = std::true_type;
+            issue_scales_wide(scl0, 0);
+            issue_ab(lds0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 16) {
+                const int g = kt / 8;
+                issue_ab(lds1, kt + 1);
+                compute_mx16(lds0, scl0, 16, 0, wide{});
+                step_end();
+                issue_ab(lds0, kt + 2);
+                compute_mx16(lds1, scl0, 16, 1, wide{});
+                step_end();
+                issue_ab(lds1, kt + 3);
+                compute_mx16(lds0, scl0, 16, 2, wide{});
+                step_end();
+                issue_ab(lds0, kt + 4);
+                compute_mx16(lds1, scl0, 16, 3, wide{});
+                step_end();
+                issue_ab(lds1, kt + 5);
+                compute_mx16(lds0, scl0, 16, 4, wide{});
+                step_end();
+                issue_ab(lds0, kt + 6);
+                compute_mx16(lds1, scl0, 16, 5, wide{});
+                step_end();
+                issue_ab(lds1, kt + 7);
+                issue_scales_wide(scl1, g + 1);
+                compute_mx16(lds0, scl0, 16, 6, wide{});
+                step_end_keep2();
+                issue_ab(lds0, kt + 8);
+                compute_mx16(lds1, scl0, 16, 7, wide{});
+                step_end();
+                issue_ab(lds1, kt + 9);
+                compute_mx16(lds0, scl1, 16, 0, wide{});
+                step_end();
+                issue_ab(lds0, kt + 10);
+                compute_mx16(lds1, scl1, 16, 1, wide{});
+                step_end();
+                issue_ab(lds1, kt + 11);
+                compute_mx16(lds0, scl1, 16, 2, wide{});
+                step_end();
+                issue_ab(lds0, kt + 12);
+                compute_mx16(lds1, scl1, 16, 3, wide{});
+                step_end();
+                issue_ab(lds1, kt + 13);
+                compute_mx16(lds0, scl1, 16, 4, wide{});
+                step_end();
+                issue_ab(lds0, kt + 14);
+                compute_mx16(lds1, scl1, 16, 5, wide{});
+                step_end();
+                issue_ab(lds1, kt + 15);
+                issue_scales_wide(scl0, min(g + 2, NG - 1));
+                compute_mx16(lds0, scl1, 16, 6, wide{});
+                step_end_keep2();
+                issue_ab(lds0, min(kt + 16, KT - 1));
+                compute_mx16(lds1, scl1, 16, 7, wide{});
                 step_end();
             }
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends
@@ -1168,30 +1361,30 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             for (int kt = 0; kt < KT; kt += 8) {
                 const int g = kt / 4;
                 issue_ab(lds1, kt + 1);
-                compute_mx16(lds0, scl0, 16, 0);
+                compute_mx16(lds0, scl0, 16, 0, std::false_type{});
                 step_end();
                 issue_ab(lds0, kt + 2);
-                compute_mx16(lds1, scl0, 16, 1);
+                compute_mx16(lds1, scl0, 16, 1, std::false_type{});
                 step_end();
                 issue_ab(lds1, kt + 3);
                 issue_scales(scl1, g + 1);
-                compute_mx16(lds0, scl0, 16, 2);
+                compute_mx16(lds0, scl0, 16, 2, std::false_type{});
                 step_end_keep1();
                 issue_ab(lds0, kt + 4);
-                compute_mx16(lds1, scl0, 16, 3);
+                compute_mx16(lds1, scl0, 16, 3, std::false_type{});
                 step_end();
                 issue_ab(lds1, kt + 5);
-                compute_mx16(lds0, scl1, 16, 0);
+                compute_mx16(lds0, scl1, 16, 0, std::false_type{});
                 step_end();
                 issue_ab(lds0, kt + 6);
-                compute_mx16(lds1, scl1, 16, 1);
+                compute_mx16(lds1, scl1, 16, 1, std::false_type{});
                 step_end();
                 issue_ab(lds1, kt + 7);
                 issue_scales(scl0, min(g + 2, NG - 1));
-                compute_mx16(lds0, scl1, 16, 2);
+                compute_mx16(lds0, scl1, 16, 2, std::false_type{});
                 step_end_keep1();
                 issue_ab(lds0, min(kt + 8, KT - 1));
-                compute_mx16(lds1, scl1, 16, 3);
+                compute_mx16(lds1, scl1, 16, 3, std::false_type{});
                 step_end();
             }
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends

@@ -186,6 +186,32 @@ MSWZ_HD constexpr int row16(int b, int x)
 // consecutive slots 16 b + x.
 MSWZ_HD constexpr int sf_slot_row(int l) { return (l & ~24) | ((l & 8) << 1) | ((l & 16) >> 1); }
 
+// Scale stage with 32 bytes per row (eight E4M3 / padded K steps, or four
+// E2M1 steps), in two 16-byte halves h: byte offset of slot `slot` (0..511),
+// half h.  Each 32-slot block holds the first halves of its slots, then the
+// second halves, so that one 16-byte copy instruction fetches both halves of
+// 32 rows (two lanes per row, in one cache line) and writes them to 1 KiB of
+// consecutive LDS; within a half, slots sit 16 bytes apart as in the
+// 16-byte stage.
+MSWZ_HD constexpr uint32_t sf_wide_offset(uint32_t slot, uint32_t h)
+{
+    return (slot >> 5) * 1024u + h * 512u + (slot & 31u) * 16u;
+}
+
+// The byte lane l reads from a wide stage for fragment block b of the
+// 16-row blocks that start at slot slot0 (a multiple of 32): slot
+// slot0 + 16b + l%16, at byte `byte` of the slot's half h.  For such slot0
+// the offset splits into a per-lane part (b = 0, h = 0, byte 0), a per-block
+// part (slot0 = 0, lane 0) and the half and byte, which the kernels add as
+// immediates.
+MSWZ_HD constexpr uint32_t sf_wide_read(uint32_t slot0, int b, uint32_t h, uint32_t byte, int lane)
+{
+    return sf_wide_offset(slot0 + 16u * uint32_t(b) + uint32_t(lane & 15), h) + byte;
+}
+static_assert(sf_wide_read(96, 5, 1, 7, 13) ==
+                  sf_wide_read(96, 0, 0, 0, 13) + sf_wide_read(0, 5, 0, 0, 0) + sf_wide_offset(0, 1) + 7,
+              "wide scale reads split into lane, block and half parts");
+
 // LDS byte offset, at sub-step 0 and first half, of this lane's piece of the
 // 32-row 32x32x16 MFMA fragment whose tile rows start at rbase (a multiple of
 // 32) in an MN-major tile, read with ds_read_b64_tr_b16.  The operand wants,

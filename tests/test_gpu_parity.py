@@ -246,6 +246,12 @@ FP4 = {
                                name="e2m1-mx-k2048"),
     "e2m1-mx-tail-k1024-beta": wl.custom(300, 292, 1024, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
                                          b_dist=("normal", 1.0), name="e2m1-mx-tail-k1024-beta"),
+    # K a multiple of 2048: 32-byte scale groups of four steps (one and three
+    # loop iterations)
+    "e2m1-mx-tail-k4096-beta": wl.custom(300, 292, 4096, "e2m1", V=32, beta=1, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="e2m1-mx-tail-k4096-beta"),
+    "e2m1-mx-k6144": wl.custom(256, 512, 6144, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e2m1-mx-k6144"),
 }
 
 
@@ -272,17 +278,19 @@ def test_fp4_half_integers_bit_exact(name):
     assert np.array_equal(got, ref.astype(np.float32))
 
 
-def test_fp4_scale_bytes_select_the_right_block():
+@pytest.mark.parametrize("K", [1024, 4096])
+def test_fp4_scale_bytes_select_the_right_block(K):
     """Scales only: every E2M1 element 1.0 (byte 0x22), so D[m,n] =
     32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a wrong scale byte, lane or word
-    for any of the eight blocks of a K step changes the value."""
-    M, N, K = 256, 512, 1024
+    for any of the eight blocks of a K step changes the value (K = 4096: the
+    32-byte scale groups)."""
+    M, N = 256, 512
     w = wl.custom(M, N, K, "e2m1", V=32, name="fp4-scale-only")
     rng = np.random.default_rng(7)
     x = {"A": np.full((M, K // 2), 0x22, np.uint8), "B": np.full((N, K // 2), 0x22, np.uint8),
          "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
          "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
-    say("[fp4] scale closed form")
+    say(f"[fp4] scale closed form K={K}")
     got = run_gpu(w, x)
     ua = x["SFA"].astype(np.int64) - 127
     ub = x["SFB"].astype(np.int64) - 127
@@ -302,6 +310,14 @@ FP6 = {
                               name="e2m3-mx-tail"),
     "e3m2-mx-k2048": wl.custom(512, 512, 2048, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                name="e3m2-mx-k2048"),
+    # 32-byte scale groups of eight steps (K a multiple of 2048), padded E2M1
+    # alone as well
+    "e2m3-mx-tail-k4096-beta": wl.custom(300, 292, 4096, "e2m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="e2m3-mx-tail-k4096-beta"),
+    "e3m2-mx-k6144": wl.custom(256, 256, 6144, "e3m2", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                               name="e3m2-mx-k6144"),
+    "e2m1p-k4096-tail-beta": wl.custom(300, 292, 4096, "e2m1p", V=32, beta=1, a_dist=("normal", 1.0),
+                                       b_dist=("normal", 1.0), name="e2m1p-k4096-tail-beta"),
 }
 
 
@@ -346,11 +362,13 @@ def test_padding_bytes_are_never_read(name):
     assert np.array_equal(run_gpu(w, y), base)
 
 
+@pytest.mark.parametrize("K", [1024, 4096])
 @pytest.mark.parametrize("kind,one", [("e2m3", 8), ("e3m2", 12)])
-def test_fp6_scale_bytes_select_the_right_block(kind, one):
+def test_fp6_scale_bytes_select_the_right_block(kind, one, K):
     """Scales only: every element 1.0, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
-    exactly; a wrong scale byte or lane for any block changes the value."""
-    M, N, K = 256, 512, 1024
+    exactly; a wrong scale byte or lane for any block changes the value (K =
+    4096: the 32-byte scale groups)."""
+    M, N = 256, 512
     w = wl.custom(M, N, K, kind, V=32, name=f"{kind}-scale-only")
     rng = np.random.default_rng(9)
     ones = wl.to_stored(np.ones((1, 16)), kind)[0]
@@ -358,7 +376,7 @@ def test_fp6_scale_bytes_select_the_right_block(kind, one):
     x = {"A": np.tile(ones, (M, K // 16)), "B": np.tile(ones, (N, K // 16)),
          "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
          "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
-    say(f"[fp6] scale closed form {kind}")
+    say(f"[fp6] scale closed form {kind} K={K}")
     got = run_gpu(w, x)
     ua = x["SFA"].astype(np.int64) - 127
     ub = x["SFB"].astype(np.int64) - 127

@@ -289,6 +289,59 @@ def test_grouped_scale_reads_conflict_two_ways_under_the_byte_model():
         assert conflicts(mswz.lds_lanes("scale_grp", b, 0), 1, PASSES_1) == 2
 
 
+def _wide_holder(pattern):
+    """Stage byte -> (operand row, scale byte) after the wide copies of one
+    group: copy q of wave w writes 1 KiB; lane l's 16 bytes are half h of a
+    row's 32 scale bytes (eight E4M3 / padded steps, four E2M1 steps)."""
+    holder = {}
+    for w in range(8):
+        for q in range(2):
+            dst, src = pairs(pattern, w, q)
+            assert dst == [2048 * w + 1024 * q + 16 * l for l in range(64)]   # 1 KiB contiguous
+            rows = {r // 2 for r in src}
+            assert len(rows) == 32                       # 32 rows, both halves of each: one line per row
+            for d, r in zip(dst, src):
+                row, h = r // 2, r % 2
+                for byte in range(16):
+                    holder[d + byte] = (64 * (w & 3) + row + (256 if w >= 4 else 0), 16 * h + byte)
+    assert sorted(holder) == list(range(512 * 32))
+    return holder
+
+
+def test_wide_scale_slots_put_each_fragment_rows_scales_where_they_are_read():
+    """32-byte-per-row stage of the 6-bit kinds (slot order of sf_slot_row):
+    every byte that lane (x, g) of fragment block b reads at step s of its
+    group of eight is byte 4 s + g of that fragment row's 32 scale bytes."""
+    holder = _wide_holder("scale_dma_wide")
+    for b in range(8):
+        for st in range(8):
+            for l, a in enumerate(mswz.lds_lanes("scale_grp_wide", b, st)):
+                x, g = l & 15, l >> 4
+                assert holder[a] == (32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3), 4 * st + g)
+
+
+def test_wide_fp4_scale_slots_put_each_fragment_rows_scales_where_they_are_read():
+    """Dense E2M1 (rows in order): the byte lane (x, g) of block b reads at
+    step s of its group of four, sub-step u, is byte 8 s + 4 u + kblk16(g) of
+    row 16 b + x's 32 scale bytes (a step's eight 32-element blocks)."""
+    holder = _wide_holder("scale_dma_wide_nat")
+    for b in range(8):
+        for st in range(4):
+            for u in range(2):
+                for l, a in enumerate(mswz.lds_lanes("scale_fp4_wide", b, 2 * st + u)):
+                    x, g = l & 15, l >> 4
+                    assert holder[a] == (16 * b + x, 8 * st + 4 * u + kblk(g))
+
+
+def test_wide_scale_reads_conflict_two_ways_under_the_byte_model():
+    """Within a half the slots sit 16 bytes apart as in the 16-byte stage, so
+    the reads keep its two-way conflict and no more."""
+    for b in range(8):
+        for st in (0, 5):
+            assert conflicts(mswz.lds_lanes("scale_grp_wide", b, st), 1, PASSES_1) == 2
+            assert conflicts(mswz.lds_lanes("scale_fp4_wide", b, st), 1, PASSES_1) == 2
+
+
 # ---- staged epilogue -------------------------------------------------------------------
 
 @pytest.mark.parametrize("rows", [0, 1, 2, 3])
