@@ -434,8 +434,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // scale-stage word 64*g + l.  Per group of four K steps (kScaleGroups, the
     // 16x16 path with eight waves and K a multiple of 1024): lane l copies the
     // 16 scale bytes of the four steps of row 64*(g%4) + sf_slot_row(l) into
-    // stage bytes 16*(64g + l) .. +15 (the slot order keeps the scale reads
-    // free of bank conflicts).  A row's scales for one step are only 4 bytes and consecutive rows
+    // stage bytes 16*(64g + l) .. +15 (the slot order makes a fragment
+    // block's 16 rows consecutive slots, whose byte reads conflict two-way and
+    // no more).  A row's scales for one step are only 4 bytes and consecutive rows
     // are K/32 bytes apart, so a per-step copy touches one cache line per lane
     // for 4 useful bytes; fetching four steps at once cuts those line accesses
     // fourfold, and they cost as much address-unit time as the operand copies.
@@ -459,8 +460,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
-    // Wide groups (K a multiple of 2048 for E4M3 and the padded kinds, 1024
-    // for E2M1): 32 bytes per row and group, two copies per wave and group.
+    // Wide groups (kWideStage: one 6- or 4-bit kind on both sides, K a
+    // multiple of 2048): 32 bytes per row and group (eight padded or four
+    // E2M1 steps), two copies per wave and group.
     // Copy q of wave g fetches rows of slots 32q .. 32q+31 of its 64-row group
     // (slot order as above), lane l the half l/32 of slot 32q + l%32, so both
     // halves of a row come from one cache line in one instruction, and
