@@ -25,6 +25,15 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The E4M3 kernels with fp32 D and 32-byte scale
+# groups fit their registers only under LLVM's iterative ILP scheduling
+# strategy (20 registers spilled and reloaded every K step under the default
+# strategy); the other units keep the default, under which they spill least.
+EXTRA_FLAGS = {
+    "gemm256_e4m3_f32.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -38,7 +47,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -383,12 +383,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr int kStepK = kPair ? 128 : kFp4 ? 256 : kByteRows ? 128 : 64;
     constexpr int kStepA = kPairA ? 256 : kStepK, kStepB = kPairB ? 256 : kStepK;
 
-    // the grouped scale copies (below) with 32-element blocks, for one
-    // 6- or 4-bit kind on both sides: their stages hold 32 bytes per row
-    // (2 x 64 KiB of operand stages + 2 x 16 KiB).  (With an E4M3 operand, or
-    // two different kinds, the wide loop left the kernel short of registers:
-    // up to 20 spilled, reloaded every step.)
-    constexpr bool kWideStage = ((kFp6 && !kMixed) || kFp4) && !kV16 && !SB;
+    // the grouped scale copies (below) with 32-element blocks, for one kind
+    // on both sides: their stages hold 32 bytes per row (2 x 64 KiB of
+    // operand stages + 2 x 16 KiB).  (With two different kinds the wide loop
+    // left the kernels short of registers, up to 21 spilled and reloaded
+    // every step; E4M3 fits with fp32 D under the scheduling strategy of its
+    // unit, gemm256_e4m3_f32.hip, and keeps the 16-byte groups otherwise.)
+    constexpr bool kWideStage =
+        ((kByteRows && !kMixed && (KIND != kE4m3 || OUT == kOutF32)) || kFp4) && !kV16 && !SB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
@@ -460,9 +462,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
     }
-    // Wide groups (kWideStage: one 6- or 4-bit kind on both sides, K a
-    // multiple of 2048): 32 bytes per row and group (eight padded or four
-    // E2M1 steps), two copies per wave and group.
+    // Wide groups (kWideStage: one block-scaled kind on both sides, K a
+    // multiple of 2048): 32 bytes per row and group (eight E4M3 or padded or
+    // four E2M1 steps), two copies per wave and group.
     // Copy q of wave g fetches rows of slots 32q .. 32q+31 of its 64-row group
     // (slot order as above), lane l the half l/32 of slot 32q + l%32, so both
     // halves of a row come from one cache line in one instruction, and

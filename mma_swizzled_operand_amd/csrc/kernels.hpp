@@ -80,6 +80,8 @@ hipError_t launch256_bf16_amn(bool b_mn, const MxArgs &args, hipStream_t stream)
 hipError_t launch256_f16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_f16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
+// fp32 D, K a multiple of 128 (gemm256_e4m3_f32.hip)
+hipError_t launch256_e4m3_f32(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);

@@ -146,6 +146,14 @@ TAILS = {
                               name="tail-e4m3-mx"),
     "tail-e4m3-mx-k1024-beta": wl.custom(264, 520, 1024, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
                                          b_dist=("normal", 1.0), name="tail-e4m3-mx-k1024-beta"),
+    # K a multiple of 2048: E4M3 with 32-byte scale groups of eight steps
+    # (two and three sixteen-step iterations), and K = 3072 (16-byte groups)
+    "tail-e4m3-mx-k4096-beta": wl.custom(300, 292, 4096, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                         b_dist=("normal", 1.0), name="tail-e4m3-mx-k4096-beta"),
+    "tail-e4m3-mx-k6144": wl.custom(264, 256, 6144, "e4m3", V=32, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="tail-e4m3-mx-k6144"),
+    "tail-e4m3-mx-k3072": wl.custom(256, 264, 3072, "e4m3", V=32, a_dist=("normal", 1.0),
+                                    b_dist=("normal", 1.0), name="tail-e4m3-mx-k3072"),
     "tail-one-row": wl.custom(1, 4, 64, "bf16", name="tail-one-row"),
     "tail-257": wl.custom(257, 256, 64, "f16", beta=1, name="tail-257"),
 }
@@ -627,12 +635,13 @@ def test_full_size_c5_quarter_exact():
     assert np.array_equal(got[:, cols].astype(np.float64), reference(w, x, cols=cols, with_mag=False))
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (512, 256, 2048), (300, 260, 1024)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (512, 256, 2048), (300, 260, 1024), (264, 300, 4096)])
 def test_scale_bytes_select_the_right_block(M, N, K):
     """Scales only: a = b = 1 everywhere, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
     exactly (block-scale closed form); a wrong byte or lane for any scale
     block changes the value.  K = 512 copies scales per K step; K a multiple
-    of 1024 copies them per group of four steps (ragged M, N too)."""
+    of 1024 copies them per group of four steps (ragged M, N too), a multiple
+    of 2048 per group of eight (32 bytes per row)."""
     w = wl.custom(M, N, K, "e4m3", V=32, name="scale-only")
     rng = np.random.default_rng(6)
     x = {"A": np.full((M, K), 0x38, np.uint8), "B": np.full((N, K), 0x38, np.uint8),
