@@ -25,12 +25,15 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source additions.  The E4M3 kernels with fp32 D and 32-byte scale
+# Per-source additions.  The kernels with an E4M3 A, fp32 D and 32-byte scale
 # groups fit their registers only under LLVM's iterative ILP scheduling
-# strategy (20 registers spilled and reloaded every K step under the default
-# strategy); the other units keep the default, under which they spill least.
+# strategy (E4M3 alone: 20 registers spilled and reloaded every K step under
+# the default strategy); the other units keep the default, under which they
+# spill least.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 EXTRA_FLAGS = {
-    "gemm256_e4m3_f32.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "gemm256_e4m3_f32.hip": _ILP,
+    "gemm256_mixed_e4m3_f32.hip": _ILP,
 }
 
 

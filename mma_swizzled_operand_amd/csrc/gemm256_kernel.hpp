@@ -387,10 +387,12 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // on both sides: their stages hold 32 bytes per row (2 x 64 KiB of
     // operand stages + 2 x 16 KiB).  (With two different kinds the wide loop
     // left the kernels short of registers, up to 21 spilled and reloaded
-    // every step; E4M3 fits with fp32 D under the scheduling strategy of its
-    // unit, gemm256_e4m3_f32.hip, and keeps the 16-byte groups otherwise.)
+    // every step; an E4M3 A (alone or with a 6-bit or padded 4-bit B) fits
+    // with fp32 D under the scheduling strategy of its units,
+    // gemm256_e4m3_f32.hip and gemm256_mixed_e4m3_f32.hip, and keeps the
+    // 16-byte groups otherwise.)
     constexpr bool kWideStage =
-        ((kByteRows && !kMixed && (KIND != kE4m3 || OUT == kOutF32)) || kFp4) && !kV16 && !SB;
+        ((kByteRows && (!kMixed || KIND == kE4m3) && (KIND != kE4m3 || OUT == kOutF32)) || kFp4) && !kV16 && !SB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];

@@ -1,6 +1,7 @@
 // gemm256_mixed.hip — instantiations of the 256x256-tile GEMM for block-scaled
 // operands of two different kinds among OCP E4M3, E2M3, E3M2 and padded E2M1
-// (both K-major; the eight-wave 16x16 pipeline only).
+// (both K-major; the eight-wave 16x16 pipeline only), except E4M3 A with fp32
+// D and K a multiple of the K step (gemm256_mixed_e4m3_f32.hip).
 #include "gemm256_kernel.hpp"
 
 namespace mswz {
@@ -13,14 +14,26 @@ hipError_t launch_pair(const MxArgs &a, hipStream_t stream)
 }
 
 // B's kind KB for A's kind KA; one kind on both sides is not a mix (those
-// plans take the single-kind kernels) and is not instantiated here
+// plans take the single-kind kernels) and is not instantiated here.  E4M3 A
+// with fp32 D and K a multiple of the K step goes to
+// gemm256_mixed_e4m3_f32.hip (compiled with another scheduling strategy).
 template <int KA, int KB>
 hipError_t launch_if_mixed(const MxArgs &a, hipStream_t stream)
 {
-    if constexpr (KA == KB)
+    if constexpr (KA == KB) {
         return hipErrorInvalidValue;
-    else
+    } else if constexpr (KA == kE4m3) {
+        if (a.K % 128 != 0)
+            return launch_out<KA, false, false, KB, 32, true>(a, stream);
+        switch (a.out) {
+        case kOutBf16: return launch_kind<KA, false, false, kOutBf16, KB>(a, stream);
+        case kOutF16: return launch_kind<KA, false, false, kOutF16, KB>(a, stream);
+        default:
+            return launch256_mixed_e4m3_f32(a, KB == kE2m3 ? kMxE2m3 : KB == kE3m2 ? kMxE3m2 : kMxE2m1p, stream);
+        }
+    } else {
         return launch_pair<KA, KB>(a, stream);
+    }
 }
 
 template <int KA>

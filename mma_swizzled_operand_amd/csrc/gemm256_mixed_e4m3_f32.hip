@@ -1,0 +1,21 @@
+// gemm256_mixed_e4m3_f32.hip — the 256x256-tile GEMM for E4M3 A with a
+// 6-bit or padded 4-bit B (block-scaled, both K-major), fp32 D and K a
+// multiple of the 128-element K step: kernels whose 32-byte scale groups fit
+// the registers only under LLVM's iterative ILP scheduling strategy, which
+// this unit is compiled with (_build.py); the other mixed kernels spill more
+// under it and stay in gemm256_mixed.hip.
+#include "gemm256_kernel.hpp"
+
+namespace mswz {
+
+hipError_t launch256_mixed_e4m3_f32(const MxArgs &a, MxKind kb, hipStream_t stream)
+{
+    switch (kb) {
+    case kMxE2m3: return launch_kind<kE4m3, false, false, kOutF32, kE2m3>(a, stream);
+    case kMxE3m2: return launch_kind<kE4m3, false, false, kOutF32, kE3m2>(a, stream);
+    case kMxE2m1p: return launch_kind<kE4m3, false, false, kOutF32, kE2m1p>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mswz

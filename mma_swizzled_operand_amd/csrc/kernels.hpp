@@ -85,6 +85,8 @@ hipError_t launch256_e4m3_f32(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_e2m1(const MxArgs &args, hipStream_t stream);
 hipError_t launch256_padded(const MxArgs &args, MxKind kind, hipStream_t stream);
 hipError_t launch256_mixed(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
+// E4M3 A, fp32 D, K a multiple of 128 (gemm256_mixed_e4m3_f32.hip)
+hipError_t launch256_mixed_e4m3_f32(const MxArgs &args, MxKind kind_b, hipStream_t stream);
 // E4M3 with dense E2M1 (either side), K % 256 == 0
 hipError_t launch256_pair(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStream_t stream);
 hipError_t launch256_v16(const MxArgs &args, MxKind kind, hipStream_t stream);

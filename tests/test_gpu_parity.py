@@ -436,6 +436,14 @@ MIXED = {
                                      b_dist=("normal", 1.0), name="e4m3xe2m1-k256-beta", b_kind="e2m1"),
     "e2m1xe4m3-k768": wl.custom(512, 264, 768, "e2m1", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
                                 name="e2m1xe4m3-k768", b_kind="e4m3"),
+    # E4M3 A with K a multiple of 2048: 32-byte scale groups of eight steps
+    "e4m3xe2m3-k4096-tail-beta": wl.custom(300, 292, 4096, "e4m3", V=32, beta=1, a_dist=("normal", 1.0),
+                                           b_dist=("normal", 1.0), name="e4m3xe2m3-k4096-tail-beta",
+                                           b_kind="e2m3"),
+    "e4m3xe2m1p-k2048": wl.custom(512, 256, 2048, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                  name="e4m3xe2m1p-k2048", b_kind="e2m1p"),
+    "e4m3xe3m2-k6144": wl.custom(256, 264, 6144, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0),
+                                 name="e4m3xe3m2-k6144", b_kind="e3m2"),
 }
 
 
@@ -460,19 +468,21 @@ def test_mixed_quarter_integers_bit_exact(name):
     assert np.array_equal(got, reference(w, x, with_mag=False).astype(np.float32))
 
 
-@pytest.mark.parametrize("ka,kb", [("e4m3", "e2m3"), ("e3m2", "e4m3"), ("e2m1p", "e2m1p"), ("e2m1p", "e4m3"),
-                                   ("e4m3", "e2m1"), ("e2m1", "e4m3")])
-def test_mixed_scale_bytes_select_the_right_block(ka, kb):
+@pytest.mark.parametrize("ka,kb,K", [("e4m3", "e2m3", 1024), ("e3m2", "e4m3", 1024), ("e2m1p", "e2m1p", 1024),
+                                     ("e2m1p", "e4m3", 1024), ("e4m3", "e2m1", 1024), ("e2m1", "e4m3", 1024),
+                                     ("e4m3", "e2m3", 4096), ("e4m3", "e2m1p", 4096), ("e4m3", "e4m3", 4096)])
+def test_mixed_scale_bytes_select_the_right_block(ka, kb, K):
     """Scales only, every element 1.0 in its own format: D[m,n] =
     32 sum_j 2^(uA[m,j]+uB[n,j]) exactly; a value meeting a partner from
-    another K block, or a wrong scale byte, changes the value."""
-    M, N, K = 256, 512, 1024
+    another K block, or a wrong scale byte, changes the value (K = 4096: the
+    32-byte scale groups of an E4M3 A)."""
+    M, N = 256, 512
     w = wl.custom(M, N, K, ka, V=32, name=f"{ka}x{kb}-scale-only", b_kind=kb)
     rng = np.random.default_rng(10)
     x = {"A": wl.to_stored(np.ones((M, K)), ka), "B": wl.to_stored(np.ones((N, K)), kb),
          "SFA": (127 + rng.integers(-4, 5, (M, K // 32))).astype(np.uint8),
          "SFB": (127 + rng.integers(-4, 5, (N, K // 32))).astype(np.uint8)}
-    say(f"[mixed] scale closed form {ka} x {kb}")
+    say(f"[mixed] scale closed form {ka} x {kb} K={K}")
     got = run_gpu(w, x)
     ua = x["SFA"].astype(np.int64) - 127
     ub = x["SFB"].astype(np.int64) - 127
