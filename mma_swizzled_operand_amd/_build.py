@@ -25,19 +25,25 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source additions: LLVM's iterative ILP scheduling strategy where it
-# measured faster.  The kernels with an E4M3 A, fp32 D and 32-byte scale
-# groups fit their registers only under it (E4M3 alone: 20 registers spilled
-# and reloaded every K step under the default strategy); the 16-bit kernels
-# with a K-major A run 1.5 % faster under it (8192^3, B K-major; 0.6 % with
-# B MN-major), those with an MN-major A 0.5-4.5 % slower.  The other units
-# keep the default, under which they spill least.
+# Per-source additions: an LLVM scheduling strategy where it measured faster
+# (8192^3, same-box A/B).  The kernels with an E4M3 A, fp32 D and 32-byte
+# scale groups fit their registers only under the iterative ILP strategy
+# (E4M3 alone: 20 registers spilled and reloaded every K step under the
+# default); under it the 16-bit kernels with a K-major A run 1.5 % faster
+# (0.6 % with B MN-major) and the padded 6-bit ones 2.3 %, the MN-major-A
+# ones 0.5-4.5 % slower.  Both operands MN-major (32x32x16 MFMAs) run 4 %
+# faster under the max-ILP strategy, which slows the others by 2-5 %.  The
+# remaining units keep the default, under which they spill least.
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+_MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA_FLAGS = {
     "gemm256_e4m3_f32.hip": _ILP,
     "gemm256_mixed_e4m3_f32.hip": _ILP,
     "gemm256_bf16_ak.hip": _ILP,
     "gemm256_f16_ak.hip": _ILP,
+    "gemm256_fp6.hip": _ILP,
+    "gemm256_bf16_amn_bmn.hip": _MAX_ILP,
+    "gemm256_f16_amn_bmn.hip": _MAX_ILP,
 }
 
 

@@ -1,7 +1,7 @@
 // gemm256.hip — run-time dispatch of the 256x256-tile GEMM (gemm256_kernel.hpp)
 // to its instantiations, one translation unit per operand kind and A major
 // (gemm256_bf16_ak.hip, gemm256_bf16_amn.hip, gemm256_f16_ak.hip,
-// gemm256_f16_amn.hip, gemm256_e4m3.hip, gemm256_e4m3_f32.hip, gemm256_e2m1.hip, gemm256_fp6.hip,
+// gemm256_f16_amn.hip, gemm256_f16_amn_bmn.hip, gemm256_e4m3.hip, gemm256_e4m3_f32.hip, gemm256_e2m1.hip, gemm256_fp6.hip,
 // gemm256_mixed.hip, gemm256_mixed_e4m3_f32.hip, gemm256_pair.hip, gemm256_v16.hip),
 // so that they
 // compile in parallel.

@@ -1,11 +1,13 @@
-// gemm256_bf16_amn.hip — instantiations of the 256x256-tile GEMM for bf16 operands, A MN-major (B either major).
+// gemm256_bf16_amn.hip — instantiations of the 256x256-tile GEMM for bf16 operands, A MN-major,
+// B K-major; both MN-major in gemm256_bf16_amn_bmn.hip (a unit compiled with
+// another scheduling strategy).
 #include "gemm256_kernel.hpp"
 
 namespace mswz {
 
 hipError_t launch256_bf16_amn(bool b_mn, const MxArgs &a, hipStream_t stream)
 {
-    return b_mn ? launch_cfg<kBf16, true, true>(a, stream) : launch_cfg<kBf16, true, false>(a, stream);
+    return b_mn ? launch256_bf16_amn_bmn(a, stream) : launch_cfg<kBf16, true, false>(a, stream);
 }
 
 }  // namespace mswz

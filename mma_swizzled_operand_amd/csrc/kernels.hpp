@@ -77,8 +77,10 @@ hipError_t launch_mx256(const MxArgs &args, MxKind kind_a, MxKind kind_b, hipStr
 // the 256x256-tile instantiations, one translation unit each (gemm256_*.hip)
 hipError_t launch256_bf16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_bf16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_bf16_amn_bmn(const MxArgs &args, hipStream_t stream);   // both MN-major
 hipError_t launch256_f16_ak(bool b_mn, const MxArgs &args, hipStream_t stream);
 hipError_t launch256_f16_amn(bool b_mn, const MxArgs &args, hipStream_t stream);
+hipError_t launch256_f16_amn_bmn(const MxArgs &args, hipStream_t stream);   // both MN-major
 hipError_t launch256_e4m3(const MxArgs &args, hipStream_t stream);
 // fp32 D, K a multiple of 128 (gemm256_e4m3_f32.hip)
 hipError_t launch256_e4m3_f32(const MxArgs &args, hipStream_t stream);
