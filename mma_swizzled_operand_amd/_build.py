@@ -32,8 +32,10 @@ HIPCC_FLAGS = [
 # default); under it the 16-bit kernels with a K-major A run 1.5 % faster
 # (0.6 % with B MN-major) and the padded 6-bit ones 2.3 %, the MN-major-A
 # ones 0.5-4.5 % slower.  Both operands MN-major (32x32x16 MFMAs) run 4 %
-# faster under the max-ILP strategy, which slows the others by 2-5 %.  The
-# remaining units keep the default, under which they spill least.
+# faster under the max-ILP strategy, which slows the others by 2-5 %; so
+# does the split-K kernel for a few rows of A (16 x 8192 x 8192: 3 %, 98
+# registers instead of 108).  The remaining units keep the default, under
+# which they spill least.
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 _MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA_FLAGS = {
@@ -44,6 +46,7 @@ EXTRA_FLAGS = {
     "gemm256_fp6.hip": _ILP,
     "gemm256_bf16_amn_bmn.hip": _MAX_ILP,
     "gemm256_f16_amn_bmn.hip": _MAX_ILP,
+    "gemm_skinny_sk.hip": _MAX_ILP,
 }
 
 
