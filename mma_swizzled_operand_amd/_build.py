@@ -33,9 +33,9 @@ HIPCC_FLAGS = [
 # (0.6 % with B MN-major) and the padded 6-bit ones 2.3 %, the MN-major-A
 # ones 0.5-4.5 % slower.  Both operands MN-major (32x32x16 MFMAs) run 4 %
 # faster under the max-ILP strategy, which slows the others by 2-5 %; so
-# does the split-K kernel for a few rows of A (16 x 8192 x 8192: 3 %, 98
-# registers instead of 108).  The remaining units keep the default, under
-# which they spill least.
+# do the weight-streaming kernels for a few rows of A (64 x 16384 x 8192,
+# K-sliced: 3 %, the same registers in another order).  The remaining units
+# keep the default, under which they spill least.
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 _MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA_FLAGS = {
