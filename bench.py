@@ -106,7 +106,11 @@ def setup(w, seed=0):
     A, B = dev(x["A"]), dev(x["B"])
     D = dev(x["D0"]) if w.beta else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
     if w.V:
-        SFA, SFB = dev(x["SFA"]), dev(x["SFB"])
+        if w.sf_major == "mn":   # the same scales stored [K/32][M] and [K/32][N]
+            mswz.gemm_plan_set_scale_major(plan, "mn")
+            SFA, SFB = dev(x["SFA"].T), dev(x["SFB"].T)
+        else:
+            SFA, SFB = dev(x["SFA"]), dev(x["SFB"])
 
         def step():
             mswz.gemm_run_blockscaled(plan, A, B, SFA, SFB, D, w.beta)
@@ -298,7 +302,7 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=250.0,
                     help="keep warming up until this many ms of back-to-back launches have passed")
     ap.add_argument("--workload", default="c3b")
-    ap.add_argument("--also", default="c5,c1,c2,c3,c4,c6,c7,c8,c9,c10,c11,c12,c13",
+    ap.add_argument("--also", default="c5,c1,c2,c3,c4,c6,c7,c8,c9,c10,c11,c12,c13,c14",
                     help="comma-separated extra workloads timed in the same run ('' for none)")
     ap.add_argument("--cold-calls", type=int, default=50,
                     help="after the timed steps, time this many single calls of each workload "

@@ -32,6 +32,7 @@
  *      (j even) or high (j odd) nibble of byte j/2, then eight padding bytes)
  *     D  [M][N] in the plan's d_dt (fp32, bf16 or fp16)
  *     SFA uint8 [M][K/V], SFB uint8 [N][K/V]: OCP E8M0 exponents, value 2^(E-127)
+ *       (or [K/V][M] and [K/V][N] after gemm_plan_set_scale_major)
  * Element formats: fp16 (IEEE binary16), bf16, fp8 = OCP E4M3 (bias 7, no
  * infinities), fp4 = OCP E2M1 (bias 1, no infinities or NaN; the pages'
  * "four-bit values"), fp6 = OCP E2M3 (bias 1) or E3M2 (bias 3), neither with
@@ -39,8 +40,9 @@
  * is fixed per plan, so a plan gives bit-identical results run to run.
  *
  * Ownership: the caller owns every device buffer and the stream.  A plan holds
- * host metadata only and is immutable once created, so one plan may be used
- * from several host threads and streams at once.  gemm_run* enqueue their
+ * host metadata only and is immutable once created (apart from its scale
+ * layout, gemm_plan_set_scale_major), so one plan may be used from several
+ * host threads and streams at once.  gemm_run* enqueue their
  * kernels on `stream` (one; two for gemm_run_ws's split path) and return; they
  * allocate nothing, do not synchronise and keep no pointer.  Buffers must stay alive until the stream has passed the kernel
  * (the pages' rule of keeping allocations alive until consumers complete).
@@ -159,6 +161,29 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
                         int a_dt, int b_dt, int d_dt, int a_major, int b_major,
                         int32_t scale_vec_len, int64_t lda, int64_t ldb,
                         int64_t ldd);
+
+/*
+ * Scale layout of a block-scaled plan.  The tcgen05.mma page ("Operands and
+ * repeat axes", the SFA / SFB rows of its shape table) gives the scale
+ * operands the K-repeat axis outside their rows; this call lets SFA and SFB
+ * be stored in that order.
+ *   sf_major  MSWZ_MAJOR_K (the plan's default): SFA uint8 [M][K/V], SFB
+ *             [N][K/V], each row's scales consecutive.  MSWZ_MAJOR_MN: SFA
+ *             uint8 [K/V][M], SFB [K/V][N], each K block's scales of all rows
+ *             consecutive (M, resp. N, bytes per K block).  Values and the
+ *             product are the same; only the addresses differ.
+ * MN-major scales are taken by the kernels that stage the scales of 32 K
+ * blocks at a time: V = 32, K a multiple of 2048, M and N multiples of 16,
+ * and A / B / D one of: E4M3 / E4M3 / fp32; E4M3 / E2M3, E3M2 or padded
+ * E2M1 / fp32; one of E2M3, E3M2, padded E2M1 or dense E2M1 on both sides
+ * with any D.  Such a plan runs the 256x256 tile (gemm_plan_describe shows
+ * it); setting MSWZ_MAJOR_K again restores the variant chosen at creation.
+ * The plan is changed in place: not while a call on it is being enqueued.
+ * Returns MSWZ_OK, MSWZ_ERR_INVALID (NULL plan, unknown sf_major),
+ * MSWZ_ERR_KIND (a dense plan) or MSWZ_ERR_UNSUPPORTED (MN-major for any
+ * other configuration; the plan is left unchanged).
+ */
+int gemm_plan_set_scale_major(gemm_plan *plan, int sf_major);
 
 /*
  * Enqueue D = beta*D + A.B^T for a dense plan on `stream` (a hipStream_t;
@@ -359,6 +384,17 @@ int mswz_tile_of_block(int block, int tiles_m, int tiles_n, int group_m,
  *   MSWZ_LDS_SCALE_FP4_WIDE  p0 = b (0..7), p1 = 2 x step in its group of
  *                       four + sub-step (0..7): the scale byte each lane
  *                       reads (dense E2M1, A side)                        (64)
+ *   MSWZ_LDS_SCALE_DMA_MN  p0 = wave (0..7), p1 = copy (0..1), MN-major
+ *                       scales: out[2l] = stage offset lane l writes (16
+ *                       bytes; B's half from 8192), out[2l+1] = 256 x (K block
+ *                       of the 32-block group) + first of the 16 rows whose
+ *                       scales for that block it copies                  (128)
+ *   MSWZ_LDS_SCALE_GRP_MN  p0 = b (0..7), p1 = step in its group of eight
+ *                       (0..7): the scale byte each lane reads, MN-major
+ *                       scales (E4M3 and padded kinds; A side, wave rows
+ *                       0..127)                                           (64)
+ *   MSWZ_LDS_SCALE_FP4_MN  p0 = b (0..7), p1 = 2 x step in its group of
+ *                       four + sub-step (0..7): the same for dense E2M1   (64)
  *   MSWZ_LDS_EPI_WRITE  p0 = quarter q (0..3), p1 = 16*rows + 4*ii + j: the
  *                       16-byte write of 16x16 block (2q + ii, j); rows 0:
  *                       16-bit, 1: split-row fragments on both sides (E4M3,
@@ -371,7 +407,8 @@ enum {
     MSWZ_LDS_FRAG_E4M3 = 5, MSWZ_LDS_FRAG_PAD = 6, MSWZ_LDS_FRAG_E4M3_MIXED = 7, MSWZ_LDS_FRAG_E2M1 = 8,
     MSWZ_LDS_SCALE_GRP = 9, MSWZ_LDS_SCALE_DMA = 10, MSWZ_LDS_EPI_WRITE = 11, MSWZ_LDS_EPI_READ = 12,
     MSWZ_LDS_FRAG_E4M3_FP4 = 13, MSWZ_LDS_SCALE_GRP_WIDE = 14, MSWZ_LDS_SCALE_DMA_WIDE = 15,
-    MSWZ_LDS_SCALE_DMA_WIDE_NAT = 16, MSWZ_LDS_SCALE_FP4_WIDE = 17
+    MSWZ_LDS_SCALE_DMA_WIDE_NAT = 16, MSWZ_LDS_SCALE_FP4_WIDE = 17, MSWZ_LDS_SCALE_DMA_MN = 18,
+    MSWZ_LDS_SCALE_GRP_MN = 19, MSWZ_LDS_SCALE_FP4_MN = 20
 };
 int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n);
 

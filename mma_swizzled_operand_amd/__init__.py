@@ -25,6 +25,7 @@ from . import _build
 __all__ = [
     "DTYPES", "MAJORS", "MswzError", "Plan", "gemm_plan_create", "gemm_plan_create_ld", "gemm_run",
     "gemm_run_blockscaled", "gemm_run_opts", "gemm_run_ws", "gemm_run_ws_noalloc", "gemm_noalloc_scratch_bytes", "GemmOpts", "gemm_plan_destroy", "gemm_status_str", "gemm_plan_describe",
+    "gemm_plan_set_scale_major",
     "desc_address", "desc_check", "tile_offset", "lds_lanes", "library_path", "load",
 ]
 
@@ -74,6 +75,8 @@ def load():
         h.gemm_plan_create_ld.restype = c_int
         h.gemm_run.argtypes = [vp, vp, vp, vp, c_int, vp]
         h.gemm_run.restype = c_int
+        h.gemm_plan_set_scale_major.argtypes = [vp, c_int]
+        h.gemm_plan_set_scale_major.restype = c_int
         h.gemm_plan_workspace_size.argtypes = [vp]
         h.gemm_plan_workspace_size.restype = i64
         h.gemm_run_ws.argtypes = [vp, vp, vp, vp, c_int, vp, i64, vp]
@@ -145,6 +148,7 @@ class Plan:
         self.lda = int(lda) or self.a_cols
         self.ldb = int(ldb) or self.b_cols
         self.ldd = int(ldd) or self.N
+        self.sf_major = "k"      # SFA [M][K/V], SFB [N][K/V]; "mn": [K/V][M], [K/V][N]
 
     @property
     def handle(self):
@@ -211,6 +215,15 @@ def gemm_plan_create_ld(M, N, K, a_dt, b_dt, d_dt="f32", a_major="k", b_major="k
 
 def gemm_plan_destroy(plan: Plan) -> None:
     plan.destroy()
+
+
+def gemm_plan_set_scale_major(plan: Plan, sf_major) -> None:
+    """Store SFA / SFB MN-major ("mn": [K/V][M] and [K/V][N]) or row-major
+    ("k", the default) for this block-scaled plan."""
+    rc = load().gemm_plan_set_scale_major(plan.handle, _code(sf_major, MAJORS, "major"))
+    if rc != 0:
+        raise MswzError(rc, "gemm_plan_set_scale_major")
+    plan.sf_major = sf_major if isinstance(sf_major, str) else _name(MAJORS, sf_major)
 
 
 def gemm_plan_describe(plan: Plan) -> dict:
@@ -371,7 +384,8 @@ def tile_offset(row, chunk) -> int:
 LDS_PATTERNS = {"dma_k": 1, "dma_mn": 2, "frag_k16": 3, "frag_mn16": 4, "frag_e4m3": 5, "frag_pad": 6,
                 "frag_e4m3_mixed": 7, "frag_e2m1": 8, "scale_grp": 9, "scale_dma": 10, "epi_write": 11,
                 "epi_read": 12, "frag_e4m3_fp4": 13, "scale_grp_wide": 14, "scale_dma_wide": 15,
-                "scale_dma_wide_nat": 16, "scale_fp4_wide": 17}
+                "scale_dma_wide_nat": 16, "scale_fp4_wide": 17, "scale_dma_mn": 18, "scale_grp_mn": 19,
+                "scale_fp4_mn": 20}
 
 
 def lds_lanes(pattern: str, p0: int = 0, p1: int = 0) -> list[int]:

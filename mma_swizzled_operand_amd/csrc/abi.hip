@@ -30,6 +30,8 @@ struct gemm_plan {
     int split_parts;        // K parts of the split weight-streaming kernel (0: none)
     int64_t ws_bytes;       // workspace gemm_run_ws needs for it
     int64_t lda, ldb, ldd;  // row pitches in elements (packed values when none were given)
+    int sf_major;           // MSWZ_MAJOR_K: SFA [M][K/V]; MSWZ_MAJOR_MN: SFA [K/V][M] (gemm_plan_set_scale_major)
+    int variant_k;          // the variant chosen at creation, for row-major scales
 };
 
 namespace mswz {
@@ -77,6 +79,20 @@ mswz::MxKind mx_kind(int dt)
 int out_kind(int d_dt)
 {
     return d_dt == MSWZ_DT_BF16 ? mswz::kOutBf16 : d_dt == MSWZ_DT_F16 ? mswz::kOutF16 : mswz::kOutF32;
+}
+
+// Whether the 256x256 kernel for these kinds stages 32 bytes of scales per
+// row (the kernels' kWideStage): 32-element blocks, K a multiple of the K
+// step, and one padded 6- or 4-bit kind or dense E2M1 on both sides, or an
+// E4M3 A (with B E4M3 or a padded kind) and fp32 D.
+bool wide_scale_stage(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
+{
+    auto padded = [](int d) { return d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2 || d == MSWZ_DT_E2M1_P64; };
+    if (v != 32 || K % (a_dt == MSWZ_DT_E2M1 ? 256 : 128) != 0)
+        return false;
+    if (a_dt == b_dt && (padded(a_dt) || a_dt == MSWZ_DT_E2M1))
+        return true;
+    return a_dt == MSWZ_DT_E4M3 && (b_dt == MSWZ_DT_E4M3 || padded(b_dt)) && d_dt == MSWZ_DT_F32;
 }
 
 // Choose the tile for an (M, N) output: the largest square tile dividing both
@@ -234,14 +250,15 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
     mswz::variant_info(p->variant, fp8, &p->info);
     if (fp4)
         p->info.tile_k = 256;                              // K elements per 128-byte row step
-    if (p->variant == mswz::kVarMx256)                 // the two scale stages: 32 bytes per row for
-        p->info.lds_bytes += 2 * 512 * ((fp4 || fp6) && !mixed && scale_vec_len == 32 && K % (fp4 ? 256 : 128) == 0
-                                            ? 32 : 16);   // one 6- or 4-bit kind (wide groups)
+    if (p->variant == mswz::kVarMx256)   // the two scale stages: 32 bytes per row where the kernel has the wide ones
+        p->info.lds_bytes += 2 * 512 * (wide_scale_stage(a_dt, b_dt, d_dt, scale_vec_len, K) ? 32 : 16);
     if (skinny) {
         p->info.tile_m = M > 32 ? 64 : 32;   // M padded to 32 or 64 rows
         p->info.lds_bytes = 8 * p->info.tile_m * 68 * 4;
     }
     p->blocks = ((M + p->info.tile_m - 1) / p->info.tile_m) * ((N + p->info.tile_n - 1) / p->info.tile_n);
+    p->sf_major = MSWZ_MAJOR_K;
+    p->variant_k = p->variant;
     if (skinny) {
         p->split_parts = mswz::skinny_split_parts(M, N, K);
         p->ws_bytes = p->split_parts ? mswz::skinny_split_workspace_bytes(M, N, p->split_parts) : 0;
@@ -253,6 +270,37 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K, int a_
 int64_t gemm_plan_workspace_size(const gemm_plan *p)
 {
     return p ? p->ws_bytes : int64_t(MSWZ_ERR_INVALID);
+}
+
+int gemm_plan_set_scale_major(gemm_plan *p, int sf_major)
+{
+    if (!p || (sf_major != MSWZ_MAJOR_K && sf_major != MSWZ_MAJOR_MN))
+        return MSWZ_ERR_INVALID;
+    if (p->scale_vec_len == 0)
+        return MSWZ_ERR_KIND;
+    int variant = p->variant_k;
+    if (sf_major == MSWZ_MAJOR_MN) {
+        // the wide scale stage with its 32-K-block loop (K % 2048), whole
+        // 16-byte chunks of 16 rows (M, N % 16), and 32-bit offsets into
+        // the [K/V][M] and [K/V][N] arrays
+        const int64_t kb = p->K / p->scale_vec_len;
+        if (!wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) || p->K % 2048 != 0 ||
+            p->M % 16 != 0 || p->N % 16 != 0 || kb * p->M >= (int64_t(1) << 32) ||
+            kb * p->N >= (int64_t(1) << 32))
+            return MSWZ_ERR_UNSUPPORTED;
+        variant = mswz::kVarMx256;
+    }
+    if (variant != p->variant) {
+        p->variant = variant;
+        mswz::variant_info(variant, true, &p->info);
+        if (p->a_dt == MSWZ_DT_E2M1)
+            p->info.tile_k = 256;
+        if (variant == mswz::kVarMx256)
+            p->info.lds_bytes += 2 * 512 * (wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) ? 32 : 16);
+        p->blocks = ((p->M + p->info.tile_m - 1) / p->info.tile_m) * ((p->N + p->info.tile_n - 1) / p->info.tile_n);
+    }
+    p->sf_major = sf_major;
+    return MSWZ_OK;
 }
 
 int gemm_run(const gemm_plan *p, const void *A, const void *B, void *D, int beta, void *stream)
@@ -307,7 +355,8 @@ int gemm_run_blockscaled(const gemm_plan *p, const void *A, const void *B, const
         !is_aligned16(SFB))
         return MSWZ_ERR_ALIGN;
     mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
-                   p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), {}, p->scale_vec_len};
+                   p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), {}, p->scale_vec_len,
+                   p->sf_major == MSWZ_MAJOR_MN};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = p->variant == mswz::kVarMx256 ? mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st)
                                                   : mswz::launch_mx(p->variant, a, st);
@@ -345,7 +394,7 @@ int gemm_run_opts(const gemm_plan *p, const void *A, const void *B, const uint8_
     if (mx) {
         mswz::MxArgs a{A, B, SFA, SFB, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
                        p->group_m, out_kind(p->d_dt), int(p->lda), int(p->ldb), int(p->ldd), e,
-                       p->scale_vec_len};
+                       p->scale_vec_len, p->sf_major == MSWZ_MAJOR_MN};
         err = mswz::launch_mx256(a, mx_kind(p->a_dt), mx_kind(p->b_dt), st);
     } else {
         mswz::DenseArgs a{A, B, static_cast<float *>(D), int(p->M), int(p->N), int(p->K), beta,
@@ -405,7 +454,7 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
                        pattern == MSWZ_LDS_FRAG_E4M3 || pattern == MSWZ_LDS_FRAG_PAD ||
                        pattern == MSWZ_LDS_FRAG_E4M3_MIXED || pattern == MSWZ_LDS_FRAG_E4M3_FP4 ||
                        pattern == MSWZ_LDS_SCALE_DMA || pattern == MSWZ_LDS_SCALE_DMA_WIDE ||
-                       pattern == MSWZ_LDS_SCALE_DMA_WIDE_NAT)
+                       pattern == MSWZ_LDS_SCALE_DMA_WIDE_NAT || pattern == MSWZ_LDS_SCALE_DMA_MN)
                           ? 128 : 64;
     if (!out || n < count)
         return MSWZ_ERR_INVALID;
@@ -492,6 +541,24 @@ int mswz_lds_lanes(int pattern, int p0, int p1, uint32_t *out, int n)
             out[2 * l + 1] = uint32_t(2 * row + (l >> 5));
             break;
         }
+        case MSWZ_LDS_SCALE_DMA_MN: {
+            if (!in(p0, 0, W) || !in(p1, 0, 2))
+                return MSWZ_ERR_INVALID;
+            const int i = 2 * (p0 & 3) + p1;
+            out[2 * l] = uint32_t(2048 * p0 + 1024 * p1 + 16 * l);
+            out[2 * l + 1] = 256u * sf_mn_copy_block(i, l) + sf_mn_copy_row(l);
+            break;
+        }
+        case MSWZ_LDS_SCALE_GRP_MN:
+            if (!in(p0, 0, 8) || !in(p1, 0, 8))
+                return MSWZ_ERR_INVALID;
+            out[l] = sf_mn_offset(uint32_t(4 * p1 + g), uint32_t(row16<true>(p0, l & 15)));
+            break;
+        case MSWZ_LDS_SCALE_FP4_MN:
+            if (!in(p0, 0, 8) || !in(p1, 0, 8))
+                return MSWZ_ERR_INVALID;
+            out[l] = sf_mn_offset(uint32_t(4 * p1 + kblk16(g)), uint32_t(16 * p0 + (l & 15)));
+            break;
         case MSWZ_LDS_EPI_WRITE: {
             const int rows = p1 >> 4, ii = (p1 >> 2) & 3, j = p1 & 3;
             if (!in(p0, 0, 4) || rows > 3 || ii > 1 || p1 < 0)

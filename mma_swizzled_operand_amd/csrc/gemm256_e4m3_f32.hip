@@ -10,6 +10,8 @@ namespace mswz {
 
 hipError_t launch256_e4m3_f32(const MxArgs &a, hipStream_t stream)
 {
+    if (a.sf_mn)
+        return launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, true>(a, stream);
     return launch_kind<kE4m3, false, false, kOutF32>(a, stream);
 }
 

@@ -11,6 +11,8 @@ namespace {
 template <int K>
 hipError_t launch_padded(const MxArgs &a, hipStream_t stream)
 {
+    if (a.sf_mn)   // MN-major scales: K a multiple of 2048 (no K tail)
+        return launch_out<K, false, false, -1, 32, false, true>(a, stream);
     return launch_cfg<K, false, false>(a, stream);
 }
 

@@ -49,6 +49,10 @@ constexpr int kScaleStage = (kBM + kBN) * 16;  // up to 16 scale bytes (four K s
 // grouped scale copies of 32 bytes per row (eight E4M3 / padded K steps or
 // four E2M1 steps; layout.hpp sf_wide_offset)
 constexpr int kScaleStageWide = (kBM + kBN) * 32;
+// MN-major scales in the wide stage: A's 32 K blocks of 256 rows
+// (sf_mn_offset), then B's
+constexpr uint32_t kSfMnB = uint32_t(kBM) * 32;
+static_assert(kScaleStageWide == 2 * int(kSfMnB) && kBM == 256 && kBN == 256, "two 8 KiB halves");
 
 
 // kE2m1p: E2M1 in the padded sixteen-per-16-byte form (eight bytes of nibbles,
@@ -338,9 +342,11 @@ constexpr int W = 8;
 // elements per scale byte (32, or 16 for E2M1 and the padded kinds); MF16:
 // 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major);
 // SB: block-scaled K that is not a multiple of the K step (scale bytes
-// assembled in registers, see below).
+// assembled in registers, see below); SM: scales stored MN-major,
+// SFA [K/SV][M] and SFB [K/SV][N] (the wide scale stage only, K a multiple of
+// 2048, M and N multiples of 16).
 template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32,
-          bool SB = false>
+          bool SB = false, bool SM = false>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -393,6 +399,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // 16-byte groups otherwise.)
     constexpr bool kWideStage =
         ((kByteRows && (!kMixed || KIND == kE4m3) && (KIND != kE4m3 || OUT == kOutF32)) || kFp4) && !kV16 && !SB;
+    static_assert(!SM || kWideStage, "MN-major scales: the wide scale stage");
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
@@ -458,8 +465,16 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int q = 0; q < kSfInstr; ++q) {
             const int g = wave + W * q;
             const bool is_b = g >= 4;
-            sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row,
-                                   uint32_t(is_b ? rows_b : rows_a) * sf_row);
+            if constexpr (SM)
+                // [K block][row] with M (N) bytes per K block: from the tile's
+                // first row to the end of the array.  Rows beyond M or N read
+                // the next K block's first rows (or zeros past the end), which
+                // only reach outputs that are not stored.
+                sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + (is_b ? n0 : m0),
+                                       sf_row * uint32_t(is_b ? N : M) - uint32_t(is_b ? n0 : m0));
+            else
+                sf_rsrc[q] = make_rsrc((is_b ? SFB : SFA) + size_t(is_b ? n0 : m0) * sf_row,
+                                       uint32_t(is_b ? rows_b : rows_a) * sf_row);
         }
         // with kScaleGroups lane l copies row sf_slot_row(l) of its group
         sf_voff = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(lane) : lane)) * sf_row;
@@ -477,13 +492,21 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // (sf_slot_row keeps bit 5, so copy 1's rows are copy 0's plus 32: one
     // per-lane offset, the second copy 32 rows further through the scalar
     // offset)
+    // With MN-major scales (SM) copy q of wave w is instruction i = 2 (w%4) + q
+    // of its operand's stage half: K blocks 4i .. 4i+3 of the group, all 256
+    // rows, lane l the chunk of sf_mn_copy_block / sf_mn_copy_row (a per-lane
+    // offset; the instruction's K blocks through the scalar offset).
     uint32_t sf_voff_w = 0;
+    const uint32_t sf_pitch = SM ? uint32_t(wave < 4 ? M : N) : 0u;   // bytes per K block (SM)
     if constexpr (kWideStage) {
         static_assert(kSfInstr == 1, "one 64-row scale group per wave");
         static_assert(sf_slot_row(32 + 5) == 32 + sf_slot_row(5), "slot order keeps bit 5");
         const int slot = lane & 31;
-        sf_voff_w = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(slot) : slot)) * sf_row +
-                    16u * uint32_t(lane >> 5);
+        if constexpr (SM)
+            sf_voff_w = sf_mn_copy_block(0, lane) * sf_pitch + sf_mn_copy_row(lane);
+        else
+            sf_voff_w = uint32_t(64 * (wave & 3) + (kScaleGroups ? sf_slot_row(slot) : slot)) * sf_row +
+                        16u * uint32_t(lane >> 5);
     }
     // kPair with grouped scale copies: the E4M3 operand's rows in the slot
     // order of sf_slot_row, the E2M1 operand's in natural order
@@ -572,7 +595,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 buffer_load_lds16(sf_rsrc[0], sstage + 2048 * wave + 1024 * q, sf_voff_w,
-                                  32u * uint32_t(grp) + uint32_t(32 * q) * sf_row);
+                                  SM ? uint32_t(32 * grp + 4 * (2 * (wave & 3) + q)) * sf_pitch
+                                     : 32u * uint32_t(grp) + uint32_t(32 * q) * sf_row);
         }
     };
 
@@ -740,14 +764,20 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         static_assert(!kScaleGroups || (32 * TN) % 64 == 0, "wave rows start 64-row groups");
         // (wide stage: sf_wide_read with the step's half widx/4 and byte
         // 4 (widx%4) + block, split into lane, block and step parts)
-        const uint32_t sfa = opaque(WD ? sf_wide_read(wm, 0, 0, lane >> 4, lane)
-                                       : uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
-        const uint32_t sfb = opaque(WD ? sf_wide_read(kBM + wn, 0, 0, lane >> 4, lane)
-                                       : uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        // (MN-major scales: sf_mn_offset of K block 4 widx + l/16 and the
+        // lane's tile row, B's stage half 8 KiB further, split likewise)
+        constexpr bool MN = WD && SM;
+        const uint32_t sfa = opaque(MN   ? sf_mn_offset(uint32_t(lane >> 4), uint32_t(wm + row16<true>(0, r16)))
+                                    : WD ? sf_wide_read(wm, 0, 0, lane >> 4, lane)
+                                         : uint32_t(sf_stride * (wm + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
+        const uint32_t sfb = opaque(MN   ? kSfMnB + sf_mn_offset(uint32_t(lane >> 4), uint32_t(wn + row16<true>(0, r16)))
+                                    : WD ? sf_wide_read(kBM + wn, 0, 0, lane >> 4, lane)
+                                         : uint32_t(sf_stride * (kBM + wn + (kScaleGroups ? r16 : row16<true>(0, r16))) + (lane >> 4)));
         auto sf_off = [&](int b) {
-            return WD ? int(sf_wide_read(0, b, 0, 0, 0)) : sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1));
+            return MN   ? int(sf_mn_offset(0, uint32_t(row16<true>(b, 0))))
+                   : WD ? int(sf_wide_read(0, b, 0, 0, 0)) : sf_stride * (kScaleGroups ? 16 * b : 32 * (b >> 1) + 8 * (b & 1));
         };
-        const int sstep = WD ? int(sf_wide_offset(0, widx >> 2)) + 4 * (widx & 3) : 4 * widx;
+        const int sstep = MN ? int(sf_mn_offset(uint32_t(4 * widx), 0)) : WD ? int(sf_wide_offset(0, widx >> 2)) + 4 * (widx & 3) : 4 * widx;
         // E4M3: chunks c and c + 4.  Padded kinds: chunks c and c ^ 1, of
         // which the first twelve (6-bit) or eight (4-bit) bytes each form
         // registers 0..2 and 3..5 (0..1 and 2..3)
@@ -826,11 +856,18 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const uint32_t sb16 = kV16 ? uint32_t(2048 * (kb >> 1) + 2 * (kb & 1)) : uint32_t(kb);
         // (wide stage: rows in natural order, read as in compute_mx16 with
         // the step's half widx/2 and byte 8 (widx%2) + 4 ks + block)
-        const uint32_t sfa = opaque(WD ? sf_wide_read(wm, 0, 0, sb16, lane) : uint32_t(sf_stride * (wm + r16)) + sb16);
-        const uint32_t sfb = opaque(WD ? sf_wide_read(kBM + wn, 0, 0, sb16, lane)
-                                       : uint32_t(sf_stride * (kBM + wn + r16)) + sb16);
+        // (MN-major scales: sf_mn_offset of K block 4 (2 widx + ks) + kblk16
+        // and the lane's tile row)
+        constexpr bool MN = WD && SM;
+        const uint32_t sfa = opaque(MN   ? sf_mn_offset(uint32_t(kb), uint32_t(wm + r16))
+                                    : WD ? sf_wide_read(wm, 0, 0, sb16, lane) : uint32_t(sf_stride * (wm + r16)) + sb16);
+        const uint32_t sfb = opaque(MN   ? kSfMnB + sf_mn_offset(uint32_t(kb), uint32_t(wn + r16))
+                                    : WD ? sf_wide_read(kBM + wn, 0, 0, sb16, lane)
+                                         : uint32_t(sf_stride * (kBM + wn + r16)) + sb16);
         const uint32_t sf_blk = 16u * uint32_t(sf_stride);   // 16 rows further
-        auto blk_off = [&](int b) { return WD ? sf_wide_read(0, b, 0, 0, 0) : sf_blk * uint32_t(b); };
+        auto blk_off = [&](int b) {
+            return MN ? sf_mn_offset(0, uint32_t(16 * b)) : WD ? sf_wide_read(0, b, 0, 0, 0) : sf_blk * uint32_t(b);
+        };
         const u32x4 zero = {0, 0, 0, 0};
         // sub-step u: K elements 128 u' .. of the step (u' = ks), and with
         // 16-element blocks each chunk in two halves h
@@ -854,6 +891,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             constexpr int ks = kV16 ? u >> 1 : u, h = kV16 ? u & 1 : 0;
             // scale byte offset of the sub-step
             const int sw = kV16 ? 2048 * 2 * ks + h
+                           : MN ? int(sf_mn_offset(uint32_t(4 * (2 * widx + ks)), 0))
                            : WD ? int(sf_wide_offset(0, widx >> 1)) + 8 * (widx & 1) + 4 * ks
                                 : sf_stride == 16 ? 8 * widx + 4 * ks : 2048 * ks;
             uint32_t sa[TM16], sb[TN16];
@@ -1211,6 +1249,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends
             goto epilogue;
         }
+        if constexpr (SM)
+            goto epilogue;   // MN-major scales come with K a multiple of 2048 (checked by the host)
         if (KT % 4 == 0) {
             // Dense E2M1, four K steps per iteration: operand stages alternate
             // lds0 / lds1, scale groups (two steps each) scl0 / scl1.  A
@@ -1335,6 +1375,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends
             goto epilogue;
         }
+        if constexpr (SM)
+            goto epilogue;   // MN-major scales come with K a multiple of 2048 (checked by the host)
     }
     if constexpr (kScaleGroups) {
         if (KT % 8 == 0) {
@@ -1579,7 +1621,8 @@ epilogue:
 // 16x16 MFMAs for every operand kind, except 16-bit operands that are both
 // MN-major, which take 32x32x16 (their 16x16 fragment reads would need more
 // than 256 VGPRs).
-template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32, bool SB = false>
+template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32, bool SB = false,
+          bool SM = false>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     constexpr bool kMf16 = !(A_MN && B_MN);
@@ -1588,24 +1631,24 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV, SB>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV, SB, SM>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV, SB>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV, SB, SM>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
 }
 
 // D's element kind chosen at run time
-template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32, bool SB = false>
+template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32, bool SB = false, bool SM = false>
 hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 {
     switch (a.out) {
-    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV, SB>(a, stream);
-    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV, SB>(a, stream);
-    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV, SB>(a, stream);
+    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV, SB, SM>(a, stream);
+    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV, SB, SM>(a, stream);
+    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV, SB, SM>(a, stream);
     }
 }
 

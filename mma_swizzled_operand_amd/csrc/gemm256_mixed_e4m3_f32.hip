@@ -8,12 +8,25 @@
 
 namespace mswz {
 
+namespace {
+
+// scales row-major or MN-major (sf_mn)
+template <int KB>
+hipError_t launch_b(const MxArgs &a, hipStream_t stream)
+{
+    if (a.sf_mn)
+        return launch_kind<kE4m3, false, false, kOutF32, KB, 32, false, true>(a, stream);
+    return launch_kind<kE4m3, false, false, kOutF32, KB>(a, stream);
+}
+
+}  // namespace
+
 hipError_t launch256_mixed_e4m3_f32(const MxArgs &a, MxKind kb, hipStream_t stream)
 {
     switch (kb) {
-    case kMxE2m3: return launch_kind<kE4m3, false, false, kOutF32, kE2m3>(a, stream);
-    case kMxE3m2: return launch_kind<kE4m3, false, false, kOutF32, kE3m2>(a, stream);
-    case kMxE2m1p: return launch_kind<kE4m3, false, false, kOutF32, kE2m1p>(a, stream);
+    case kMxE2m3: return launch_b<kE2m3>(a, stream);
+    case kMxE3m2: return launch_b<kE3m2>(a, stream);
+    case kMxE2m1p: return launch_b<kE2m1p>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -60,6 +60,7 @@ struct MxArgs {
     int lda = 0, ldb = 0, ldd = 0;   // as in DenseArgs (scale arrays are packed)
     EpiOpts opts = {};
     int sv = 32;                     // K elements per scale byte (32, or 16)
+    int sf_mn = 0;                   // scales stored [K/sv][M] and [K/sv][N] (wide-stage kernels only)
 };
 
 struct VariantInfo {

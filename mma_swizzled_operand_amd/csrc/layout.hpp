@@ -212,6 +212,49 @@ static_assert(sf_wide_read(96, 5, 1, 7, 13) ==
                   sf_wide_read(96, 0, 0, 0, 13) + sf_wide_read(0, 5, 0, 0, 0) + sf_wide_offset(0, 1) + 7,
               "wide scale reads split into lane, block and half parts");
 
+// Scale stage for scales stored MN-major, [K block][row] (the pages'
+// canonical SFA / SFB order, tcgen05.mma page, "Operands and repeat axes":
+// the K-repeat axis outside the rows): per operand 32 K blocks (eight E4M3 /
+// padded K steps, four E2M1 steps) of 256 rows, 8 KiB.  A 16-byte chunk holds
+// the scales of 16 consecutive rows for one K block; K block g, rows
+// 16r .. 16r+15 sit at chunk 64 (g/4) + 4r + g%4, so the chunks of four
+// consecutive K blocks and one 16-row run are consecutive.  One 16-byte copy
+// instruction (sf_mn_copy_block, sf_mn_copy_row) fetches four K blocks of all
+// 256 rows, i.e. four 256-byte runs of memory (8 cache lines, against 32 for
+// the row-major wide stage), and writes 1 KiB of consecutive LDS.  A byte read
+// for four K blocks of 16 rows lands in distinct bank groups (the K block
+// picks the chunk's position among four, and a split 16-row block's two runs
+// are four chunks apart), so it is free of conflicts under the byte model.
+MSWZ_HD constexpr uint32_t sf_mn_offset(uint32_t g, uint32_t row)
+{
+    return (g >> 2) * 1024u + (row >> 4) * 64u + (g & 3u) * 16u + (row & 15u);
+}
+// lane l of copy instruction i (K blocks 4i .. 4i+3 of the stage): K block
+// and first row of its 16-byte chunk
+MSWZ_HD constexpr uint32_t sf_mn_copy_block(int i, int l) { return 4u * uint32_t(i) + uint32_t(l & 3); }
+MSWZ_HD constexpr uint32_t sf_mn_copy_row(int l) { return 16u * uint32_t(l >> 2); }
+static_assert(sf_mn_offset(sf_mn_copy_block(5, 39), sf_mn_copy_row(39)) == 1024u * 5 + 16u * 39,
+              "copy lane l of instruction i writes LDS bytes 1024 i + 16 l");
+// The reads add a per-lane part (K block within the group of four, first row
+// of the lane), a per-fragment-block part and a per-step part: no carries
+// between them for the fragments' rows (row16) and steps.
+template <bool MX>
+MSWZ_HD constexpr bool sf_mn_reads_split()
+{
+    for (uint32_t wm = 0; wm < 256; wm += 64)
+        for (int b = 0; b < (MX ? 8 : 4); ++b)
+            for (int x = 0; x < 16; ++x)
+                for (uint32_t q = 0; q < 4; ++q)
+                    for (uint32_t t = 0; t < 8; ++t)
+                        if (sf_mn_offset(4 * t + q, wm + uint32_t(row16<MX>(b, x))) !=
+                            sf_mn_offset(q, wm + uint32_t(row16<MX>(0, x))) + sf_mn_offset(0, uint32_t(row16<MX>(b, 0))) +
+                                sf_mn_offset(4 * t, 0))
+                            return false;
+    return true;
+}
+static_assert(sf_mn_reads_split<true>() && sf_mn_reads_split<false>(),
+              "MN-major scale reads split into lane, block and step parts");
+
 // LDS byte offset, at sub-step 0 and first half, of this lane's piece of the
 // 32-row 32x32x16 MFMA fragment whose tile rows start at rbase (a multiple of
 // 32) in an MN-major tile, read with ds_read_b64_tr_b16.  The operand wants,

@@ -200,6 +200,70 @@ def test_tile_choice():
     assert mswz.gemm_plan_create(16, 2048, 1024, "bf16", "bf16", "bf16").describe()["variant"] != 21
 
 
+def test_scale_major_switches_plans_of_the_wide_stage_kernels():
+    """MN-major scales ([K/V][M], [K/V][N]): the 256x256 tile with the 32-byte
+    scale stages (LDS 2 x 64 + 2 x 16 KiB); back to row-major restores the
+    variant chosen at creation."""
+    wide_lds = 2 * 512 * 128 + 2 * 512 * 32
+    for a, b, d, K in (("e4m3", "e4m3", "f32", 8192), ("e4m3", "e2m3", "f32", 2048), ("e4m3", "e2m1p", "f32", 4096),
+                       ("e2m3", "e2m3", "bf16", 2048), ("e3m2", "e3m2", "f16", 6144), ("e2m1p", "e2m1p", "f32", 2048),
+                       ("e2m1", "e2m1", "f32", 8192), ("e2m1", "e2m1", "bf16", 2048)):
+        p = mswz.gemm_plan_create(4096, 1040, K, a, b, d, scale_vec_len=32)
+        before = p.describe()
+        mswz.gemm_plan_set_scale_major(p, "mn")
+        after = p.describe()
+        assert p.sf_major == "mn"
+        assert (after["tile_m"], after["tile_n"], after["lds_bytes"]) == (256, 256, wide_lds), (a, b, d, after)
+        assert after["blocks"] == 16 * 5
+        mswz.gemm_plan_set_scale_major(p, "k")
+        assert p.describe() == before and p.sf_major == "k"
+    # a grid the creation gives the 128 tile: MN-major scales take the 256 one
+    p = mswz.gemm_plan_create(2048, 2048, 2048, "e4m3", "e4m3", scale_vec_len=32)
+    assert p.describe()["tile_m"] == 128
+    mswz.gemm_plan_set_scale_major(p, "mn")
+    assert (p.describe()["tile_m"], p.describe()["blocks"], p.describe()["lds_bytes"]) == (256, 64, wide_lds)
+    mswz.gemm_plan_set_scale_major(p, "k")
+    assert p.describe()["tile_m"] == 128
+
+
+@pytest.mark.parametrize("args, expect", [
+    ((4096, 4096, 3072, "e4m3", "e4m3", "f32", 32), -2),      # K not a multiple of 2048
+    ((4096, 4096, 2048 + 128, "e2m3", "e2m3", "f32", 32), -2),
+    ((4104, 4096, 2048, "e4m3", "e4m3", "f32", 32), -2),      # M not a multiple of 16
+    ((4096, 4100, 2048, "e2m1", "e2m1", "f32", 32), -2),      # N not a multiple of 16
+    ((4096, 4096, 2048, "e4m3", "e4m3", "bf16", 32), -2),     # E4M3 A with a narrow D
+    ((4096, 4096, 2048, "e4m3", "e2m3", "f16", 32), -2),
+    ((4096, 4096, 2048, "e2m3", "e4m3", "f32", 32), -2),      # mixed kinds with a padded A
+    ((4096, 4096, 2048, "e2m3", "e3m2", "f32", 32), -2),
+    ((4096, 4096, 2048, "e4m3", "e2m1", "f32", 32), -2),      # E4M3 with dense E2M1
+    ((4096, 4096, 2048, "e2m1", "e2m1", "f32", 16), -2),      # 16-element blocks
+    ((4096, 4096, 2048, "e2m3", "e2m3", "f32", 16), -2),
+    ((4096, 4096, 2048, "bf16", "bf16", "f32", 0), -5),       # dense plan
+])
+def test_scale_major_rejections_leave_the_plan_unchanged(args, expect):
+    M, N, K, a, b, d, v = args
+    p = mswz.gemm_plan_create(M, N, K, a, b, d, scale_vec_len=v)
+    before = p.describe()
+    lib = mswz.load()
+    assert lib.gemm_plan_set_scale_major(p.handle, 1) == expect
+    assert p.describe() == before
+    if expect == -2:
+        assert lib.gemm_plan_set_scale_major(p.handle, 0) == 0      # row-major stays available
+
+
+def test_scale_major_argument_checks():
+    lib = mswz.load()
+    p = mswz.gemm_plan_create(4096, 4096, 2048, "e4m3", "e4m3", scale_vec_len=32)
+    assert lib.gemm_plan_set_scale_major(None, 1) == -1
+    assert lib.gemm_plan_set_scale_major(p.handle, 2) == -1
+    assert lib.gemm_plan_set_scale_major(p.handle, -1) == -1
+    # 32-bit offsets into [K/V][M]: K/V * M below 2^32
+    big = mswz.gemm_plan_create(1 << 20, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
+    assert lib.gemm_plan_set_scale_major(big.handle, 1) == -2
+    ok = mswz.gemm_plan_create((1 << 20) - 16, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
+    assert lib.gemm_plan_set_scale_major(ok.handle, 1) == 0
+
+
 # ---- run-time rejections (fake pointers: never dereferenced) -------------------
 
 def test_run_rejections_before_gpu_work():

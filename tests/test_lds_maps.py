@@ -342,6 +342,71 @@ def test_wide_scale_reads_conflict_two_ways_under_the_byte_model():
             assert conflicts(mswz.lds_lanes("scale_fp4_wide", b, st), 1, PASSES_1) == 2
 
 
+def _mn_holder():
+    """Stage byte -> (operand row, K block of the 32-block group) after the
+    MN-major scale copies of one group (scales stored [K block][row]): copy q
+    of wave w writes 1 KiB; lane l's 16 bytes are one K block's scales of 16
+    consecutive rows."""
+    holder = {}
+    for w in range(8):
+        for q in range(2):
+            dst, src = pairs("scale_dma_mn", w, q)
+            assert dst == [2048 * w + 1024 * q + 16 * l for l in range(64)]   # 1 KiB contiguous
+            blocks = {}
+            for r in src:
+                blocks.setdefault(r // 256, set()).add(r % 256)
+            # four K blocks, each all 256 rows: four 256-byte runs of memory
+            assert len(blocks) == 4 and all(v == set(range(0, 256, 16)) for v in blocks.values())
+            for d, r in zip(dst, src):
+                for byte in range(16):
+                    holder[d + byte] = (r % 256 + byte + (256 if w >= 4 else 0), r // 256)
+    assert sorted(holder) == list(range(512 * 32))
+    assert sorted(set(holder.values())) == [(row, g) for row in range(512) for g in range(32)]
+    return holder
+
+
+def test_mn_scale_copies_put_each_fragment_rows_scales_where_they_are_read():
+    """MN-major scales, E4M3 and padded kinds (split-row fragments): the byte
+    lane (x, g) of fragment block b reads at step s of its group of eight is
+    K block 4 s + g of that fragment row."""
+    holder = _mn_holder()
+    for b in range(8):
+        for st in range(8):
+            for l, a in enumerate(mswz.lds_lanes("scale_grp_mn", b, st)):
+                x, g = l & 15, l >> 4
+                assert holder[a] == (32 * (b >> 1) + 8 * (b & 1) + (x & 7) + 16 * (x >> 3), 4 * st + g)
+
+
+def test_mn_fp4_scale_copies_put_each_fragment_rows_scales_where_they_are_read():
+    """MN-major scales, dense E2M1 (rows in order): lane (x, g) of block b at
+    step s of its group of four, sub-step u, reads K block 8 s + 4 u +
+    kblk16(g) of row 16 b + x."""
+    holder = _mn_holder()
+    for b in range(8):
+        for st in range(4):
+            for u in range(2):
+                for l, a in enumerate(mswz.lds_lanes("scale_fp4_mn", b, 2 * st + u)):
+                    x, g = l & 15, l >> 4
+                    assert holder[a] == (16 * b + x, 8 * st + 4 * u + kblk(g))
+
+
+def test_mn_scale_reads_are_conflict_free_under_the_byte_model():
+    """The four K blocks of one read sit in four consecutive chunks (and a
+    split block's second run four chunks further), so the 64 byte reads
+    touch distinct banks or share a word."""
+    for b in range(8):
+        for st in range(8):
+            assert conflicts(mswz.lds_lanes("scale_grp_mn", b, st), 1, PASSES_1) == 1
+            assert conflicts(mswz.lds_lanes("scale_fp4_mn", b, st), 1, PASSES_1) == 1
+
+
+def test_mn_scale_patterns_reject_out_of_range_arguments():
+    for pat, p0, p1 in (("scale_dma_mn", 8, 0), ("scale_dma_mn", 0, 2), ("scale_grp_mn", 8, 0),
+                        ("scale_grp_mn", 0, 8), ("scale_fp4_mn", -1, 0)):
+        with pytest.raises(mswz.MswzError):
+            mswz.lds_lanes(pat, p0, p1)
+
+
 # ---- staged epilogue -------------------------------------------------------------------
 
 @pytest.mark.parametrize("rows", [0, 1, 2, 3])

@@ -20,6 +20,9 @@ saturating at 7.5 and 28, then packed sixteen per 16-byte block in bits
 bytes zero; "e2m1p" rounds like e2m1 and stores sixteen per 16-byte block,
 eight bytes of nibbles then eight zero bytes);
 e8m0 scale bytes are 127 + u with u a uniform integer in [-4, 4].
+SFA and SFB are generated [M,K/32] and [N,K/32] for every config; a config
+with sf_major "mn" hands the library their transposes, [K/32,M] and
+[K/32,N] (the same values).
 The quarter-integer variant (the tcgen05.mma page's example test draws
 integers in [-4, 4] divided by 4) replaces every operand value, keeps D0's
 recipe and sets every scale byte to 127, so every product and partial sum is
@@ -58,6 +61,7 @@ class Workload:
     b_dist: tuple = ("uniform", 1.0)
     tags: tuple = field(default=())
     b_kind: str = ""          # B's element kind when it differs from A's
+    sf_major: str = "k"       # scales handed to the library [M,K/32] ("k") or [K/32,M] ("mn")
 
     @property
     def kind_b(self) -> str:
@@ -112,6 +116,8 @@ WORKLOADS = {
                     b_dist=("normal", 1.0)),
     "c13": Workload("c13", "MX mixed 8192^3: A e4m3, B e2m1 dense (two per byte), K-major, N(0,1) rounded to each format, one e8m0 scale 2^u (u in [-4,4]) per 32 K per row",
                     8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), b_kind="e2m1"),
+    "c14": Workload("c14", "MX-fp8 8192^3 e4m3 K-major as c5, scales stored MN-major ([K/32,M] and [K/32,N])",
+                    8192, 8192, 8192, "e4m3", V=32, a_dist=("normal", 1.0), b_dist=("normal", 1.0), sf_major="mn"),
 }
 
 
