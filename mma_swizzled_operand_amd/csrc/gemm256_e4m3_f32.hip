@@ -12,6 +12,8 @@ hipError_t launch256_e4m3_f32(const MxArgs &a, hipStream_t stream)
 {
     if (a.sf_mn)
         return launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, true>(a, stream);
+    if (a.K % 2048 == 0)   // the wide loop alone (8192^3 MX-fp8 -1.9 %)
+        return launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, false, true>(a, stream);
     return launch_kind<kE4m3, false, false, kOutF32>(a, stream);
 }
 

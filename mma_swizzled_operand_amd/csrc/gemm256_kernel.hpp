@@ -344,9 +344,10 @@ constexpr int W = 8;
 // SB: block-scaled K that is not a multiple of the K step (scale bytes
 // assembled in registers, see below); SM: scales stored MN-major,
 // SFA [K/SV][M] and SFB [K/SV][N] (the wide scale stage only, K a multiple of
-// 2048, M and N multiples of 16).
+// 2048, M and N multiples of 16); WO: K a multiple of 2048, only the wide
+// loop compiled (implied by SM).
 template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32,
-          bool SB = false, bool SM = false>
+          bool SB = false, bool SM = false, bool WO = false>
 __global__ void __launch_bounds__(64 * W)
 gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                const uint8_t *__restrict__ SFA, const uint8_t *__restrict__ SFB,
@@ -400,6 +401,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr bool kWideStage =
         ((kByteRows && (!kMixed || KIND == kE4m3) && (KIND != kE4m3 || OUT == kOutF32)) || kFp4) && !kV16 && !SB;
     static_assert(!SM || kWideStage, "MN-major scales: the wide scale stage");
+    // only the 32-K-block loop (K % 2048 == 0, checked by the host): without
+    // the fallback loops the kernels keep more registers for the K loop
+    constexpr bool kWideOnly = SM || WO;
+    static_assert(!kWideOnly || kWideStage, "wide-only kernels: the wide scale stage");
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
@@ -802,10 +807,10 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // MFMA ahead: that frees the registers the epilogue needs (with two,
         // the compiler spilled inside the loop); the loop alone is 1.4 %
         // slower, the kernel with the staged epilogue 4 % faster (8192^3
-        // MX-fp8).  With MN-major scales (SM) the kernels skip the fallback
-        // loops and have the registers for two (8192^3: E4M3 -1.7 %, E4M3
-        // with padded E2M1 -2.2 %, with E2M3 level).
-        constexpr int kAhead = kStagedEpi && (KIND == kE4m3 || kKindB == kE4m3) && !SM ? 1 : 2;
+        // MX-fp8).  Without the fallback loops (kWideOnly) the kernels have
+        // the registers for two (8192^3 with MN-major scales: E4M3 -1.7 %,
+        // E4M3 with padded E2M1 -2.2 %, with E2M3 level).
+        constexpr int kAhead = kStagedEpi && (KIND == kE4m3 || kKindB == kE4m3) && !kWideOnly ? 1 : 2;
         using Sched = FragSchedule<TM16, TN16, kAhead>;
         uint32_t sa[TM16], sb[TN16];
         i32x8 bf[TN16], af[TM16];
@@ -1251,8 +1256,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends
             goto epilogue;
         }
-        if constexpr (SM)
-            goto epilogue;   // MN-major scales come with K a multiple of 2048 (checked by the host)
+        if constexpr (kWideOnly)
+            goto epilogue;   // K is a multiple of 2048 (checked by the host)
         if (KT % 4 == 0) {
             // Dense E2M1, four K steps per iteration: operand stages alternate
             // lds0 / lds1, scale groups (two steps each) scl0 / scl1.  A
@@ -1377,8 +1382,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             __syncthreads();   // no copy may still be writing LDS when the workgroup ends
             goto epilogue;
         }
-        if constexpr (SM)
-            goto epilogue;   // MN-major scales come with K a multiple of 2048 (checked by the host)
+        if constexpr (kWideOnly)
+            goto epilogue;   // K is a multiple of 2048 (checked by the host)
     }
     if constexpr (kScaleGroups) {
         if (KT % 8 == 0) {
@@ -1624,7 +1629,7 @@ epilogue:
 // MN-major, which take 32x32x16 (their 16x16 fragment reads would need more
 // than 256 VGPRs).
 template <int KIND, bool A_MN, bool B_MN, int OUT = kOutF32, int KB = -1, int SV = 32, bool SB = false,
-          bool SM = false>
+          bool SM = false, bool WO = false>
 hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 {
     constexpr bool kMf16 = !(A_MN && B_MN);
@@ -1633,11 +1638,11 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
     const uint8_t *A = static_cast<const uint8_t *>(a.A);
     const uint8_t *B = static_cast<const uint8_t *>(a.B);
     if (a.beta)
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV, SB, SM>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, true, kMf16, OUT, KB, SV, SB, SM, WO>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     else
-        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV, SB, SM>), dim3(blocks), dim3(64 * W),
+        hipLaunchKernelGGL((gemm256_kernel<KIND, A_MN, B_MN, false, kMf16, OUT, KB, SV, SB, SM, WO>), dim3(blocks), dim3(64 * W),
                            0, stream, A, B, a.SFA, a.SFB, a.D, a.M, a.N, a.K, a.lda, a.ldb, a.ldd, tiles_m,
                            tiles_n, a.group_m, a.opts);
     return hipGetLastError();
