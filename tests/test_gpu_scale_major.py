@@ -154,3 +154,24 @@ def test_mn_scales_full_size_mx_fp8():
     rows, cols = wl.sample_points(w, 8, 8)
     print(compare(w, got[rows], reference(w, x, rows=rows)), compare(w, got[:, cols], reference(w, x, cols=cols)))
     assert np.array_equal(got, run_gpu(w, x, row_major_plan(w)))
+
+
+@pytest.mark.parametrize("name", ["e4m3-1040x528-k2048", "e4m3xe2m3-528x1040-k2048-beta", "e2m1-304x528-k4096-beta"])
+def test_mn_scales_with_call_options_match_row_major_scales(name):
+    """gemm_run_opts (negated A, saturated D, a row mask and a zero-column
+    mask) on an MN-major-scale plan stores the same bits as on the row-major
+    plan, whose options tests/test_gpu_opts.py checks against the oracle."""
+    w = CASES[name]
+    say(f"[sf-mn-opts] {name}")
+    x = wl.generate(w, seed=45)
+    rng = np.random.default_rng(46)
+    row_mask = to_device(rng.integers(0, 2**31, (w.M + 31) // 32, dtype=np.int64).astype(np.int32))
+    col_zero = to_device(rng.integers(0, 2**31, (w.N + 31) // 32, dtype=np.int64).astype(np.int32))
+    outs = []
+    for plan, xs in ((row_major_plan(w), x), (mn_plan(w), mn_scales(x))):
+        D = to_device(x["D0"]) if w.beta else torch.full((w.M, w.N), 7.0, dtype=torch.float32, device="cuda")
+        mswz.gemm_run_opts(plan, to_device(xs["A"]), to_device(xs["B"]), D, w.beta, SFA=to_device(xs["SFA"]),
+                           SFB=to_device(xs["SFB"]), neg_a=True, sat_d=True, row_mask=row_mask, col_zero=col_zero)
+        torch.cuda.synchronize()
+        outs.append(D.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
