@@ -280,13 +280,14 @@ int gemm_plan_set_scale_major(gemm_plan *p, int sf_major)
         return MSWZ_ERR_KIND;
     int variant = p->variant_k;
     if (sf_major == MSWZ_MAJOR_MN) {
-        // the wide scale stage with its 32-K-block loop (K % 2048), whole
-        // 16-byte chunks of 16 rows (M, N % 16), and 32-bit offsets into
-        // the [K/V][M] and [K/V][N] arrays
+        // the kinds with the wide scale stage (K a multiple of the K step),
+        // whole 16-byte chunks of 16 rows (M, N % 16), and the [K/V][M] and
+        // [K/V][N] arrays below 2^31 bytes (32-bit offsets; the kernels'
+        // unused copies point at 2^31, outside every array's range)
         const int64_t kb = p->K / p->scale_vec_len;
-        if (!wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) || p->K % 2048 != 0 ||
-            p->M % 16 != 0 || p->N % 16 != 0 || kb * p->M >= (int64_t(1) << 32) ||
-            kb * p->N >= (int64_t(1) << 32))
+        if (!wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) ||
+            p->M % 16 != 0 || p->N % 16 != 0 || kb * p->M > (int64_t(1) << 31) ||
+            kb * p->N > (int64_t(1) << 31))
             return MSWZ_ERR_UNSUPPORTED;
         variant = mswz::kVarMx256;
     }

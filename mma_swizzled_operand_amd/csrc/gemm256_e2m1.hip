@@ -6,8 +6,9 @@ namespace mswz {
 
 hipError_t launch256_e2m1(const MxArgs &a, hipStream_t stream)
 {
-    if (a.sf_mn)   // MN-major scales: K a multiple of 2048 (no K tail)
-        return launch_out<kE2m1, false, false, -1, 32, false, true>(a, stream);
+    if (a.sf_mn)   // MN-major scales (K a multiple of the step): the wide loop alone, or the per-step loop
+        return a.K % 2048 == 0 ? launch_out<kE2m1, false, false, -1, 32, false, true, true>(a, stream)
+                               : launch_out<kE2m1, false, false, -1, 32, false, true, false>(a, stream);
     return launch_cfg<kE2m1, false, false>(a, stream);
 }
 

@@ -10,8 +10,9 @@ namespace mswz {
 
 hipError_t launch256_e4m3_f32(const MxArgs &a, hipStream_t stream)
 {
-    if (a.sf_mn)
-        return launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, true>(a, stream);
+    if (a.sf_mn)   // MN-major scales: the wide loop alone, or the per-step loop alone
+        return a.K % 2048 == 0 ? launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, true, true>(a, stream)
+                               : launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, true, false>(a, stream);
     if (a.K % 2048 == 0)   // the wide loop alone (8192^3 MX-fp8 -1.9 %)
         return launch_kind<kE4m3, false, false, kOutF32, -1, 32, false, false, true>(a, stream);
     return launch_kind<kE4m3, false, false, kOutF32>(a, stream);

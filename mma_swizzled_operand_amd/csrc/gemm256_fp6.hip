@@ -11,8 +11,9 @@ namespace {
 template <int K>
 hipError_t launch_padded(const MxArgs &a, hipStream_t stream)
 {
-    if (a.sf_mn)   // MN-major scales: K a multiple of 2048 (no K tail)
-        return launch_out<K, false, false, -1, 32, false, true>(a, stream);
+    if (a.sf_mn)   // MN-major scales (K a multiple of the step): the wide loop alone, or the per-step loop
+        return a.K % 2048 == 0 ? launch_out<K, false, false, -1, 32, false, true, true>(a, stream)
+                               : launch_out<K, false, false, -1, 32, false, true, false>(a, stream);
     return launch_cfg<K, false, false>(a, stream);
 }
 

@@ -343,9 +343,9 @@ constexpr int W = 8;
 // 16x16 MFMAs (every kind), else 32x32x16 (16-bit operands, both MN-major);
 // SB: block-scaled K that is not a multiple of the K step (scale bytes
 // assembled in registers, see below); SM: scales stored MN-major,
-// SFA [K/SV][M] and SFB [K/SV][N] (the wide scale stage only, K a multiple of
-// 2048, M and N multiples of 16); WO: K a multiple of 2048, only the wide
-// loop compiled (implied by SM).
+// SFA [K/SV][M] and SFB [K/SV][N] (the wide-stage kinds, K a multiple of the
+// K step, M and N multiples of 16); WO: K a multiple of 2048, only the wide
+// loop compiled (with SM and not WO: only the per-step loop).
 template <int KIND, bool A_MN, bool B_MN, bool BETA, bool MF16, int OUT = kOutF32, int KB = -1, int SV = 32,
           bool SB = false, bool SM = false, bool WO = false>
 __global__ void __launch_bounds__(64 * W)
@@ -403,8 +403,12 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     static_assert(!SM || kWideStage, "MN-major scales: the wide scale stage");
     // only the 32-K-block loop (K % 2048 == 0, checked by the host): without
     // the fallback loops the kernels keep more registers for the K loop
-    constexpr bool kWideOnly = SM || WO;
+    constexpr bool kWideOnly = WO;
     static_assert(!kWideOnly || kWideStage, "wide-only kernels: the wide scale stage");
+    // MN-major scales for other K: the per-step loop alone, each step's
+    // scales of 256 rows copied as one (E2M1: two) 1 KiB instruction per
+    // operand into the wide stage's first K blocks
+    constexpr bool kMnStep = SM && !WO;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
@@ -561,6 +565,12 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         }
     };
 
+    // per-step MN-major scale copies (kMnStep): kMnInstr 1 KiB instructions
+    // per operand and step, issued by waves 0.. and 4..; the others' offset
+    // lies beyond the buffer range (below 2^31 bytes, checked by the host)
+    constexpr int kMnInstr = kFp4 ? 2 : 1, kMnBlocks = 4 * kMnInstr;
+    const bool mn_active = (wave & 3) < kMnInstr;
+    const uint32_t sf_voff_step = mn_active ? sf_voff_w : 0x80000000u;
     auto issue_step = [&](uint8_t *stage, uint8_t *sstage, int kt) {
         if constexpr (kDmaA)
             da.issue(stage, kt);
@@ -572,6 +582,15 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             db.issue(stage, kt);
         if constexpr (SB) {
             load_scale_bytes(kt);
+        } else if constexpr (kMnStep) {
+            // instruction i = wave % 4 of the operand's step: K blocks
+            // kMnBlocks kt + 4i .. +3 of all 256 rows (sf_mn_offset); the
+            // other waves issue theirs out of the buffer's range (no memory
+            // access) into stage bytes that no read touches, so that every
+            // wave runs the same code (a branch here split the loop's
+            // schedule and spilled 115-135 registers)
+            buffer_load_lds16(sf_rsrc[0], sstage + (wave >> 2) * kSfMnB + 1024 * (wave & 3), sf_voff_step,
+                              mn_active ? uint32_t(kMnBlocks * kt + 4 * (wave & 3)) * sf_pitch : 0u);
         } else if constexpr (kMx) {
 #pragma unroll
             for (int q = 0; q < kSfInstr; ++q)
@@ -1059,7 +1078,11 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     };
 
     auto compute = [&](const uint8_t *s, const uint8_t *ss) {
-        if constexpr (kFp4)
+        if constexpr (kMnStep && kFp4)
+            compute_fp4(s, ss, 16, 0, std::true_type{});     // MN-major stage, first K blocks
+        else if constexpr (kMnStep)
+            compute_mx16(s, ss, 16, 0, std::true_type{});
+        else if constexpr (kFp4)
             compute_fp4(s, ss, 4, 0, std::false_type{});
         else if constexpr (kFp6 && kV16)
             compute_pad16(s, ss);
@@ -1199,7 +1222,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         __syncthreads();   // no copy may still be writing LDS when the workgroup ends
         goto epilogue;
     }
-    if constexpr (kFp4Groups) {
+    if constexpr (kFp4Groups && !kMnStep) {
         if (KT % 8 == 0) {
             // Dense E2M1, K a multiple of 2048: eight K steps per iteration,
             // wide scale groups of four steps (scl0 for the first four, scl1
@@ -1302,7 +1325,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             goto epilogue;
         }
     }
-    if constexpr (kScaleGroups && kWideStage) {
+    if constexpr (kScaleGroups && kWideStage && !kMnStep) {
         if (KT % 16 == 0) {
             // K a multiple of 2048: sixteen K steps per iteration, wide scale
             // groups of eight steps (scl0 for the first eight, scl1 for the
@@ -1385,7 +1408,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         if constexpr (kWideOnly)
             goto epilogue;   // K is a multiple of 2048 (checked by the host)
     }
-    if constexpr (kScaleGroups) {
+    if constexpr (kScaleGroups && !kMnStep) {
         if (KT % 8 == 0) {
             // Eight K steps per iteration: operand stages alternate lds0 /
             // lds1, scale groups alternate scl0 / scl1 every four steps.  A
@@ -1649,13 +1672,14 @@ hipError_t launch_kind(const MxArgs &a, hipStream_t stream)
 }
 
 // D's element kind chosen at run time
-template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32, bool SB = false, bool SM = false>
+template <int KIND, bool A_MN, bool B_MN, int KB = -1, int SV = 32, bool SB = false, bool SM = false,
+          bool WO = false>
 hipError_t launch_out(const MxArgs &a, hipStream_t stream)
 {
     switch (a.out) {
-    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV, SB, SM>(a, stream);
-    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV, SB, SM>(a, stream);
-    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV, SB, SM>(a, stream);
+    case kOutBf16: return launch_kind<KIND, A_MN, B_MN, kOutBf16, KB, SV, SB, SM, WO>(a, stream);
+    case kOutF16: return launch_kind<KIND, A_MN, B_MN, kOutF16, KB, SV, SB, SM, WO>(a, stream);
+    default: return launch_kind<KIND, A_MN, B_MN, kOutF32, KB, SV, SB, SM, WO>(a, stream);
     }
 }
 

@@ -15,8 +15,9 @@ namespace {
 template <int KB>
 hipError_t launch_b(const MxArgs &a, hipStream_t stream)
 {
-    if (a.sf_mn)
-        return launch_kind<kE4m3, false, false, kOutF32, KB, 32, false, true>(a, stream);
+    if (a.sf_mn)   // MN-major scales: the wide loop alone, or the per-step loop alone
+        return a.K % 2048 == 0 ? launch_kind<kE4m3, false, false, kOutF32, KB, 32, false, true, true>(a, stream)
+                               : launch_kind<kE4m3, false, false, kOutF32, KB, 32, false, true, false>(a, stream);
     if constexpr (KB == kE2m1p) {
         if (a.K % 2048 == 0)   // the wide loop alone (8192^3 -3.2 %; with a 6-bit B 0.6 % slower)
             return launch_kind<kE4m3, false, false, kOutF32, KB, 32, false, false, true>(a, stream);

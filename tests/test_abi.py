@@ -207,7 +207,8 @@ def test_scale_major_switches_plans_of_the_wide_stage_kernels():
     wide_lds = 2 * 512 * 128 + 2 * 512 * 32
     for a, b, d, K in (("e4m3", "e4m3", "f32", 8192), ("e4m3", "e2m3", "f32", 2048), ("e4m3", "e2m1p", "f32", 4096),
                        ("e2m3", "e2m3", "bf16", 2048), ("e3m2", "e3m2", "f16", 6144), ("e2m1p", "e2m1p", "f32", 2048),
-                       ("e2m1", "e2m1", "f32", 8192), ("e2m1", "e2m1", "bf16", 2048)):
+                       ("e2m1", "e2m1", "f32", 8192), ("e2m1", "e2m1", "bf16", 2048), ("e4m3", "e4m3", "f32", 3072),
+                       ("e4m3", "e3m2", "f32", 128), ("e2m3", "e2m3", "f32", 1152), ("e2m1", "e2m1", "f16", 768)):
         p = mswz.gemm_plan_create(4096, 1040, K, a, b, d, scale_vec_len=32)
         before = p.describe()
         mswz.gemm_plan_set_scale_major(p, "mn")
@@ -227,8 +228,9 @@ def test_scale_major_switches_plans_of_the_wide_stage_kernels():
 
 
 @pytest.mark.parametrize("args, expect", [
-    ((4096, 4096, 3072, "e4m3", "e4m3", "f32", 32), -2),      # K not a multiple of 2048
-    ((4096, 4096, 2048 + 128, "e2m3", "e2m3", "f32", 32), -2),
+    ((4096, 4096, 3104, "e4m3", "e4m3", "f32", 32), -2),      # K not a multiple of the K step
+    ((4096, 4096, 2048 + 32, "e2m3", "e2m3", "f32", 32), -2),
+    ((4096, 4096, 2048 + 128, "e2m1", "e2m1", "f32", 32), -2),
     ((4104, 4096, 2048, "e4m3", "e4m3", "f32", 32), -2),      # M not a multiple of 16
     ((4096, 4100, 2048, "e2m1", "e2m1", "f32", 32), -2),      # N not a multiple of 16
     ((4096, 4096, 2048, "e4m3", "e4m3", "bf16", 32), -2),     # E4M3 A with a narrow D
@@ -257,11 +259,13 @@ def test_scale_major_argument_checks():
     assert lib.gemm_plan_set_scale_major(None, 1) == -1
     assert lib.gemm_plan_set_scale_major(p.handle, 2) == -1
     assert lib.gemm_plan_set_scale_major(p.handle, -1) == -1
-    # 32-bit offsets into [K/V][M]: K/V * M below 2^32
-    big = mswz.gemm_plan_create(1 << 20, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
+    # scale arrays of at most 2^31 bytes: K/V * M <= 2^31
+    big = mswz.gemm_plan_create((1 << 19) + 16, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
     assert lib.gemm_plan_set_scale_major(big.handle, 1) == -2
-    ok = mswz.gemm_plan_create((1 << 20) - 16, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
+    ok = mswz.gemm_plan_create(1 << 19, 256, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
     assert lib.gemm_plan_set_scale_major(ok.handle, 1) == 0
+    wide_n = mswz.gemm_plan_create(256, (1 << 19) + 16, 1 << 17, "e2m1", "e2m1", scale_vec_len=32)
+    assert lib.gemm_plan_set_scale_major(wide_n.handle, 1) == -2
 
 
 # ---- run-time rejections (fake pointers: never dereferenced) -------------------

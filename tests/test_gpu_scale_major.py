@@ -26,7 +26,8 @@ def _w(name, M, N, K, ka, kb="", beta=0):
 
 
 # every kind combination that takes MN-major scales; M and N multiples of 16
-# with tail tiles of 16 .. 240 rows, K one, two and three 32-block groups
+# with tail tiles of 16 .. 240 rows; K one, two and three 32-block groups
+# (the wide loop) and other multiples of the K step (the per-step loop)
 CASES = {w.name: w for w in [
     _w("e4m3-1040x528-k2048", 1040, 528, 2048, "e4m3"),
     _w("e4m3-256x512-k4096-beta", 256, 512, 4096, "e4m3", beta=1),
@@ -41,6 +42,18 @@ CASES = {w.name: w for w in [
     _w("e2m1-1040x272-k2048", 1040, 272, 2048, "e2m1"),
     _w("e2m1-304x528-k4096-beta", 304, 528, 4096, "e2m1", beta=1),
     _w("e2m1-256x256-k6144", 256, 256, 6144, "e2m1"),
+    # K not a multiple of 2048: the per-step loop (one K step's scales per
+    # copy), single-step K included
+    _w("e4m3-528x272-k640", 528, 272, 640, "e4m3"),
+    _w("e4m3-272x528-k3072-beta", 272, 528, 3072, "e4m3", beta=1),
+    _w("e4m3xe2m1p-304x400-k1152", 304, 400, 1152, "e4m3", "e2m1p"),
+    _w("e4m3xe3m2-256x256-k1024", 256, 256, 1024, "e4m3", "e3m2"),
+    _w("e2m3-272x304-k1408-beta", 272, 304, 1408, "e2m3", beta=1),
+    _w("e3m2-400x272-k128", 400, 272, 128, "e3m2"),
+    _w("e2m1p-256x528-k384", 256, 528, 384, "e2m1p"),
+    _w("e2m1-528x272-k768", 528, 272, 768, "e2m1"),
+    _w("e2m1-304x304-k1280-beta", 304, 304, 1280, "e2m1", beta=1),
+    _w("e2m1-256x256-k256", 256, 256, 256, "e2m1"),
 ]}
 
 
@@ -100,7 +113,8 @@ def test_mn_scales_random_scales_bit_exact(name):
 
 @pytest.mark.parametrize("ka,kb,K", [("e4m3", "e4m3", 2048), ("e4m3", "e4m3", 6144), ("e4m3", "e2m3", 4096),
                                      ("e3m2", "e3m2", 2048), ("e2m1p", "e2m1p", 4096), ("e2m1", "e2m1", 2048),
-                                     ("e2m1", "e2m1", 6144)])
+                                     ("e2m1", "e2m1", 6144), ("e4m3", "e4m3", 1152), ("e4m3", "e2m1p", 640),
+                                     ("e3m2", "e3m2", 384), ("e2m1", "e2m1", 1280)])
 def test_mn_scale_bytes_select_the_right_block(ka, kb, K):
     """Scales only: every element 1.0, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
     exactly; a wrong row, K block or group of the MN-major stage changes it."""
