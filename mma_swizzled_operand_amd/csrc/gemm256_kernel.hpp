@@ -826,9 +826,9 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         // MFMA ahead: that frees the registers the epilogue needs (with two,
         // the compiler spilled inside the loop); the loop alone is 1.4 %
         // slower, the kernel with the staged epilogue 4 % faster (8192^3
-        // MX-fp8).  Without the fallback loops (kWideOnly) the kernels have
-        // the registers for two (8192^3 with MN-major scales: E4M3 -1.7 %,
-        // E4M3 with padded E2M1 -2.2 %, with E2M3 level).
+        // MX-fp8).  With the wide loop alone (kWideOnly) the kernels have the
+        // registers for two (8192^3, row-major scales: E4M3 -1.9 %, E4M3 with
+        // padded E2M1 -3.2 %; MN-major: -1.7 % and -2.2 %, with E2M3 level).
         constexpr int kAhead = kStagedEpi && (KIND == kE4m3 || kKindB == kE4m3) && !kWideOnly ? 1 : 2;
         using Sched = FragSchedule<TM16, TN16, kAhead>;
         uint32_t sa[TM16], sb[TN16];
