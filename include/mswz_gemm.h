@@ -175,7 +175,7 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
  * MN-major scales are taken by the kernels with the 32-byte scale stage:
  * V = 32, K a multiple of the K step (128; 256 for dense E2M1), M and N
  * multiples of 16, K/V * M and K/V * N at most 2^31 (bytes of each scale
- * array), and A / B / D one of: E4M3 / E4M3 / fp32; E4M3 / E2M3,
+ * array), and A / B / D one of: E4M3 / E4M3 / any; E4M3 / E2M3,
  * E3M2 or padded E2M1 / fp32; one of E2M3, E3M2, padded E2M1 or dense E2M1
  * on both sides with any D.  Such a plan runs the 256x256 tile (gemm_plan_describe shows
  * it); setting MSWZ_MAJOR_K again restores the variant chosen at creation.

@@ -95,6 +95,15 @@ bool wide_scale_stage(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
     return a_dt == MSWZ_DT_E4M3 && (b_dt == MSWZ_DT_E4M3 || padded(b_dt)) && d_dt == MSWZ_DT_F32;
 }
 
+// Whether the 256x256 kernels take MN-major scales for these kinds: the
+// wide-stage kinds, and E4M3 on both sides with a bf16 / fp16 D (its
+// one-loop MN-major kernels have the wide stage too).
+bool mn_scales(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
+{
+    return wide_scale_stage(a_dt, b_dt, d_dt, v, K) ||
+           (a_dt == MSWZ_DT_E4M3 && b_dt == MSWZ_DT_E4M3 && v == 32 && K % 128 == 0);
+}
+
 // Choose the tile for an (M, N) output: the largest square tile dividing both
 // sizes, dropping to a smaller one while the grid would leave most compute
 // units idle (fewer than 128 tiles of 256 or 256 tiles of 128).  The
@@ -285,21 +294,21 @@ int gemm_plan_set_scale_major(gemm_plan *p, int sf_major)
         // [K/V][N] arrays below 2^31 bytes (32-bit offsets; the kernels'
         // unused copies point at 2^31, outside every array's range)
         const int64_t kb = p->K / p->scale_vec_len;
-        if (!wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) ||
+        if (!mn_scales(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) ||
             p->M % 16 != 0 || p->N % 16 != 0 || kb * p->M > (int64_t(1) << 31) ||
             kb * p->N > (int64_t(1) << 31))
             return MSWZ_ERR_UNSUPPORTED;
         variant = mswz::kVarMx256;
     }
-    if (variant != p->variant) {
-        p->variant = variant;
-        mswz::variant_info(variant, true, &p->info);
-        if (p->a_dt == MSWZ_DT_E2M1)
-            p->info.tile_k = 256;
-        if (variant == mswz::kVarMx256)
-            p->info.lds_bytes += 2 * 512 * (wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K) ? 32 : 16);
-        p->blocks = ((p->M + p->info.tile_m - 1) / p->info.tile_m) * ((p->N + p->info.tile_n - 1) / p->info.tile_n);
-    }
+    p->variant = variant;
+    mswz::variant_info(variant, true, &p->info);
+    if (p->a_dt == MSWZ_DT_E2M1)
+        p->info.tile_k = 256;
+    if (variant == mswz::kVarMx256)   // MN-major scales always take the 32-byte stages
+        p->info.lds_bytes += 2 * 512 * (sf_major == MSWZ_MAJOR_MN ||
+                                                wide_scale_stage(p->a_dt, p->b_dt, p->d_dt, p->scale_vec_len, p->K)
+                                            ? 32 : 16);
+    p->blocks = ((p->M + p->info.tile_m - 1) / p->info.tile_m) * ((p->N + p->info.tile_n - 1) / p->info.tile_n);
     p->sf_major = sf_major;
     return MSWZ_OK;
 }

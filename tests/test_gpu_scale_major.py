@@ -135,7 +135,9 @@ def test_mn_scale_bytes_select_the_right_block(ka, kb, K):
 
 
 @pytest.mark.parametrize("name,d_dt", [("e2m3-1040x272-k2048", "bf16"), ("e3m2-256x512-k4096-beta", "f16"),
-                                       ("e2m1-304x528-k4096-beta", "bf16"), ("e2m1p-304x528-k2048", "f16")])
+                                       ("e2m1-304x528-k4096-beta", "bf16"), ("e2m1p-304x528-k2048", "f16"),
+                                       ("e4m3-1040x528-k2048", "bf16"), ("e4m3-256x512-k4096-beta", "f16"),
+                                       ("e4m3-272x528-k3072-beta", "bf16"), ("e4m3-528x272-k640", "f16")])
 def test_mn_scales_narrow_d_match_row_major_scales(name, d_dt):
     """bf16 / fp16 D (the fp32 result rounded once; beta reads the old D in
     D's format): the MN-major plan stores the same bits as the row-major one,
