@@ -172,12 +172,11 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
  *             uint8 [K/V][M], SFB [K/V][N], each K block's scales of all rows
  *             consecutive (M, resp. N, bytes per K block).  Values and the
  *             product are the same; only the addresses differ.
- * MN-major scales are taken by the kernels with the 32-byte scale stage:
- * V = 32, K a multiple of the K step (128; 256 for dense E2M1), M and N
- * multiples of 16, K/V * M and K/V * N at most 2^31 (bytes of each scale
- * array), and A / B / D one of: E4M3 / E4M3 / any; E4M3 / E2M3,
- * E3M2 or padded E2M1 / fp32; one of E2M3, E3M2, padded E2M1 or dense E2M1
- * on both sides with any D.  Such a plan runs the 256x256 tile (gemm_plan_describe shows
+ * MN-major scales are taken with V = 32, K a multiple of the K step (128;
+ * 256 for dense E2M1), M and N multiples of 16, K/V * M and K/V * N at most
+ * 2^31 (bytes of each scale array), any D, and A and B each one of E4M3,
+ * E2M3, E3M2 and padded E2M1 (mixed or not), or dense E2M1 on both sides
+ * (not E4M3 with dense E2M1, not 16-element blocks).  Such a plan runs the 256x256 tile (gemm_plan_describe shows
  * it); setting MSWZ_MAJOR_K again restores the variant chosen at creation.
  * The plan is changed in place: not while a call on it is being enqueued.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID (NULL plan, unknown sf_major),

@@ -95,13 +95,19 @@ bool wide_scale_stage(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
     return a_dt == MSWZ_DT_E4M3 && (b_dt == MSWZ_DT_E4M3 || padded(b_dt)) && d_dt == MSWZ_DT_F32;
 }
 
-// Whether the 256x256 kernels take MN-major scales for these kinds: the
-// wide-stage kinds, and E4M3 on both sides with a bf16 / fp16 D (its
-// one-loop MN-major kernels have the wide stage too).
+// Whether the 256x256 kernels take MN-major scales for these kinds (their
+// one-loop MN-major kernels all have the 32-byte stage): 32-element blocks,
+// K a multiple of the K step, dense E2M1 on both sides or any of E4M3, E2M3,
+// E3M2 and padded E2M1 on either side, any D.
 bool mn_scales(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
 {
-    return wide_scale_stage(a_dt, b_dt, d_dt, v, K) ||
-           (a_dt == MSWZ_DT_E4M3 && b_dt == MSWZ_DT_E4M3 && v == 32 && K % 128 == 0);
+    auto byte_row = [](int d) {
+        return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2 || d == MSWZ_DT_E2M1_P64;
+    };
+    (void)d_dt;
+    if (v != 32 || K % (a_dt == MSWZ_DT_E2M1 ? 256 : 128) != 0)
+        return false;
+    return (a_dt == MSWZ_DT_E2M1 && b_dt == MSWZ_DT_E2M1) || (byte_row(a_dt) && byte_row(b_dt));
 }
 
 // Choose the tile for an (M, N) output: the largest square tile dividing both

@@ -391,8 +391,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr int kStepA = kPairA ? 256 : kStepK, kStepB = kPairB ? 256 : kStepK;
 
     // the grouped scale copies (below) with 32-element blocks, for one kind
-    // on both sides (E4M3 with a narrow D only with MN-major scales, whose
-    // kernels have one loop): their stages hold 32 bytes per row (2 x 64 KiB of
+    // on both sides (with MN-major scales, whose kernels have one loop, for
+    // every byte-row kind, mix and D): their stages hold 32 bytes per row (2 x 64 KiB of
     // operand stages + 2 x 16 KiB).  (With two different kinds the wide loop
     // left the kernels short of registers, up to 21 spilled and reloaded
     // every step; an E4M3 A (alone or with a 6-bit or padded 4-bit B) fits
@@ -400,7 +400,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // gemm256_e4m3_f32.hip and gemm256_mixed_e4m3_f32.hip, and keeps the
     // 16-byte groups otherwise.)
     constexpr bool kWideStage =
-        ((kByteRows && (!kMixed || KIND == kE4m3) && (KIND != kE4m3 || OUT == kOutF32 || SM)) || kFp4) && !kV16 && !SB;
+        ((kByteRows && (!kMixed || KIND == kE4m3 || SM) && (KIND != kE4m3 || OUT == kOutF32 || SM)) || kFp4) && !kV16 && !SB;
     static_assert(!SM || kWideStage, "MN-major scales: the wide scale stage");
     // only the 32-K-block loop (K % 2048 == 0, checked by the host): without
     // the fallback loops the kernels keep more registers for the K loop

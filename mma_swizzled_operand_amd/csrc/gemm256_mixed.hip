@@ -10,7 +10,20 @@ namespace {
 template <int KA, int KB>
 hipError_t launch_pair(const MxArgs &a, hipStream_t stream)
 {
+    // MN-major scales: the per-step loop for every K (with the wide loop
+    // alone an fp32 D spilled 28-44 registers; the per-step kernels none)
+    if (a.sf_mn)
+        return launch_out<KA, false, false, KB, 32, false, true, false>(a, stream);
     return launch_cfg<KA, false, false, KB>(a, stream);
+}
+
+// E4M3 A with a bf16 / fp16 D and MN-major scales: the wide loop alone for K
+// a multiple of 2048, else the per-step loop
+template <int KB, int OUT>
+hipError_t launch_e4m3_mn(const MxArgs &a, hipStream_t stream)
+{
+    return a.K % 2048 == 0 ? launch_kind<kE4m3, false, false, OUT, KB, 32, false, true, true>(a, stream)
+                           : launch_kind<kE4m3, false, false, OUT, KB, 32, false, true, false>(a, stream);
 }
 
 // B's kind KB for A's kind KA; one kind on both sides is not a mix (those
@@ -26,8 +39,10 @@ hipError_t launch_if_mixed(const MxArgs &a, hipStream_t stream)
         if (a.K % 128 != 0)
             return launch_out<KA, false, false, KB, 32, true>(a, stream);
         switch (a.out) {
-        case kOutBf16: return launch_kind<KA, false, false, kOutBf16, KB>(a, stream);
-        case kOutF16: return launch_kind<KA, false, false, kOutF16, KB>(a, stream);
+        case kOutBf16:
+            return a.sf_mn ? launch_e4m3_mn<KB, kOutBf16>(a, stream) : launch_kind<KA, false, false, kOutBf16, KB>(a, stream);
+        case kOutF16:
+            return a.sf_mn ? launch_e4m3_mn<KB, kOutF16>(a, stream) : launch_kind<KA, false, false, kOutF16, KB>(a, stream);
         default:
             return launch256_mixed_e4m3_f32(a, KB == kE2m3 ? kMxE2m3 : KB == kE3m2 ? kMxE3m2 : kMxE2m1p, stream);
         }
