@@ -175,8 +175,9 @@ int gemm_plan_create_ld(gemm_plan **out, int64_t M, int64_t N, int64_t K,
  * MN-major scales are taken with V = 32, K a multiple of the K step (128;
  * 256 for dense E2M1), M and N multiples of 16, K/V * M and K/V * N at most
  * 2^31 (bytes of each scale array), any D, and A and B each one of E4M3,
- * E2M3, E3M2 and padded E2M1 (mixed or not), or dense E2M1 on both sides
- * (not E4M3 with dense E2M1, not 16-element blocks).  Such a plan runs the 256x256 tile (gemm_plan_describe shows
+ * E2M3, E3M2 and padded E2M1 (mixed or not), dense E2M1 on both sides, or
+ * E4M3 A with dense E2M1 B (K a multiple of 256); not dense E2M1 A with
+ * E4M3 B, not 16-element blocks.  Such a plan runs the 256x256 tile (gemm_plan_describe shows
  * it); setting MSWZ_MAJOR_K again restores the variant chosen at creation.
  * The plan is changed in place: not while a call on it is being enqueued.
  * Returns MSWZ_OK, MSWZ_ERR_INVALID (NULL plan, unknown sf_major),

@@ -97,17 +97,19 @@ bool wide_scale_stage(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
 
 // Whether the 256x256 kernels take MN-major scales for these kinds (their
 // one-loop MN-major kernels all have the 32-byte stage): 32-element blocks,
-// K a multiple of the K step, dense E2M1 on both sides or any of E4M3, E2M3,
-// E3M2 and padded E2M1 on either side, any D.
+// K a multiple of the K step, dense E2M1 on both sides, any of E4M3, E2M3,
+// E3M2 and padded E2M1 on either side, or E4M3 A with dense E2M1 B (K a
+// multiple of 256), any D.
 bool mn_scales(int a_dt, int b_dt, int d_dt, int32_t v, int64_t K)
 {
     auto byte_row = [](int d) {
         return d == MSWZ_DT_E4M3 || d == MSWZ_DT_E2M3 || d == MSWZ_DT_E3M2 || d == MSWZ_DT_E2M1_P64;
     };
     (void)d_dt;
-    if (v != 32 || K % (a_dt == MSWZ_DT_E2M1 ? 256 : 128) != 0)
+    const bool pair = a_dt == MSWZ_DT_E4M3 && b_dt == MSWZ_DT_E2M1;   // (not E2M1 A with E4M3 B)
+    if (v != 32 || K % (a_dt == MSWZ_DT_E2M1 || pair ? 256 : 128) != 0)
         return false;
-    return (a_dt == MSWZ_DT_E2M1 && b_dt == MSWZ_DT_E2M1) || (byte_row(a_dt) && byte_row(b_dt));
+    return (a_dt == MSWZ_DT_E2M1 && b_dt == MSWZ_DT_E2M1) || (byte_row(a_dt) && byte_row(b_dt)) || pair;
 }
 
 // Choose the tile for an (M, N) output: the largest square tile dividing both

@@ -401,7 +401,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // 16-byte groups otherwise.)
     constexpr bool kWideStage =
         ((kByteRows && (!kMixed || KIND == kE4m3 || SM) && (KIND != kE4m3 || OUT == kOutF32 || SM)) || kFp4) && !kV16 && !SB;
-    static_assert(!SM || kWideStage, "MN-major scales: the wide scale stage");
+    static_assert(!SM || kWideStage || (kPair && !WO), "MN-major scales: the wide scale stage (pairs: per step)");
     // only the 32-K-block loop (K % 2048 == 0, checked by the host): without
     // the fallback loops the kernels keep more registers for the K loop
     constexpr bool kWideOnly = WO;
@@ -412,8 +412,8 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     constexpr bool kMnStep = SM && !WO;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
-    __shared__ __attribute__((aligned(256))) uint8_t scl1[!kMx ? 4 : kWideStage ? kScaleStageWide : kScaleStage];
+    __shared__ __attribute__((aligned(256))) uint8_t scl0[!kMx ? 4 : kWideStage || SM ? kScaleStageWide : kScaleStage];
+    __shared__ __attribute__((aligned(256))) uint8_t scl1[!kMx ? 4 : kWideStage || SM ? kScaleStageWide : kScaleStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -508,7 +508,7 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // offset; the instruction's K blocks through the scalar offset).
     uint32_t sf_voff_w = 0;
     const uint32_t sf_pitch = SM ? uint32_t(wave < 4 ? M : N) : 0u;   // bytes per K block (SM)
-    if constexpr (kWideStage) {
+    if constexpr (kWideStage || SM) {
         static_assert(kSfInstr == 1, "one 64-row scale group per wave");
         static_assert(sf_slot_row(32 + 5) == 32 + sf_slot_row(5), "slot order keeps bit 5");
         const int slot = lane & 31;
@@ -1029,12 +1029,19 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             bb[j] = opaque(bbase16[j]);
         const int r16 = lane & 15, kb = kblk16(lane >> 4);
         const bool grp = sf_stride == 16;
-        const uint32_t sfa = opaque(uint32_t(sf_stride * (wm + (kRowsA && !grp ? row16<true>(0, r16) : r16)) + kb +
-                                             4 * widx));
-        const uint32_t sfb = opaque(uint32_t(sf_stride * (kBM + wn + (kRowsB && !grp ? row16<true>(0, r16) : r16)) +
-                                             kb + 4 * widx));
+        // (MN-major scales, SM: the per-step stage, sf_mn_offset of K block
+        // kb and the lane's tile row on each side, B's half 8 KiB further)
+        const uint32_t sfa = opaque(SM ? sf_mn_offset(uint32_t(kb), uint32_t(wm + row16<kRowsA>(0, r16)))
+                                       : uint32_t(sf_stride * (wm + (kRowsA && !grp ? row16<true>(0, r16) : r16)) + kb +
+                                                  4 * widx));
+        const uint32_t sfb = opaque(SM ? kSfMnB + sf_mn_offset(uint32_t(kb), uint32_t(wn + row16<kRowsB>(0, r16)))
+                                       : uint32_t(sf_stride * (kBM + wn + (kRowsB && !grp ? row16<true>(0, r16) : r16)) +
+                                                  kb + 4 * widx));
         auto sf_off = [&](bool split, int b) {
-            return sf_stride * (split && !grp ? 32 * (b >> 1) + 8 * (b & 1) : 16 * b);
+            if constexpr (SM)
+                return int(split ? sf_mn_offset(0, uint32_t(row16<true>(b, 0))) : sf_mn_offset(0, uint32_t(16 * b)));
+            else
+                return sf_stride * (split && !grp ? 32 * (b >> 1) + 8 * (b & 1) : 16 * b);
         };
         const u32x4 zero = {0, 0, 0, 0};
         auto frag8 = [&](uint32_t base) {
@@ -1115,10 +1122,14 @@ gemm256_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         DmaOperand<W> &d4 = kPairB ? db : da;
         const int NP = KT / 2;
         auto issue_sf = [&](uint8_t *sstage, int kt) {
-            buffer_load_lds4(sf_rsrc[0], sstage + 256 * wave, sf_voff, 4u * uint32_t(kt));
+            if constexpr (SM)   // K blocks 4kt .. 4kt+3 of 256 rows per operand (as issue_step)
+                buffer_load_lds16(sf_rsrc[0], sstage + (wave >> 2) * kSfMnB + 1024 * (wave & 3), sf_voff_step,
+                                  mn_active ? uint32_t(4 * kt) * sf_pitch : 0u);
+            else
+                buffer_load_lds4(sf_rsrc[0], sstage + 256 * wave, sf_voff, 4u * uint32_t(kt));
         };
         static_assert(kSfInstr == 1 && kWords == 1, "one per-step scale word per row, one copy per wave");
-        if (KT % 8 == 0) {
+        if (!SM && KT % 8 == 0) {
             // K a multiple of 1024: scale words copied per group of four
             // steps (16 bytes per row, as for E4M3 alone), into scl0 / scl1
             // alternating every four steps, each as the last copy of the third

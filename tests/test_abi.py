@@ -211,7 +211,7 @@ def test_scale_major_switches_plans_of_the_wide_stage_kernels():
                        ("e4m3", "e3m2", "f32", 128), ("e2m3", "e2m3", "f32", 1152), ("e2m1", "e2m1", "f16", 768),
                        ("e4m3", "e4m3", "bf16", 2048), ("e4m3", "e4m3", "f16", 640), ("e4m3", "e2m3", "f16", 2048),
                        ("e4m3", "e2m1p", "bf16", 1024), ("e2m3", "e4m3", "f32", 2048), ("e2m3", "e3m2", "f32", 384),
-                       ("e2m1p", "e3m2", "bf16", 4096)):
+                       ("e2m1p", "e3m2", "bf16", 4096), ("e4m3", "e2m1", "f32", 2048), ("e4m3", "e2m1", "bf16", 768)):
         p = mswz.gemm_plan_create(4096, 1040, K, a, b, d, scale_vec_len=32)
         before = p.describe()
         mswz.gemm_plan_set_scale_major(p, "mn")
@@ -236,7 +236,7 @@ def test_scale_major_switches_plans_of_the_wide_stage_kernels():
     ((4096, 4096, 2048 + 128, "e2m1", "e2m1", "f32", 32), -2),
     ((4104, 4096, 2048, "e4m3", "e4m3", "f32", 32), -2),      # M not a multiple of 16
     ((4096, 4100, 2048, "e2m1", "e2m1", "f32", 32), -2),      # N not a multiple of 16
-    ((4096, 4096, 2048, "e4m3", "e2m1", "f32", 32), -2),      # E4M3 with dense E2M1
+    ((4096, 4096, 2048, "e2m1", "e4m3", "f32", 32), -2),      # dense E2M1 A with E4M3 B
     ((4096, 4096, 2048, "e2m1", "e2m1", "f32", 16), -2),      # 16-element blocks
     ((4096, 4096, 2048, "e2m3", "e2m3", "f32", 16), -2),
     ((4096, 4096, 2048, "bf16", "bf16", "f32", 0), -5),       # dense plan

@@ -60,6 +60,10 @@ CASES = {w.name: w for w in [
     _w("e3m2xe2m1p-304x400-k1152-beta", 304, 400, 1152, "e3m2", "e2m1p", beta=1),
     _w("e2m1pxe2m3-272x272-k4096", 272, 272, 4096, "e2m1p", "e2m3"),
     _w("e2m3xe3m2-256x528-k640", 256, 528, 640, "e2m3", "e3m2"),
+    # E4M3 A with dense E2M1 B (K a multiple of 256; the per-step loop)
+    _w("e4m3xe2m1-528x272-k2048", 528, 272, 2048, "e4m3", "e2m1"),
+    _w("e4m3xe2m1-304x400-k1280-beta", 304, 400, 1280, "e4m3", "e2m1", beta=1),
+    _w("e4m3xe2m1-256x256-k256", 256, 256, 256, "e4m3", "e2m1"),
 ]}
 
 
@@ -121,7 +125,7 @@ def test_mn_scales_random_scales_bit_exact(name):
                                      ("e3m2", "e3m2", 2048), ("e2m1p", "e2m1p", 4096), ("e2m1", "e2m1", 2048),
                                      ("e2m1", "e2m1", 6144), ("e4m3", "e4m3", 1152), ("e4m3", "e2m1p", 640),
                                      ("e3m2", "e3m2", 384), ("e2m1", "e2m1", 1280), ("e2m3", "e4m3", 2048),
-                                     ("e3m2", "e2m1p", 1152)])
+                                     ("e3m2", "e2m1p", 1152), ("e4m3", "e2m1", 1024)])
 def test_mn_scale_bytes_select_the_right_block(ka, kb, K):
     """Scales only: every element 1.0, so D[m,n] = 32 sum_j 2^(uA[m,j]+uB[n,j])
     exactly; a wrong row, K block or group of the MN-major stage changes it."""
@@ -146,7 +150,8 @@ def test_mn_scale_bytes_select_the_right_block(ka, kb, K):
                                        ("e4m3-1040x528-k2048", "bf16"), ("e4m3-256x512-k4096-beta", "f16"),
                                        ("e4m3-272x528-k3072-beta", "bf16"), ("e4m3-528x272-k640", "f16"),
                                        ("e4m3xe2m3-528x1040-k2048-beta", "bf16"), ("e4m3xe2m1p-304x400-k1152", "f16"),
-                                       ("e2m3xe4m3-528x272-k2048", "bf16"), ("e3m2xe2m1p-304x400-k1152-beta", "f16")])
+                                       ("e2m3xe4m3-528x272-k2048", "bf16"), ("e3m2xe2m1p-304x400-k1152-beta", "f16"),
+                                       ("e4m3xe2m1-304x400-k1280-beta", "bf16")])
 def test_mn_scales_narrow_d_match_row_major_scales(name, d_dt):
     """bf16 / fp16 D (the fp32 result rounded once; beta reads the old D in
     D's format): the MN-major plan stores the same bits as the row-major one,
